@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Throughput of the TurboQuant-style KV-cache hot path on one MI355X.
+
+Default workload (GQA decode, Llama-8B-like shape): batch 16, 32 query heads,
+8 KV heads, head_dim 128, context 8192; keys 4-bit Lloyd-Max with fp32
+corrected norm, values 4-bit uniform with fp32 min/scale.  One step = quantize
+and append the new token of every sequence (K and V, 16 x 8 token-heads) into
+the paged cache, then decode attention of the 16 new queries over their 8192
+cached tokens.  Steps rotate over --layers independent caches (one per layer)
+so the 147 MB working set does not stay in the 256 MB Infinity Cache.
+
+`--workload prefill_append`: quantize-append of 131072 tokens x 8 KV heads into
+16-token pages followed by decode at batch 1 over the 131072-token context.
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.  `value` is packed-KV
+GB/s: algorithmic bytes of the step (bf16 inputs read, packed rows written,
+packed rows of the attended context read, queries, outputs, tables) divided by
+the step time, with every input already resident in HBM.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+TOKEN_HEAD_BYTES = {"gqa_decode": 140, "prefill_append": 140}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def counter_traffic(kernel_key: str, source: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    rec = data.get(kernel_key)
+    if not rec:
+        return None
+    digest = hashlib.sha256(open(os.path.join(ROOT, "kv_cache_vector_randomized_amd", "csrc", source), "rb").read()).hexdigest()
+    return rec.get("bytes_per_launch") if rec.get("source_sha256") == digest else None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=4, help="independent layer caches rotated over the steps")
+    ap.add_argument("--workload", default="gqa_decode", choices=["gqa_decode", "prefill_append"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from kv_cache_vector_randomized_amd import synth, tq
+    from kv_cache_vector_randomized_amd.torch_api import PagedKVCache, bf16_from_bits
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.init()
+    w = synth.WORKLOADS[args.workload]
+    B, T, Hkv, Hq, d = w.batch, w.context, w.num_kv_heads, w.num_q_heads, w.head_dim
+    cfg = tq.make_config(d, Hkv, Hq, w.key_bits, w.key_mode, w.val_bits, w.val_mode)
+    ctx = tq.Context(cfg, synth.sign_vector(w.seed))
+    lay = synth.paged_layout(B, [T] * B, w.seed)
+    scale = 1.0 / math.sqrt(d)
+    log(f"[bench] workload={w.name} B={B} T={T} Hkv={Hkv} Hq={Hq} page_bytes={ctx.page_bytes}")
+
+    t0 = time.time()
+    k_all = synth.kv_tensor(w, B * T, "k")
+    v_all = synth.kv_tensor(w, B * T, "v")
+    q_np = synth.query_tensor(w)
+    log(f"[bench] generated inputs in {time.time() - t0:.1f}s")
+    k_dev = bf16_from_bits(k_all)
+    v_dev = bf16_from_bits(v_all)
+    q_dev = bf16_from_bits(q_np)
+    slots_all = torch.from_numpy(np.concatenate([lay.slots(b, 0, T) for b in range(B)])).cuda()
+    tables = torch.from_numpy(lay.block_tables).cuda()
+    seq_lens = torch.from_numpy(lay.seq_lens).cuda()
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    last = torch.tensor([b * T + T - 1 for b in range(B)], device="cuda")
+    k_new = k_dev[last].contiguous()
+    v_new = v_dev[last].contiguous()
+    slots_new = slots_all[last].contiguous()
+
+    th = ctx.layout.token_head_bytes
+    n_layers = max(1, args.layers)
+    caches = [PagedKVCache(ctx, lay.num_blocks) for _ in range(n_layers)]
+    stream = torch.cuda.current_stream()
+
+    if args.workload == "gqa_decode":
+        for c in caches:                               # prefill every layer (not timed)
+            c.append(k_dev, v_dev, slots_all)
+        torch.cuda.synchronize()
+        del k_dev, v_dev
+        append_bytes = B * Hkv * (2 * d * 2 + th) + B * 8
+        decode_bytes = B * Hkv * T * th + B * Hq * d * 2 + B * Hq * d * 4 + lay.block_tables.nbytes + B * 4
+        step_bytes = append_bytes + decode_bytes
+        dominant, dom_bytes, dom_source = "decode_kernel", decode_bytes, "tq_decode.hip"
+
+        def step(i, ev=None):
+            c = caches[i % n_layers]
+            c.append(k_new, v_new, slots_new)
+            if ev is not None:
+                ev[0].record(stream)
+            c.decode(q_dev, tables, seq_lens, T, scale, out=out)
+            if ev is not None:
+                ev[1].record(stream)
+    else:
+        append_bytes = B * T * Hkv * (2 * d * 2 + th) + B * T * 8
+        decode_bytes = B * Hkv * T * th + B * Hq * d * 2 + B * Hq * d * 4 + lay.block_tables.nbytes + B * 4
+        step_bytes = append_bytes + decode_bytes
+        dominant, dom_bytes, dom_source = "append (keys + values kernels)", append_bytes, "tq_append.hip"
+
+        def step(i, ev=None):
+            c = caches[i % n_layers]
+            if ev is not None:
+                ev[0].record(stream)
+            c.append(k_dev, v_dev, slots_all)
+            if ev is not None:
+                ev[1].record(stream)
+            c.decode(q_dev, tables, seq_lens, T, scale, out=out)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    dom_ms = [a.elapsed_time(b) for a, b in evs]
+    dom_avg = statistics.mean(dom_ms)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = dom_bytes / (dom_avg * 1e-3) / 1e9
+    log(f"[bench] step {ms_step * 1e3:.1f} us; {dominant} avg {dom_avg * 1e3:.1f} us "
+        f"(p10 {np.percentile(dom_ms, 10) * 1e3:.1f}, p90 {np.percentile(dom_ms, 90) * 1e3:.1f}); "
+        f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of HBM peak")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, k_all, v_all, q_np, lay, np)
+
+    rec = {
+        "metric": "packed-KV GB/s (% HBM peak) for quantize-append and decode attention",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; bf16 N(0,1) K/V with outlier channels, N(0,1) queries)",
+        "config": {
+            "workload": w.name, "batch": B, "context": T, "num_q_heads": Hq, "num_kv_heads": Hkv,
+            "head_dim": d, "key_bits": w.key_bits, "key_mode": w.key_mode, "val_bits": w.val_bits,
+            "val_mode": w.val_mode, "block_tokens": 16, "layer_caches": n_layers,
+            "step": ("append 1 token/seq + decode" if w.name == "gqa_decode" else "append all tokens + decode"),
+            "step_bytes": step_bytes,
+        },
+        "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
+        "tokens_per_s": {"decode_queries": round(B / (ms_step * 1e-3), 1),
+                         "context_token_heads": round(B * T * Hkv / (ms_step * 1e-3), 1)},
+        "roofline": {
+            "kernel": dominant,
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": counter_traffic(w.name + ":" + dominant, dom_source),
+            "algorithmic_bytes_per_launch": dom_bytes,
+            "avg_launch_us": round(dom_avg * 1e3, 2),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(w, k_all, v_all, q_np, lay, np):
+    """The fp64 oracle (untuned) on a bounded sample of the same step: one sequence's
+    new-token quantize-append plus its decode attention over the whole context."""
+    from oracle import tq_oracle as O
+    from kv_cache_vector_randomized_amd import synth
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    T, Hkv, Hq, d = w.context, w.num_kv_heads, w.num_q_heads, w.head_dim
+    cfg = O.Config(d, Hkv, Hq, w.key_bits, w.key_mode, w.val_bits, w.val_mode)
+    signs = synth.sign_vector(w.seed)
+    kcb = O.codebook(w.key_bits, d)
+    f64 = lambda x: synth.bf16_bits_to_f32(x).astype(np.float64)
+    b = 0
+    slots = lay.slots(b, 0, T)
+    cache = O.new_cache(cfg, lay.num_blocks)
+    t0 = time.time()
+    O.quantize_append(cfg, cache, f64(k_all[: T - 1]), f64(v_all[: T - 1]), slots[: T - 1], signs, kcb)
+    log(f"[cpu] oracle prefill of the sample sequence took {time.time() - t0:.1f}s (not timed)")
+    times = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        O.quantize_append(cfg, cache, f64(k_all[T - 1:T]), f64(v_all[T - 1:T]), slots[T - 1:T], signs, kcb)
+        O.decode_attention(cfg, f64(q_np[b:b + 1]), cache, lay.block_tables[b:b + 1], lay.seq_lens[b:b + 1],
+                           1.0 / math.sqrt(d), signs, kcb)
+        times.append(time.perf_counter() - t0)
+    sec = statistics.median(times)
+    th = O.page_bytes(cfg) // 16
+    sample_bytes = Hkv * (2 * d * 2 + th) + 8 + Hkv * T * th + Hq * d * 2 + Hq * d * 4 + lay.block_tables.shape[1] * 4 + 4
+    log(f"[cpu] oracle sample step {sec:.2f}s -> {sample_bytes / sec / 1e9:.4f} GB/s")
+    return {"value": round(sample_bytes / sec / 1e9, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"one sequence of the step (append 1 token x {Hkv} kv heads, decode {Hq} q heads over {T} "
+                      f"tokens), median of 5 runs, {sec:.2f} s each"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,134 @@
+// Device helpers shared by the HIP kernel files (rows, bit streams, the
+// Hadamard butterfly, the code look-up grid).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr float kInvSqrtDim = 0.08838834764831845f;   // 1/sqrt(128)
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// One row of 128 activations (bf16 or fp32) into fp32 registers.
+template <bool BF16>
+__device__ __forceinline__ void load_row(const void* base, int64_t row, float (&x)[kDim]) {
+  if (BF16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + row * kDim);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint4 w = p[j];
+      x[8 * j + 0] = bf16lo(w.x); x[8 * j + 1] = bf16hi(w.x);
+      x[8 * j + 2] = bf16lo(w.y); x[8 * j + 3] = bf16hi(w.y);
+      x[8 * j + 4] = bf16lo(w.z); x[8 * j + 5] = bf16hi(w.z);
+      x[8 * j + 6] = bf16lo(w.w); x[8 * j + 7] = bf16hi(w.w);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + row * kDim);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float4 w = p[j];
+      x[4 * j + 0] = w.x; x[4 * j + 1] = w.y; x[4 * j + 2] = w.z; x[4 * j + 3] = w.w;
+    }
+  }
+}
+
+// In-place Sylvester (natural order) Walsh-Hadamard transform, unnormalized.
+__device__ __forceinline__ void wht128(float (&x)[kDim]) {
+#pragma unroll
+  for (int len = 1; len < kDim; len <<= 1) {
+#pragma unroll
+    for (int i = 0; i < kDim; i += 2 * len) {
+#pragma unroll
+      for (int j = i; j < i + len; ++j) {
+        const float a = x[j], b = x[j + len];
+        x[j] = a + b;
+        x[j + len] = a - b;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ float sum_squares(const float (&x)[kDim]) {
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+#pragma unroll
+  for (int i = 0; i < kDim; i += 4) {
+    s0 = fmaf(x[i], x[i], s0);
+    s1 = fmaf(x[i + 1], x[i + 1], s1);
+    s2 = fmaf(x[i + 2], x[i + 2], s2);
+    s3 = fmaf(x[i + 3], x[i + 3], s3);
+  }
+  return (s0 + s1) + (s2 + s3);
+}
+
+// code = #{j : t_j <= y} through the look-up grid; also returns C[code].
+__device__ __forceinline__ int lut_code(const QLut* lut, float y, float sc, float bi, float& c) {
+  const float f = fminf(fmaxf(fmaf(y, sc, bi), 0.f), (float)(kLutCells - 1));
+  const QLut e = lut[(int)f];
+  const bool up = y >= e.t;
+  c = up ? e.c_hi : e.c_lo;
+  return e.base + (up ? 1 : 0);
+}
+
+// Put code i (B bits) into an LSB-first bit stream held in 32-bit words.
+template <int B>
+__device__ __forceinline__ void put_code(uint32_t (&w)[B * 4], int i, uint32_t code) {
+  const int bit = B * i, wi = bit >> 5, sh = bit & 31;
+  w[wi] |= code << sh;
+  if (sh + B > 32) w[wi + 1] |= code >> (32 - sh);
+}
+
+template <int B>
+__device__ __forceinline__ uint32_t get_code(const uint32_t* w, int i) {
+  const int bit = B * i, wi = bit >> 5, sh = bit & 31;
+  uint32_t v = w[wi] >> sh;
+  if (sh + B > 32) v |= w[wi + 1] << (32 - sh);
+  return v & ((1u << B) - 1u);
+}
+
+template <int B>
+__device__ __forceinline__ void store_words(uint8_t* dst, const uint32_t (&w)[B * 4]) {
+  uint4* d = reinterpret_cast<uint4*>(dst);
+#pragma unroll
+  for (int j = 0; j < B; ++j) d[j] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+}
+
+__device__ __forceinline__ void apply_signs(float (&x)[kDim], const uint32_t (&sb)[4]) {
+#pragma unroll
+  for (int i = 0; i < kDim; ++i)
+    x[i] = __uint_as_float(__float_as_uint(x[i]) ^ (((sb[i >> 5] >> (i & 31)) & 1u) << 31));
+}
+
+// Stage 1 on a vector already in registers: signs, norm, rotation, codes.
+// On return x[i] holds the rotated, unnormalized coordinate H(s*x)_i and c[i]
+// is not kept; returns the fp32 norm and fills the packed words and sum C^2.
+template <int B, bool KEEP_C>
+__device__ __forceinline__ float lloyd_codes(float (&x)[kDim], const uint32_t (&sb)[4], const QLut* lut,
+                                             float lsc, float lbi, uint32_t (&w)[B * 4], float& cn2,
+                                             float* cvals) {
+  apply_signs(x, sb);
+  const float n = sqrtf(sum_squares(x));
+  wht128(x);
+  const float inv = n > 0.f ? 1.f / (n * 11.313708498984761f) : 0.f;
+#pragma unroll
+  for (int j = 0; j < B * 4; ++j) w[j] = 0u;
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < kDim; ++i) {
+    float c;
+    const int code = lut_code(lut, x[i] * inv, lsc, lbi, c);
+    put_code<B>(w, i, (uint32_t)code);
+    if (i & 1) a1 = fmaf(c, c, a1); else a0 = fmaf(c, c, a0);
+    if (KEEP_C) cvals[i] = c;
+  }
+  cn2 = a0 + a1;
+  return n;
+}
+
+}  // namespace tq

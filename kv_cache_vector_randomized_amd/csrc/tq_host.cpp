@@ -1,0 +1,392 @@
+// Host runtime of the C ABI: argument checking, the fp32 Lloyd-Max codebook,
+// the page layout, context set-up and launch planning.  All device work is in
+// tq_kernels.hip.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "tq_internal.h"
+
+struct tq_ctx {
+  tq_config cfg;
+  tq_layout layout;
+  int device;
+  uint32_t sign_bits[4];
+  tq::DevConsts* consts;   // device
+  float klut_scale, klut_bias, vlut_scale, vlut_bias;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+tq_status fail(tq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+tq_status hip_fail(hipError_t e, const char* what) {
+  return fail(TQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool is_pow2(uint32_t x) { return x && !(x & (x - 1)); }
+
+// ---------------------------------------------------------------------------
+// Lloyd-Max for a Gaussian coordinate (issoh.co.jp page, stage-1 section:
+// per-coordinate Lloyd-Max, representatives placed for the value distribution).
+// A rotated unit vector's coordinate is modelled as N(0, 1/d).  Solved for the
+// standard normal in long double by alternating the two optimality conditions
+// (midpoint thresholds, conditional-mean centroids) from a uniform start.
+// ---------------------------------------------------------------------------
+long double npdf(long double x) { return std::exp(-0.5L * x * x) * 0.39894228040143267793994605993438L; }
+long double ntail(long double x) {  // P(Z > x)
+  if (std::isinf(x)) return x > 0 ? 0.0L : 1.0L;
+  return 0.5L * std::erfc(x * 0.70710678118654752440084436210485L);
+}
+
+void lloyd_max_std(int bits, std::vector<double>& centroids, std::vector<double>& thresholds) {
+  const int levels = 1 << bits, half = levels / 2;
+  std::vector<long double> c(half);       // positive centroids, ascending
+  for (int i = 0; i < half; ++i) c[i] = (i + 0.5L) * 3.0L / half;
+  std::vector<long double> t(half + 1);
+  for (int it = 0; it < 200000; ++it) {
+    t[0] = 0.0L;
+    t[half] = std::numeric_limits<long double>::infinity();
+    for (int i = 1; i < half; ++i) t[i] = 0.5L * (c[i - 1] + c[i]);
+    long double moved = 0.0L;
+    for (int i = 0; i < half; ++i) {
+      long double mass = ntail(t[i]) - ntail(t[i + 1]);
+      long double num = npdf(t[i]) - (std::isinf(t[i + 1]) ? 0.0L : npdf(t[i + 1]));
+      long double nc = num / mass;
+      moved = std::fmax(moved, std::fabs(nc - c[i]));
+      c[i] = nc;
+    }
+    if (moved < 1e-17L) break;
+  }
+  centroids.assign(levels, 0.0);
+  thresholds.assign(levels - 1, 0.0);
+  for (int i = 0; i < half; ++i) {
+    centroids[half + i] = (double)c[i];
+    centroids[half - 1 - i] = -(double)c[i];
+  }
+  for (int i = 1; i < half; ++i) {
+    double m = (double)(0.5L * (c[i - 1] + c[i]));
+    thresholds[half - 1 + i] = m;
+    thresholds[half - 1 - i] = -m;
+  }
+  thresholds[half - 1] = 0.0;
+}
+
+void codebook_f32(int bits, int d, float* c, float* t) {
+  std::vector<double> cd, td;
+  lloyd_max_std(bits, cd, td);
+  const double s = 1.0 / std::sqrt((double)d);
+  for (int i = 0; i < (1 << bits); ++i) c[i] = (float)(cd[i] * s);
+  for (int i = 0; i < (1 << bits) - 1; ++i) t[i] = (float)(td[i] * s);
+}
+
+// Uniform grid over [-range, range) that resolves every fp32 threshold with one
+// comparison.  range is a power of two so that y * scale is exact.
+bool build_lut(int bits, const float* c, const float* t, tq::QLut* lut, float* scale, float* bias) {
+  const int nt = (1 << bits) - 1;
+  double tmax = 0;
+  for (int i = 0; i < nt; ++i) tmax = std::fmax(tmax, std::fabs((double)t[i]));
+  double range = 1.0 / 64;
+  while (range < 1.1 * tmax) range *= 2;
+  const int cells = tq::kLutCells;
+  const double w = 2 * range / cells;
+  for (int k = 0; k < cells; ++k) {
+    double lo = (k == 0) ? -INFINITY : -range + k * w - 0.25 * w;
+    double hi = (k == cells - 1) ? INFINITY : -range + (k + 1) * w + 0.25 * w;
+    int base = 0, inside = 0;
+    float tin = INFINITY;
+    for (int j = 0; j < nt; ++j) {
+      if ((double)t[j] < lo) ++base;
+      else if ((double)t[j] <= hi) { ++inside; tin = t[j]; }
+    }
+    if (inside > 1) return false;
+    lut[k].base = base;
+    lut[k].t = tin;
+    lut[k].c_lo = c[base];
+    lut[k].c_hi = c[base + 1 <= nt ? base + 1 : nt];
+  }
+  *scale = (float)((cells / 2) / range);
+  *bias = (float)(cells / 2);
+  return true;
+}
+
+tq_status layout_of(const tq_config* c, tq_layout* L) {
+  const size_t T = TQ_BLOCK_TOKENS, d = c->head_dim;
+  std::memset(L, 0, sizeof *L);
+  L->format_version = TQ_FORMAT_VERSION;
+  const size_t none = (size_t)-1;
+  size_t off = 0;
+  L->off_kcodes = off; L->row_kcodes = d * c->key_bits / 8; off += T * L->row_kcodes;
+  L->off_knorm = off; off += T * 4;
+  if (c->key_mode == TQ_KEY_LLOYD_QJL) {
+    L->off_ksigns = off; L->row_ksigns = d / 8; off += T * L->row_ksigns;
+    L->off_kresid = off; off += T * 4;
+  } else {
+    L->off_ksigns = none; L->row_ksigns = 0; L->off_kresid = none;
+  }
+  L->off_vcodes = off; L->row_vcodes = d * c->val_bits / 8; off += T * L->row_vcodes;
+  L->off_vmin = off; off += T * 4;
+  if (c->val_mode == TQ_VAL_UNIFORM) { L->off_vscale = off; off += T * 4; } else L->off_vscale = none;
+  L->page_bytes = off;
+  L->token_head_bytes = off / T;
+  return TQ_OK;
+}
+
+tq::FieldOffsets offsets_of(const tq_layout& L) {
+  tq::FieldOffsets f;
+  f.page_bytes = (uint32_t)L.page_bytes;
+  f.kcodes = (uint32_t)L.off_kcodes;
+  f.knorm = (uint32_t)L.off_knorm;
+  f.ksigns = L.off_ksigns == (size_t)-1 ? 0u : (uint32_t)L.off_ksigns;
+  f.kres = L.off_kresid == (size_t)-1 ? 0u : (uint32_t)L.off_kresid;
+  f.vcodes = (uint32_t)L.off_vcodes;
+  f.vmin = (uint32_t)L.off_vmin;
+  f.vscale = L.off_vscale == (size_t)-1 ? 0u : (uint32_t)L.off_vscale;
+  return f;
+}
+
+// Split the context of every (sequence, kv head) into pieces of whole 64-token
+// tiles so that the grid has about 1024 work-groups (4 per CU on 256 CUs).
+void plan_splits(int batch, int hkv, int max_seq, int* splits, int* tiles_per_split) {
+  const int tiles = std::max(1, (max_seq + 63) / 64);
+  const int pairs = std::max(1, batch * hkv);
+  int want = (1024 + pairs - 1) / pairs;
+  want = std::max(1, std::min(want, (tiles + 3) / 4));      // >= 4 tiles per split
+  int tps = (tiles + want - 1) / want;
+  *tiles_per_split = tps;
+  *splits = (tiles + tps - 1) / tps;
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) == hipSuccess && prev != dev) hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) hipSetDevice(prev);
+  }
+};
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int tq_abi_version(void) { return TQ_ABI_VERSION; }
+
+const char* tq_status_string(tq_status s) {
+  switch (s) {
+    case TQ_OK: return "TQ_OK";
+    case TQ_ERR_INVALID_ARG: return "TQ_ERR_INVALID_ARG";
+    case TQ_ERR_UNSUPPORTED: return "TQ_ERR_UNSUPPORTED";
+    case TQ_ERR_WORKSPACE_TOO_SMALL: return "TQ_ERR_WORKSPACE_TOO_SMALL";
+    case TQ_ERR_HIP: return "TQ_ERR_HIP";
+    case TQ_ERR_OUT_OF_MEMORY: return "TQ_ERR_OUT_OF_MEMORY";
+  }
+  return "TQ_ERR_UNKNOWN";
+}
+
+const char* tq_last_error_message(void) { return g_err.c_str(); }
+
+tq_status tq_validate_config(const tq_config* c) {
+  if (!c) return fail(TQ_ERR_INVALID_ARG, "cfg is null");
+  if (c->abi_version != TQ_ABI_VERSION) return fail(TQ_ERR_INVALID_ARG, "abi_version %u != %d", c->abi_version, TQ_ABI_VERSION);
+  if (c->block_tokens != TQ_BLOCK_TOKENS) return fail(TQ_ERR_INVALID_ARG, "block_tokens must be %d", TQ_BLOCK_TOKENS);
+  if (!is_pow2(c->head_dim) || c->head_dim < 8 || c->head_dim > 1024)
+    return fail(TQ_ERR_INVALID_ARG, "head_dim %u is not a power of two in [8, 1024]", c->head_dim);
+  if (c->num_kv_heads == 0 || c->num_q_heads == 0 || c->num_q_heads % c->num_kv_heads)
+    return fail(TQ_ERR_INVALID_ARG, "num_q_heads (%u) must be a positive multiple of num_kv_heads (%u)",
+                c->num_q_heads, c->num_kv_heads);
+  if (c->key_mode > TQ_KEY_LLOYD_QJL) return fail(TQ_ERR_INVALID_ARG, "bad key_mode %u", c->key_mode);
+  if (c->val_mode > TQ_VAL_LLOYD) return fail(TQ_ERR_INVALID_ARG, "bad val_mode %u", c->val_mode);
+  if (c->key_bits < 1 || c->key_bits > 8) return fail(TQ_ERR_INVALID_ARG, "key_bits %u out of [1, 8]", c->key_bits);
+  if (c->val_bits < 1 || c->val_bits > 8) return fail(TQ_ERR_INVALID_ARG, "val_bits %u out of [1, 8]", c->val_bits);
+  if (c->head_dim != (uint32_t)tq::kDim) return fail(TQ_ERR_UNSUPPORTED, "head_dim %u: kernels are built for 128", c->head_dim);
+  if (c->key_bits < 2 || c->key_bits > 4) return fail(TQ_ERR_UNSUPPORTED, "key_bits %u: supported 2..4", c->key_bits);
+  if (c->val_bits < 2 || c->val_bits > 4) return fail(TQ_ERR_UNSUPPORTED, "val_bits %u: supported 2..4", c->val_bits);
+  const uint32_t g = c->num_q_heads / c->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4) return fail(TQ_ERR_UNSUPPORTED, "group size %u: supported 1, 2, 4", g);
+  if (c->num_kv_heads > 65535) return fail(TQ_ERR_UNSUPPORTED, "num_kv_heads too large");
+  return TQ_OK;
+}
+
+tq_status tq_layout_for_config(const tq_config* cfg, tq_layout* out) {
+  tq_status s = tq_validate_config(cfg);
+  if (s != TQ_OK) return s;
+  if (!out) return fail(TQ_ERR_INVALID_ARG, "out is null");
+  return layout_of(cfg, out);
+}
+
+tq_status tq_codebook(uint32_t bits, uint32_t head_dim, float* centroids, float* thresholds) {
+  if (bits < 1 || bits > 8 || !is_pow2(head_dim) || !centroids || !thresholds)
+    return fail(TQ_ERR_INVALID_ARG, "bad codebook request (bits %u, head_dim %u)", bits, head_dim);
+  codebook_f32((int)bits, (int)head_dim, centroids, thresholds);
+  return TQ_OK;
+}
+
+tq_status tq_create(const tq_config* cfg, const int8_t* signs_host, const float* S_host, tq_ctx** out) {
+  if (!out) return fail(TQ_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  tq_status s = tq_validate_config(cfg);
+  if (s != TQ_OK) return s;
+  if (!signs_host) return fail(TQ_ERR_INVALID_ARG, "signs_host is null");
+  const int d = (int)cfg->head_dim;
+  for (int i = 0; i < d; ++i)
+    if (signs_host[i] != 1 && signs_host[i] != -1) return fail(TQ_ERR_INVALID_ARG, "signs_host[%d] = %d is not +-1", i, signs_host[i]);
+  if (cfg->key_mode == TQ_KEY_LLOYD_QJL && !S_host) return fail(TQ_ERR_INVALID_ARG, "QJL keys need qjl_S_host");
+
+  tq::DevConsts* h = new (std::nothrow) tq::DevConsts();
+  if (!h) return fail(TQ_ERR_OUT_OF_MEMORY, "host allocation failed");
+  std::memset(h, 0, sizeof *h);
+  for (int i = 0; i < d; ++i) h->signs[i] = (float)signs_host[i];
+  float kt[15] = {0}, vt[15] = {0};
+  codebook_f32((int)cfg->key_bits, d, h->kc, kt);
+  tq_ctx* ctx = new (std::nothrow) tq_ctx();
+  if (!ctx) { delete h; return fail(TQ_ERR_OUT_OF_MEMORY, "host allocation failed"); }
+  ctx->cfg = *cfg;
+  layout_of(cfg, &ctx->layout);
+  bool ok = build_lut((int)cfg->key_bits, h->kc, kt, h->klut, &ctx->klut_scale, &ctx->klut_bias);
+  if (cfg->val_mode == TQ_VAL_LLOYD) {
+    codebook_f32((int)cfg->val_bits, d, h->vc, vt);
+    ok = ok && build_lut((int)cfg->val_bits, h->vc, vt, h->vlut, &ctx->vlut_scale, &ctx->vlut_bias);
+  }
+  if (!ok) { delete h; delete ctx; return fail(TQ_ERR_UNSUPPORTED, "codebook thresholds too dense for the look-up grid"); }
+  if (cfg->key_mode == TQ_KEY_LLOYD_QJL)
+    for (int m = 0; m < d; ++m)
+      for (int k = 0; k < d; ++k) h->St[k * d + m] = S_host[m * d + k];
+  for (int i = 0; i < 4; ++i) ctx->sign_bits[i] = 0;
+  for (int i = 0; i < d; ++i)
+    if (signs_host[i] < 0) ctx->sign_bits[i >> 5] |= 1u << (i & 31);
+
+  hipError_t e = hipGetDevice(&ctx->device);
+  if (e != hipSuccess) { delete h; delete ctx; return hip_fail(e, "hipGetDevice"); }
+  e = hipMalloc((void**)&ctx->consts, sizeof(tq::DevConsts));
+  if (e != hipSuccess) { delete h; delete ctx; return e == hipErrorOutOfMemory ? fail(TQ_ERR_OUT_OF_MEMORY, "hipMalloc") : hip_fail(e, "hipMalloc"); }
+  e = hipMemcpy(ctx->consts, h, sizeof(tq::DevConsts), hipMemcpyHostToDevice);
+  delete h;
+  if (e != hipSuccess) { hipFree(ctx->consts); delete ctx; return hip_fail(e, "hipMemcpy"); }
+  *out = ctx;
+  return TQ_OK;
+}
+
+void tq_destroy(tq_ctx* ctx) {
+  if (!ctx) return;
+  DeviceGuard g(ctx->device);
+  hipFree(ctx->consts);
+  delete ctx;
+}
+
+tq_status tq_layout_query(const tq_ctx* ctx, tq_layout* out) {
+  if (!ctx || !out) return fail(TQ_ERR_INVALID_ARG, "null argument");
+  *out = ctx->layout;
+  return TQ_OK;
+}
+
+tq_status tq_quantize_append(tq_ctx* ctx, const void* k, const void* v, tq_dtype dt, int64_t num_tokens,
+                             const int64_t* slot_mapping, void* cache, int64_t num_blocks, hipStream_t stream) {
+  if (!ctx) return fail(TQ_ERR_INVALID_ARG, "ctx is null");
+  if (dt != TQ_F32 && dt != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad dtype %d", (int)dt);
+  if (num_tokens < 0 || num_blocks < 0) return fail(TQ_ERR_INVALID_ARG, "negative size");
+  if (num_tokens == 0) return TQ_OK;
+  if (!k || !v || !slot_mapping || !cache) return fail(TQ_ERR_INVALID_ARG, "null device pointer");
+  if (!aligned(cache, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(slot_mapping, 8))
+    return fail(TQ_ERR_INVALID_ARG, "k, v and cache must be 16-byte aligned");
+  if (num_tokens * (int64_t)ctx->cfg.num_kv_heads > ((int64_t)1 << 38))
+    return fail(TQ_ERR_UNSUPPORTED, "num_tokens * num_kv_heads too large for one launch");
+  DeviceGuard g(ctx->device);
+  tq::AppendArgs a;
+  a.k = k; a.v = v; a.num_tokens = num_tokens; a.hkv = (int32_t)ctx->cfg.num_kv_heads;
+  for (int i = 0; i < 4; ++i) a.sign_bits[i] = ctx->sign_bits[i];
+  a.key_nc = ctx->cfg.key_mode == TQ_KEY_LLOYD_NC;
+  a.slots = slot_mapping; a.cache = (uint8_t*)cache; a.num_blocks = num_blocks;
+  a.f = offsets_of(ctx->layout); a.c = ctx->consts;
+  a.klut_scale = ctx->klut_scale; a.klut_bias = ctx->klut_bias;
+  a.vlut_scale = ctx->vlut_scale; a.vlut_bias = ctx->vlut_bias;
+  hipError_t e = tq::launch_append(a, (int)dt, (int)ctx->cfg.key_bits, (int)ctx->cfg.key_mode,
+                                   (int)ctx->cfg.val_bits, (int)ctx->cfg.val_mode, stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "append launch");
+}
+
+size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t max_seq_len) {
+  if (!ctx || batch <= 0 || max_seq_len < 0) return 0;
+  int splits, tps;
+  plan_splits(batch, (int)ctx->cfg.num_kv_heads, max_seq_len, &splits, &tps);
+  return tq::kCounterBytes +
+         (size_t)batch * ctx->cfg.num_kv_heads * splits * tq::kMaxGroup * (2 + tq::kDim) * sizeof(float);
+}
+
+tq_status tq_decode_attention(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cache, int64_t num_blocks,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                              int32_t batch, int32_t max_seq_len, float softmax_scale, float* out,
+                              float* logits_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!ctx) return fail(TQ_ERR_INVALID_ARG, "ctx is null");
+  if (dt != TQ_F32 && dt != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad dtype %d", (int)dt);
+  if (batch < 0 || max_seq_len < 0 || max_blocks_per_seq < 0 || num_blocks < 0)
+    return fail(TQ_ERR_INVALID_ARG, "negative size");
+  if (!std::isfinite(softmax_scale)) return fail(TQ_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (batch == 0) return TQ_OK;
+  if (batch > 65535) return fail(TQ_ERR_UNSUPPORTED, "batch > 65535");
+  if ((size_t)batch * ctx->cfg.num_kv_heads * sizeof(uint32_t) > tq::kCounterBytes)
+    return fail(TQ_ERR_UNSUPPORTED, "batch * num_kv_heads > %zu", tq::kCounterBytes / sizeof(uint32_t));
+  if (!q || !cache || !block_tables || !seq_lens || !out || !workspace)
+    return fail(TQ_ERR_INVALID_ARG, "null device pointer");
+  if (!aligned(cache, 16) || !aligned(workspace, 16) || !aligned(q, 4) || !aligned(out, 4))
+    return fail(TQ_ERR_INVALID_ARG, "misaligned pointer (cache/workspace need 16 bytes)");
+  const size_t need = tq_decode_workspace_bytes(ctx, batch, max_seq_len);
+  if (workspace_bytes < need)
+    return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  DeviceGuard g(ctx->device);
+  tq::DecodeArgs a;
+  a.q = q; a.q_dtype = (int32_t)dt; a.cache = (const uint8_t*)cache; a.num_blocks = num_blocks;
+  a.block_tables = block_tables; a.max_blocks = max_blocks_per_seq; a.seq_lens = seq_lens;
+  a.batch = batch; a.max_seq = max_seq_len; a.hkv = (int32_t)ctx->cfg.num_kv_heads; a.hq = (int32_t)ctx->cfg.num_q_heads;
+  a.group = a.hq / a.hkv; a.scale = softmax_scale;
+  a.qjl_coef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / ctx->cfg.head_dim);
+  a.logits = logits_out; a.out = out;
+  a.counters = (uint32_t*)workspace;
+  a.ws = (float*)((uint8_t*)workspace + tq::kCounterBytes);
+  plan_splits(batch, a.hkv, max_seq_len, &a.splits, &a.tiles_per_split);
+  a.f = offsets_of(ctx->layout); a.c = ctx->consts;
+  hipError_t e = tq::launch_decode(a, (int)ctx->cfg.key_bits, (int)ctx->cfg.key_mode, (int)ctx->cfg.val_bits,
+                                   (int)ctx->cfg.val_mode, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return TQ_OK;
+}
+
+tq_status tq_dequantize(tq_ctx* ctx, const void* cache, int64_t num_blocks, const int64_t* slots, int64_t n,
+                        float* k_out, float* v_out, hipStream_t stream) {
+  if (!ctx) return fail(TQ_ERR_INVALID_ARG, "ctx is null");
+  if (n < 0 || num_blocks < 0) return fail(TQ_ERR_INVALID_ARG, "negative size");
+  if (n == 0) return TQ_OK;
+  if (!cache || !slots || !k_out || !v_out) return fail(TQ_ERR_INVALID_ARG, "null device pointer");
+  if (!aligned(cache, 16) || !aligned(k_out, 16) || !aligned(v_out, 16))
+    return fail(TQ_ERR_INVALID_ARG, "cache and outputs must be 16-byte aligned");
+  DeviceGuard g(ctx->device);
+  tq::DequantArgs a;
+  for (int i = 0; i < 4; ++i) a.sign_bits[i] = ctx->sign_bits[i];
+  a.cache = (const uint8_t*)cache; a.num_blocks = num_blocks; a.slots = slots; a.n = n;
+  a.hkv = (int32_t)ctx->cfg.num_kv_heads; a.k_out = k_out; a.v_out = v_out;
+  a.f = offsets_of(ctx->layout); a.c = ctx->consts;
+  hipError_t e = tq::launch_dequant(a, (int)ctx->cfg.key_bits, (int)ctx->cfg.key_mode, (int)ctx->cfg.val_bits,
+                                    (int)ctx->cfg.val_mode, stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "dequantize launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Internal declarations shared by the host runtime (tq_host.cpp) and the HIP
+// kernels (tq_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr int kDim = 128;          // head_dim the kernels are specialised for
+constexpr int kLutCells = 256;     // cells of the code look-up grid (see QLut)
+constexpr int kMaxGroup = 4;       // q heads per kv head handled by one work-group
+constexpr int kBlockTokensDev = TQ_BLOCK_TOKENS;
+constexpr size_t kCounterBytes = 65536;   // arrival counters at the start of the decode workspace
+
+// One cell of the uniform grid that maps a rotated coordinate y to its code.
+// The grid covers [-range, range) with kLutCells cells; `base` counts the
+// thresholds lying entirely to the left of the (slightly widened) cell and `t`
+// is the only threshold inside it (or +inf).  code = base + (y >= t) equals
+// #{j : t_j <= y} exactly.  c_lo / c_hi are the centroids of codes base and
+// base + 1, so the kernel also gets C[code] without another lookup.
+struct QLut {
+  int32_t base;
+  float t;
+  float c_lo;
+  float c_hi;
+};
+
+// Constants of one context, stored in one device allocation.
+struct DevConsts {
+  float signs[kDim];          // +-1 of the rotation
+  float kc[16];               // key centroids (fp32), 2^key_bits used
+  float vc[16];               // value centroids (Lloyd-Max values only)
+  QLut klut[kLutCells];
+  QLut vlut[kLutCells];
+  float St[kDim * kDim];      // QJL projection transposed: St[k*d + m] = S[m][k]
+};
+
+struct FieldOffsets {
+  uint32_t page_bytes;
+  uint32_t kcodes, knorm, ksigns, kres, vcodes, vmin, vscale;
+};
+
+struct AppendArgs {
+  const void* k;
+  const void* v;
+  int64_t num_tokens;
+  int32_t hkv;
+  int32_t key_nc;             // 1: corrected norm
+  const int64_t* slots;
+  uint8_t* cache;
+  int64_t num_blocks;
+  FieldOffsets f;
+  const DevConsts* c;
+  uint32_t sign_bits[4];      // bit i set when sign i is -1
+  float klut_scale, klut_bias;   // cell = clamp(y * scale + bias)
+  float vlut_scale, vlut_bias;
+};
+
+struct DecodeArgs {
+  const void* q;
+  int32_t q_dtype;
+  const uint8_t* cache;
+  int64_t num_blocks;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  int32_t batch, max_seq, hkv, hq, group;
+  float scale;                // softmax scale
+  float qjl_coef;             // sqrt(pi/2) / m
+  float* logits;              // may be null
+  float* out;                 // [batch][hq][128]
+  float* ws;                  // partials [batch][hkv][splits][4][2 + 128]
+  uint32_t* counters;         // [batch][hkv] arrival counters, zero between calls
+  int32_t splits;
+  int32_t tiles_per_split;    // tile = 64 tokens
+  FieldOffsets f;
+  const DevConsts* c;
+};
+
+
+struct DequantArgs {
+  uint32_t sign_bits[4];
+  const uint8_t* cache;
+  int64_t num_blocks;
+  const int64_t* slots;
+  int64_t n;
+  int32_t hkv;
+  float* k_out;
+  float* v_out;
+  FieldOffsets f;
+  const DevConsts* c;
+};
+
+// Launchers (tq_kernels.hip).  Return hipSuccess or the launch error.
+hipError_t launch_append(const AppendArgs& a, int dtype, int key_bits, int key_mode, int val_bits,
+                         int val_mode, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int key_bits, int key_mode, int val_bits, int val_mode,
+                         hipStream_t s);
+hipError_t launch_dequant(const DequantArgs& a, int key_bits, int key_mode, int val_bits, int val_mode,
+                          hipStream_t s);
+
+}  // namespace tq

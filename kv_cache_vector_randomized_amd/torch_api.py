@@ -1,0 +1,75 @@
+"""PyTorch-side convenience layer: allocates the paged cache, workspace and
+outputs as torch tensors and calls the C ABI through `tq` (no compute here)."""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import tq
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return tq.TQ_BF16
+    if t.dtype == torch.float32:
+        return tq.TQ_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+class PagedKVCache:
+    """One layer's packed KV cache [num_blocks, num_kv_heads, page_bytes] (uint8) on a GPU."""
+
+    def __init__(self, ctx: tq.Context, num_blocks: int, device="cuda", fill: Optional[int] = None):
+        self.ctx = ctx
+        self.num_blocks = int(num_blocks)
+        shape = (self.num_blocks, ctx.cfg.num_kv_heads, ctx.page_bytes)
+        if fill is None:
+            self.data = torch.empty(shape, dtype=torch.uint8, device=device)
+        else:
+            self.data = torch.full(shape, fill, dtype=torch.uint8, device=device)
+        self._ws = None
+
+    def append(self, k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, stream=None):
+        """Quantize and store k, v [N, Hkv, d] at slot_mapping (int64 [N])."""
+        assert k.is_contiguous() and v.is_contiguous() and k.shape == v.shape and k.dtype == v.dtype
+        assert slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous()
+        assert slot_mapping.shape[0] == k.shape[0]
+        self.ctx.quantize_append(k, v, slot_mapping, self.data, self.num_blocks, _dtype_code(k), k.shape[0], stream)
+
+    def workspace(self, batch: int, max_seq_len: int) -> torch.Tensor:
+        need = self.ctx.workspace_bytes(batch, max_seq_len)
+        if self._ws is None or self._ws.numel() < need:
+            # zero-filled once: the leading counter region must start at zero
+            self._ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=self.data.device)
+        return self._ws
+
+    def decode(self, q: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+               softmax_scale: float, out: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+        """Attention of q [B, Hq, d] over the cache; returns out [B, Hq, d] fp32."""
+        assert q.is_contiguous() and block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32
+        assert block_tables.is_contiguous() and seq_lens.is_contiguous()
+        B = q.shape[0]
+        if out is None:
+            out = torch.empty((B, q.shape[1], q.shape[2]), dtype=torch.float32, device=q.device)
+        ws = self.workspace(B, max_seq_len)
+        self.ctx.decode_attention(q, _dtype_code(q), self.data, self.num_blocks, block_tables,
+                                  block_tables.shape[1], seq_lens, B, max_seq_len, softmax_scale, out, ws,
+                                  ws.numel(), logits_out=logits, stream=stream)
+        return out
+
+    def dequantize(self, slots: torch.Tensor, stream=None):
+        """Reconstruct (k_hat, v_hat) [n, Hkv, d] fp32 for int64 slots [n]."""
+        n = slots.shape[0]
+        shape = (n, self.ctx.cfg.num_kv_heads, self.ctx.cfg.head_dim)
+        k = torch.empty(shape, dtype=torch.float32, device=self.data.device)
+        v = torch.empty(shape, dtype=torch.float32, device=self.data.device)
+        self.ctx.dequantize(self.data, self.num_blocks, slots, n, k, v, stream)
+        return k, v
+
+
+def bf16_from_bits(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    """Upload bf16 bit patterns (uint16) as a torch.bfloat16 tensor."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)

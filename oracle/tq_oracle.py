@@ -26,7 +26,8 @@ Readings taken where the pages are silent (each is listed in the design notes):
   R2  codebook = Lloyd-Max for N(0, 1/d), solved on the positive half and mirrored.
   R5  norm correction: stored norm = ||k|| / ||C[code]||, so ||k_hat|| = ||k||.
   R6  zero key: codes = 2^(b-1), stored norm 0.
-  R11 uniform values: scale = fl32((max-min)/(2^b-1)), round half to even.
+  R11 uniform values: fp32 scale = (max-min)/(2^b-1), code = rint((v-min)/scale) in
+      fp32 (the stored precision), round half to even.
   R12 bit order: LSB-first stream per vector (generalises [P4]'s nibble order).
   R13 QJL: residual in the rotated frame, m = d rows, sign(0) -> bit 1.
   R14 GQA: q head h reads kv head h // (Hq/Hkv); softmax scale supplied by caller.
@@ -225,22 +226,27 @@ class ValueCodes:
 def quantize_values_uniform(v: np.ndarray, bits: int) -> ValueCodes:
     """Per-vector uniform quantizer with fp32 min and scale (R11).
 
-    scale = fl32((max - min) / (2^b - 1)); code = clamp(rint((v - min)/scale)).
-    A constant vector has scale 0 and all codes 0.
+    scale = (max - min) / (2^b - 1) and code = clamp(rint((v - min) / scale)), each
+    operation taken in fp32, the precision in which min and scale are stored, so
+    that the integer decision is made in the same precision as the kernel's.
+    A constant vector has scale 0 and all codes 0.  The band (distance of the
+    quotient to a rounding boundary) is measured on the fp64 quotient.
     """
-    v = np.asarray(v, dtype=np.float64)
+    v64 = np.asarray(v, dtype=np.float64)
+    v32 = v64.astype(np.float32)                 # inputs are bf16/fp32 values: exact
     levels = (1 << bits) - 1
-    mn = v.min(axis=-1)
-    mx = v.max(axis=-1)
-    sc = fl32((mx - mn) / levels)
-    safe = np.where(sc > 0, sc, 1.0)
-    x = (v - mn[..., None]) / safe[..., None]
-    x = np.where((sc > 0)[..., None], x, 0.0)
+    mn = v32.min(axis=-1)
+    mx = v32.max(axis=-1)
+    sc = (mx - mn) / np.float32(levels)          # fp32, correctly rounded
+    safe = np.where(sc > 0, sc, np.float32(1.0))
+    x = (v32 - mn[..., None]) / safe[..., None]  # fp32, correctly rounded
+    x = np.where((sc > 0)[..., None], x, np.float32(0.0))
     codes = np.clip(np.rint(x), 0, levels).astype(np.int64)
-    frac = x - np.floor(x)
+    x64 = (v64 - mn[..., None].astype(np.float64)) / safe[..., None].astype(np.float64)
+    frac = x64 - np.floor(x64)
     band = np.abs(frac - 0.5) / levels
     band = np.where((sc > 0)[..., None], band, np.inf)
-    return ValueCodes(codes=codes, vmin=fl32(mn), scale=sc, band=band)
+    return ValueCodes(codes=codes, vmin=mn.astype(np.float64), scale=sc.astype(np.float64), band=band)
 
 
 def dequantize_values_uniform(codes, vmin, scale) -> np.ndarray:

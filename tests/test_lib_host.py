@@ -1,0 +1,101 @@
+"""Host-side checks of the C-ABI library (no GPU): it loads, exports every entry
+point that include/tq.h declares, validates configurations, reports the page
+layout of the format, and builds the same fp32 codebook as the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from kv_cache_vector_randomized_amd import tq
+from oracle import tq_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "tq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tq.library()
+    declared = _declared_functions()
+    assert set(declared) == set(tq.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.tq_abi_version() == tq.ABI_VERSION
+
+
+def test_status_strings():
+    for s in range(6):
+        assert tq.status_string(s).startswith("TQ_")
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(), tq.TQ_OK),
+    (dict(num_kv_heads=8, num_q_heads=32), tq.TQ_OK),
+    (dict(num_kv_heads=8, num_q_heads=12), tq.TQ_ERR_INVALID_ARG),
+    (dict(num_kv_heads=2, num_q_heads=16), tq.TQ_ERR_UNSUPPORTED),   # group 8
+    (dict(head_dim=96), tq.TQ_ERR_INVALID_ARG),
+    (dict(head_dim=64), tq.TQ_ERR_UNSUPPORTED),
+    (dict(key_bits=0), tq.TQ_ERR_INVALID_ARG),
+    (dict(key_bits=8), tq.TQ_ERR_UNSUPPORTED),
+    (dict(val_bits=1), tq.TQ_ERR_UNSUPPORTED),
+    (dict(key_mode=3), tq.TQ_ERR_INVALID_ARG),
+    (dict(val_mode=2), tq.TQ_ERR_INVALID_ARG),
+    (dict(block_tokens=32), tq.TQ_ERR_INVALID_ARG),
+    (dict(abi_version=2), tq.TQ_ERR_INVALID_ARG),
+])
+def test_validate_config(kw, expect):
+    assert tq.validate_config(tq.make_config(**kw)) == expect
+
+
+def test_null_config_and_context():
+    lib = tq.library()
+    assert lib.tq_validate_config(None) == tq.TQ_ERR_INVALID_ARG
+    assert lib.tq_quantize_append(None, None, None, 1, 1, None, None, 1, None) == tq.TQ_ERR_INVALID_ARG
+    assert lib.tq_decode_workspace_bytes(None, 1, 1) == 0
+    assert lib.tq_destroy(None) is None
+    assert b"ctx" in lib.tq_last_error_message() or lib.tq_last_error_message()
+
+
+@pytest.mark.parametrize("kb,km,vb,vm", [(4, "lloyd", 4, "lloyd"), (4, "lloyd_nc", 4, "uniform"),
+                                         (3, "lloyd_nc", 3, "uniform"), (2, "lloyd_qjl", 4, "uniform"),
+                                         (2, "lloyd", 2, "uniform"), (3, "lloyd_qjl", 3, "lloyd")])
+def test_layout_matches_format(kb, km, vb, vm):
+    lay = tq.layout_for_config(tq.make_config(128, 8, 32, kb, km, vb, vm)).as_dict()
+    f = O.page_fields(O.Config(128, 8, 32, kb, km, vb, vm))
+    none = (1 << 64) - 1
+    assert lay["format_version"] == O.FORMAT_VERSION
+    assert lay["page_bytes"] == O.page_bytes(O.Config(128, 8, 32, kb, km, vb, vm))
+    assert lay["token_head_bytes"] * 16 == lay["page_bytes"]
+    assert (lay["off_kcodes"], lay["row_kcodes"]) == f["kcodes"]
+    assert lay["off_knorm"] == f["knorm"][0]
+    assert (lay["off_vcodes"], lay["row_vcodes"]) == f["vcodes"]
+    if km == "lloyd_qjl":
+        assert (lay["off_ksigns"], lay["row_ksigns"]) == f["ksigns"]
+        assert lay["off_kresid"] == f["kres"][0]
+    else:
+        assert lay["off_ksigns"] == none and lay["off_kresid"] == none
+    if vm == "uniform":
+        assert lay["off_vmin"] == f["vmin"][0] and lay["off_vscale"] == f["vscale"][0]
+    else:
+        assert lay["off_vmin"] == f["vnorm"][0] and lay["off_vscale"] == none
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_library_codebook_equals_oracle_rounded(bits):
+    """The library solves Lloyd-Max on its own (C++, long double); its fp32 tables must be the
+    fp32 rounding of the oracle's fp64 solution (at most 1 ulp apart)."""
+    c, t = tq.codebook(bits, 128)
+    cb = O.codebook(bits, 128)
+    c_ref = cb.centroids.astype(np.float32)
+    t_ref = cb.thresholds.astype(np.float32)
+    ulp_c = np.abs(c.view(np.int32).astype(np.int64) - c_ref.view(np.int32).astype(np.int64))
+    ulp_t = np.abs(t.view(np.int32).astype(np.int64) - t_ref.view(np.int32).astype(np.int64))
+    assert ulp_c.max() <= 1 and ulp_t.max() <= 1, (ulp_c, ulp_t)
+    assert np.all(np.diff(c) > 0) and np.all(np.diff(t) > 0)
+    assert t[len(t) // 2] == 0.0
