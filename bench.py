@@ -62,6 +62,8 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="independent layer caches rotated over the steps")
     ap.add_argument("--workload", default="gqa_decode", choices=["gqa_decode", "prefill_append"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="also run one plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path.",
@@ -140,6 +142,12 @@ def main():
                 ev[1].record(stream)
             c.decode(q_dev, tables, seq_lens, T, scale, out=out)
 
+    if args.copy_calibration_mb:
+        src = torch.empty(args.copy_calibration_mb << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()

@@ -168,6 +168,7 @@ void plan_splits(int batch, int hkv, int max_seq, int* splits, int* tiles_per_sp
   int want = (1024 + pairs - 1) / pairs;
   want = std::max(1, std::min(want, (tiles + 3) / 4));      // >= 4 tiles per split
   int tps = (tiles + want - 1) / want;
+  tps = std::min(tps, tq::kMaxPagesPerSplit / 4);
   *tiles_per_split = tps;
   *splits = (tiles + tps - 1) / tps;
 }

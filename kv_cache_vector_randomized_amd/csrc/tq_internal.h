@@ -14,6 +14,7 @@ constexpr int kDim = 128;          // head_dim the kernels are specialised for
 constexpr int kLutCells = 256;     // cells of the code look-up grid (see QLut)
 constexpr int kMaxGroup = 4;       // q heads per kv head handled by one work-group
 constexpr int kBlockTokensDev = TQ_BLOCK_TOKENS;
+constexpr int kMaxPagesPerSplit = 256;   // 64 tiles of 64 tokens
 constexpr size_t kCounterBytes = 65536;   // arrival counters at the start of the decode workspace
 
 // One cell of the uniform grid that maps a rotated coordinate y to its code.
