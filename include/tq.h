@@ -37,12 +37,15 @@
  * Cache format (TQ_FORMAT_VERSION 1)
  *   The cache is an array [num_blocks][num_kv_heads][page_bytes] of bytes.  A page
  *   holds the 16 token slots of one block for one KV head; slot = block*16 + offset.
- *   Inside a page the fields follow one another, each as 16 rows (one per slot):
+ *   Inside a page the fields follow one another, each holding one row per slot;
+ *   rows are slot-major (row of slot s at field + s*row_bytes) except the value
+ *   codes (see below):
  *     key codes   d*key_bits/8 bytes per row, LSB-first bit stream
  *     key norm    fp32 (plain: ||k||; corrected: ||k|| / ||C[code]||)
  *     [QJL only]  sign bits d/8 bytes per row (bit i = 1 if (S r)_i >= 0), then
  *                 residual norm fp32
- *     value codes d*val_bits/8 bytes per row, LSB-first bit stream
+ *     value codes d*val_bits/8 bytes per row, LSB-first bit stream, stored
+ *                 plane-major: byte p of slot s's row at field + 16*p + s
  *     uniform values: value min fp32, then value scale fp32
  *     Lloyd-Max values: value norm fp32
  *   Code i of a vector occupies stream bits [b*i, b*i+b); stream bit k is bit

@@ -180,7 +180,7 @@ __global__ __launch_bounds__(256) void append_values_kernel(AppendArgs a) {
     reinterpret_cast<float*>(page + a.f.vmin)[so] = mn;
     reinterpret_cast<float*>(page + a.f.vscale)[so] = sc;
   }
-  store_words<VB>(page + a.f.vcodes + so * (VB * 16), w);
+  store_planes<VB>(page + a.f.vcodes + so, w);
 }
 
 namespace {

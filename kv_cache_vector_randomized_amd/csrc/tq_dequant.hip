@@ -11,15 +11,19 @@ namespace tq {
 // ---------------------------------------------------------------------------
 // Dequantize: one lane per (slot, head); keys k_hat = nhat * diag(s) H C[code] / sqrt(d).
 // ---------------------------------------------------------------------------
-template <int B>
+template <int B, bool PLANES>
 __device__ __forceinline__ void lloyd_decode_row(const uint8_t* row, float nrm, const float* cb,
                                                  const uint32_t (&sb)[4], float* out) {
   uint32_t w[B * 4];
-  const uint4* src = reinterpret_cast<const uint4*>(row);
+  if constexpr (PLANES) {
+    load_planes<B>(row, w);
+  } else {
+    const uint4* src = reinterpret_cast<const uint4*>(row);
 #pragma unroll
-  for (int j = 0; j < B; ++j) {
-    const uint4 u = src[j];
-    w[4 * j] = u.x; w[4 * j + 1] = u.y; w[4 * j + 2] = u.z; w[4 * j + 3] = u.w;
+    for (int j = 0; j < B; ++j) {
+      const uint4 u = src[j];
+      w[4 * j] = u.x; w[4 * j + 1] = u.y; w[4 * j + 2] = u.z; w[4 * j + 3] = u.w;
+    }
   }
   float x[kDim];
 #pragma unroll
@@ -59,19 +63,14 @@ __global__ __launch_bounds__(128) void dequant_kernel(DequantArgs a) {
   const uint8_t* page = a.cache + ((slot >> 4) * a.hkv + h) * (int64_t)a.f.page_bytes;
   const int so = (int)(slot & 15);
   uint32_t sb[4] = {a.sign_bits[0], a.sign_bits[1], a.sign_bits[2], a.sign_bits[3]};
-  lloyd_decode_row<KB>(page + a.f.kcodes + so * (KB * 16), reinterpret_cast<const float*>(page + a.f.knorm)[so],
+  lloyd_decode_row<KB, false>(page + a.f.kcodes + so * (KB * 16), reinterpret_cast<const float*>(page + a.f.knorm)[so],
                        kcb, sb, ko);
   if constexpr (VLM) {
-    lloyd_decode_row<VB>(page + a.f.vcodes + so * (VB * 16), reinterpret_cast<const float*>(page + a.f.vmin)[so],
+    lloyd_decode_row<VB, true>(page + a.f.vcodes + so, reinterpret_cast<const float*>(page + a.f.vmin)[so],
                          vcb, sb, vo);
   } else {
     uint32_t w[VB * 4];
-    const uint4* src = reinterpret_cast<const uint4*>(page + a.f.vcodes + so * (VB * 16));
-#pragma unroll
-    for (int j = 0; j < VB; ++j) {
-      const uint4 u = src[j];
-      w[4 * j] = u.x; w[4 * j + 1] = u.y; w[4 * j + 2] = u.z; w[4 * j + 3] = u.w;
-    }
+    load_planes<VB>(page + a.f.vcodes + so, w);
     const float mn = reinterpret_cast<const float*>(page + a.f.vmin)[so];
     const float sc = reinterpret_cast<const float*>(page + a.f.vscale)[so];
 #pragma unroll

@@ -99,6 +99,24 @@ __device__ __forceinline__ void store_words(uint8_t* dst, const uint32_t (&w)[B 
   for (int j = 0; j < B; ++j) d[j] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
 }
 
+// Value codes are stored plane-major inside a page: byte p of the row of slot s
+// sits at p * 16 + s (the 16 slots of one byte position are contiguous).
+template <int B>
+__device__ __forceinline__ void store_planes(uint8_t* dst_slot, const uint32_t (&w)[B * 4]) {
+#pragma unroll
+  for (int j = 0; j < B * 4; ++j)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dst_slot[(4 * j + k) * 16] = (uint8_t)(w[j] >> (8 * k));
+}
+
+template <int B>
+__device__ __forceinline__ void load_planes(const uint8_t* src_slot, uint32_t (&w)[B * 4]) {
+#pragma unroll
+  for (int j = 0; j < B * 4; ++j)
+    w[j] = (uint32_t)src_slot[(4 * j) * 16] | ((uint32_t)src_slot[(4 * j + 1) * 16] << 8) |
+           ((uint32_t)src_slot[(4 * j + 2) * 16] << 16) | ((uint32_t)src_slot[(4 * j + 3) * 16] << 24);
+}
+
 __device__ __forceinline__ void apply_signs(float (&x)[kDim], const uint32_t (&sb)[4]) {
 #pragma unroll
   for (int i = 0; i < kDim; ++i)

@@ -276,9 +276,12 @@ def unpack_codes(packed: np.ndarray, bits: int, n: int) -> np.ndarray:
 
 # ----------------------------------------------------------------------------
 # Paged cache format (format version 1).  A page holds 16 tokens of one KV head;
-# fields are stored one after another, each as 16 rows (one per token slot):
+# fields are stored one after another, each holding one row per token slot:
 #   key codes, key norm (f32), [QJL sign bits, QJL residual norm (f32)],
 #   value codes, value min or value norm (f32), [value scale (f32)].
+# Every field is slot-major (row of slot s at field + s * row_bytes) except the
+# value codes, which are plane-major: byte p of slot s's row sits at
+# field + 16 * p + s (the 16 slots of one byte position are contiguous).
 # The cache is [num_blocks][num_kv_heads][page_bytes]; slot = block*16 + offset.
 # [P4 transfer section: the reader must know the format id/version and layout]
 # ----------------------------------------------------------------------------
@@ -373,8 +376,11 @@ def write_tokens(cfg: Config, cache: np.ndarray, slots: np.ndarray, qz: Quantize
         base, size = f[name]
         for i in range(slots.shape[0]):
             for h in range(cfg.num_kv_heads):
-                start = base + off[i] * size
-                cache[blk[i], h, start:start + size] = data[i, h]
+                if name == "vcodes":
+                    cache[blk[i], h, base + BLOCK_TOKENS * np.arange(size) + off[i]] = data[i, h]
+                else:
+                    start = base + off[i] * size
+                    cache[blk[i], h, start:start + size] = data[i, h]
 
 
 def read_tokens(cfg: Config, cache: np.ndarray, slots: np.ndarray, head: int) -> Dict[str, np.ndarray]:
@@ -386,7 +392,10 @@ def read_tokens(cfg: Config, cache: np.ndarray, slots: np.ndarray, head: int) ->
     for name, (base, size) in f.items():
         if name == "_page":
             continue
-        idx = base + off[:, None] * size + np.arange(size)[None, :]
+        if name == "vcodes":
+            idx = base + off[:, None] + BLOCK_TOKENS * np.arange(size)[None, :]
+        else:
+            idx = base + off[:, None] * size + np.arange(size)[None, :]
         raw = cache[blk[:, None], head, idx]
         if name == "kcodes":
             out[name] = unpack_codes(raw, cfg.key_bits, cfg.head_dim)

@@ -61,7 +61,9 @@ def written_mask(cfg: O.Config, shape, slots):
         if s < 0 or s >= shape[0] * 16:
             continue
         for name, (base, size) in f.items():
-            if name != "_page":
+            if name == "vcodes":
+                m[s // 16, :, base + (s % 16) + 16 * np.arange(size)] = True
+            elif name != "_page":
                 m[s // 16, :, base + (s % 16) * size: base + (s % 16 + 1) * size] = True
     return m
 

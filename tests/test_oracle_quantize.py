@@ -179,7 +179,9 @@ def test_paged_write_keeps_sentinel_and_round_trips():
     touched = np.zeros(cache.shape, bool)
     for s in slots:
         for name, (base, size) in f.items():
-            if name != "_page":
+            if name == "vcodes":       # plane-major: byte p of slot s at base + 16 p + s
+                touched[s // 16, :, base + (s % 16) + 16 * np.arange(size)] = True
+            elif name != "_page":
                 touched[s // 16, :, base + (s % 16) * size: base + (s % 16 + 1) * size] = True
     assert np.all(cache[~touched] == 0xA5)
     copy = cache.copy()
