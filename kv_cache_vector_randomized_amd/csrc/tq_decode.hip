@@ -44,20 +44,20 @@ __device__ __forceinline__ float load_agent(const float* p) {
 }
 
 // Wave-wide max: DPP within rows of 16 lanes, then the four row results.
-template <int CTRL>
+// Rows outside ROW_MASK keep their own value, which is neutral for max.
+template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
 }
 __device__ __forceinline__ float wave_max_dpp(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));    // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp<0x141>(v));   // row_half_mirror
-  v = fmaxf(v, dpp<0x140>(v));   // row_mirror
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+  v = fmaxf(v, dpp<0xB1, 0xF>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp<0x4E, 0xF>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp<0x141, 0xF>(v));   // row_half_mirror
+  v = fmaxf(v, dpp<0x140, 0xF>(v));   // row_mirror: every lane of a row holds the row max
+  v = fmaxf(v, dpp<0x142, 0xA>(v));   // row_bcast:15 into rows 1 and 3
+  v = fmaxf(v, dpp<0x143, 0xC>(v));   // row_bcast:31 into rows 2 and 3: lane 63 holds the max
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Value codes of coordinates 2*lane, 2*lane+1 for the four tokens of one 32-bit
@@ -88,18 +88,19 @@ struct TileRegs {
   uint4 sg;
 };
 
-// Loads of one 64-token tile (4 pages of one kv head).
 // Block ids of the 4 pages of one tile (wave-uniform; -1: absent or out of range).
 struct TilePages {
   int b[4];
-  __device__ __forceinline__ int of_lane(int lane) const {
-    const int q = lane >> 4;
-    return q == 0 ? b[0] : q == 1 ? b[1] : q == 2 ? b[2] : b[3];
-  }
 };
 
 // The wave keeps the block ids of all its tiles in one register: lane 4k + pg
-// holds page pg of the wave's k-th tile.
+// holds page pg of the wave's k-th tile.  lane_block returns the block id of the
+// page that lane `lane` reads in the k-th tile (lanes 16*pg .. 16*pg+15 read page
+// pg), fetched across lanes without a branch.
+__device__ __forceinline__ int lane_block(int blk_reg, int k, int lane) {
+  return __builtin_amdgcn_ds_bpermute((4 * k + (lane >> 4)) << 2, blk_reg);
+}
+
 __device__ __forceinline__ TilePages pages_of(int blk_reg, int k) {
   TilePages p;
 #pragma unroll
@@ -107,43 +108,40 @@ __device__ __forceinline__ TilePages pages_of(int blk_reg, int k) {
   return p;
 }
 
+// Loads of one 64-token tile (4 pages of one kv head).  Loads are unconditional:
+// an absent page (block id -1) reads block 0 in its place and the lanes of
+// absent pages and of tokens past the end are masked after the loads, which
+// keeps the load path free of branches.  The caller guarantees num_blocks >= 1.
+__device__ __forceinline__ int64_t page_offset(int blk, int kvh, int64_t blk_stride, int64_t head_stride) {
+  return (int64_t)(blk >= 0 ? blk : 0) * blk_stride + kvh * head_stride;
+}
+
 template <int KB, bool QJL, int VB, bool VLM>
-__device__ __forceinline__ void load_tile(TileRegs<KB, VB>& r, const DecodeArgs& a, const TilePages& tp, int tile,
-                                          int tok_end, int kvh, int lane, int64_t blk_stride,
-                                          int64_t head_stride) {
+__device__ __forceinline__ void load_tile(TileRegs<KB, VB>& r, const DecodeArgs& a, int blk, int kvh, int lane,
+                                          int64_t blk_stride, int64_t head_stride) {
   constexpr int KROW = kDim * KB / 8;
-  constexpr int VROW = kDim * VB / 8;
-  const int t = tile * 64 + lane;
-  const int blk = tp.of_lane(lane);
-  const bool valid = t < tok_end && blk >= 0;
-  const uint8_t* page = a.cache + (valid ? (int64_t)blk * blk_stride + kvh * head_stride : 0);
-  const int so = t & 15;
-  r.knorm = 0.f;
-  r.va = 0.f;
-  r.vb = 0.f;
-  r.kres = 0.f;
-  r.sg = make_uint4(0u, 0u, 0u, 0u);
+  const uint8_t* page = a.cache + page_offset(blk, kvh, blk_stride, head_stride);
+  const int so = lane & 15;
+  const uint4* src = reinterpret_cast<const uint4*>(page + a.f.kcodes + so * KROW);
 #pragma unroll
-  for (int j = 0; j < KB * 4; ++j) r.kw[j] = 0u;
-  if (valid) {
-    const uint4* src = reinterpret_cast<const uint4*>(page + a.f.kcodes + so * KROW);
-#pragma unroll
-    for (int j = 0; j < KB; ++j) {
-      const uint4 u = src[j];
-      r.kw[4 * j] = u.x; r.kw[4 * j + 1] = u.y; r.kw[4 * j + 2] = u.z; r.kw[4 * j + 3] = u.w;
-    }
-    r.knorm = reinterpret_cast<const float*>(page + a.f.knorm)[so];
-    r.va = reinterpret_cast<const float*>(page + a.f.vmin)[so];
-    if (!VLM) r.vb = reinterpret_cast<const float*>(page + a.f.vscale)[so];
-    if (QJL) {
-      r.sg = reinterpret_cast<const uint4*>(page + a.f.ksigns)[so];
-      r.kres = reinterpret_cast<const float*>(page + a.f.kres)[so];
-    }
+  for (int j = 0; j < KB; ++j) {
+    const uint4 u = src[j];
+    r.kw[4 * j] = u.x; r.kw[4 * j + 1] = u.y; r.kw[4 * j + 2] = u.z; r.kw[4 * j + 3] = u.w;
+  }
+  r.knorm = reinterpret_cast<const float*>(page + a.f.knorm)[so];
+  r.va = reinterpret_cast<const float*>(page + a.f.vmin)[so];
+  r.vb = VLM ? 0.f : reinterpret_cast<const float*>(page + a.f.vscale)[so];
+  if (QJL) {
+    r.sg = reinterpret_cast<const uint4*>(page + a.f.ksigns)[so];
+    r.kres = reinterpret_cast<const float*>(page + a.f.kres)[so];
+  } else {
+    r.sg = make_uint4(0u, 0u, 0u, 0u);
+    r.kres = 0.f;
   }
 }
 
-// Value byte plane(s) of this lane's two coordinates for the tile's 4 pages
-// (16 tokens per page, one coalesced 16-byte load per page and plane).
+// Lloyd-Max values: byte plane(s) of this lane's two coordinates for the tile's
+// 4 pages (16 tokens per page, one coalesced 16-byte load per page and plane).
 template <int VB>
 __device__ __forceinline__ void load_value_planes(uint4 (&vp)[VB == 3 ? 8 : 4], const DecodeArgs& a,
                                                   const TilePages& tp, int kvh, int lane, int64_t blk_stride,
@@ -153,14 +151,9 @@ __device__ __forceinline__ void load_value_planes(uint4 (&vp)[VB == 3 ? 8 : 4], 
   const int p1 = (6 * lane >> 3) + 1 < VROW ? (6 * lane >> 3) + 1 : VROW - 1;
 #pragma unroll
   for (int pg = 0; pg < 4; ++pg) {
-    const int pblk = tp.b[pg];
-    vp[pg] = make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (VB == 3) vp[4 + pg] = make_uint4(0u, 0u, 0u, 0u);
-    if (pblk >= 0) {
-      const uint8_t* vbase = a.cache + (int64_t)pblk * blk_stride + kvh * head_stride + a.f.vcodes;
-      vp[pg] = *reinterpret_cast<const uint4*>(vbase + p0 * 16);
-      if constexpr (VB == 3) vp[4 + pg] = *reinterpret_cast<const uint4*>(vbase + p1 * 16);
-    }
+    const uint8_t* vbase = a.cache + page_offset(tp.b[pg], kvh, blk_stride, head_stride) + a.f.vcodes;
+    vp[pg] = *reinterpret_cast<const uint4*>(vbase + p0 * 16);
+    if constexpr (VB == 3) vp[4 + pg] = *reinterpret_cast<const uint4*>(vbase + p1 * 16);
   }
 }
 
@@ -168,25 +161,112 @@ __device__ __forceinline__ uint32_t u4get(const uint4& v, int k) {
   return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
 }
 
+// Uniform values: lane l loads, from page l/16 of the tile, the byte planes of
+// coordinates 8j..8j+7 (j = l%16): VB planes of 16 slots, contiguous in the page.
+template <int VB>
+__device__ __forceinline__ void load_value_group(uint4 (&vq)[VB], const DecodeArgs& a, int blk, int kvh, int lane,
+                                                 int64_t blk_stride, int64_t head_stride) {
+  const uint4* src = reinterpret_cast<const uint4*>(a.cache + page_offset(blk, kvh, blk_stride, head_stride) +
+                                                    a.f.vcodes + 16 * VB * (lane & 15));
+#pragma unroll
+  for (int i = 0; i < VB; ++i) vq[i] = src[i];
+}
+
+typedef int intx4 __attribute__((ext_vector_type(4)));
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+
+// Wave-wide maxima of five values at once.  Each DPP step combines a lane with
+// another lane of its row (quad swaps, half-row and row mirrors), then the row
+// broadcasts carry row 0 into row 1, row 2 into row 3 and rows 0-1 into rows
+// 2-3, so lane 63 ends with the maximum.  The five reductions are interleaved,
+// so every DPP source was written at least four instructions earlier (the DPP
+// read-after-write hazard needs two); the leading s_nop covers the producers.
+__device__ __forceinline__ void wave_max5(float& v0, float& v1, float& v2, float& v3, float& v4) {
+#define TQ_DPP5(CTL)                                                   \
+  "v_max_f32_dpp %0, %0, %0 " CTL "\n\t"                               \
+  "v_max_f32_dpp %1, %1, %1 " CTL "\n\t"                               \
+  "v_max_f32_dpp %2, %2, %2 " CTL "\n\t"                               \
+  "v_max_f32_dpp %3, %3, %3 " CTL "\n\t"                               \
+  "v_max_f32_dpp %4, %4, %4 " CTL "\n\t"
+  asm volatile("s_nop 1\n\t"
+               TQ_DPP5("quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf")
+               TQ_DPP5("quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf")
+               TQ_DPP5("row_half_mirror row_mask:0xf bank_mask:0xf")
+               TQ_DPP5("row_mirror row_mask:0xf bank_mask:0xf")
+               TQ_DPP5("row_bcast:15 row_mask:0xa bank_mask:0xf")
+               TQ_DPP5("row_bcast:31 row_mask:0xc bank_mask:0xf")
+               "s_nop 1"
+               : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3), "+v"(v4));
+#undef TQ_DPP5
+  v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v0), 63));
+  v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v1), 63));
+  v2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v2), 63));
+  v3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v3), 63));
+  v4 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v4), 63));
+}
+
+// Value codes of this lane's page and coordinates 8j..8j+7 (j = lane % 16) as
+// the B operand of the int8 MFMA for coordinate 8j + m: one code per byte, byte s
+// of dword w is slot 4w + s of the page.  Codes are packed LSB-first, so within a
+// byte plane the shifts and masks below act on four slots at once.
+template <int VB, int M>
+__device__ __forceinline__ intx4 value_codes(const uint4 (&vq)[VB]) {
+  uint32_t r[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if constexpr (VB == 4) {
+      const uint32_t x = u4get(vq[M >> 1], w);
+      r[w] = (M & 1) ? ((x >> 4) & 0x0F0F0F0Fu) : (x & 0x0F0F0F0Fu);
+    } else if constexpr (VB == 2) {
+      const uint32_t x = u4get(vq[M >> 2], w);
+      r[w] = (x >> (2 * (M & 3))) & 0x03030303u;
+    } else {
+      // 8 codes of 3 bits span the three planes p0, p1, p2 of the group
+      const uint32_t p0 = u4get(vq[0], w), p1 = u4get(vq[1], w), p2 = u4get(vq[2], w);
+      if constexpr (M == 0) r[w] = p0 & 0x07070707u;
+      else if constexpr (M == 1) r[w] = (p0 >> 3) & 0x07070707u;
+      else if constexpr (M == 2) r[w] = ((p0 >> 6) & 0x03030303u) | ((p1 << 2) & 0x04040404u);
+      else if constexpr (M == 3) r[w] = (p1 >> 1) & 0x07070707u;
+      else if constexpr (M == 4) r[w] = (p1 >> 4) & 0x07070707u;
+      else if constexpr (M == 5) r[w] = ((p1 >> 7) & 0x01010101u) | ((p2 << 1) & 0x06060606u);
+      else if constexpr (M == 6) r[w] = (p2 >> 2) & 0x07070707u;
+      else r[w] = (p2 >> 5) & 0x07070707u;
+    }
+  }
+  return intx4{(int)r[0], (int)r[1], (int)r[2], (int)r[3]};
+}
+
+// Seven-bit limb `sh/7` of four weights, one per byte.
+__device__ __forceinline__ int limb4(const uint4& x, uint32_t sh) {
+  const uint32_t b0 = (x.x >> sh) & 0x7Fu, b1 = (x.y >> sh) & 0x7Fu;
+  const uint32_t b2 = (x.z >> sh) & 0x7Fu, b3 = (x.w >> sh) & 0x7Fu;
+  return (int)(b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
+}
+
 template <int KB, bool QJL, int VB, bool VLM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // Each wave owns its copy of the rotated query rows and the codebooks, so the
   // waves never wait for each other before the final merge.  Rows are padded by
-  // 4 floats so the 4 heads' 16-byte reads fall in different banks.
+  // 4 words so the 4 heads' 16-byte reads fall in different banks.
   __shared__ __align__(16) float q_all[4][4][kDim + 4];
   __shared__ __align__(16) float p_all[QJL ? 4 : 1][QJL ? 4 : 1][kDim + 4];
-  __shared__ float kcb_all[4][16];
-  __shared__ float vcb_all[4][16];
-  __shared__ __align__(16) float wT[4][4][68];      // softmax weight x scale: [wave][head][token]
+  __shared__ __align__(16) float kcb_all[4][16];
+  __shared__ float vcb_all[VLM ? 4 : 1][16];
+  // per wave and head, the 64 tokens' value weights: fp32 (Lloyd-Max values) or
+  // the fixed-point integers fed to the int8 MFMA (uniform values)
+  __shared__ __align__(16) uint32_t wT[4][4][68];
   __shared__ float part_ml[4][4][2];
   __shared__ __align__(16) float part_o[4][4][kDim];
 
   const int G = a.group;
   int seq_len = a.seq_lens[b];
   seq_len = max(0, min(seq_len, min(a.max_seq, 16 * a.max_blocks)));
+  if (a.num_blocks <= 0) seq_len = 0;     // no page exists: every block id is absent
   const int tile_begin = split * a.tiles_per_split;
   const int tile_end = tile_begin + a.tiles_per_split;
   const int tok_end = min(seq_len, tile_end * 64);
@@ -195,8 +275,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
 
   float (&q_lds)[4][kDim + 4] = q_all[wave];
   float (&p_lds)[QJL ? 4 : 1][kDim + 4] = p_all[QJL ? wave : 0];
-  float* kcb = kcb_all[wave];
-  float* vcb = vcb_all[wave];
+  float* vcb = vcb_all[VLM ? wave : 0];
+  uint32_t (&wt)[4][68] = wT[wave];
 
   // Prologue (per wave, no work-group barrier): the block ids of the wave's
   // pages (lane 4k + pg: page pg of the wave's k-th tile; at most 16 tiles per
@@ -213,8 +293,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     }
   }
   if (lane < 16) {
-    kcb[lane] = a.c->kc[lane];
-    vcb[lane] = a.c->vc[lane];
+    kcb_all[wave][lane] = a.c->kc[lane];
+    if (VLM) vcb[lane] = a.c->vc[lane];
   }
   float qx[4][2], sg0 = 0.f, sg1 = 0.f;
 #pragma unroll
@@ -237,17 +317,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
   sg1 = a.c->signs[2 * lane + 1];
 
   TileRegs<KB, VB> nx;
-  uint4 vp[VB == 3 ? 8 : 4];
+  uint4 vp[VB == 3 ? 8 : 4];     // Lloyd-Max values: byte planes of coordinates 2*lane, 2*lane+1
+  uint4 vq[VB];                  // uniform values: the planes of coordinates 8j..8j+7 of page lane/16
   int tile = tile_begin + wave;
   if (tile < tile_end && tile * 64 < tok_end) {
-    const TilePages tp = pages_of(blk_reg, 0);
-    load_tile<KB, QJL, VB, VLM>(nx, a, tp, tile, tok_end, kvh, lane, blk_stride, head_stride);
-    load_value_planes<VB>(vp, a, tp, kvh, lane, blk_stride, head_stride);
+    const int blk = lane_block(blk_reg, 0, lane);
+    load_tile<KB, QJL, VB, VLM>(nx, a, blk, kvh, lane, blk_stride, head_stride);
+    if constexpr (VLM) load_value_planes<VB>(vp, a, pages_of(blk_reg, 0), kvh, lane, blk_stride, head_stride);
+    else load_value_group<VB>(vq, a, blk, kvh, lane, blk_stride, head_stride);
   }
 
-  // Rotate the group's query heads once: q'' = scale * H(s*q)/sqrt(d).
+  // Rotate the group's query heads once: q'' = log2(e) * scale * H(s*q)/sqrt(d),
+  // so that logits come out in base-2 units for exp2.
   {
-    const float f = a.scale * kInvSqrtDim;
+    const float f = a.scale * kInvSqrtDim * kLog2e;
 #pragma unroll
     for (int hh = 0; hh < 4; ++hh) {
       float x0 = qx[hh][0] * sg0, x1 = qx[hh][1] * sg1;
@@ -296,46 +379,59 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     l_lane[h] = 0.f;
     s_lane[h] = 0.f;
   }
+  // Uniform values: lane l accumulates head l/16, coordinates 8(l%16) + m.
+  float O[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) O[m] = 0.f;
+  // Lloyd-Max values: rows = heads, columns = coordinates 2*lane, 2*lane+1.
   floatx4 O0 = {0.f, 0.f, 0.f, 0.f}, O1 = O0, O2 = O0, O3 = O0;
   const int vsh = (VB == 2) ? 4 * (lane & 1) : (VB == 3) ? ((6 * lane) & 7) : 0;
+  const uint32_t wbase = (uint32_t)wave * 0x40404040u;   // this wave's key table, in every byte
+  const char* cbf = reinterpret_cast<const char*>(&kcb_all[0][0]);
+  const int ho = lane >> 4;                              // head of this lane's value outputs
 
   for (int k = 0; tile < tile_end && tile * 64 < tok_end; tile += 4, ++k) {
     const int t = tile * 64 + lane;
-    const TilePages tp = pages_of(blk_reg, k);
-    const bool valid = t < tok_end && tp.of_lane(lane) >= 0;
-    const float knorm = nx.knorm, va = nx.va, vb = nx.vb, kres = nx.kres;
+    const bool has_next = tile + 4 < tile_end && (tile + 4) * 64 < tok_end;
+    const bool valid = t < tok_end && lane_block(blk_reg, k, lane) >= 0;
+    const int nblk = lane_block(blk_reg, k + 1, lane);
+    // masked lanes may have read another page: their scalars must not reach a sum
+    const float knorm = nx.knorm, kres = nx.kres;
+    const float va = valid ? nx.va : 0.f, vb = valid ? nx.vb : 0.f;
 
     // Logits: rows = 4 query heads, columns = this lane's token, one coordinate per
     // MFMA; two independent accumulators keep the matrix pipe busy.
     floatx4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0;
-    const char* cb = reinterpret_cast<const char*>(kcb);
     if constexpr (KB == 4) {
-      // Two masks per 32-bit word put its eight codes, already multiplied by 4 (the
-      // table stride), into byte lanes; each code then costs one byte extract.
+      // Two masks per 32-bit word put its eight codes, multiplied by 4 (the table
+      // stride) and offset to this wave's table, into byte lanes; each code then
+      // costs one byte extract.
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const uint32_t e = (nx.kw[j] << 2) & 0x3C3C3C3Cu;   // codes 8j, 8j+2, 8j+4, 8j+6
-        const uint32_t o = (nx.kw[j] >> 2) & 0x3C3C3C3Cu;   // codes 8j+1, 8j+3, 8j+5, 8j+7
+        const uint32_t e = ((nx.kw[j] << 2) & 0x3C3C3C3Cu) | wbase;   // codes 8j, 8j+2, 8j+4, 8j+6
+        const uint32_t o = ((nx.kw[j] >> 2) & 0x3C3C3C3Cu) | wbase;   // codes 8j+1, 8j+3, 8j+5, 8j+7
         const float4 qa = *reinterpret_cast<const float4*>(&q_lds[lane & 3][8 * j]);
         const float4 qb = *reinterpret_cast<const float4*>(&q_lds[lane & 3][8 * j + 4]);
-        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(qa.x, *(const float*)(cb + (e & 0xFF)), c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(qa.y, *(const float*)(cb + (o & 0xFF)), c1, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(qa.z, *(const float*)(cb + ((e >> 8) & 0xFF)), c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(qa.w, *(const float*)(cb + ((o >> 8) & 0xFF)), c1, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(qb.x, *(const float*)(cb + ((e >> 16) & 0xFF)), c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(qb.y, *(const float*)(cb + ((o >> 16) & 0xFF)), c1, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(qb.z, *(const float*)(cb + (e >> 24)), c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(qb.w, *(const float*)(cb + (o >> 24)), c1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(qa.x, *(const float*)(cbf + (e & 0xFF)), c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(qa.y, *(const float*)(cbf + (o & 0xFF)), c1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(qa.z, *(const float*)(cbf + ((e >> 8) & 0xFF)), c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(qa.w, *(const float*)(cbf + ((o >> 8) & 0xFF)), c1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(qb.x, *(const float*)(cbf + ((e >> 16) & 0xFF)), c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(qb.y, *(const float*)(cbf + ((o >> 16) & 0xFF)), c1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(qb.z, *(const float*)(cbf + (e >> 24)), c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(qb.w, *(const float*)(cbf + (o >> 24)), c1, 0, 0, 0);
         if ((j & 1) == 1) __builtin_amdgcn_sched_barrier(0);   // bound the look-ups in flight
       }
     } else {
+      const uint32_t w64 = (uint32_t)wave * 64u;
 #pragma unroll
       for (int i = 0; i < kDim; i += 4) {
         const float4 q4 = *reinterpret_cast<const float4*>(&q_lds[lane & 3][i]);
-        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.x, *(const float*)(cb + (get_code<KB>(nx.kw, i) << 2)), c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.y, *(const float*)(cb + (get_code<KB>(nx.kw, i + 1) << 2)), c1, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.z, *(const float*)(cb + (get_code<KB>(nx.kw, i + 2) << 2)), c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.w, *(const float*)(cb + (get_code<KB>(nx.kw, i + 3) << 2)), c1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.x, *(const float*)(cbf + ((get_code<KB>(nx.kw, i) << 2) | w64)), c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.y, *(const float*)(cbf + ((get_code<KB>(nx.kw, i + 1) << 2) | w64)), c1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.z, *(const float*)(cbf + ((get_code<KB>(nx.kw, i + 2) << 2) | w64)), c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.w, *(const float*)(cbf + ((get_code<KB>(nx.kw, i + 3) << 2) | w64)), c1, 0, 0, 0);
+        if ((i & 15) == 12) __builtin_amdgcn_sched_barrier(0);
       }
     }
     floatx4 acc = c0 + c1;
@@ -354,9 +450,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
       acc2 = d0 + d1;
     }
     // The key row is consumed: fetch the next tile while this one finishes.
-    if (tile + 4 < tile_end && (tile + 4) * 64 < tok_end)
-      load_tile<KB, QJL, VB, VLM>(nx, a, pages_of(blk_reg, k + 1), tile + 4, tok_end, kvh, lane, blk_stride,
-                                  head_stride);
+    if (has_next) load_tile<KB, QJL, VB, VLM>(nx, a, nblk, kvh, lane, blk_stride, head_stride);
 
     float lg[4];
 #pragma unroll
@@ -368,91 +462,140 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
     if (a.logits != nullptr && valid) {
 #pragma unroll
       for (int h = 0; h < 4; ++h)
-        if (h < G) a.logits[((int64_t)b * a.hq + (int64_t)kvh * G + h) * a.max_seq + t] = lg[h];
+        if (h < G) a.logits[((int64_t)b * a.hq + (int64_t)kvh * G + h) * a.max_seq + t] = lg[h] * kLn2;
     }
-    // Online softmax: the running max is wave-uniform, sums stay per lane; the
-    // accumulators are rescaled only when a head's max moved.
-    float mnew[4];
+    // Online softmax (base 2): the running max is wave-uniform, sums stay per lane;
+    // the accumulators are rescaled only when a head's max moved.
+    float mnew[4] = {lg[0], lg[1], lg[2], lg[3]};
+    float smax = vb;                        // largest value scale of the tile (masked lanes: 0)
+    wave_max5(mnew[0], mnew[1], mnew[2], mnew[3], smax);
     bool moved = false;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      mnew[h] = fmaxf(m_run[h], wave_max_dpp(lg[h]));
+      mnew[h] = fmaxf(m_run[h], mnew[h]);
       moved = moved || (mnew[h] != m_run[h]);
     }
     if (moved) {
+      float al[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const float alpha = (mnew[h] == -INFINITY) ? 1.f : __expf(m_run[h] - mnew[h]);
-        l_lane[h] *= alpha;
-        s_lane[h] *= alpha;
-        O0[h] *= alpha;
-        O1[h] *= alpha;
-        O2[h] *= alpha;
-        O3[h] *= alpha;
+        al[h] = (mnew[h] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[h] - mnew[h]);
+        l_lane[h] *= al[h];
+        s_lane[h] *= al[h];
         m_run[h] = mnew[h];
       }
+      if constexpr (VLM) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          O0[h] *= al[h];
+          O1[h] *= al[h];
+          O2[h] *= al[h];
+          O3[h] *= al[h];
+        }
+      } else {
+        const float ah = ho == 0 ? al[0] : ho == 1 ? al[1] : ho == 2 ? al[2] : al[3];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) O[m] *= ah;
+      }
     }
+    float pr[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const float pr = (valid && m_run[h] != -INFINITY) ? __expf(lg[h] - m_run[h]) : 0.f;
-      l_lane[h] += pr;
-      if (!VLM) s_lane[h] = fmaf(pr, va, s_lane[h]);
-      wT[wave][h][lane] = pr * (VLM ? va : vb);
+      const float ms = (m_run[h] == -INFINITY) ? 0.f : m_run[h];
+      pr[h] = __builtin_amdgcn_exp2f(lg[h] - ms);          // 0 for masked tokens
+      l_lane[h] += pr[h];
+      if (!VLM) s_lane[h] = fmaf(pr[h], va, s_lane[h]);
     }
-    wave_sync_lds();
-    // Values: rows = 4 heads, columns = coordinates 2*lane / 2*lane+1, one token per
-    // MFMA; even and odd tokens go to separate accumulators.
+    if constexpr (VLM) {
 #pragma unroll
-    for (int pg = 0; pg < 4; ++pg) {
+      for (int h = 0; h < 4; ++h) wt[h][lane] = __float_as_uint(pr[h] * va);
+      wave_sync_lds();
+      // Values: rows = 4 heads, columns = coordinates 2*lane / 2*lane+1, one token per
+      // MFMA; even and odd tokens go to separate accumulators.
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int tt = pg * 16 + 4 * k;
-        const float4 w4 = *reinterpret_cast<const float4*>(&wT[wave][lane & 3][tt]);
-        uint32_t lo, hi;
-        uint32_t x1 = 0u;
-        if constexpr (VB == 3) x1 = u4get(vp[4 + pg], k);
-        value_nibbles<VB>(u4get(vp[pg], k), x1, vsh, lo, hi);
-        float b0[4], b1[4];
-        if (VLM) {
+      for (int pg = 0; pg < 4; ++pg) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int tt = pg * 16 + 4 * kk;
+          const uint4 wu = *reinterpret_cast<const uint4*>(&wt[lane & 3][tt]);
+          const float4 w4 = make_float4(__uint_as_float(wu.x), __uint_as_float(wu.y), __uint_as_float(wu.z),
+                                        __uint_as_float(wu.w));
+          uint32_t lo, hi;
+          uint32_t x1 = 0u;
+          if constexpr (VB == 3) x1 = u4get(vp[4 + pg], kk);
+          value_nibbles<VB>(u4get(vp[pg], kk), x1, vsh, lo, hi);
+          float b0[4], b1[4];
           b0[0] = vcb[lo & 0xFF]; b0[1] = vcb[(lo >> 8) & 0xFF]; b0[2] = vcb[(lo >> 16) & 0xFF]; b0[3] = vcb[lo >> 24];
           b1[0] = vcb[hi & 0xFF]; b1[1] = vcb[(hi >> 8) & 0xFF]; b1[2] = vcb[(hi >> 16) & 0xFF]; b1[3] = vcb[hi >> 24];
-        } else {
-          // byte -> float (v_cvt_f32_ubyte0..3)
-          b0[0] = (float)(lo & 0xFF); b0[1] = (float)((lo >> 8) & 0xFF);
-          b0[2] = (float)((lo >> 16) & 0xFF); b0[3] = (float)(lo >> 24);
-          b1[0] = (float)(hi & 0xFF); b1[1] = (float)((hi >> 8) & 0xFF);
-          b1[2] = (float)((hi >> 16) & 0xFF); b1[3] = (float)(hi >> 24);
+          O0 = __builtin_amdgcn_mfma_f32_4x4x1f32(w4.x, b0[0], O0, 0, 0, 0);
+          O1 = __builtin_amdgcn_mfma_f32_4x4x1f32(w4.x, b1[0], O1, 0, 0, 0);
+          O2 = __builtin_amdgcn_mfma_f32_4x4x1f32(w4.y, b0[1], O2, 0, 0, 0);
+          O3 = __builtin_amdgcn_mfma_f32_4x4x1f32(w4.y, b1[1], O3, 0, 0, 0);
+          O0 = __builtin_amdgcn_mfma_f32_4x4x1f32(w4.z, b0[2], O0, 0, 0, 0);
+          O1 = __builtin_amdgcn_mfma_f32_4x4x1f32(w4.z, b1[2], O1, 0, 0, 0);
+          O2 = __builtin_amdgcn_mfma_f32_4x4x1f32(w4.w, b0[3], O2, 0, 0, 0);
+          O3 = __builtin_amdgcn_mfma_f32_4x4x1f32(w4.w, b1[3], O3, 0, 0, 0);
         }
-        O0 = __builtin_amdgcn_mfma_f32_4x4x1f32(w4.x, b0[0], O0, 0, 0, 0);
-        O1 = __builtin_amdgcn_mfma_f32_4x4x1f32(w4.x, b1[0], O1, 0, 0, 0);
-        O2 = __builtin_amdgcn_mfma_f32_4x4x1f32(w4.y, b0[1], O2, 0, 0, 0);
-        O3 = __builtin_amdgcn_mfma_f32_4x4x1f32(w4.y, b1[1], O3, 0, 0, 0);
-        O0 = __builtin_amdgcn_mfma_f32_4x4x1f32(w4.z, b0[2], O0, 0, 0, 0);
-        O1 = __builtin_amdgcn_mfma_f32_4x4x1f32(w4.z, b1[2], O1, 0, 0, 0);
-        O2 = __builtin_amdgcn_mfma_f32_4x4x1f32(w4.w, b0[3], O2, 0, 0, 0);
-        O3 = __builtin_amdgcn_mfma_f32_4x4x1f32(w4.w, b1[3], O3, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);   // keep one page's operands live at a time
       }
-      __builtin_amdgcn_sched_barrier(0);   // keep one page's operands live at a time
+      if (has_next) load_value_planes<VB>(vp, a, pages_of(blk_reg, k + 1), kvh, lane, blk_stride, head_stride);
+    } else {
+      // Uniform values, o_h += sum_t p_t (min_t + scale_t * code_t): the min part is
+      // a per-head scalar (s_lane); the code part is an exact integer product.  The
+      // weights p_t * scale_t become fixed-point integers on a grid shared by the
+      // tile, 2^(E-27) with 2^E just above the tile's largest scale (p <= 1), split
+      // into four 7-bit limbs: rows of the 16x16x64 int8 MFMA are (head, limb),
+      // columns 16 coordinates, and K the tile's 64 tokens.
+      const int E = __builtin_amdgcn_frexp_expf(smax);
+      const float vbs = ldexpf(vb, 27 - E);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) wt[h][lane] = (uint32_t)fmaf(pr[h], vbs, 0.5f);   // round to nearest
+      wave_sync_lds();
+      // A operand: row lane%16 = (head (lane/4)%4, limb lane%4), tokens 16g..16g+15
+      // of page g = lane/16, one per byte.
+      const uint4* wsrc = reinterpret_cast<const uint4*>(&wt[(lane >> 2) & 3][16 * (lane >> 4)]);
+      const uint32_t lsh = 7u * (uint32_t)(lane & 3);
+      const intx4 A = {limb4(wsrc[0], lsh), limb4(wsrc[1], lsh), limb4(wsrc[2], lsh), limb4(wsrc[3], lsh)};
+      const float bsc = ldexpf(1.f, E - 27);
+      const intx4 zero = {0, 0, 0, 0};
+#define TQ_PV(M)                                                                                   \
+      {                                                                                            \
+        const intx4 d = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, value_codes<VB, M>(vq), zero, 0, 0, 0); \
+        const uint32_t u = (uint32_t)d[0] + ((uint32_t)d[1] << 7) + ((uint32_t)d[2] << 14);        \
+        O[M] = fmaf(fmaf((float)d[3], 2097152.f, (float)u), bsc, O[M]);                             \
+      }
+      TQ_PV(0) TQ_PV(1) TQ_PV(2) TQ_PV(3) TQ_PV(4) TQ_PV(5) TQ_PV(6) TQ_PV(7)
+#undef TQ_PV
+      if (has_next) load_value_group<VB>(vq, a, nblk, kvh, lane, blk_stride, head_stride);
     }
-    // value planes of the next tile (its key rows are already on the way)
-    if (tile + 4 < tile_end && (tile + 4) * 64 < tok_end)
-      load_value_planes<VB>(vp, a, pages_of(blk_reg, k + 1), kvh, lane, blk_stride, head_stride);
     wave_sync_lds();
   }
-  O0 += O2;
-  O1 += O3;
 
   // Per-wave totals, then merge the 4 waves of the work-group.
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
     const float lsum = wave_sum(l_lane[h]);
-    const float ssum = VLM ? 0.f : wave_sum(s_lane[h]);
     if (lane == 0) {
       part_ml[wave][h][0] = m_run[h];
       part_ml[wave][h][1] = lsum;
     }
-    part_o[wave][h][2 * lane] = O0[h] + ssum;
-    part_o[wave][h][2 * lane + 1] = O1[h] + ssum;
+  }
+  if constexpr (VLM) {
+    O0 += O2;
+    O1 += O3;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      part_o[wave][h][2 * lane] = O0[h];
+      part_o[wave][h][2 * lane + 1] = O1[h];
+    }
+  } else {
+    float ssum[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) ssum[h] = wave_sum(s_lane[h]);
+    const float sh = ho == 0 ? ssum[0] : ho == 1 ? ssum[1] : ho == 2 ? ssum[2] : ssum[3];
+    float4* dst = reinterpret_cast<float4*>(&part_o[wave][ho][8 * (lane & 15)]);
+    dst[0] = make_float4(O[0] + sh, O[1] + sh, O[2] + sh, O[3] + sh);
+    dst[1] = make_float4(O[4] + sh, O[5] + sh, O[6] + sh, O[7] + sh);
   }
   __syncthreads();
   // Merge the 4 waves: thread (head h = wave, coordinates 2*lane, 2*lane+1).
@@ -464,7 +607,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const float mw = part_ml[w][h][0];
-      const float f = (mw == -INFINITY) ? 0.f : __expf(mw - M);
+      const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       L = fmaf(f, part_ml[w][h][1], L);
       o0 = fmaf(f, part_o[w][h][2 * lane], o0);
       o1 = fmaf(f, part_o[w][h][2 * lane + 1], o1);
@@ -504,7 +647,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
       for (int sp = 0; sp < a.splits; ++sp) {
         const float ms = load_agent(src + sp * stride);
         if (ms != -INFINITY) {
-          const float f = __expf(ms - M);
+          const float f = __builtin_amdgcn_exp2f(ms - M);
           L = fmaf(f, load_agent(src + sp * stride + 1), L);
           o0 = fmaf(f, load_agent(src + sp * stride + 2 + 2 * lane), o0);
           o1 = fmaf(f, load_agent(src + sp * stride + 3 + 2 * lane), o1);
