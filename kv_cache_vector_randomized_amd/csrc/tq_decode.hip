@@ -207,6 +207,33 @@ __device__ __forceinline__ void wave_max5(float& v0, float& v1, float& v2, float
   v4 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v4), 63));
 }
 
+// Wave-wide sums of eight values at once, with the same DPP pattern as
+// wave_max5 (a lane is always combined with a lane of the complementary group,
+// so nothing is counted twice); lane 63 ends with the totals.
+__device__ __forceinline__ void wave_sum8(float (&v)[8]) {
+#define TQ_DPP8(CTL)                                                   \
+  "v_add_f32_dpp %0, %0, %0 " CTL "\n\t"                               \
+  "v_add_f32_dpp %1, %1, %1 " CTL "\n\t"                               \
+  "v_add_f32_dpp %2, %2, %2 " CTL "\n\t"                               \
+  "v_add_f32_dpp %3, %3, %3 " CTL "\n\t"                               \
+  "v_add_f32_dpp %4, %4, %4 " CTL "\n\t"                               \
+  "v_add_f32_dpp %5, %5, %5 " CTL "\n\t"                               \
+  "v_add_f32_dpp %6, %6, %6 " CTL "\n\t"                               \
+  "v_add_f32_dpp %7, %7, %7 " CTL "\n\t"
+  asm volatile("s_nop 1\n\t"
+               TQ_DPP8("quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf")
+               TQ_DPP8("quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf")
+               TQ_DPP8("row_half_mirror row_mask:0xf bank_mask:0xf")
+               TQ_DPP8("row_mirror row_mask:0xf bank_mask:0xf")
+               TQ_DPP8("row_bcast:15 row_mask:0xa bank_mask:0xf")
+               TQ_DPP8("row_bcast:31 row_mask:0xc bank_mask:0xf")
+               "s_nop 1"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
+#undef TQ_DPP8
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 63));
+}
+
 // Value codes of this lane's page and coordinates 8j..8j+7 (j = lane % 16) as
 // the B operand of the int8 MFMA for coordinate 8j + m: one code per byte, byte s
 // of dword w is slot 4w + s of the page.  Codes are packed LSB-first, so within a
@@ -250,13 +277,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // Each wave owns its copy of the rotated query rows and the codebooks, so the
-  // waves never wait for each other before the final merge.  Rows are padded by
-  // 4 words so the 4 heads' 16-byte reads fall in different banks.
-  __shared__ __align__(16) float q_all[4][4][kDim + 4];
-  __shared__ __align__(16) float p_all[QJL ? 4 : 1][QJL ? 4 : 1][kDim + 4];
-  __shared__ __align__(16) float kcb_all[4][16];
-  __shared__ float vcb_all[VLM ? 4 : 1][16];
+  // Shared by the 4 waves: the rotated query rows (each wave rotates one head),
+  // their QJL projections and the codebooks.  Rows are padded by 4 words so the
+  // 4 heads' 16-byte reads fall in different banks.
+  __shared__ __align__(16) float q_sh[4][kDim + 4];
+  __shared__ __align__(16) float p_sh[QJL ? 4 : 1][kDim + 4];
+  __shared__ __align__(16) float kcb[16];
+  __shared__ float vcb[16];
   // per wave and head, the 64 tokens' value weights: fp32 (Lloyd-Max values) or
   // the fixed-point integers fed to the int8 MFMA (uniform values)
   __shared__ __align__(16) uint32_t wT[4][4][68];
@@ -272,17 +299,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int tok_end = min(seq_len, tile_end * 64);
   const int64_t head_stride = a.f.page_bytes;
   const int64_t blk_stride = head_stride * a.hkv;
-
-  float (&q_lds)[4][kDim + 4] = q_all[wave];
-  float (&p_lds)[QJL ? 4 : 1][kDim + 4] = p_all[QJL ? wave : 0];
-  float* vcb = vcb_all[VLM ? wave : 0];
   uint32_t (&wt)[4][68] = wT[wave];
 
-  // Prologue (per wave, no work-group barrier): the block ids of the wave's
-  // pages (lane 4k + pg: page pg of the wave's k-th tile; at most 16 tiles per
-  // wave since tiles_per_split <= 64) and the query rows are fetched together;
-  // the first tile's loads are issued before the query is rotated so that their
-  // latency overlaps the rotation.
+  // Prologue: the block ids of the wave's pages (lane 4k + pg: page pg of the
+  // wave's k-th tile; at most 16 tiles per wave since tiles_per_split <= 64) and
+  // the query row of head `wave` are fetched together; the first tile's loads
+  // are issued before the query is rotated so that their latency overlaps the
+  // rotation and the one work-group barrier.
   int blk_reg = -1;
   {
     const int tl = tile_begin + wave + 4 * (lane >> 2);
@@ -292,29 +315,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       blk_reg = (raw < 0 || (int64_t)raw >= a.num_blocks) ? -1 : raw;
     }
   }
-  if (lane < 16) {
-    kcb_all[wave][lane] = a.c->kc[lane];
-    if (VLM) vcb[lane] = a.c->vc[lane];
-  }
-  float qx[4][2], sg0 = 0.f, sg1 = 0.f;
-#pragma unroll
-  for (int hh = 0; hh < 4; ++hh) {
-    qx[hh][0] = qx[hh][1] = 0.f;
-    if (hh < G) {
-      const int64_t qo = ((int64_t)b * a.hq + (int64_t)kvh * G + hh) * kDim + 2 * lane;
-      if (a.q_dtype == TQ_BF16) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.q) + qo);
-        qx[hh][0] = bf16lo(w);
-        qx[hh][1] = bf16hi(w);
-      } else {
-        const float2 f = *reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + qo);
-        qx[hh][0] = f.x;
-        qx[hh][1] = f.y;
-      }
+  if (wave == 0 && lane < 16) kcb[lane] = a.c->kc[lane];
+  if (VLM && wave == 1 && lane < 16) vcb[lane] = a.c->vc[lane];
+  float qx0 = 0.f, qx1 = 0.f;
+  if (wave < G) {
+    const int64_t qo = ((int64_t)b * a.hq + (int64_t)kvh * G + wave) * kDim + 2 * lane;
+    if (a.q_dtype == TQ_BF16) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.q) + qo);
+      qx0 = bf16lo(w);
+      qx1 = bf16hi(w);
+    } else {
+      const float2 f = *reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + qo);
+      qx0 = f.x;
+      qx1 = f.y;
     }
   }
-  sg0 = a.c->signs[2 * lane];
-  sg1 = a.c->signs[2 * lane + 1];
+  const float sg0 = a.c->signs[2 * lane], sg1 = a.c->signs[2 * lane + 1];
 
   TileRegs<KB, VB> nx;
   uint4 vp[VB == 3 ? 8 : 4];     // Lloyd-Max values: byte planes of coordinates 2*lane, 2*lane+1
@@ -327,50 +343,39 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     else load_value_group<VB>(vq, a, blk, kvh, lane, blk_stride, head_stride);
   }
 
-  // Rotate the group's query heads once: q'' = log2(e) * scale * H(s*q)/sqrt(d),
-  // so that logits come out in base-2 units for exp2.
+  // Rotate query head `wave`: q'' = log2(e) * scale * H(s*q)/sqrt(d), so that the
+  // logits come out in base-2 units for exp2.  Heads >= G stay zero.
   {
+    float x0 = qx0 * sg0, x1 = qx1 * sg1;
+    const float s0 = x0 + x1, d0 = x0 - x1;
+    x0 = s0;
+    x1 = d0;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const float p0 = __shfl_xor(x0, m), p1 = __shfl_xor(x1, m);
+      const bool upper = (lane & m) != 0;
+      x0 = upper ? p0 - x0 : x0 + p0;
+      x1 = upper ? p1 - x1 : x1 + p1;
+    }
     const float f = a.scale * kInvSqrtDim * kLog2e;
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      float x0 = qx[hh][0] * sg0, x1 = qx[hh][1] * sg1;
-      const float s0 = x0 + x1, d0 = x0 - x1;
-      x0 = s0;
-      x1 = d0;
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) {
-        const float p0 = __shfl_xor(x0, m), p1 = __shfl_xor(x1, m);
-        const bool upper = (lane & m) != 0;
-        x0 = upper ? p0 - x0 : x0 + p0;
-        x1 = upper ? p1 - x1 : x1 + p1;
+    q_sh[wave][2 * lane] = x0 * f;
+    q_sh[wave][2 * lane + 1] = x1 * f;
+    if constexpr (QJL) {
+      // p'' = coef * S q''  (coef = sqrt(pi/2)/m): lane computes rows 2*lane, 2*lane+1
+      wave_sync_lds();
+      float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll 8
+      for (int k = 0; k < kDim; ++k) {
+        const float2 sv = *reinterpret_cast<const float2*>(&a.c->St[k * kDim + 2 * lane]);
+        const float qk = q_sh[wave][k];
+        acc0 = fmaf(sv.x, qk, acc0);
+        acc1 = fmaf(sv.y, qk, acc1);
       }
-      q_lds[hh][2 * lane] = x0 * f;
-      q_lds[hh][2 * lane + 1] = x1 * f;
+      p_sh[wave][2 * lane] = acc0 * a.qjl_coef;
+      p_sh[wave][2 * lane + 1] = acc1 * a.qjl_coef;
     }
   }
-  wave_sync_lds();
-  if constexpr (QJL) {
-    // p'' = coef * S q''  (coef = sqrt(pi/2)/m): lane computes rows 2*lane, 2*lane+1
-    float acc[4][2];
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) acc[hh][0] = acc[hh][1] = 0.f;
-#pragma unroll 4
-    for (int k = 0; k < kDim; ++k) {
-      const float2 sv = *reinterpret_cast<const float2*>(&a.c->St[k * kDim + 2 * lane]);
-#pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        const float qk = q_lds[hh][k];
-        acc[hh][0] = fmaf(sv.x, qk, acc[hh][0]);
-        acc[hh][1] = fmaf(sv.y, qk, acc[hh][1]);
-      }
-    }
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      p_lds[hh][2 * lane] = acc[hh][0] * a.qjl_coef;
-      p_lds[hh][2 * lane + 1] = acc[hh][1] * a.qjl_coef;
-    }
-    wave_sync_lds();
-  }
+  __syncthreads();
 
   float m_run[4], l_lane[4], s_lane[4];
 #pragma unroll
@@ -386,8 +391,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // Lloyd-Max values: rows = heads, columns = coordinates 2*lane, 2*lane+1.
   floatx4 O0 = {0.f, 0.f, 0.f, 0.f}, O1 = O0, O2 = O0, O3 = O0;
   const int vsh = (VB == 2) ? 4 * (lane & 1) : (VB == 3) ? ((6 * lane) & 7) : 0;
-  const uint32_t wbase = (uint32_t)wave * 0x40404040u;   // this wave's key table, in every byte
-  const char* cbf = reinterpret_cast<const char*>(&kcb_all[0][0]);
+  const char* cbf = reinterpret_cast<const char*>(&kcb[0]);
   const int ho = lane >> 4;                              // head of this lane's value outputs
 
   for (int k = 0; tile < tile_end && tile * 64 < tok_end; tile += 4, ++k) {
@@ -404,14 +408,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     floatx4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0;
     if constexpr (KB == 4) {
       // Two masks per 32-bit word put its eight codes, multiplied by 4 (the table
-      // stride) and offset to this wave's table, into byte lanes; each code then
-      // costs one byte extract.
+      // stride), into byte lanes; each code then costs one byte extract.
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const uint32_t e = ((nx.kw[j] << 2) & 0x3C3C3C3Cu) | wbase;   // codes 8j, 8j+2, 8j+4, 8j+6
-        const uint32_t o = ((nx.kw[j] >> 2) & 0x3C3C3C3Cu) | wbase;   // codes 8j+1, 8j+3, 8j+5, 8j+7
-        const float4 qa = *reinterpret_cast<const float4*>(&q_lds[lane & 3][8 * j]);
-        const float4 qb = *reinterpret_cast<const float4*>(&q_lds[lane & 3][8 * j + 4]);
+        uint32_t e = (nx.kw[j] << 2) & 0x3C3C3C3Cu;   // codes 8j, 8j+2, 8j+4, 8j+6
+        uint32_t o = (nx.kw[j] >> 2) & 0x3C3C3C3Cu;   // codes 8j+1, 8j+3, 8j+5, 8j+7
+        // keep the two masked words: folding the masks into each byte extract
+        // would cost two instructions per code instead of one
+        asm volatile("" : "+v"(e), "+v"(o));
+        const float4 qa = *reinterpret_cast<const float4*>(&q_sh[lane & 3][8 * j]);
+        const float4 qb = *reinterpret_cast<const float4*>(&q_sh[lane & 3][8 * j + 4]);
         c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(qa.x, *(const float*)(cbf + (e & 0xFF)), c0, 0, 0, 0);
         c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(qa.y, *(const float*)(cbf + (o & 0xFF)), c1, 0, 0, 0);
         c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(qa.z, *(const float*)(cbf + ((e >> 8) & 0xFF)), c0, 0, 0, 0);
@@ -423,14 +429,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         if ((j & 1) == 1) __builtin_amdgcn_sched_barrier(0);   // bound the look-ups in flight
       }
     } else {
-      const uint32_t w64 = (uint32_t)wave * 64u;
 #pragma unroll
       for (int i = 0; i < kDim; i += 4) {
-        const float4 q4 = *reinterpret_cast<const float4*>(&q_lds[lane & 3][i]);
-        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.x, *(const float*)(cbf + ((get_code<KB>(nx.kw, i) << 2) | w64)), c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.y, *(const float*)(cbf + ((get_code<KB>(nx.kw, i + 1) << 2) | w64)), c1, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.z, *(const float*)(cbf + ((get_code<KB>(nx.kw, i + 2) << 2) | w64)), c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.w, *(const float*)(cbf + ((get_code<KB>(nx.kw, i + 3) << 2) | w64)), c1, 0, 0, 0);
+        const float4 q4 = *reinterpret_cast<const float4*>(&q_sh[lane & 3][i]);
+        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.x, *(const float*)(cbf + (get_code<KB>(nx.kw, i) << 2)), c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.y, *(const float*)(cbf + (get_code<KB>(nx.kw, i + 1) << 2)), c1, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.z, *(const float*)(cbf + (get_code<KB>(nx.kw, i + 2) << 2)), c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.w, *(const float*)(cbf + (get_code<KB>(nx.kw, i + 3) << 2)), c1, 0, 0, 0);
         if ((i & 15) == 12) __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -441,7 +446,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       const uint32_t sgw[4] = {nx.sg.x, nx.sg.y, nx.sg.z, nx.sg.w};
 #pragma unroll
       for (int i = 0; i < kDim; i += 2) {
-        const float2 p2 = *reinterpret_cast<const float2*>(&p_lds[lane & 3][i]);
+        const float2 p2 = *reinterpret_cast<const float2*>(&p_sh[lane & 3][i]);
         const float s0 = ((sgw[i >> 5] >> (i & 31)) & 1u) ? 1.f : -1.f;
         const float s1 = ((sgw[(i + 1) >> 5] >> ((i + 1) & 31)) & 1u) ? 1.f : -1.f;
         d0 = __builtin_amdgcn_mfma_f32_4x4x1f32(p2.x, s0, d0, 0, 0, 0);
@@ -572,12 +577,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
 
   // Per-wave totals, then merge the 4 waves of the work-group.
+  float tot[8] = {l_lane[0], l_lane[1], l_lane[2], l_lane[3], s_lane[0], s_lane[1], s_lane[2], s_lane[3]};
+  wave_sum8(tot);
+  if (lane == 0) {
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const float lsum = wave_sum(l_lane[h]);
-    if (lane == 0) {
+    for (int h = 0; h < 4; ++h) {
       part_ml[wave][h][0] = m_run[h];
-      part_ml[wave][h][1] = lsum;
+      part_ml[wave][h][1] = tot[h];
     }
   }
   if constexpr (VLM) {
@@ -589,10 +595,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       part_o[wave][h][2 * lane + 1] = O1[h];
     }
   } else {
-    float ssum[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) ssum[h] = wave_sum(s_lane[h]);
-    const float sh = ho == 0 ? ssum[0] : ho == 1 ? ssum[1] : ho == 2 ? ssum[2] : ssum[3];
+    const float sh = ho == 0 ? tot[4] : ho == 1 ? tot[5] : ho == 2 ? tot[6] : tot[7];
     float4* dst = reinterpret_cast<float4*>(&part_o[wave][ho][8 * (lane & 15)]);
     dst[0] = make_float4(O[0] + sh, O[1] + sh, O[2] + sh, O[3] + sh);
     dst[1] = make_float4(O[4] + sh, O[5] + sh, O[6] + sh, O[7] + sh);
@@ -702,7 +705,28 @@ hipError_t decode_vb(const DecodeArgs& a, int val_bits, int val_mode, hipStream_
   return hipErrorInvalidValue;
 }
 
+template <int KB, bool QJL>
+const void* kernel_vb(int val_bits, int val_mode) {
+  const bool lm = val_mode == TQ_VAL_LLOYD;
+  switch (val_bits) {
+    case 2: return lm ? (const void*)decode_kernel<KB, QJL, 2, true> : (const void*)decode_kernel<KB, QJL, 2, false>;
+    case 3: return lm ? (const void*)decode_kernel<KB, QJL, 3, true> : (const void*)decode_kernel<KB, QJL, 3, false>;
+    case 4: return lm ? (const void*)decode_kernel<KB, QJL, 4, true> : (const void*)decode_kernel<KB, QJL, 4, false>;
+  }
+  return nullptr;
+}
+
 }  // namespace
+
+const void* decode_kernel_ptr(int key_bits, int key_mode, int val_bits, int val_mode) {
+  const bool qjl = key_mode == TQ_KEY_LLOYD_QJL;
+  switch (key_bits) {
+    case 2: return qjl ? kernel_vb<2, true>(val_bits, val_mode) : kernel_vb<2, false>(val_bits, val_mode);
+    case 3: return qjl ? kernel_vb<3, true>(val_bits, val_mode) : kernel_vb<3, false>(val_bits, val_mode);
+    case 4: return qjl ? kernel_vb<4, true>(val_bits, val_mode) : kernel_vb<4, false>(val_bits, val_mode);
+  }
+  return nullptr;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int key_bits, int key_mode, int val_bits, int val_mode,
                          hipStream_t s) {

@@ -19,6 +19,7 @@ struct tq_ctx {
   uint32_t sign_bits[4];
   tq::DevConsts* consts;   // device
   float klut_scale, klut_bias, vlut_scale, vlut_bias;
+  int decode_wgs;          // decode grid target: resident work-groups on the whole device
 };
 
 namespace {
@@ -161,11 +162,13 @@ tq::FieldOffsets offsets_of(const tq_layout& L) {
 }
 
 // Split the context of every (sequence, kv head) into pieces of whole 64-token
-// tiles so that the grid has about 1024 work-groups (4 per CU on 256 CUs).
-void plan_splits(int batch, int hkv, int max_seq, int* splits, int* tiles_per_split) {
+// tiles so that the grid is about one round of resident work-groups (`target`,
+// from the kernel's occupancy): more, shorter splits only add prologues and
+// merges, fewer leave SIMDs idle.
+void plan_splits(int target, int batch, int hkv, int max_seq, int* splits, int* tiles_per_split) {
   const int tiles = std::max(1, (max_seq + 63) / 64);
   const int pairs = std::max(1, batch * hkv);
-  int want = (1024 + pairs - 1) / pairs;
+  int want = (target + pairs - 1) / pairs;
   want = std::max(1, std::min(want, (tiles + 3) / 4));      // >= 4 tiles per split
   int tps = (tiles + want - 1) / want;
   tps = std::min(tps, tq::kMaxPagesPerSplit / 4);
@@ -283,6 +286,18 @@ tq_status tq_create(const tq_config* cfg, const int8_t* signs_host, const float*
   e = hipMemcpy(ctx->consts, h, sizeof(tq::DevConsts), hipMemcpyHostToDevice);
   delete h;
   if (e != hipSuccess) { hipFree(ctx->consts); delete ctx; return hip_fail(e, "hipMemcpy"); }
+  // One round of resident decode work-groups on this device.
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, tq::decode_kernel_ptr((int)cfg->key_bits, (int)cfg->key_mode, (int)cfg->val_bits,
+                                         (int)cfg->val_mode),
+          256, 0) != hipSuccess ||
+      per_cu <= 0)
+    per_cu = 2;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, ctx->device) != hipSuccess || cus <= 0)
+    cus = 256;
+  (void)hipGetLastError();
+  ctx->decode_wgs = per_cu * cus;
   *out = ctx;
   return TQ_OK;
 }
@@ -328,7 +343,7 @@ tq_status tq_quantize_append(tq_ctx* ctx, const void* k, const void* v, tq_dtype
 size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t max_seq_len) {
   if (!ctx || batch <= 0 || max_seq_len < 0) return 0;
   int splits, tps;
-  plan_splits(batch, (int)ctx->cfg.num_kv_heads, max_seq_len, &splits, &tps);
+  plan_splits(ctx->decode_wgs, batch, (int)ctx->cfg.num_kv_heads, max_seq_len, &splits, &tps);
   return tq::kCounterBytes +
          (size_t)batch * ctx->cfg.num_kv_heads * splits * tq::kMaxGroup * (2 + tq::kDim) * sizeof(float);
 }
@@ -363,7 +378,7 @@ tq_status tq_decode_attention(tq_ctx* ctx, const void* q, tq_dtype dt, const voi
   a.logits = logits_out; a.out = out;
   a.counters = (uint32_t*)workspace;
   a.ws = (float*)((uint8_t*)workspace + tq::kCounterBytes);
-  plan_splits(batch, a.hkv, max_seq_len, &a.splits, &a.tiles_per_split);
+  plan_splits(ctx->decode_wgs, batch, a.hkv, max_seq_len, &a.splits, &a.tiles_per_split);
   a.f = offsets_of(ctx->layout); a.c = ctx->consts;
   hipError_t e = tq::launch_decode(a, (int)ctx->cfg.key_bits, (int)ctx->cfg.key_mode, (int)ctx->cfg.val_bits,
                                    (int)ctx->cfg.val_mode, stream);

@@ -99,6 +99,8 @@ struct DequantArgs {
 // Launchers (tq_kernels.hip).  Return hipSuccess or the launch error.
 hipError_t launch_append(const AppendArgs& a, int dtype, int key_bits, int key_mode, int val_bits,
                          int val_mode, hipStream_t s);
+// Address of the decode kernel instance for a configuration (for occupancy queries).
+const void* decode_kernel_ptr(int key_bits, int key_mode, int val_bits, int val_mode);
 hipError_t launch_decode(const DecodeArgs& a, int key_bits, int key_mode, int val_bits, int val_mode,
                          hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, int key_bits, int key_mode, int val_bits, int val_mode,
