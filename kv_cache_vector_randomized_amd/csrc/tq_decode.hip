@@ -6,29 +6,42 @@
 // be fused over the compressed cache); lilting.ch TurboQuant article, QJL section
 // (query kept in full precision, projected with the same S; corrected score).
 //
-// One work-group per (split of the context, kv head, sequence); each wave owns
-// 64-token tiles (4 pages).  Lane l holds token l's packed key row (prefetched one
-// tile ahead); codes become centroids through a 16-entry LDS table and are
-// contracted with the group's 4 rotated query heads on the fp32 4x4x1 (16-block)
-// MFMA, which keeps exact fp32 products.  Value codes are stored plane-major in a
-// page (byte p of the 16 slots is contiguous), so lane l loads the byte plane of
-// its two coordinates for 16 tokens with one coalesced 16-byte load per page and
-// converts four tokens per 32-bit word.  The online softmax runs per lane; the
-// weights are contracted with the value codes on the same MFMA.  Per-split
-// partials (max, sum, 128 outputs) go to the workspace; the last work-group of
-// each (sequence, kv head) to finish, found with a self-resetting arrival
-// counter, merges them by log-sum-exp and writes the output.
+// One work-group of 4 waves per (split of the context, kv head, sequence); each
+// wave owns 64-token tiles (4 pages of 16 tokens).
+//
+// Logits: per tile, rows = (query head, term of the query), columns = 16 tokens
+// of one page, K = 32 coordinates, on the f16 16x16x32 MFMA.  The rotated query
+// and the centroids are each split into f16 terms (query: three, codebook: two,
+// both scaled by powers of two into f16's normal range), so the products carry
+// about 22 significant bits; the fp32 accumulation keeps them.  Lane (j, g) of
+// the B operand holds coordinates 32g..32g+31 of token j, one 16-byte load per
+// page, and turns each byte of codes into the f16 centroid pair of both terms
+// with one table read.  The MFMA output leaves head l/16 in the row of lanes l,
+// so the running max, the sums and the output rows of a head stay in one row of
+// 16 lanes.
+//
+// Values (uniform): sum_t p_t (min_t + scale_t * code_t).  The min part is a
+// per-head scalar; the code part is an exact integer product on the int8 16x16x64
+// MFMA: per tile the weights p_t * scale_t go on a fixed-point grid tied to the
+// tile's largest scale, split into four 7-bit limbs (rows = head x limb, columns
+// = coordinates, K = the tile's 64 tokens).  Value codes are plane-major in a
+// page, so lane l loads the planes of coordinates 8j..8j+7 (j = l%16) of page
+// l/16 with contiguous 16-byte loads.  Lloyd-Max values are accumulated on the
+// fp32 4x4x1 MFMA in the rotated basis and rotated back once at the end.
+//
+// Per-split partials (max, sum, 128 outputs) go to the workspace; the last
+// work-group of each (sequence, kv head) to finish, found with a self-resetting
+// arrival counter, merges them by log-sum-exp and writes the output.
 #include <hip/hip_runtime.h>
 
 #include "tq_device.h"
 
 namespace tq {
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
-}
+typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -43,21 +56,186 @@ __device__ __forceinline__ float load_agent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wave-wide max: DPP within rows of 16 lanes, then the four row results.
-// Rows outside ROW_MASK keep their own value, which is neutral for max.
+// Wave-wide max (prologue only): DPP within rows of 16 lanes, then the row
+// broadcasts; rows outside ROW_MASK keep their own value, neutral for max.
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(
       __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
 }
-__device__ __forceinline__ float wave_max_dpp(float v) {
+__device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp<0xB1, 0xF>(v));    // quad_perm [1,0,3,2]
   v = fmaxf(v, dpp<0x4E, 0xF>(v));    // quad_perm [2,3,0,1]
   v = fmaxf(v, dpp<0x141, 0xF>(v));   // row_half_mirror
-  v = fmaxf(v, dpp<0x140, 0xF>(v));   // row_mirror: every lane of a row holds the row max
-  v = fmaxf(v, dpp<0x142, 0xA>(v));   // row_bcast:15 into rows 1 and 3
-  v = fmaxf(v, dpp<0x143, 0xC>(v));   // row_bcast:31 into rows 2 and 3: lane 63 holds the max
+  v = fmaxf(v, dpp<0x140, 0xF>(v));   // row_mirror
+  v = fmaxf(v, dpp<0x142, 0xA>(v));   // row_bcast:15
+  v = fmaxf(v, dpp<0x143, 0xC>(v));   // row_bcast:31
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Reductions of two values within each row of 16 lanes: every lane of a row ends
+// with its row's result.  Each step pairs a lane with one of the complementary
+// group (quad swaps, half-row mirror, row mirror), so nothing is counted twice.
+// The s_nop instructions cover the DPP read-after-VALU-write hazard.
+#define TQ_ROW2(OP, CTL) OP " %0, %0, %0 " CTL "\n\t" OP " %1, %1, %1 " CTL "\n\ts_nop 0\n\t"
+#define TQ_ROW2_ALL(OP)                                                     \
+  "s_nop 1\n\t" TQ_ROW2(OP, "quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf") \
+      TQ_ROW2(OP, "quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf")           \
+          TQ_ROW2(OP, "row_half_mirror row_mask:0xf bank_mask:0xf")           \
+              TQ_ROW2(OP, "row_mirror row_mask:0xf bank_mask:0xf")
+__device__ __forceinline__ void row_max2(float& a, float& b) {
+  asm volatile(TQ_ROW2_ALL("v_max_f32_dpp") : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void row_sum2(float& a, float& b) {
+  asm volatile(TQ_ROW2_ALL("v_add_f32_dpp") : "+v"(a), "+v"(b));
+}
+#undef TQ_ROW2_ALL
+#undef TQ_ROW2
+
+// Byte BYTE of x shifted left by SH, in one instruction (sub-dword operand select).
+template <int SH, int BYTE>
+__device__ __forceinline__ uint32_t byte_shl(uint32_t x) {
+  uint32_t r;
+  asm("v_lshlrev_b32_sdwa %0, %2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_%3"
+      : "=v"(r)
+      : "v"(x), "i"(SH), "i"(BYTE));
+  return r;
+}
+
+__device__ __forceinline__ uint32_t f16bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+// x = hi + lo (+ lo2) in f16, each term the rounding of what the previous left
+__device__ __forceinline__ void split_f16(float x, float& hi, float& lo, float& lo2) {
+  hi = (float)(_Float16)x;
+  const float r = x - hi;
+  lo = (float)(_Float16)r;
+  lo2 = (float)(_Float16)(r - lo);
+}
+
+__device__ __forceinline__ floatx4 mfma_f16(const uint4& a, const uint4& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c, 0, 0,
+                                                0);
+}
+
+__device__ __forceinline__ uint32_t u4get(const uint4& v, int k) {
+  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+
+// Block ids of the 4 pages of one tile (wave-uniform; -1: absent or out of range).
+struct TilePages {
+  int b[4];
+};
+
+// The wave keeps the block ids of all its tiles in one register: lane 4k + pg
+// holds page pg of the wave's k-th tile.  lane_block returns the block id of the
+// page that lane `lane` reads in the k-th tile (lanes 16*pg .. 16*pg+15 read page
+// pg), fetched across lanes without a branch.
+__device__ __forceinline__ int lane_block(int blk_reg, int k, int lane) {
+  return __builtin_amdgcn_ds_bpermute((4 * k + (lane >> 4)) << 2, blk_reg);
+}
+
+__device__ __forceinline__ TilePages pages_of(int blk_reg, int k) {
+  TilePages p;
+#pragma unroll
+  for (int pg = 0; pg < 4; ++pg) p.b[pg] = __builtin_amdgcn_readlane(blk_reg, 4 * k + pg);
+  return p;
+}
+
+// Loads are unconditional: an absent page (block id -1) reads block 0 in its
+// place and the lanes of absent pages and of tokens past the end are masked
+// after the loads, which keeps the load path free of branches.  The caller
+// guarantees num_blocks >= 1.
+__device__ __forceinline__ int64_t page_offset(int blk, int kvh, int64_t blk_stride, int64_t head_stride) {
+  return (int64_t)(blk >= 0 ? blk : 0) * blk_stride + kvh * head_stride;
+}
+
+// Key data of one tile for lane (j = lane%16, g = lane/16): for each page pg of
+// the tile, bytes 4*KB*g .. 4*KB*g + 4*KB - 1 of token j's code row (coordinates
+// 32g..32g+31) and token j's scalars.  Every load of one page is wave-uniform in
+// its page, so the page address stays scalar.
+template <int KB, bool QJL>
+struct KeyTile {
+  uint32_t kc[4][KB];
+  uint32_t sg[4];      // QJL: dword g of token j's sign row (coordinates 32g..32g+31)
+  float knorm[4], va[4], vb[4], kres[4];
+};
+
+template <int KB, bool QJL, bool VLM>
+__device__ __forceinline__ void load_keys(KeyTile<KB, QJL>& r, const DecodeArgs& a, const TilePages& tp, int kvh,
+                                          int lane, int64_t blk_stride, int64_t head_stride) {
+  const int j = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int pg = 0; pg < 4; ++pg) {
+    const uint8_t* page = a.cache + page_offset(tp.b[pg], kvh, blk_stride, head_stride);
+    const uint8_t* row = page + a.f.kcodes + j * (16 * KB) + g * (4 * KB);
+    if constexpr (KB == 4) {
+      const uint4 u = *reinterpret_cast<const uint4*>(row);
+      r.kc[pg][0] = u.x; r.kc[pg][1] = u.y; r.kc[pg][2] = u.z; r.kc[pg][3] = u.w;
+    } else if constexpr (KB == 2) {
+      const uint2 u = *reinterpret_cast<const uint2*>(row);
+      r.kc[pg][0] = u.x; r.kc[pg][1] = u.y;
+    } else {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(row);
+      r.kc[pg][0] = w[0]; r.kc[pg][1] = w[1]; r.kc[pg][2] = w[2];
+    }
+    r.knorm[pg] = reinterpret_cast<const float*>(page + a.f.knorm)[j];
+    r.va[pg] = reinterpret_cast<const float*>(page + a.f.vmin)[j];
+    r.vb[pg] = VLM ? 0.f : reinterpret_cast<const float*>(page + a.f.vscale)[j];
+    if constexpr (QJL) {
+      r.sg[pg] = reinterpret_cast<const uint32_t*>(page + a.f.ksigns + 16 * j)[g];
+      r.kres[pg] = reinterpret_cast<const float*>(page + a.f.kres)[j];
+    } else {
+      r.sg[pg] = 0u;
+      r.kres[pg] = 0.f;
+    }
+  }
+}
+
+// Uniform values: lane l loads, from page l/16 of the tile, the byte planes of
+// coordinates 8j..8j+7 (j = l%16): VB planes of 16 slots, contiguous in the page.
+template <int VB>
+__device__ __forceinline__ void load_value_group(uint4 (&vq)[VB], const DecodeArgs& a, int blk, int kvh, int lane,
+                                                 int64_t blk_stride, int64_t head_stride) {
+  const uint4* src = reinterpret_cast<const uint4*>(a.cache + page_offset(blk, kvh, blk_stride, head_stride) +
+                                                    a.f.vcodes + 16 * VB * (lane & 15));
+#pragma unroll
+  for (int i = 0; i < VB; ++i) vq[i] = src[i];
+}
+
+// Centroid table of the key codes: for each byte of codes (KB = 4: two codes;
+// KB = 3: a 6-bit pair; KB = 2: four codes), the f16 terms (hi, lo) of C * 2^s of
+// each code in coordinate order, hi first.  Interleaving the terms along K lets
+// one MFMA add both terms of the centroid: the query terms are duplicated to
+// match (see qd below).
+template <int KB>
+struct KeyTable {
+  static constexpr int kEntries = KB == 3 ? 64 : 256;
+  static constexpr int kWords = KB == 2 ? 4 : 2;
+};
+
+// B operand of the logits MFMA for coordinates 32g + 4*KAP .. 32g + 4*KAP + 3 of
+// this lane's chunk (K = coordinate x term, 8 halves).
+template <int KB, int KAP>
+__device__ __forceinline__ uint4 key_operand(const uint32_t (&kc)[KB], const uint32_t* tab) {
+  const char* t = reinterpret_cast<const char*>(tab);
+  if constexpr (KB == 4) {
+    const uint32_t x = kc[KAP >> 1];
+    const uint2 e0 = *reinterpret_cast<const uint2*>(t + byte_shl<3, 2 * (KAP & 1)>(x));
+    const uint2 e1 = *reinterpret_cast<const uint2*>(t + byte_shl<3, 2 * (KAP & 1) + 1>(x));
+    return make_uint4(e0.x, e0.y, e1.x, e1.y);
+  } else if constexpr (KB == 2) {
+    return *reinterpret_cast<const uint4*>(t + byte_shl<4, KAP & 3>(kc[KAP >> 2]));
+  } else {
+    // 12 bits per group of 4 codes: bits 12*KAP .. 12*KAP + 11 of the chunk
+    constexpr int bit = 12 * KAP, w = bit >> 5, sh = bit & 31;
+    uint32_t v;
+    if constexpr (sh + 12 <= 32) v = kc[w] >> sh;
+    else v = __builtin_amdgcn_alignbit(kc[w + 1], kc[w], sh);
+    const uint2 e0 = *reinterpret_cast<const uint2*>(t + ((v << 3) & 0x1F8u));
+    const uint2 e1 = *reinterpret_cast<const uint2*>(t + ((v >> 3) & 0x1F8u));
+    return make_uint4(e0.x, e0.y, e1.x, e1.y);
+  }
 }
 
 // Value codes of coordinates 2*lane, 2*lane+1 for the four tokens of one 32-bit
@@ -81,65 +259,6 @@ __device__ __forceinline__ void value_nibbles(uint32_t x0, uint32_t x1, int sh, 
   }
 }
 
-template <int KB, int VB>
-struct TileRegs {
-  uint32_t kw[KB * 4];          // this lane's key row
-  float knorm, va, vb, kres;
-  uint4 sg;
-};
-
-// Block ids of the 4 pages of one tile (wave-uniform; -1: absent or out of range).
-struct TilePages {
-  int b[4];
-};
-
-// The wave keeps the block ids of all its tiles in one register: lane 4k + pg
-// holds page pg of the wave's k-th tile.  lane_block returns the block id of the
-// page that lane `lane` reads in the k-th tile (lanes 16*pg .. 16*pg+15 read page
-// pg), fetched across lanes without a branch.
-__device__ __forceinline__ int lane_block(int blk_reg, int k, int lane) {
-  return __builtin_amdgcn_ds_bpermute((4 * k + (lane >> 4)) << 2, blk_reg);
-}
-
-__device__ __forceinline__ TilePages pages_of(int blk_reg, int k) {
-  TilePages p;
-#pragma unroll
-  for (int pg = 0; pg < 4; ++pg) p.b[pg] = __builtin_amdgcn_readlane(blk_reg, 4 * k + pg);
-  return p;
-}
-
-// Loads of one 64-token tile (4 pages of one kv head).  Loads are unconditional:
-// an absent page (block id -1) reads block 0 in its place and the lanes of
-// absent pages and of tokens past the end are masked after the loads, which
-// keeps the load path free of branches.  The caller guarantees num_blocks >= 1.
-__device__ __forceinline__ int64_t page_offset(int blk, int kvh, int64_t blk_stride, int64_t head_stride) {
-  return (int64_t)(blk >= 0 ? blk : 0) * blk_stride + kvh * head_stride;
-}
-
-template <int KB, bool QJL, int VB, bool VLM>
-__device__ __forceinline__ void load_tile(TileRegs<KB, VB>& r, const DecodeArgs& a, int blk, int kvh, int lane,
-                                          int64_t blk_stride, int64_t head_stride) {
-  constexpr int KROW = kDim * KB / 8;
-  const uint8_t* page = a.cache + page_offset(blk, kvh, blk_stride, head_stride);
-  const int so = lane & 15;
-  const uint4* src = reinterpret_cast<const uint4*>(page + a.f.kcodes + so * KROW);
-#pragma unroll
-  for (int j = 0; j < KB; ++j) {
-    const uint4 u = src[j];
-    r.kw[4 * j] = u.x; r.kw[4 * j + 1] = u.y; r.kw[4 * j + 2] = u.z; r.kw[4 * j + 3] = u.w;
-  }
-  r.knorm = reinterpret_cast<const float*>(page + a.f.knorm)[so];
-  r.va = reinterpret_cast<const float*>(page + a.f.vmin)[so];
-  r.vb = VLM ? 0.f : reinterpret_cast<const float*>(page + a.f.vscale)[so];
-  if (QJL) {
-    r.sg = reinterpret_cast<const uint4*>(page + a.f.ksigns)[so];
-    r.kres = reinterpret_cast<const float*>(page + a.f.kres)[so];
-  } else {
-    r.sg = make_uint4(0u, 0u, 0u, 0u);
-    r.kres = 0.f;
-  }
-}
-
 // Lloyd-Max values: byte plane(s) of this lane's two coordinates for the tile's
 // 4 pages (16 tokens per page, one coalesced 16-byte load per page and plane).
 template <int VB>
@@ -155,83 +274,6 @@ __device__ __forceinline__ void load_value_planes(uint4 (&vp)[VB == 3 ? 8 : 4], 
     vp[pg] = *reinterpret_cast<const uint4*>(vbase + p0 * 16);
     if constexpr (VB == 3) vp[4 + pg] = *reinterpret_cast<const uint4*>(vbase + p1 * 16);
   }
-}
-
-__device__ __forceinline__ uint32_t u4get(const uint4& v, int k) {
-  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
-}
-
-// Uniform values: lane l loads, from page l/16 of the tile, the byte planes of
-// coordinates 8j..8j+7 (j = l%16): VB planes of 16 slots, contiguous in the page.
-template <int VB>
-__device__ __forceinline__ void load_value_group(uint4 (&vq)[VB], const DecodeArgs& a, int blk, int kvh, int lane,
-                                                 int64_t blk_stride, int64_t head_stride) {
-  const uint4* src = reinterpret_cast<const uint4*>(a.cache + page_offset(blk, kvh, blk_stride, head_stride) +
-                                                    a.f.vcodes + 16 * VB * (lane & 15));
-#pragma unroll
-  for (int i = 0; i < VB; ++i) vq[i] = src[i];
-}
-
-typedef int intx4 __attribute__((ext_vector_type(4)));
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-
-// Wave-wide maxima of five values at once.  Each DPP step combines a lane with
-// another lane of its row (quad swaps, half-row and row mirrors), then the row
-// broadcasts carry row 0 into row 1, row 2 into row 3 and rows 0-1 into rows
-// 2-3, so lane 63 ends with the maximum.  The five reductions are interleaved,
-// so every DPP source was written at least four instructions earlier (the DPP
-// read-after-write hazard needs two); the leading s_nop covers the producers.
-__device__ __forceinline__ void wave_max5(float& v0, float& v1, float& v2, float& v3, float& v4) {
-#define TQ_DPP5(CTL)                                                   \
-  "v_max_f32_dpp %0, %0, %0 " CTL "\n\t"                               \
-  "v_max_f32_dpp %1, %1, %1 " CTL "\n\t"                               \
-  "v_max_f32_dpp %2, %2, %2 " CTL "\n\t"                               \
-  "v_max_f32_dpp %3, %3, %3 " CTL "\n\t"                               \
-  "v_max_f32_dpp %4, %4, %4 " CTL "\n\t"
-  asm volatile("s_nop 1\n\t"
-               TQ_DPP5("quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf")
-               TQ_DPP5("quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf")
-               TQ_DPP5("row_half_mirror row_mask:0xf bank_mask:0xf")
-               TQ_DPP5("row_mirror row_mask:0xf bank_mask:0xf")
-               TQ_DPP5("row_bcast:15 row_mask:0xa bank_mask:0xf")
-               TQ_DPP5("row_bcast:31 row_mask:0xc bank_mask:0xf")
-               "s_nop 1"
-               : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3), "+v"(v4));
-#undef TQ_DPP5
-  v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v0), 63));
-  v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v1), 63));
-  v2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v2), 63));
-  v3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v3), 63));
-  v4 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v4), 63));
-}
-
-// Wave-wide sums of eight values at once, with the same DPP pattern as
-// wave_max5 (a lane is always combined with a lane of the complementary group,
-// so nothing is counted twice); lane 63 ends with the totals.
-__device__ __forceinline__ void wave_sum8(float (&v)[8]) {
-#define TQ_DPP8(CTL)                                                   \
-  "v_add_f32_dpp %0, %0, %0 " CTL "\n\t"                               \
-  "v_add_f32_dpp %1, %1, %1 " CTL "\n\t"                               \
-  "v_add_f32_dpp %2, %2, %2 " CTL "\n\t"                               \
-  "v_add_f32_dpp %3, %3, %3 " CTL "\n\t"                               \
-  "v_add_f32_dpp %4, %4, %4 " CTL "\n\t"                               \
-  "v_add_f32_dpp %5, %5, %5 " CTL "\n\t"                               \
-  "v_add_f32_dpp %6, %6, %6 " CTL "\n\t"                               \
-  "v_add_f32_dpp %7, %7, %7 " CTL "\n\t"
-  asm volatile("s_nop 1\n\t"
-               TQ_DPP8("quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf")
-               TQ_DPP8("quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf")
-               TQ_DPP8("row_half_mirror row_mask:0xf bank_mask:0xf")
-               TQ_DPP8("row_mirror row_mask:0xf bank_mask:0xf")
-               TQ_DPP8("row_bcast:15 row_mask:0xa bank_mask:0xf")
-               TQ_DPP8("row_bcast:31 row_mask:0xc bank_mask:0xf")
-               "s_nop 1"
-               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
-#undef TQ_DPP8
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 63));
 }
 
 // Value codes of this lane's page and coordinates 8j..8j+7 (j = lane % 16) as
@@ -276,14 +318,21 @@ template <int KB, bool QJL, int VB, bool VLM>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j16 = lane & 15, grp = lane >> 4;   // column (token of a page) and row group (head) of the lane
 
-  // Shared by the 4 waves: the rotated query rows (each wave rotates one head),
-  // their QJL projections and the codebooks.  Rows are padded by 4 words so the
-  // 4 heads' 16-byte reads fall in different banks.
-  __shared__ __align__(16) float q_sh[4][kDim + 4];
-  __shared__ __align__(16) float p_sh[QJL ? 4 : 1][kDim + 4];
-  __shared__ __align__(16) float kcb[16];
+  using Tab = KeyTable<KB>;
+  // Shared by the 4 waves: the f16 terms of the rotated query rows ([head][term]
+  // [coordinate], each half duplicated into both halves of a word to meet the
+  // two centroid terms; the 4th term is zero) and of their QJL projections
+  // ([head][term][coordinate pair]), the key centroid table, the sign table, the
+  // fp32 query rows (QJL only) and the Lloyd-Max value codebook.
+  __shared__ __align__(16) uint32_t qd[4][4][132];
+  __shared__ __align__(16) uint32_t pt[QJL ? 4 : 1][4][68];
+  __shared__ __align__(16) uint32_t ktab[Tab::kEntries * Tab::kWords];
+  __shared__ __align__(16) uint4 stab[QJL ? 256 : 1];
+  __shared__ __align__(16) float q_sh[QJL ? 4 : 1][kDim + 4];
   __shared__ float vcb[16];
+  __shared__ int qexp[4], pexp[4];
   // per wave and head, the 64 tokens' value weights: fp32 (Lloyd-Max values) or
   // the fixed-point integers fed to the int8 MFMA (uniform values)
   __shared__ __align__(16) uint32_t wT[4][4][68];
@@ -301,11 +350,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int64_t blk_stride = head_stride * a.hkv;
   uint32_t (&wt)[4][68] = wT[wave];
 
-  // Prologue: the block ids of the wave's pages (lane 4k + pg: page pg of the
-  // wave's k-th tile; at most 16 tiles per wave since tiles_per_split <= 64) and
-  // the query row of head `wave` are fetched together; the first tile's loads
-  // are issued before the query is rotated so that their latency overlaps the
-  // rotation and the one work-group barrier.
+  // ---- Prologue.  The block ids of the wave's pages (lane 4k + pg: page pg of
+  // the wave's k-th tile; at most 16 tiles per wave since tiles_per_split <= 64)
+  // and the query row of head `wave` are fetched together; the first tile's
+  // loads are issued before the query is rotated, so their latency overlaps the
+  // rotation, the tables and the one work-group barrier.
   int blk_reg = -1;
   {
     const int tl = tile_begin + wave + 4 * (lane >> 2);
@@ -315,8 +364,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       blk_reg = (raw < 0 || (int64_t)raw >= a.num_blocks) ? -1 : raw;
     }
   }
-  if (wave == 0 && lane < 16) kcb[lane] = a.c->kc[lane];
-  if (VLM && wave == 1 && lane < 16) vcb[lane] = a.c->vc[lane];
   float qx0 = 0.f, qx1 = 0.f;
   if (wave < G) {
     const int64_t qo = ((int64_t)b * a.hq + (int64_t)kvh * G + wave) * kDim + 2 * lane;
@@ -332,16 +379,40 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   }
   const float sg0 = a.c->signs[2 * lane], sg1 = a.c->signs[2 * lane + 1];
 
-  TileRegs<KB, VB> nx;
+  KeyTile<KB, QJL> nx;
   uint4 vp[VB == 3 ? 8 : 4];     // Lloyd-Max values: byte planes of coordinates 2*lane, 2*lane+1
   uint4 vq[VB];                  // uniform values: the planes of coordinates 8j..8j+7 of page lane/16
   int tile = tile_begin + wave;
   if (tile < tile_end && tile * 64 < tok_end) {
-    const int blk = lane_block(blk_reg, 0, lane);
-    load_tile<KB, QJL, VB, VLM>(nx, a, blk, kvh, lane, blk_stride, head_stride);
-    if constexpr (VLM) load_value_planes<VB>(vp, a, pages_of(blk_reg, 0), kvh, lane, blk_stride, head_stride);
-    else load_value_group<VB>(vq, a, blk, kvh, lane, blk_stride, head_stride);
+    const TilePages tp = pages_of(blk_reg, 0);
+    load_keys<KB, QJL, VLM>(nx, a, tp, kvh, lane, blk_stride, head_stride);
+    if constexpr (VLM) load_value_planes<VB>(vp, a, tp, kvh, lane, blk_stride, head_stride);
+    else load_value_group<VB>(vq, a, lane_block(blk_reg, 0, lane), kvh, lane, blk_stride, head_stride);
   }
+
+  // Key centroid table: C * 2^s2 with 2^s2 bringing the largest |C| (the last,
+  // the codebook being symmetric) into [2^14, 2^15).
+  const int s2 = 15 - __builtin_amdgcn_frexp_expf(a.c->kc[(1 << KB) - 1]);
+  if (tid < Tab::kEntries) {
+    constexpr int per = KB == 2 ? 4 : 2;
+    uint32_t* e = &ktab[tid * Tab::kWords];
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      const int code = (tid >> (KB * i)) & ((1 << KB) - 1);
+      float hi, lo, unused;
+      split_f16(ldexpf(a.c->kc[code], s2), hi, lo, unused);
+      e[i] = f16bits(hi) | (f16bits(lo) << 16);
+    }
+  }
+  if constexpr (QJL) {
+    // bit e of a sign byte -> f16 +1 (bit set) or -1, for the 8 coordinates of the byte
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = ((tid >> (2 * i)) & 1 ? 0x3C00u : 0xBC00u) | (((tid >> (2 * i + 1)) & 1 ? 0x3C00u : 0xBC00u) << 16);
+    stab[tid] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  if (VLM && tid < 16) vcb[tid] = a.c->vc[tid];
 
   // Rotate query head `wave`: q'' = log2(e) * scale * H(s*q)/sqrt(d), so that the
   // logits come out in base-2 units for exp2.  Heads >= G stay zero.
@@ -358,10 +429,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       x1 = upper ? p1 - x1 : x1 + p1;
     }
     const float f = a.scale * kInvSqrtDim * kLog2e;
-    q_sh[wave][2 * lane] = x0 * f;
-    q_sh[wave][2 * lane + 1] = x1 * f;
+    x0 *= f;
+    x1 *= f;
+    // f16 terms of q'' * 2^s1, 2^s1 bringing the head's largest |q''| into [2^14, 2^15)
+    const float qm = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+    const int s1 = qm > 0.f ? 15 - __builtin_amdgcn_frexp_expf(qm) : 0;
+    float h0, l0, m0, h1, l1, m1;
+    split_f16(ldexpf(x0, s1), h0, l0, m0);
+    split_f16(ldexpf(x1, s1), h1, l1, m1);
+    *reinterpret_cast<uint2*>(&qd[wave][0][2 * lane]) = make_uint2(f16bits(h0) * 0x10001u, f16bits(h1) * 0x10001u);
+    *reinterpret_cast<uint2*>(&qd[wave][1][2 * lane]) = make_uint2(f16bits(l0) * 0x10001u, f16bits(l1) * 0x10001u);
+    *reinterpret_cast<uint2*>(&qd[wave][2][2 * lane]) = make_uint2(f16bits(m0) * 0x10001u, f16bits(m1) * 0x10001u);
+    *reinterpret_cast<uint2*>(&qd[wave][3][2 * lane]) = make_uint2(0u, 0u);
+    if (lane == 0) qexp[wave] = s1;
     if constexpr (QJL) {
       // p'' = coef * S q''  (coef = sqrt(pi/2)/m): lane computes rows 2*lane, 2*lane+1
+      q_sh[wave][2 * lane] = x0;
+      q_sh[wave][2 * lane + 1] = x1;
       wave_sync_lds();
       float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll 8
@@ -371,19 +455,31 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         acc0 = fmaf(sv.x, qk, acc0);
         acc1 = fmaf(sv.y, qk, acc1);
       }
-      p_sh[wave][2 * lane] = acc0 * a.qjl_coef;
-      p_sh[wave][2 * lane + 1] = acc1 * a.qjl_coef;
+      acc0 *= a.qjl_coef;
+      acc1 *= a.qjl_coef;
+      const float pm = wave_max(fmaxf(fabsf(acc0), fabsf(acc1)));
+      const int sp = pm > 0.f ? 15 - __builtin_amdgcn_frexp_expf(pm) : 0;
+      split_f16(ldexpf(acc0, sp), h0, l0, m0);
+      split_f16(ldexpf(acc1, sp), h1, l1, m1);
+      pt[wave][0][lane] = f16bits(h0) | (f16bits(h1) << 16);
+      pt[wave][1][lane] = f16bits(l0) | (f16bits(l1) << 16);
+      pt[wave][2][lane] = f16bits(m0) | (f16bits(m1) << 16);
+      pt[wave][3][lane] = 0u;
+      if (lane == 0) pexp[wave] = sp;
     }
   }
   __syncthreads();
 
-  float m_run[4], l_lane[4], s_lane[4];
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    m_run[h] = -INFINITY;
-    l_lane[h] = 0.f;
-    s_lane[h] = 0.f;
-  }
+  // A operands of the logits MFMA: row lane%16 = (head (lane/4)%4, term lane%4),
+  // coordinates 32g + 4*kap + (0..3), each twice (g = lane/16).
+  const uint32_t* qa_src = &qd[(lane >> 2) & 3][lane & 3][32 * grp];
+  // base-2 logit of head grp = D * 2^-(s1 + s2) * norm (and the QJL part: D2 * 2^-sp * residual norm)
+  const float lscale = ldexpf(1.f, -(qexp[grp] + s2));
+  const float pscale = QJL ? ldexpf(1.f, -pexp[grp]) : 0.f;
+  const uint32_t* ktab_p = ktab;
+
+  // Running max (base 2) and partial sums of head grp over this lane's tokens.
+  float m_run = -INFINITY, l_lane = 0.f, s_lane = 0.f;
   // Uniform values: lane l accumulates head l/16, coordinates 8(l%16) + m.
   float O[8];
 #pragma unroll
@@ -391,129 +487,97 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // Lloyd-Max values: rows = heads, columns = coordinates 2*lane, 2*lane+1.
   floatx4 O0 = {0.f, 0.f, 0.f, 0.f}, O1 = O0, O2 = O0, O3 = O0;
   const int vsh = (VB == 2) ? 4 * (lane & 1) : (VB == 3) ? ((6 * lane) & 7) : 0;
-  const char* cbf = reinterpret_cast<const char*>(&kcb[0]);
-  const int ho = lane >> 4;                              // head of this lane's value outputs
 
   for (int k = 0; tile < tile_end && tile * 64 < tok_end; tile += 4, ++k) {
-    const int t = tile * 64 + lane;
     const bool has_next = tile + 4 < tile_end && (tile + 4) * 64 < tok_end;
-    const bool valid = t < tok_end && lane_block(blk_reg, k, lane) >= 0;
-    const int nblk = lane_block(blk_reg, k + 1, lane);
-    // masked lanes may have read another page: their scalars must not reach a sum
-    const float knorm = nx.knorm, kres = nx.kres;
-    const float va = valid ? nx.va : 0.f, vb = valid ? nx.vb : 0.f;
+    const TilePages tp = pages_of(blk_reg, k);
+    const KeyTile<KB, QJL> cur = nx;
 
-    // Logits: rows = 4 query heads, columns = this lane's token, one coordinate per
-    // MFMA; two independent accumulators keep the matrix pipe busy.
-    floatx4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0;
-    if constexpr (KB == 4) {
-      // Two masks per 32-bit word put its eight codes, multiplied by 4 (the table
-      // stride), into byte lanes; each code then costs one byte extract.
+    // Logits of head grp for tokens 16*pg + j16 of the tile's 4 pages.
+    floatx4 D[4], D2[4];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        uint32_t e = (nx.kw[j] << 2) & 0x3C3C3C3Cu;   // codes 8j, 8j+2, 8j+4, 8j+6
-        uint32_t o = (nx.kw[j] >> 2) & 0x3C3C3C3Cu;   // codes 8j+1, 8j+3, 8j+5, 8j+7
-        // keep the two masked words: folding the masks into each byte extract
-        // would cost two instructions per code instead of one
-        asm volatile("" : "+v"(e), "+v"(o));
-        const float4 qa = *reinterpret_cast<const float4*>(&q_sh[lane & 3][8 * j]);
-        const float4 qb = *reinterpret_cast<const float4*>(&q_sh[lane & 3][8 * j + 4]);
-        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(qa.x, *(const float*)(cbf + (e & 0xFF)), c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(qa.y, *(const float*)(cbf + (o & 0xFF)), c1, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(qa.z, *(const float*)(cbf + ((e >> 8) & 0xFF)), c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(qa.w, *(const float*)(cbf + ((o >> 8) & 0xFF)), c1, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(qb.x, *(const float*)(cbf + ((e >> 16) & 0xFF)), c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(qb.y, *(const float*)(cbf + ((o >> 16) & 0xFF)), c1, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(qb.z, *(const float*)(cbf + (e >> 24)), c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(qb.w, *(const float*)(cbf + (o >> 24)), c1, 0, 0, 0);
-        if ((j & 1) == 1) __builtin_amdgcn_sched_barrier(0);   // bound the look-ups in flight
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kDim; i += 4) {
-        const float4 q4 = *reinterpret_cast<const float4*>(&q_sh[lane & 3][i]);
-        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.x, *(const float*)(cbf + (get_code<KB>(nx.kw, i) << 2)), c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.y, *(const float*)(cbf + (get_code<KB>(nx.kw, i + 1) << 2)), c1, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.z, *(const float*)(cbf + (get_code<KB>(nx.kw, i + 2) << 2)), c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_4x4x1f32(q4.w, *(const float*)(cbf + (get_code<KB>(nx.kw, i + 3) << 2)), c1, 0, 0, 0);
-        if ((i & 15) == 12) __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int pg = 0; pg < 4; ++pg) {
+      D[pg] = floatx4{0.f, 0.f, 0.f, 0.f};
+      D2[pg] = D[pg];
     }
-    floatx4 acc = c0 + c1;
-    floatx4 acc2 = {0.f, 0.f, 0.f, 0.f};
+#define TQ_KAP(KAP)                                                         \
+  {                                                                         \
+    const uint4 qa = *reinterpret_cast<const uint4*>(qa_src + 4 * (KAP));  \
+    _Pragma("unroll") for (int pg = 0; pg < 4; ++pg)                        \
+        D[pg] = mfma_f16(qa, key_operand<KB, KAP>(cur.kc[pg], ktab_p), D[pg]); \
+  }
+    TQ_KAP(0) TQ_KAP(1) TQ_KAP(2) TQ_KAP(3) TQ_KAP(4) TQ_KAP(5) TQ_KAP(6) TQ_KAP(7)
+#undef TQ_KAP
     if constexpr (QJL) {
-      floatx4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = d0;
-      const uint32_t sgw[4] = {nx.sg.x, nx.sg.y, nx.sg.z, nx.sg.w};
 #pragma unroll
-      for (int i = 0; i < kDim; i += 2) {
-        const float2 p2 = *reinterpret_cast<const float2*>(&p_sh[lane & 3][i]);
-        const float s0 = ((sgw[i >> 5] >> (i & 31)) & 1u) ? 1.f : -1.f;
-        const float s1 = ((sgw[(i + 1) >> 5] >> ((i + 1) & 31)) & 1u) ? 1.f : -1.f;
-        d0 = __builtin_amdgcn_mfma_f32_4x4x1f32(p2.x, s0, d0, 0, 0, 0);
-        d1 = __builtin_amdgcn_mfma_f32_4x4x1f32(p2.y, s1, d1, 0, 0, 0);
+      for (int kap = 0; kap < 4; ++kap) {
+        const uint4 pa = *reinterpret_cast<const uint4*>(&pt[(lane >> 2) & 3][lane & 3][16 * grp + 4 * kap]);
+#pragma unroll
+        for (int pg = 0; pg < 4; ++pg) {
+          const uint4 sb = stab[(cur.sg[pg] >> (8 * kap)) & 0xFFu];
+          D2[pg] = mfma_f16(pa, sb, D2[pg]);
+        }
       }
-      acc2 = d0 + d1;
     }
-    // The key row is consumed: fetch the next tile while this one finishes.
-    if (has_next) load_tile<KB, QJL, VB, VLM>(nx, a, nblk, kvh, lane, blk_stride, head_stride);
+    // The key chunks are consumed: fetch the next tile's while this one finishes.
+    if (has_next) load_keys<KB, QJL, VLM>(nx, a, pages_of(blk_reg, k + 1), kvh, lane, blk_stride, head_stride);
 
-    float lg[4];
+    float lg[4], va[4], vb[4];
+    bool valid[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      float v = knorm * acc[h];
-      if (QJL) v = fmaf(kres, acc2[h], v);
-      lg[h] = valid ? v : -INFINITY;
+    for (int pg = 0; pg < 4; ++pg) {
+      valid[pg] = tile * 64 + 16 * pg + j16 < tok_end && tp.b[pg] >= 0;
+      float v = (D[pg][0] + D[pg][1] + D[pg][2]) * (lscale * cur.knorm[pg]);
+      if (QJL) v = fmaf((D2[pg][0] + D2[pg][1] + D2[pg][2]) * pscale, cur.kres[pg], v);
+      lg[pg] = valid[pg] ? v : -INFINITY;
+      // masked lanes may have read another page: their scalars must not reach a sum
+      va[pg] = valid[pg] ? cur.va[pg] : 0.f;
+      vb[pg] = valid[pg] ? cur.vb[pg] : 0.f;
     }
-    if (a.logits != nullptr && valid) {
+    if (a.logits != nullptr && grp < G) {
+      float* lrow = a.logits + ((int64_t)b * a.hq + (int64_t)kvh * G + grp) * a.max_seq + tile * 64 + j16;
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
-        if (h < G) a.logits[((int64_t)b * a.hq + (int64_t)kvh * G + h) * a.max_seq + t] = lg[h] * kLn2;
+      for (int pg = 0; pg < 4; ++pg)
+        if (valid[pg]) lrow[16 * pg] = lg[pg] * kLn2;
     }
-    // Online softmax (base 2): the running max is wave-uniform, sums stay per lane;
-    // the accumulators are rescaled only when a head's max moved.
-    float mnew[4] = {lg[0], lg[1], lg[2], lg[3]};
-    float smax = vb;                        // largest value scale of the tile (masked lanes: 0)
-    wave_max5(mnew[0], mnew[1], mnew[2], mnew[3], smax);
-    bool moved = false;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      mnew[h] = fmaxf(m_run[h], mnew[h]);
-      moved = moved || (mnew[h] != m_run[h]);
-    }
-    if (moved) {
-      float al[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        al[h] = (mnew[h] == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[h] - mnew[h]);
-        l_lane[h] *= al[h];
-        s_lane[h] *= al[h];
-        m_run[h] = mnew[h];
-      }
+    // Online softmax (base 2) of head grp: the row of 16 lanes shares the max;
+    // the accumulators are rescaled only when some head's max moved.
+    float mt = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+    float smax = fmaxf(fmaxf(vb[0], vb[1]), fmaxf(vb[2], vb[3]));   // largest value scale of the tile
+    row_max2(mt, smax);
+    const float mnew = fmaxf(m_run, mt);
+    if (__builtin_amdgcn_read_exec() & __ballot(mnew != m_run)) {
+      const float al = (mnew == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
+      l_lane *= al;
+      s_lane *= al;
+      m_run = mnew;
       if constexpr (VLM) {
+        float ah[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) ah[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), 16 * h));
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
-          O0[h] *= al[h];
-          O1[h] *= al[h];
-          O2[h] *= al[h];
-          O3[h] *= al[h];
+          O0[h] *= ah[h];
+          O1[h] *= ah[h];
+          O2[h] *= ah[h];
+          O3[h] *= ah[h];
         }
       } else {
-        const float ah = ho == 0 ? al[0] : ho == 1 ? al[1] : ho == 2 ? al[2] : al[3];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) O[m] *= ah;
+        for (int m = 0; m < 8; ++m) O[m] *= al;
       }
     }
+    const float ms = (m_run == -INFINITY) ? 0.f : m_run;
     float pr[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float ms = (m_run[h] == -INFINITY) ? 0.f : m_run[h];
-      pr[h] = __builtin_amdgcn_exp2f(lg[h] - ms);          // 0 for masked tokens
-      l_lane[h] += pr[h];
-      if (!VLM) s_lane[h] = fmaf(pr[h], va, s_lane[h]);
+    for (int pg = 0; pg < 4; ++pg) {
+      pr[pg] = __builtin_amdgcn_exp2f(lg[pg] - ms);    // 0 for masked tokens
+      l_lane += pr[pg];
+      if (!VLM) s_lane = fmaf(pr[pg], va[pg], s_lane);
     }
     if constexpr (VLM) {
 #pragma unroll
-      for (int h = 0; h < 4; ++h) wt[h][lane] = __float_as_uint(pr[h] * va);
+      for (int pg = 0; pg < 4; ++pg) wt[grp][16 * pg + j16] = __float_as_uint(pr[pg] * va[pg]);
       wave_sync_lds();
       // Values: rows = 4 heads, columns = coordinates 2*lane / 2*lane+1, one token per
       // MFMA; even and odd tokens go to separate accumulators.
@@ -545,20 +609,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
       if (has_next) load_value_planes<VB>(vp, a, pages_of(blk_reg, k + 1), kvh, lane, blk_stride, head_stride);
     } else {
-      // Uniform values, o_h += sum_t p_t (min_t + scale_t * code_t): the min part is
-      // a per-head scalar (s_lane); the code part is an exact integer product.  The
-      // weights p_t * scale_t become fixed-point integers on a grid shared by the
-      // tile, 2^(E-27) with 2^E just above the tile's largest scale (p <= 1), split
-      // into four 7-bit limbs: rows of the 16x16x64 int8 MFMA are (head, limb),
-      // columns 16 coordinates, and K the tile's 64 tokens.
+      // Fixed-point weights on the grid 2^(E-27), 2^E just above the tile's
+      // largest scale (p <= 1, so every weight is below 2^27, four 7-bit limbs).
       const int E = __builtin_amdgcn_frexp_expf(smax);
-      const float vbs = ldexpf(vb, 27 - E);
 #pragma unroll
-      for (int h = 0; h < 4; ++h) wt[h][lane] = (uint32_t)fmaf(pr[h], vbs, 0.5f);   // round to nearest
+      for (int pg = 0; pg < 4; ++pg)
+        wt[grp][16 * pg + j16] = (uint32_t)fmaf(pr[pg], ldexpf(vb[pg], 27 - E), 0.5f);   // round to nearest
       wave_sync_lds();
       // A operand: row lane%16 = (head (lane/4)%4, limb lane%4), tokens 16g..16g+15
       // of page g = lane/16, one per byte.
-      const uint4* wsrc = reinterpret_cast<const uint4*>(&wt[(lane >> 2) & 3][16 * (lane >> 4)]);
+      const uint4* wsrc = reinterpret_cast<const uint4*>(&wt[(lane >> 2) & 3][16 * grp]);
       const uint32_t lsh = 7u * (uint32_t)(lane & 3);
       const intx4 A = {limb4(wsrc[0], lsh), limb4(wsrc[1], lsh), limb4(wsrc[2], lsh), limb4(wsrc[3], lsh)};
       const float bsc = ldexpf(1.f, E - 27);
@@ -571,20 +631,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
       TQ_PV(0) TQ_PV(1) TQ_PV(2) TQ_PV(3) TQ_PV(4) TQ_PV(5) TQ_PV(6) TQ_PV(7)
 #undef TQ_PV
-      if (has_next) load_value_group<VB>(vq, a, nblk, kvh, lane, blk_stride, head_stride);
+      if (has_next) load_value_group<VB>(vq, a, lane_block(blk_reg, k + 1, lane), kvh, lane, blk_stride, head_stride);
     }
     wave_sync_lds();
   }
 
-  // Per-wave totals, then merge the 4 waves of the work-group.
-  float tot[8] = {l_lane[0], l_lane[1], l_lane[2], l_lane[3], s_lane[0], s_lane[1], s_lane[2], s_lane[3]};
-  wave_sum8(tot);
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      part_ml[wave][h][0] = m_run[h];
-      part_ml[wave][h][1] = tot[h];
-    }
+  // ---- Per-wave totals of head grp (every lane of the row), then merge the 4
+  // waves of the work-group.
+  row_sum2(l_lane, s_lane);
+  if (j16 == 0) {
+    part_ml[wave][grp][0] = m_run;
+    part_ml[wave][grp][1] = l_lane;
   }
   if constexpr (VLM) {
     O0 += O2;
@@ -595,10 +652,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       part_o[wave][h][2 * lane + 1] = O1[h];
     }
   } else {
-    const float sh = ho == 0 ? tot[4] : ho == 1 ? tot[5] : ho == 2 ? tot[6] : tot[7];
-    float4* dst = reinterpret_cast<float4*>(&part_o[wave][ho][8 * (lane & 15)]);
-    dst[0] = make_float4(O[0] + sh, O[1] + sh, O[2] + sh, O[3] + sh);
-    dst[1] = make_float4(O[4] + sh, O[5] + sh, O[6] + sh, O[7] + sh);
+    float4* dst = reinterpret_cast<float4*>(&part_o[wave][grp][8 * j16]);
+    dst[0] = make_float4(O[0] + s_lane, O[1] + s_lane, O[2] + s_lane, O[3] + s_lane);
+    dst[1] = make_float4(O[4] + s_lane, O[5] + s_lane, O[6] + s_lane, O[7] + s_lane);
   }
   __syncthreads();
   // Merge the 4 waves: thread (head h = wave, coordinates 2*lane, 2*lane+1).
