@@ -355,13 +355,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // and the query row of head `wave` are fetched together; the first tile's
   // loads are issued before the query is rotated, so their latency overlaps the
   // rotation, the tables and the one work-group barrier.
+  // The table read does not wait for the sequence length: entries past the end
+  // of the sequence are dropped once it is known.
   int blk_reg = -1;
   {
     const int tl = tile_begin + wave + 4 * (lane >> 2);
     const int page = tl * 4 + (lane & 3);
-    if (tl < tile_end && page * 16 < tok_end) {
+    if (tl < tile_end && page < a.max_blocks) {
       const int raw = a.block_tables[(int64_t)b * a.max_blocks + page];
-      blk_reg = (raw < 0 || (int64_t)raw >= a.num_blocks) ? -1 : raw;
+      blk_reg = (raw < 0 || (int64_t)raw >= a.num_blocks || page * 16 >= tok_end) ? -1 : raw;
     }
   }
   float qx0 = 0.f, qx1 = 0.f;
@@ -700,17 +702,36 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     M = -INFINITY;
     L = o0 = o1 = 0.f;
     if (h < G) {
+      // Splits are merged 8 at a time, all loads of a batch in flight together.
       const int64_t stride = 4 * (2 + kDim);
       const float* src = a.ws + (((int64_t)b * a.hkv + kvh) * a.splits * 4 + h) * (2 + kDim);
-      for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, load_agent(src + sp * stride));
-      for (int sp = 0; sp < a.splits; ++sp) {
-        const float ms = load_agent(src + sp * stride);
-        if (ms != -INFINITY) {
-          const float f = __builtin_amdgcn_exp2f(ms - M);
-          L = fmaf(f, load_agent(src + sp * stride + 1), L);
-          o0 = fmaf(f, load_agent(src + sp * stride + 2 + 2 * lane), o0);
-          o1 = fmaf(f, load_agent(src + sp * stride + 3 + 2 * lane), o1);
+      for (int sp0 = 0; sp0 < a.splits; sp0 += 8) {
+        float ms[8], ls[8], p0[8], p1[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float* s = src + (int64_t)min(sp0 + u, a.splits - 1) * stride;
+          ms[u] = load_agent(s);
+          ls[u] = load_agent(s + 1);
+          p0[u] = load_agent(s + 2 + 2 * lane);
+          p1[u] = load_agent(s + 3 + 2 * lane);
         }
+        float mc = M;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (sp0 + u < a.splits) mc = fmaxf(mc, ms[u]);
+        if (mc == -INFINITY) continue;
+        const float r = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - mc);
+        L *= r;
+        o0 *= r;
+        o1 *= r;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float f = (sp0 + u < a.splits && ms[u] != -INFINITY) ? __builtin_amdgcn_exp2f(ms[u] - mc) : 0.f;
+          L = fmaf(f, ls[u], L);
+          o0 = fmaf(f, p0[u], o0);
+          o1 = fmaf(f, p1[u], o1);
+        }
+        M = mc;
       }
     }
   }
