@@ -92,14 +92,11 @@ __device__ __forceinline__ void row_sum2(float& a, float& b) {
 #undef TQ_ROW2_ALL
 #undef TQ_ROW2
 
-// Byte BYTE of x shifted left by SH, in one instruction (sub-dword operand select).
+// Byte BYTE of x shifted left by SH (the compiler folds the byte select into a
+// sub-dword operand of the shift).
 template <int SH, int BYTE>
 __device__ __forceinline__ uint32_t byte_shl(uint32_t x) {
-  uint32_t r;
-  asm("v_lshlrev_b32_sdwa %0, %2, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_%3"
-      : "=v"(r)
-      : "v"(x), "i"(SH), "i"(BYTE));
-  return r;
+  return ((x >> (8 * BYTE)) & 0xFFu) << SH;
 }
 
 __device__ __forceinline__ uint32_t f16bits(float x) {
@@ -127,21 +124,6 @@ struct TilePages {
   int b[4];
 };
 
-// The wave keeps the block ids of all its tiles in one register: lane 4k + pg
-// holds page pg of the wave's k-th tile.  lane_block returns the block id of the
-// page that lane `lane` reads in the k-th tile (lanes 16*pg .. 16*pg+15 read page
-// pg), fetched across lanes without a branch.
-__device__ __forceinline__ int lane_block(int blk_reg, int k, int lane) {
-  return __builtin_amdgcn_ds_bpermute((4 * k + (lane >> 4)) << 2, blk_reg);
-}
-
-__device__ __forceinline__ TilePages pages_of(int blk_reg, int k) {
-  TilePages p;
-#pragma unroll
-  for (int pg = 0; pg < 4; ++pg) p.b[pg] = __builtin_amdgcn_readlane(blk_reg, 4 * k + pg);
-  return p;
-}
-
 // Loads are unconditional: an absent page (block id -1) reads block 0 in its
 // place and the lanes of absent pages and of tokens past the end are masked
 // after the loads, which keeps the load path free of branches.  The caller
@@ -161,9 +143,9 @@ struct KeyTile {
   float knorm[4], va[4], vb[4], kres[4];
 };
 
-template <int KB, bool QJL, bool VLM>
-__device__ __forceinline__ void load_keys(KeyTile<KB, QJL>& r, const DecodeArgs& a, const TilePages& tp, int kvh,
-                                          int lane, int64_t blk_stride, int64_t head_stride) {
+template <int KB, bool QJL>
+__device__ __forceinline__ void load_key_codes(KeyTile<KB, QJL>& r, const DecodeArgs& a, const TilePages& tp, int kvh,
+                                               int lane, int64_t blk_stride, int64_t head_stride) {
   const int j = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int pg = 0; pg < 4; ++pg) {
@@ -179,16 +161,22 @@ __device__ __forceinline__ void load_keys(KeyTile<KB, QJL>& r, const DecodeArgs&
       const uint32_t* w = reinterpret_cast<const uint32_t*>(row);
       r.kc[pg][0] = w[0]; r.kc[pg][1] = w[1]; r.kc[pg][2] = w[2];
     }
+    if constexpr (QJL) r.sg[pg] = reinterpret_cast<const uint32_t*>(page + a.f.ksigns + 16 * j)[g];
+    else r.sg[pg] = 0u;
+  }
+}
+
+template <int KB, bool QJL, bool VLM>
+__device__ __forceinline__ void load_key_scalars(KeyTile<KB, QJL>& r, const DecodeArgs& a, const TilePages& tp,
+                                                 int kvh, int lane, int64_t blk_stride, int64_t head_stride) {
+  const int j = lane & 15;
+#pragma unroll
+  for (int pg = 0; pg < 4; ++pg) {
+    const uint8_t* page = a.cache + page_offset(tp.b[pg], kvh, blk_stride, head_stride);
     r.knorm[pg] = reinterpret_cast<const float*>(page + a.f.knorm)[j];
     r.va[pg] = reinterpret_cast<const float*>(page + a.f.vmin)[j];
     r.vb[pg] = VLM ? 0.f : reinterpret_cast<const float*>(page + a.f.vscale)[j];
-    if constexpr (QJL) {
-      r.sg[pg] = reinterpret_cast<const uint32_t*>(page + a.f.ksigns + 16 * j)[g];
-      r.kres[pg] = reinterpret_cast<const float*>(page + a.f.kres)[j];
-    } else {
-      r.sg[pg] = 0u;
-      r.kres[pg] = 0.f;
-    }
+    r.kres[pg] = QJL ? reinterpret_cast<const float*>(page + a.f.kres)[j] : 0.f;
   }
 }
 
@@ -339,70 +327,98 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   __shared__ float part_ml[4][4][2];
   __shared__ __align__(16) float part_o[4][4][kDim];
 
+  // Block ids of the work-group's pages ([tile - tile_begin][page]; -1: absent):
+  // tiles are handed to the waves one at a time, so every wave may need any of them.
+  __shared__ int blk_lds[kMaxPagesPerSplit];
+  __shared__ unsigned tile_ctr;
+
   const int G = a.group;
   int seq_len = a.seq_lens[b];
   seq_len = max(0, min(seq_len, min(a.max_seq, 16 * a.max_blocks)));
   if (a.num_blocks <= 0) seq_len = 0;     // no page exists: every block id is absent
-  const int tile_begin = split * a.tiles_per_split;
-  const int tile_end = tile_begin + a.tiles_per_split;
+  // Split `split` owns tiles [tile_begin, tile_end): an even share of the longest
+  // sequence's tiles (at most 64).
+  const int tile_begin = (int)((uint32_t)(split * a.tiles_total) / (uint32_t)a.splits);
+  const int tile_end = (int)((uint32_t)((split + 1) * a.tiles_total) / (uint32_t)a.splits);
   const int tok_end = min(seq_len, tile_end * 64);
   const int64_t head_stride = a.f.page_bytes;
   const int64_t blk_stride = head_stride * a.hkv;
+  const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
   uint32_t (&wt)[4][68] = wT[wave];
 
-  // ---- Prologue.  The block ids of the wave's pages (lane 4k + pg: page pg of
-  // the wave's k-th tile; at most 16 tiles per wave since tiles_per_split <= 64)
-  // and the query row of head `wave` are fetched together; the first tile's
-  // loads are issued before the query is rotated, so their latency overlaps the
-  // rotation, the tables and the one work-group barrier.
-  // The table read does not wait for the sequence length: entries past the end
-  // of the sequence are dropped once it is known.
-  int blk_reg = -1;
+  // ---- Prologue.  The constants the shared tables need are fetched first (the
+  // work-group barrier below then does not wait for page data), then the block
+  // ids and the query row of head `wave`; each wave's first tile (tile_begin +
+  // wave) is loaded before the query is rotated, so that its latency overlaps the
+  // rotation, the tables and the barrier.  Block-table reads do not wait for the
+  // sequence length: entries past the end are dropped once it is known.
+  const float kc_top = a.c->kc[(1 << KB) - 1];
+  float kc_e[KB == 2 ? 4 : 2];
   {
-    const int tl = tile_begin + wave + 4 * (lane >> 2);
-    const int page = tl * 4 + (lane & 3);
-    if (tl < tile_end && page < a.max_blocks) {
-      const int raw = a.block_tables[(int64_t)b * a.max_blocks + page];
-      blk_reg = (raw < 0 || (int64_t)raw >= a.num_blocks || page * 16 >= tok_end) ? -1 : raw;
-    }
+    const int ent = tid & (KeyTable<KB>::kEntries - 1);
+#pragma unroll
+    for (int i = 0; i < (KB == 2 ? 4 : 2); ++i) kc_e[i] = a.c->kc[(ent >> (KB * i)) & ((1 << KB) - 1)];
   }
-  float qx0 = 0.f, qx1 = 0.f;
-  if (wave < G) {
-    const int64_t qo = ((int64_t)b * a.hq + (int64_t)kvh * G + wave) * kDim + 2 * lane;
-    if (a.q_dtype == TQ_BF16) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.q) + qo);
-      qx0 = bf16lo(w);
-      qx1 = bf16hi(w);
-    } else {
-      const float2 f = *reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + qo);
-      qx0 = f.x;
-      qx1 = f.y;
-    }
+  // Loads of the prologue are unconditional (heads >= G read head 0 and are
+  // zeroed, a wave without a tile reads block 0): conditional loads would make
+  // the compiler wait for every earlier load before the first use of any.
+  // The query pair of this lane (coordinates 2*lane, 2*lane+1) is one word in
+  // bf16 or two in fp32; both words are always read (the second re-reads the
+  // first for bf16) so that no branch separates the load from its use.
+  uint32_t qw0, qw1;
+  {
+    const bool f32 = a.q_dtype != TQ_BF16;
+    const int64_t qo = ((int64_t)b * a.hq + (int64_t)kvh * G + (wave < G ? wave : 0)) * kDim + 2 * lane;
+    const uint32_t* qp = f32 ? reinterpret_cast<const uint32_t*>(static_cast<const float*>(a.q) + qo)
+                             : reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.q) + qo);
+    qw0 = qp[0];
+    qw1 = qp[f32 ? 1 : 0];
   }
   const float sg0 = a.c->signs[2 * lane], sg1 = a.c->signs[2 * lane + 1];
+  // (a table row with no entries is never read: seq_lens stands in for it)
+  const int32_t* trow = a.max_blocks > 0 ? table : a.seq_lens + b;
+  const int tmax = max(a.max_blocks - 1, 0);
+  {
+    const int page = 4 * tile_begin + tid;
+    int raw = trow[min(page, tmax)];
+    asm volatile("" : "+v"(raw));   // keep the read here, ahead of the tile loads
+    blk_lds[tid] = (tid >= 4 * (tile_end - tile_begin) || page >= a.max_blocks || raw < 0 ||
+                    (int64_t)raw >= a.num_blocks || page * 16 >= tok_end)
+                       ? -1 : raw;
+  }
+  if (tid == 0) tile_ctr = 4;   // tiles tile_begin .. tile_begin + 3 go to waves 0..3
+  int t_cur = tile_begin + wave;
+  bool have = t_cur < tile_end && t_cur * 64 < tok_end;
+  TilePages tp;
+  int vblk;            // block of the page this lane reads value planes from (page lane/16)
+  {
+    const int page = 4 * t_cur + (lane & 3);
+    int raw = trow[min(page, tmax)];
+    asm volatile("" : "+v"(raw));
+    const int v = (!have || page >= a.max_blocks || raw < 0 || (int64_t)raw >= a.num_blocks || page * 16 >= tok_end)
+                      ? -1 : raw;
+#pragma unroll
+    for (int pg = 0; pg < 4; ++pg) tp.b[pg] = __builtin_amdgcn_readlane(v, pg);
+    vblk = __builtin_amdgcn_ds_bpermute(grp << 2, v);
+  }
 
   KeyTile<KB, QJL> nx;
   uint4 vp[VB == 3 ? 8 : 4];     // Lloyd-Max values: byte planes of coordinates 2*lane, 2*lane+1
   uint4 vq[VB];                  // uniform values: the planes of coordinates 8j..8j+7 of page lane/16
-  int tile = tile_begin + wave;
-  if (tile < tile_end && tile * 64 < tok_end) {
-    const TilePages tp = pages_of(blk_reg, 0);
-    load_keys<KB, QJL, VLM>(nx, a, tp, kvh, lane, blk_stride, head_stride);
-    if constexpr (VLM) load_value_planes<VB>(vp, a, tp, kvh, lane, blk_stride, head_stride);
-    else load_value_group<VB>(vq, a, lane_block(blk_reg, 0, lane), kvh, lane, blk_stride, head_stride);
-  }
+  load_key_codes<KB, QJL>(nx, a, tp, kvh, lane, blk_stride, head_stride);
+  load_key_scalars<KB, QJL, VLM>(nx, a, tp, kvh, lane, blk_stride, head_stride);
+  if constexpr (VLM) load_value_planes<VB>(vp, a, tp, kvh, lane, blk_stride, head_stride);
+  else load_value_group<VB>(vq, a, vblk, kvh, lane, blk_stride, head_stride);
 
   // Key centroid table: C * 2^s2 with 2^s2 bringing the largest |C| (the last,
   // the codebook being symmetric) into [2^14, 2^15).
-  const int s2 = 15 - __builtin_amdgcn_frexp_expf(a.c->kc[(1 << KB) - 1]);
-  if (tid < Tab::kEntries) {
-    constexpr int per = KB == 2 ? 4 : 2;
+  const int s2 = 15 - __builtin_amdgcn_frexp_expf(kc_top);
+  if (tid < KeyTable<KB>::kEntries) {
     uint32_t* e = &ktab[tid * Tab::kWords];
 #pragma unroll
-    for (int i = 0; i < per; ++i) {
-      const int code = (tid >> (KB * i)) & ((1 << KB) - 1);
+    for (int i = 0; i < (KB == 2 ? 4 : 2); ++i) {
       float hi, lo, unused;
-      split_f16(ldexpf(a.c->kc[code], s2), hi, lo, unused);
+      split_f16(ldexpf(kc_e[i], s2), hi, lo, unused);
       e[i] = f16bits(hi) | (f16bits(lo) << 16);
     }
   }
@@ -419,6 +435,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // Rotate query head `wave`: q'' = log2(e) * scale * H(s*q)/sqrt(d), so that the
   // logits come out in base-2 units for exp2.  Heads >= G stay zero.
   {
+    const bool f32 = a.q_dtype != TQ_BF16;
+    float qx0 = f32 ? __uint_as_float(qw0) : bf16lo(qw0);
+    float qx1 = f32 ? __uint_as_float(qw1) : bf16hi(qw0);
+    if (wave >= G) qx0 = qx1 = 0.f;
     float x0 = qx0 * sg0, x1 = qx1 * sg1;
     const float s0 = x0 + x1, d0 = x0 - x1;
     x0 = s0;
@@ -490,9 +510,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   floatx4 O0 = {0.f, 0.f, 0.f, 0.f}, O1 = O0, O2 = O0, O3 = O0;
   const int vsh = (VB == 2) ? 4 * (lane & 1) : (VB == 3) ? ((6 * lane) & 7) : 0;
 
-  for (int k = 0; tile < tile_end && tile * 64 < tok_end; tile += 4, ++k) {
-    const bool has_next = tile + 4 < tile_end && (tile + 4) * 64 < tok_end;
-    const TilePages tp = pages_of(blk_reg, k);
+  while (have) {
+    // The next tile of the work-group's range for this wave (handed out in order).
+    unsigned got = 0;
+    if (lane == 0) got = atomicAdd(&tile_ctr, 1u);
+    const int t_nx = tile_begin + (int)__builtin_amdgcn_readfirstlane(got);
+    const bool has_next = t_nx < tile_end && t_nx * 64 < tok_end;
+    // Without a next tile the loads below re-read the current pages (cache hits,
+    // results unused): unconditional loads keep the compiler's waits exact.
+    TilePages tpn = tp;
+    int nvblk = vblk;
+    if (has_next) {
+      const int* nb = &blk_lds[4 * (t_nx - tile_begin)];
+#pragma unroll
+      for (int pg = 0; pg < 4; ++pg) tpn.b[pg] = __builtin_amdgcn_readfirstlane(nb[pg]);
+      nvblk = nb[grp];
+    }
+    const int tile = t_cur;
     const KeyTile<KB, QJL> cur = nx;
 
     // Logits of head grp for tokens 16*pg + j16 of the tile's 4 pages.
@@ -521,8 +555,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         }
       }
     }
-    // The key chunks are consumed: fetch the next tile's while this one finishes.
-    if (has_next) load_keys<KB, QJL, VLM>(nx, a, pages_of(blk_reg, k + 1), kvh, lane, blk_stride, head_stride);
+    // The key chunks are consumed: fetch the next tile's while this one finishes
+    // (its scalars follow once this tile's are used).
+    load_key_codes<KB, QJL>(nx, a, tpn, kvh, lane, blk_stride, head_stride);
 
     float lg[4], va[4], vb[4];
     bool valid[4];
@@ -577,6 +612,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       l_lane += pr[pg];
       if (!VLM) s_lane = fmaf(pr[pg], va[pg], s_lane);
     }
+    load_key_scalars<KB, QJL, VLM>(nx, a, tpn, kvh, lane, blk_stride, head_stride);
     if constexpr (VLM) {
 #pragma unroll
       for (int pg = 0; pg < 4; ++pg) wt[grp][16 * pg + j16] = __float_as_uint(pr[pg] * va[pg]);
@@ -609,7 +645,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);   // keep one page's operands live at a time
       }
-      if (has_next) load_value_planes<VB>(vp, a, pages_of(blk_reg, k + 1), kvh, lane, blk_stride, head_stride);
+      load_value_planes<VB>(vp, a, tpn, kvh, lane, blk_stride, head_stride);
     } else {
       // Fixed-point weights on the grid 2^(E-27), 2^E just above the tile's
       // largest scale (p <= 1, so every weight is below 2^27, four 7-bit limbs).
@@ -633,9 +669,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
       TQ_PV(0) TQ_PV(1) TQ_PV(2) TQ_PV(3) TQ_PV(4) TQ_PV(5) TQ_PV(6) TQ_PV(7)
 #undef TQ_PV
-      if (has_next) load_value_group<VB>(vq, a, lane_block(blk_reg, k + 1, lane), kvh, lane, blk_stride, head_stride);
+      load_value_group<VB>(vq, a, nvblk, kvh, lane, blk_stride, head_stride);
     }
     wave_sync_lds();
+    t_cur = t_nx;
+    tp = tpn;
+    vblk = nvblk;
+    have = has_next;
   }
 
   // ---- Per-wave totals of head grp (every lane of the row), then merge the 4

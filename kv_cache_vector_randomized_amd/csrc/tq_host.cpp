@@ -161,19 +161,18 @@ tq::FieldOffsets offsets_of(const tq_layout& L) {
   return f;
 }
 
-// Split the context of every (sequence, kv head) into pieces of whole 64-token
-// tiles so that the grid is about one round of resident work-groups (`target`,
-// from the kernel's occupancy): more, shorter splits only add prologues and
-// merges, fewer leave SIMDs idle.
-void plan_splits(int target, int batch, int hkv, int max_seq, int* splits, int* tiles_per_split) {
+// Split the context of every (sequence, kv head) into `splits` even shares of
+// whole 64-token tiles so that the grid is about one round of resident
+// work-groups (`target`, from the kernel's occupancy): more, shorter splits only
+// add prologues and merges, fewer leave SIMDs idle.  A split holds 4 to 64 tiles.
+void plan_splits(int target, int batch, int hkv, int max_seq, int* splits, int* tiles_total) {
   const int tiles = std::max(1, (max_seq + 63) / 64);
   const int pairs = std::max(1, batch * hkv);
   int want = (target + pairs - 1) / pairs;
-  want = std::max(1, std::min(want, (tiles + 3) / 4));      // >= 4 tiles per split
-  int tps = (tiles + want - 1) / want;
-  tps = std::min(tps, tq::kMaxPagesPerSplit / 4);
-  *tiles_per_split = tps;
-  *splits = (tiles + tps - 1) / tps;
+  want = std::max(1, std::min(want, (tiles + 3) / 4));
+  want = std::max(want, (tiles + tq::kMaxPagesPerSplit / 4 - 1) / (tq::kMaxPagesPerSplit / 4));
+  *splits = want;
+  *tiles_total = tiles;
 }
 
 struct DeviceGuard {
@@ -378,7 +377,9 @@ tq_status tq_decode_attention(tq_ctx* ctx, const void* q, tq_dtype dt, const voi
   a.logits = logits_out; a.out = out;
   a.counters = (uint32_t*)workspace;
   a.ws = (float*)((uint8_t*)workspace + tq::kCounterBytes);
-  plan_splits(ctx->decode_wgs, batch, a.hkv, max_seq_len, &a.splits, &a.tiles_per_split);
+  plan_splits(ctx->decode_wgs, batch, a.hkv, max_seq_len, &a.splits, &a.tiles_total);
+  if ((int64_t)(a.splits + 1) * a.tiles_total >= ((int64_t)1 << 31))
+    return fail(TQ_ERR_UNSUPPORTED, "max_seq_len too large");
   a.f = offsets_of(ctx->layout); a.c = ctx->consts;
   hipError_t e = tq::launch_decode(a, (int)ctx->cfg.key_bits, (int)ctx->cfg.key_mode, (int)ctx->cfg.val_bits,
                                    (int)ctx->cfg.val_mode, stream);

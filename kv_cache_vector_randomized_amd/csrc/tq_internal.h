@@ -77,7 +77,7 @@ struct DecodeArgs {
   float* ws;                  // partials [batch][hkv][splits][4][2 + 128]
   uint32_t* counters;         // [batch][hkv] arrival counters, zero between calls
   int32_t splits;
-  int32_t tiles_per_split;    // tile = 64 tokens
+  int32_t tiles_total;        // 64-token tiles of the longest sequence, split evenly
   FieldOffsets f;
   const DevConsts* c;
 };
