@@ -241,204 +241,216 @@ __device__ __forceinline__ void pack32(const uint4 (&cb)[2], uint32_t (&w)[B]) {
 }
 
 template <int KB, int VB>
-__global__ __launch_bounds__(256) void append_page_kernel(AppendArgs a) {
+__global__ __launch_bounds__(128) void append_page_kernel(AppendArgs a) {
   constexpr int KROW = 16 * KB;            // bytes of a packed key row
   constexpr int VROW = 16 * VB;            // bytes of a packed value row (= planes)
+  // Wave 0 quantizes the 16 keys, wave 1 the 16 values of the group; each uses
+  // only its own LDS, so the two never wait for each other.
   __shared__ QLut lut[kLutCells];
-  __shared__ __align__(16) uint8_t kcode[4][16][kDim];      // key codes, one byte each [wave][token][coord]
-  __shared__ __align__(16) uint8_t vplane[4][64][16];       // value planes [wave][plane][token]
-  __shared__ float knorm_s[4][16], vmin_s[4][16], vsc_s[4][16];
-  for (int i = threadIdx.x; i < kLutCells; i += blockDim.x) lut[i] = a.c->klut[i];
-  __syncthreads();
+  __shared__ __align__(16) uint8_t kcode[16][kDim];       // key codes, one byte each [token][coord]
+  __shared__ __align__(16) uint8_t vplane[64][16];        // value planes [plane][token]
+  __shared__ float knorm_s[16], vmin_s[16], vsc_s[16];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const bool keys = threadIdx.x < 64;
   const int j = lane & 15, g = lane >> 4;
-  const int64_t ntb = (a.num_tokens + 15) / 16;
-  const int64_t grp = (int64_t)blockIdx.x * 4 + wave;
-  if (grp >= ntb * a.hkv) return;                      // no barrier follows
+  const int64_t grp = blockIdx.x;
   const int h = (int)(grp % a.hkv);
   const int64_t t0 = (grp / a.hkv) * 16;
   const int64_t tmax = a.num_tokens - 1;
-
-  // Slot of token t0 + j (every row of the wave reads the same 16).
-  const int64_t tj = t0 + j;
-  int64_t slot = tj <= tmax ? a.slots[tj] : -1;
-  const bool ok = slot >= 0 && slot < a.num_blocks * kBlockTokensDev;
-  if (!ok) slot = -1;
-  const int64_t slot0 = __builtin_amdgcn_readfirstlane((int)slot) |
-                        ((int64_t)__builtin_amdgcn_readfirstlane((int)(slot >> 32)) << 32);
-  const bool whole = (__ballot(!(ok && slot == slot0 + j)) == 0ull) && slot0 >= 0 && (slot0 & 15) == 0;
-
   const uint16_t* kin = static_cast<const uint16_t*>(a.k);
   const uint16_t* vin = static_cast<const uint16_t*>(a.v);
   auto row_of = [&](int v) -> int64_t { return (min(t0 + v, tmax) * a.hkv + h) * kDim; };
+  auto page_of = [&](int64_t s) -> uint8_t* { return a.cache + ((s >> 4) * a.hkv + h) * (int64_t)a.f.page_bytes; };
 
-  // ---- loads: key blocks (A operands) and the value rows of the 4 passes
-  uint2 ka[8];
-  {
-    const uint2* src = reinterpret_cast<const uint2*>(kin + row_of(j) + 4 * g);
+  if (keys) {
+    // inputs first, then the code grid, so the two latencies overlap
+    uint2 ka[8];
+    {
+      const uint2* src = reinterpret_cast<const uint2*>(kin + row_of(j) + 4 * g);
 #pragma unroll
-    for (int kh = 0; kh < 8; ++kh) ka[kh] = src[4 * kh];
-  }
-  uint4 va[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) va[p] = *reinterpret_cast<const uint4*>(vin + row_of(4 * p + g) + 8 * j);
-
-  // ---- keys: signs, H16 on the matrix cores, H8 in registers
-  shortx4 hb;                                  // B operand: H16[j][4g + e]
-#pragma unroll
-  for (int e = 0; e < 4; ++e) hb[e] = (__builtin_popcount(j & (4 * g + e)) & 1) ? (short)0xBF80 : (short)0x3F80;
-  floatx4 z[8];
-#pragma unroll
-  for (int kh = 0; kh < 8; ++kh) {
-    const int c0 = 16 * kh + 4 * g;            // first coordinate of this lane's 4 inputs
-    const uint32_t sb = (a.sign_bits[c0 >> 5] >> (c0 & 31)) & 0xFu;
-    uint2 x = ka[kh];
-    x.x ^= ((sb & 1u) << 15) | ((sb & 2u) << 30);
-    x.y ^= ((sb & 4u) << 13) | ((sb & 8u) << 28);
-    const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-    z[kh] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, x), hb, zero, 0, 0, 0);
-  }
-  // y[ch][r] = sum_kh H8[ch][kh] z[kh][r]: coordinate 16 ch + j of token 4g + r
-#pragma unroll
-  for (int len = 1; len < 8; len <<= 1)
-#pragma unroll
-    for (int i = 0; i < 8; i += 2 * len)
-#pragma unroll
-      for (int m = i; m < i + len; ++m) {
-        const floatx4 p = z[m], q = z[m + len];
-        z[m] = p + q;
-        z[m + len] = p - q;
-      }
-  float ss[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ch = 0; ch < 8; ++ch)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ss[r] = fmaf(z[ch][r], z[ch][r], ss[r]);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) ss[r] = row_reduce<false>(ss[r]);
-  float cn2[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    // u = y / ||y||; a zero key gives u = 0, codes 2^(b-1) and norm 0
-    const float inv = ss[r] > 0.f ? 1.f / sqrtf(ss[r]) : 0.f;
-    float c2 = 0.f;
-#pragma unroll
-    for (int ch = 0; ch < 8; ++ch) {
-      float c;
-      const int code = lut_code(lut, z[ch][r] * inv, a.klut_scale, a.klut_bias, c);
-      c2 = fmaf(c, c, c2);
-      kcode[wave][4 * g + r][16 * ch + j] = (uint8_t)code;
+      for (int kh = 0; kh < 8; ++kh) ka[kh] = src[4 * kh];
     }
-    cn2[r] = c2;
-  }
+    for (int i = lane; i < kLutCells; i += 64) lut[i] = a.c->klut[i];
+    const int64_t tj = t0 + j;
+    int64_t slot = tj <= tmax ? a.slots[tj] : -1;
+    if (!(slot >= 0 && slot < a.num_blocks * kBlockTokensDev)) slot = -1;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- keys: signs, H16 on the matrix cores, H8 in registers
+    shortx4 hb;                                  // B operand: H16[j][4g + e]
 #pragma unroll
-  for (int r = 0; r < 4; ++r) cn2[r] = row_reduce<false>(cn2[r]);
-  if (j == 0) {
+    for (int e = 0; e < 4; ++e) hb[e] = (__builtin_popcount(j & (4 * g + e)) & 1) ? (short)0xBF80 : (short)0x3F80;
+    floatx4 z[8];
+#pragma unroll
+    for (int kh = 0; kh < 8; ++kh) {
+      const int c0 = 16 * kh + 4 * g;            // first coordinate of this lane's 4 inputs
+      const uint32_t sb = (a.sign_bits[c0 >> 5] >> (c0 & 31)) & 0xFu;
+      uint2 x = ka[kh];
+      x.x ^= ((sb & 1u) << 15) | ((sb & 2u) << 30);
+      x.y ^= ((sb & 4u) << 13) | ((sb & 8u) << 28);
+      const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+      z[kh] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, x), hb, zero, 0, 0, 0);
+    }
+    // y[ch][r] = sum_kh H8[ch][kh] z[kh][r]: coordinate 16 ch + j of token 4g + r
+#pragma unroll
+    for (int len = 1; len < 8; len <<= 1)
+#pragma unroll
+      for (int i = 0; i < 8; i += 2 * len)
+#pragma unroll
+        for (int m = i; m < i + len; ++m) {
+          const floatx4 p = z[m], q = z[m + len];
+          z[m] = p + q;
+          z[m + len] = p - q;
+        }
+    float ss[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ss[r] = fmaf(z[ch][r], z[ch][r], ss[r]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ss[r] = row_reduce<false>(ss[r]);
+    float cn2[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float n = sqrtf(ss[r]) * kInvSqrtDim;           // ||k|| (H/sqrt(d) is orthogonal)
-      knorm_s[wave][4 * g + r] = a.key_nc ? (n > 0.f ? n / sqrtf(cn2[r]) : 0.f) : n;
+      // u = y / ||y||; a zero key gives u = 0, codes 2^(b-1) and norm 0
+      const float inv = ss[r] > 0.f ? 1.f / sqrtf(ss[r]) : 0.f;
+      float c2 = 0.f;
+#pragma unroll
+      for (int ch = 0; ch < 8; ++ch) {
+        float c;
+        const int code = lut_code(lut, z[ch][r] * inv, a.klut_scale, a.klut_bias, c);
+        c2 = fmaf(c, c, c2);
+        kcode[4 * g + r][16 * ch + j] = (uint8_t)code;
+      }
+      cn2[r] = c2;
     }
-  }
-
-  // ---- values: row g takes token 4p + g in pass p; lane j holds coordinates 8j..8j+7
-  constexpr float levels = (float)((1 << VB) - 1);
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int v = 4 * p + g;
-    const uint32_t wv[4] = {va[p].x, va[p].y, va[p].z, va[p].w};
-    float x[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = bf16lo(wv[i]);
-      x[2 * i + 1] = bf16hi(wv[i]);
-    }
-    float mn = x[0], mx = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) {
-      mn = fminf(mn, x[i]);
-      mx = fmaxf(mx, x[i]);
-    }
-    mn = row_min(mn);
-    mx = row_reduce<true>(mx);
-    const float sc = (mx - mn) / levels;                  // correctly rounded division
-    const float inv = sc > 0.f ? 1.f / sc : 0.f;
-    // code = rint(fl32((x - mn) / sc)); the reciprocal product is within 2 ulp of the
-    // correctly rounded quotient, so only values within 2^-18 of a rounding boundary
-    // need the exact division
-    float xq[8];
-    uint32_t near = 0u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      xq[i] = (x[i] - mn) * inv;
-      if (fabsf(xq[i] - floorf(xq[i]) - 0.5f) < 3.814697265625e-06f) near |= 1u << i;
-    }
-    if (near) {                                           // rare: exact quotients
-#pragma unroll 1
-      for (int i = 0; i < 8; ++i)
-        if (near & (1u << i)) {
-          float d = 0.f;
-#pragma unroll
-          for (int m = 0; m < 8; ++m) d = (m == i) ? x[m] - mn : d;
-          const float qe = d / sc;
-#pragma unroll
-          for (int m = 0; m < 8; ++m) xq[m] = (m == i) ? qe : xq[m];
-        }
-    }
-    uint32_t w = 0u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w |= (uint32_t)fminf(rintf(xq[i]), levels) << (VB * i);   // half to even
-    // bytes VB*j .. VB*j + VB - 1 of the row are planes VB*j + i
-#pragma unroll
-    for (int i = 0; i < VB; ++i) vplane[wave][VB * j + i][v] = (uint8_t)(w >> (8 * i));
+    for (int r = 0; r < 4; ++r) cn2[r] = row_reduce<false>(cn2[r]);
     if (j == 0) {
-      vmin_s[wave][v] = mn;
-      vsc_s[wave][v] = sc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float n = sqrtf(ss[r]) * kInvSqrtDim;           // ||k|| (H/sqrt(d) is orthogonal)
+        knorm_s[4 * g + r] = a.key_nc ? (n > 0.f ? n / sqrtf(cn2[r]) : 0.f) : n;
+      }
     }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // ---- stores.  Key rows: lane l packs coordinates 32(l%4)..32(l%4)+31 of token l/4.
-  const int kv = lane >> 2, kq = lane & 3;
-  uint32_t kw[KB];
-  {
-    const uint4 cb[2] = {*reinterpret_cast<const uint4*>(&kcode[wave][kv][32 * kq]),
-                         *reinterpret_cast<const uint4*>(&kcode[wave][kv][32 * kq + 16])};
-    pack32<KB>(cb, kw);
-  }
-  const int64_t slot_kv = __builtin_amdgcn_ds_bpermute(kv << 2, (int)slot) |
-                          ((int64_t)__builtin_amdgcn_ds_bpermute(kv << 2, (int)(slot >> 32)) << 32);
-  auto page_of = [&](int64_t s) -> uint8_t* { return a.cache + ((s >> 4) * a.hkv + h) * (int64_t)a.f.page_bytes; };
-  if (slot_kv >= 0) {
-    uint8_t* dst = page_of(slot_kv) + a.f.kcodes + (slot_kv & 15) * KROW + 4 * KB * kq;
-    if constexpr (KB == 4) *reinterpret_cast<uint4*>(dst) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
-    else if constexpr (KB == 2) *reinterpret_cast<uint2*>(dst) = make_uint2(kw[0], kw[1]);
-    else {
-      uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
-      d32[0] = kw[0]; d32[1] = kw[1]; d32[2] = kw[2];
+
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // Key rows: lane l packs coordinates 32(l%4)..32(l%4)+31 of token l/4.
+    const int kv = lane >> 2, kq = lane & 3;
+    uint32_t kw[KB];
+    {
+      const uint4 cb[2] = {*reinterpret_cast<const uint4*>(&kcode[kv][32 * kq]),
+                           *reinterpret_cast<const uint4*>(&kcode[kv][32 * kq + 16])};
+      pack32<KB>(cb, kw);
     }
-  }
-  if (lane < 16 && slot >= 0) {
-    uint8_t* pg = page_of(slot);
-    reinterpret_cast<float*>(pg + a.f.knorm)[slot & 15] = knorm_s[wave][lane];
-    reinterpret_cast<float*>(pg + a.f.vmin)[slot & 15] = vmin_s[wave][lane];
-    reinterpret_cast<float*>(pg + a.f.vscale)[slot & 15] = vsc_s[wave][lane];
-  }
-  // Value planes: a whole page takes one 16-byte store per plane; otherwise
-  // each token's byte of each plane goes to its own slot.
-  if (whole) {
-    if (lane < VROW)
-      *reinterpret_cast<uint4*>(page_of(slot0) + a.f.vcodes + 16 * lane) =
-          *reinterpret_cast<const uint4*>(&vplane[wave][lane][0]);
+    const int64_t slot_kv = __builtin_amdgcn_ds_bpermute(kv << 2, (int)slot) |
+                            ((int64_t)__builtin_amdgcn_ds_bpermute(kv << 2, (int)(slot >> 32)) << 32);
+    if (slot_kv >= 0) {
+      uint8_t* dst = page_of(slot_kv) + a.f.kcodes + (slot_kv & 15) * KROW + 4 * KB * kq;
+      if constexpr (KB == 4) *reinterpret_cast<uint4*>(dst) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+      else if constexpr (KB == 2) *reinterpret_cast<uint2*>(dst) = make_uint2(kw[0], kw[1]);
+      else {
+        uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
+        d32[0] = kw[0]; d32[1] = kw[1]; d32[2] = kw[2];
+      }
+    }
+    if (lane < 16 && slot >= 0) reinterpret_cast<float*>(page_of(slot) + a.f.knorm)[slot & 15] = knorm_s[lane];
   } else {
+    uint4 va[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) va[p] = *reinterpret_cast<const uint4*>(vin + row_of(4 * p + g) + 8 * j);
+    const int64_t tj = t0 + j;
+    int64_t slot = tj <= tmax ? a.slots[tj] : -1;
+    const bool ok = slot >= 0 && slot < a.num_blocks * kBlockTokensDev;
+    if (!ok) slot = -1;
+    const int64_t slot0 = __builtin_amdgcn_readfirstlane((int)slot) |
+                          ((int64_t)__builtin_amdgcn_readfirstlane((int)(slot >> 32)) << 32);
+    // the 16 tokens fill one page in order
+    const bool whole = (__ballot(!(ok && slot == slot0 + j)) == 0ull) && slot0 >= 0 && (slot0 & 15) == 0;
+
+    // ---- values: row g takes token 4p + g in pass p; lane j holds coordinates 8j..8j+7
+    constexpr float levels = (float)((1 << VB) - 1);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int v = 4 * p + g;
+      const uint32_t wv[4] = {va[p].x, va[p].y, va[p].z, va[p].w};
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16lo(wv[i]);
+        x[2 * i + 1] = bf16hi(wv[i]);
+      }
+      float mn = x[0], mx = x[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) {
+        mn = fminf(mn, x[i]);
+        mx = fmaxf(mx, x[i]);
+      }
+      mn = row_min(mn);
+      mx = row_reduce<true>(mx);
+      const float sc = (mx - mn) / levels;                  // correctly rounded division
+      const float inv = sc > 0.f ? 1.f / sc : 0.f;
+      // code = rint(fl32((x - mn) / sc)); the reciprocal product is within 2 ulp of the
+      // correctly rounded quotient, so only values within 2^-18 of a rounding boundary
+      // need the exact division
+      float xq[8];
+      uint32_t near = 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        xq[i] = (x[i] - mn) * inv;
+        if (fabsf(xq[i] - floorf(xq[i]) - 0.5f) < 3.814697265625e-06f) near |= 1u << i;
+      }
+      if (near) {                                           // rare: exact quotients
 #pragma unroll 1
-    for (int v = 0; v < 16; ++v) {
-      const int64_t sv = __builtin_amdgcn_readlane((int)slot, v) |
-                         ((int64_t)__builtin_amdgcn_readlane((int)(slot >> 32), v) << 32);
-      if (sv >= 0 && lane < VROW) page_of(sv)[a.f.vcodes + 16 * lane + (sv & 15)] = vplane[wave][lane][v];
+        for (int i = 0; i < 8; ++i)
+          if (near & (1u << i)) {
+            float d = 0.f;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) d = (m == i) ? x[m] - mn : d;
+            const float qe = d / sc;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) xq[m] = (m == i) ? qe : xq[m];
+          }
+      }
+      uint32_t w = 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w |= (uint32_t)fminf(rintf(xq[i]), levels) << (VB * i);   // half to even
+      // bytes VB*j .. VB*j + VB - 1 of the row are planes VB*j + i
+#pragma unroll
+      for (int i = 0; i < VB; ++i) vplane[VB * j + i][v] = (uint8_t)(w >> (8 * i));
+      if (j == 0) {
+        vmin_s[v] = mn;
+        vsc_s[v] = sc;
+      }
+    }
+
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < 16 && slot >= 0) {
+      uint8_t* pg = page_of(slot);
+      reinterpret_cast<float*>(pg + a.f.vmin)[slot & 15] = vmin_s[lane];
+      reinterpret_cast<float*>(pg + a.f.vscale)[slot & 15] = vsc_s[lane];
+    }
+    // Value planes: a whole page takes one 16-byte store per plane; otherwise
+    // each token's byte of each plane goes to its own slot.
+    if (whole) {
+      if (lane < VROW)
+        *reinterpret_cast<uint4*>(page_of(slot0) + a.f.vcodes + 16 * lane) =
+            *reinterpret_cast<const uint4*>(&vplane[lane][0]);
+    } else {
+#pragma unroll 1
+      for (int v = 0; v < 16; ++v) {
+        const int64_t sv = __builtin_amdgcn_readlane((int)slot, v) |
+                           ((int64_t)__builtin_amdgcn_readlane((int)(slot >> 32), v) << 32);
+        if (sv >= 0 && lane < VROW) page_of(sv)[a.f.vcodes + 16 * lane + (sv & 15)] = vplane[lane][v];
+      }
     }
   }
 }
@@ -477,12 +489,11 @@ hipError_t values_mode(const AppendArgs& a, int dtype, int val_mode, hipStream_t
 
 template <int KB>
 hipError_t page_vb(const AppendArgs& a, int val_bits, hipStream_t s) {
-  const int64_t groups = (a.num_tokens + 15) / 16 * a.hkv;
-  const dim3 grid(blocks_for(groups, 4));
+  const dim3 grid((unsigned)((a.num_tokens + 15) / 16 * a.hkv));
   switch (val_bits) {
-    case 2: hipLaunchKernelGGL((append_page_kernel<KB, 2>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((append_page_kernel<KB, 3>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((append_page_kernel<KB, 4>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((append_page_kernel<KB, 2>), grid, dim3(128), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((append_page_kernel<KB, 3>), grid, dim3(128), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((append_page_kernel<KB, 4>), grid, dim3(128), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
