@@ -1,0 +1,81 @@
+"""GPU parity at the full sizes the benchmark runs, in the launch configuration it
+times (same shapes, same split plan, no logits buffer), checked on samples the
+oracle computes one by one:
+
+* append: every field of 512 seeded random tokens (all KV heads) against the
+  oracle's quantization of those tokens, to the same bars as the small cases;
+* decode: outputs of whole (sequence, KV head) groups of query heads against the
+  oracle attending over the GPU-written cache bytes of that sequence (1e-4
+  relative per vector); a second launch with a logits buffer checks the logits
+  of the same heads.  Tiles are handed to waves dynamically, so the fp32
+  summation order may differ between launches; the two must agree to 1e-5.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from kv_cache_vector_randomized_amd import synth
+from tests import gpu_helpers as H
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+# workload -> (sequence, kv head) pairs whose query heads are checked
+SAMPLES = {
+    "gqa_decode": [(0, 0), (7, 3), (15, 7)],
+    "prefill_append": [(0, 0), (0, 5)],
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+@pytest.mark.parametrize("name", list(SAMPLES))
+def test_full_size_append_and_decode_sampled(name):
+    from kv_cache_vector_randomized_amd.torch_api import PagedKVCache
+    w = synth.WORKLOADS[name]
+    print(f"[full size] {name}", flush=True)
+    B, T, G = w.batch, w.context, w.num_q_heads // w.num_kv_heads
+    lay = synth.paged_layout(B, [T] * B, w.seed)          # the benchmark's layout and inputs
+    k = synth.kv_tensor(w, B * T, "k")
+    v = synth.kv_tensor(w, B * T, "v")
+    q = synth.query_tensor(w)
+    slots = np.concatenate([lay.slots(b, 0, T) for b in range(B)])
+    ctx = H.make_context(w)
+    cache = PagedKVCache(ctx, lay.num_blocks)
+    cache.append(H.upload(k, w, torch), H.upload(v, w, torch), torch.from_numpy(slots).cuda())
+    tables = torch.from_numpy(lay.block_tables).cuda()
+    lens = torch.from_numpy(lay.seq_lens).cuda()
+    qd = H.upload(q, w, torch)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    out = cache.decode(qd, tables, lens, T, scale).cpu().numpy().astype(np.float64)
+    logits = torch.full((B, w.num_q_heads, T), float("nan"), device="cuda")
+    out2 = cache.decode(qd, tables, lens, T, scale, logits=logits).cpu().numpy().astype(np.float64)
+    torch.cuda.synchronize()
+    drift = max(H.rel_err(out2[b, h], out[b, h]) for b in range(B) for h in range(w.num_q_heads))
+    assert drift <= 1e-5, f"two launches differ by {drift:.2e}"
+    logits = logits.cpu().numpy().astype(np.float64)
+    cache_np = cache.data.cpu().numpy()
+
+    # append: sampled tokens, every KV head
+    pick = np.sort(np.random.default_rng(99).choice(B * T, size=512, replace=False))
+    qz = H.oracle_quantize(w, k[pick], v[pick])
+    report = {}
+    H.compare_append(w, cache_np, slots[pick], qz, report)
+    print(f"  append sample: {report}")
+
+    # decode: whole kv-head groups of query heads of sampled sequences
+    heads = [(b, kvh * G + i) for b, kvh in SAMPLES[name] for i in range(G)]
+    ref_logits, ref_out = H.oracle_decode(w, q, cache_np, lay, heads=heads)
+    worst = 0.0
+    for b, h in heads:
+        el = H.rel_err(logits[b, h], ref_logits[(b, h)])
+        eo = H.rel_err(out[b, h], ref_out[b, h])
+        worst = max(worst, el, eo)
+        assert el <= H.REL_TOL and eo <= H.REL_TOL, (b, h, el, eo)
+    print(f"  decode sample of {len(heads)} heads: worst relative error {worst:.3e}")
