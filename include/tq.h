@@ -90,7 +90,7 @@ typedef enum {
 
 typedef struct {
   uint32_t abi_version;   /* must equal TQ_ABI_VERSION                              */
-  uint32_t head_dim;      /* d; this build supports 128                             */
+  uint32_t head_dim;      /* d; the library supports 128                           */
   uint32_t num_kv_heads;  /* Hkv >= 1                                               */
   uint32_t num_q_heads;   /* Hq, a multiple of Hkv; Hq/Hkv must be 1, 2 or 4        */
   uint32_t key_bits;      /* 2, 3 or 4                                              */
@@ -121,7 +121,7 @@ typedef struct tq_ctx tq_ctx;
 int tq_abi_version(void);
 
 /* Check a configuration on the host (no GPU needed).  TQ_ERR_INVALID_ARG for
- * malformed values, TQ_ERR_UNSUPPORTED for valid ones this build does not run. */
+ * malformed values, TQ_ERR_UNSUPPORTED for valid ones the library does not run. */
 tq_status tq_validate_config(const tq_config* cfg);
 
 /* Page layout of a configuration, on the host (no GPU needed). */

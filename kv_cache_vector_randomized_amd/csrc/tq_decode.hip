@@ -6,8 +6,9 @@
 // be fused over the compressed cache); lilting.ch TurboQuant article, QJL section
 // (query kept in full precision, projected with the same S; corrected score).
 //
-// One work-group of 4 waves per (split of the context, kv head, sequence); each
-// wave owns 64-token tiles (4 pages of 16 tokens).
+// One work-group of 8 waves per (split of the context, kv head, sequence), one
+// work-group per compute unit; the waves take the split's 64-token tiles (4 pages
+// of 16 tokens) one at a time from a counter in LDS, so they finish together.
 //
 // Logits: per tile, rows = (query head, term of the query), columns = 16 tokens
 // of one page, K = 32 coordinates, on the f16 16x16x32 MFMA.  The rotated query
@@ -303,7 +304,7 @@ __device__ __forceinline__ int limb4(const uint4& x, uint32_t sh) {
 }
 
 template <int KB, bool QJL, int VB, bool VLM>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j16 = lane & 15, grp = lane >> 4;   // column (token of a page) and row group (head) of the lane
@@ -323,9 +324,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   __shared__ int qexp[4], pexp[4];
   // per wave and head, the 64 tokens' value weights: fp32 (Lloyd-Max values) or
   // the fixed-point integers fed to the int8 MFMA (uniform values)
-  __shared__ __align__(16) uint32_t wT[4][4][68];
-  __shared__ float part_ml[4][4][2];
-  __shared__ __align__(16) float part_o[4][4][kDim];
+  __shared__ __align__(16) uint32_t wT[kDecodeWaves][4][68];
+  __shared__ float part_ml[kDecodeWaves][4][2];
+  __shared__ __align__(16) float part_o[kDecodeWaves][4][kDim];
 
   // Block ids of the work-group's pages ([tile - tile_begin][page]; -1: absent):
   // tiles are handed to the waves one at a time, so every wave may need any of them.
@@ -379,14 +380,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int32_t* trow = a.max_blocks > 0 ? table : a.seq_lens + b;
   const int tmax = max(a.max_blocks - 1, 0);
   {
-    const int page = 4 * tile_begin + tid;
+    const int e = min(tid, kMaxPagesPerSplit - 1);
+    const int page = 4 * tile_begin + e;
     int raw = trow[min(page, tmax)];
     asm volatile("" : "+v"(raw));   // keep the read here, ahead of the tile loads
-    blk_lds[tid] = (tid >= 4 * (tile_end - tile_begin) || page >= a.max_blocks || raw < 0 ||
+    if (tid < kMaxPagesPerSplit)
+      blk_lds[e] = (e >= 4 * (tile_end - tile_begin) || page >= a.max_blocks || raw < 0 ||
                     (int64_t)raw >= a.num_blocks || page * 16 >= tok_end)
                        ? -1 : raw;
   }
-  if (tid == 0) tile_ctr = 4;   // tiles tile_begin .. tile_begin + 3 go to waves 0..3
+  if (tid == 0) tile_ctr = kDecodeWaves;   // the first kDecodeWaves tiles go to the waves in order
   int t_cur = tile_begin + wave;
   bool have = t_cur < tile_end && t_cur * 64 < tok_end;
   TilePages tp;
@@ -428,13 +431,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       w[i] = ((tid >> (2 * i)) & 1 ? 0x3C00u : 0xBC00u) | (((tid >> (2 * i + 1)) & 1 ? 0x3C00u : 0xBC00u) << 16);
-    stab[tid] = make_uint4(w[0], w[1], w[2], w[3]);
+    if (tid < 256) stab[tid] = make_uint4(w[0], w[1], w[2], w[3]);
   }
   if (VLM && tid < 16) vcb[tid] = a.c->vc[tid];
 
-  // Rotate query head `wave`: q'' = log2(e) * scale * H(s*q)/sqrt(d), so that the
-  // logits come out in base-2 units for exp2.  Heads >= G stay zero.
-  {
+  // Rotate query head `wave` (waves 0..3): q'' = log2(e) * scale * H(s*q)/sqrt(d),
+  // so that the logits come out in base-2 units for exp2.  Heads >= G stay zero.
+  if (wave < kMaxGroup) {
     const bool f32 = a.q_dtype != TQ_BF16;
     float qx0 = f32 ? __uint_as_float(qw0) : bf16lo(qw0);
     float qx1 = f32 ? __uint_as_float(qw1) : bf16hi(qw0);
@@ -678,7 +681,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     have = has_next;
   }
 
-  // ---- Per-wave totals of head grp (every lane of the row), then merge the 4
+  // ---- Per-wave totals of head grp (every lane of the row), then merge the
   // waves of the work-group.
   row_sum2(l_lane, s_lane);
   if (j16 == 0) {
@@ -699,14 +702,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     dst[1] = make_float4(O[4] + s_lane, O[5] + s_lane, O[6] + s_lane, O[7] + s_lane);
   }
   __syncthreads();
-  // Merge the 4 waves: thread (head h = wave, coordinates 2*lane, 2*lane+1).
+  // Merge the waves: thread (head h = wave < G, coordinates 2*lane, 2*lane+1).
   const int h = wave;
   float M = -INFINITY, L = 0.f, o0 = 0.f, o1 = 0.f;
   if (h < G) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, part_ml[w][h][0]);
+    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, part_ml[w][h][0]);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kDecodeWaves; ++w) {
       const float mw = part_ml[w][h][0];
       const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       L = fmaf(f, part_ml[w][h][1], L);
@@ -807,8 +810,8 @@ namespace {
 template <int KB, bool QJL, int VB>
 hipError_t decode_v(const DecodeArgs& a, int val_mode, hipStream_t s) {
   const dim3 grid((unsigned)a.splits, (unsigned)a.hkv, (unsigned)a.batch);
-  if (val_mode == TQ_VAL_LLOYD) hipLaunchKernelGGL((decode_kernel<KB, QJL, VB, true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((decode_kernel<KB, QJL, VB, false>), grid, dim3(256), 0, s, a);
+  if (val_mode == TQ_VAL_LLOYD) hipLaunchKernelGGL((decode_kernel<KB, QJL, VB, true>), grid, dim3(64 * kDecodeWaves), 0, s, a);
+  else hipLaunchKernelGGL((decode_kernel<KB, QJL, VB, false>), grid, dim3(64 * kDecodeWaves), 0, s, a);
   return hipGetLastError();
 }
 

@@ -285,14 +285,16 @@ tq_status tq_create(const tq_config* cfg, const int8_t* signs_host, const float*
   e = hipMemcpy(ctx->consts, h, sizeof(tq::DevConsts), hipMemcpyHostToDevice);
   delete h;
   if (e != hipSuccess) { hipFree(ctx->consts); delete ctx; return hip_fail(e, "hipMemcpy"); }
-  // One round of resident decode work-groups on this device.
+  // Decode grid target: kDecodeWgsPerCu work-groups per compute unit (fewer if
+  // fewer fit), all resident at once.
   int per_cu = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
           &per_cu, tq::decode_kernel_ptr((int)cfg->key_bits, (int)cfg->key_mode, (int)cfg->val_bits,
                                          (int)cfg->val_mode),
-          256, 0) != hipSuccess ||
+          64 * tq::kDecodeWaves, 0) != hipSuccess ||
       per_cu <= 0)
-    per_cu = 2;
+    per_cu = 1;
+  per_cu = std::min(per_cu, tq::kDecodeWgsPerCu);
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, ctx->device) != hipSuccess || cus <= 0)
     cus = 256;
   (void)hipGetLastError();

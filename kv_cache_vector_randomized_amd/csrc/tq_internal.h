@@ -15,6 +15,8 @@ constexpr int kLutCells = 256;     // cells of the code look-up grid (see QLut)
 constexpr int kMaxGroup = 4;       // q heads per kv head handled by one work-group
 constexpr int kBlockTokensDev = TQ_BLOCK_TOKENS;
 constexpr int kMaxPagesPerSplit = 256;   // 64 tiles of 64 tokens
+constexpr int kDecodeWaves = 8;           // waves of a decode work-group (they share its tiles)
+constexpr int kDecodeWgsPerCu = 1;        // decode work-groups per compute unit the split plan aims at
 constexpr size_t kCounterBytes = 65536;   // arrival counters at the start of the decode workspace
 
 // One cell of the uniform grid that maps a rotated coordinate y to its code.
