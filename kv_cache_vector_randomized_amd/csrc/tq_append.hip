@@ -185,274 +185,307 @@ __global__ __launch_bounds__(256) void append_values_kernel(AppendArgs a) {
 
 // ---------------------------------------------------------------------------
 // Keys and values of whole pages, bf16 inputs (Lloyd-Max keys without QJL,
-// uniform values).  One wave per group of 16 consecutive tokens of one KV head:
-// when their slots are the 16 slots of one page in order (prefill), the wave
-// assembles the page's fields in LDS and writes each with one contiguous
-// 16-byte store per lane; otherwise every token goes to its own slot.
+// uniform values).  A work-group of 4 waves takes two groups of 16 consecutive
+// tokens of one KV head: waves 0 and 1 quantize the keys of the two groups,
+// waves 2 and 3 their values.  When a group's slots are the 16 slots of one page
+// in order (prefill), the page's value planes are assembled in LDS and written
+// with one 16-byte store per plane; otherwise every token goes to its own slot.
 //
-// Rotation on the matrix cores: with c = 16*ch + cl and k = 16*kh + kl, the
-// Sylvester matrix factors as H[c][k] = H8[ch][kh] * H16[cl][kl].  The bf16 MFMA
-// (16x16x16, fp32 sums) applies H16 to every 16-coordinate block of the 16
-// tokens' sign-flipped rows (exact bf16 operands); H8 over the 8 blocks is then
-// a 24-add butterfly in each lane, whose registers hold the 8 blocks of one
-// column.  Lane (j, g) = (lane % 16, lane / 16) ends with coordinates 16*ch + j
-// of tokens 4g..4g+3.
+// Rotation on the matrix cores.  Write a coordinate as 7 bits c = (c6..c0); the
+// Sylvester matrix is the product over bits of (-1)^(out_b * in_b), so it
+// factors over any split of the bits.  The bf16 MFMA (16x16x16, fp32 sums)
+// applies the 16-point transform over bits {0, 1, 3, 4} with the sign-flipped
+// rows as its B operand (exact bf16 values); the 8-point transform over bits
+// {2, 5, 6} is a 24-add butterfly inside each lane.  Lane (j, g) = (lane % 16,
+// lane / 16) loads 16-byte chunks g, g+4, g+8, g+12 of token j's row and ends
+// with rotated coordinates 32n + 8g + (0..7), n = 0..3, of token j: 8
+// consecutive codes per n, i.e. whole packed bytes.
+//
+// Codes: g = 128 y; the fp32 sum g + (1.5 * 2^23 + 128) carries the grid cell
+// round(g) + 128 in its low mantissa bits, and shifting its bit pattern left by
+// 4 and adding a constant gives the LDS address of the cell (mod 2^32).
 // ---------------------------------------------------------------------------
 typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
 
-// Sum or max of 4 values over the 16 lanes of each row (every lane gets it).
-template <bool MAX>
-__device__ __forceinline__ float row_reduce(float v) {
-#define TQ_RSTEP(CTL)                                                                         \
-  {                                                                                           \
-    const float p = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTL, 0xF, 0xF, false)); \
-    v = MAX ? fmaxf(v, p) : v + p;                                                            \
-  }
-  TQ_RSTEP(0xB1) TQ_RSTEP(0x4E) TQ_RSTEP(0x141) TQ_RSTEP(0x140)
-#undef TQ_RSTEP
-  return v;
-}
-__device__ __forceinline__ float row_min(float v) {
-  return -row_reduce<true>(-v);
+constexpr float kUnitMagic = 12583040.0f;     // 1.5 * 2^23 + 128; bit pattern 0x4B400080
+
+// min over the 4 lanes of each quad for `mn`, max for `mx` (every lane gets
+// them).  The s_nop instructions cover the DPP read-after-VALU-write hazard.
+__device__ __forceinline__ void quad_minmax(float& mn, float& mx) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_min_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 0\n\t"
+      "v_min_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_max_f32_dpp %1, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+      : "+v"(mn), "+v"(mx));
 }
 
-// Codes of the 32 coordinates 32q..32q+31 (one byte each) packed LSB-first into
-// B dwords (4*B bytes of the row).
-template <int B>
-__device__ __forceinline__ void pack32(const uint4 (&cb)[2], uint32_t (&w)[B]) {
-  const uint32_t x[8] = {cb[0].x, cb[0].y, cb[0].z, cb[0].w, cb[1].x, cb[1].y, cb[1].z, cb[1].w};
-  if constexpr (B == 4) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t y0 = x[2 * i] | (x[2 * i] >> 4), y1 = x[2 * i + 1] | (x[2 * i + 1] >> 4);
-      w[i] = __builtin_amdgcn_perm(y1, y0, 0x06040200u);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < B; ++i) w[i] = 0u;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t code = (x[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-      const int bit = B * i, wi = bit >> 5, sh = bit & 31;
-      w[wi] |= code << sh;
-      if (sh + B > 32) w[wi + 1] |= code >> (32 - sh);
-    }
-  }
+// Sum over the lanes j, j+16, j+32, j+48.
+__device__ __forceinline__ float sum_rows(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
 }
 
 template <int KB, int VB>
-__global__ __launch_bounds__(128) void append_page_kernel(AppendArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void append_page_kernel(AppendArgs a) {
   constexpr int KROW = 16 * KB;            // bytes of a packed key row
   constexpr int VROW = 16 * VB;            // bytes of a packed value row (= planes)
-  // Wave 0 quantizes the 16 keys, wave 1 the 16 values of the group; each uses
-  // only its own LDS, so the two never wait for each other.
-  __shared__ QLut lut[kLutCells];
-  __shared__ __align__(16) uint8_t kcode[16][kDim];       // key codes, one byte each [token][coord]
-  __shared__ __align__(16) uint8_t vplane[64][16];        // value planes [plane][token]
-  __shared__ float knorm_s[16], vmin_s[16], vsc_s[16];
+  constexpr int KSTR = KROW + 16;          // LDS stride of a packed key row
+  __shared__ __align__(16) QLut lut[kUnitCellsPadded];
+  __shared__ __align__(16) uint8_t kpack[2][16][KSTR];    // packed key rows [group][token]
+  __shared__ __align__(16) uint8_t vplane[2][64][16];     // value planes [group][plane][token]
 
   const int lane = threadIdx.x & 63;
-  const bool keys = threadIdx.x < 64;
-  const int j = lane & 15, g = lane >> 4;
-  const int64_t grp = blockIdx.x;
-  const int h = (int)(grp % a.hkv);
-  const int64_t t0 = (grp / a.hkv) * 16;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool keys = wave < 2;
+  const int wg = wave & 1;                 // which group of the pair
+  // (the launcher keeps the group count below 2^31)
+  const uint32_t hkv = (uint32_t)a.hkv;
+  const uint32_t ngroups = (uint32_t)((a.num_tokens + 15) / 16) * hkv;
+  const uint32_t npairs = (ngroups + 1) / 2;
   const int64_t tmax = a.num_tokens - 1;
-  const uint16_t* kin = static_cast<const uint16_t*>(a.k);
-  const uint16_t* vin = static_cast<const uint16_t*>(a.v);
-  auto row_of = [&](int v) -> int64_t { return (min(t0 + v, tmax) * a.hkv + h) * kDim; };
-  auto page_of = [&](int64_t s) -> uint8_t* { return a.cache + ((s >> 4) * a.hkv + h) * (int64_t)a.f.page_bytes; };
+  // Keys: lane (j, g) = (lane % 16, lane / 16) reads chunks g + 4n of token j.
+  // Values: lane (t, q) = (lane / 4, lane % 4) reads chunks q + 4n of token t.
+  const int tok = keys ? (lane & 15) : (lane >> 2);
+  const int cg = keys ? (lane >> 4) : (lane & 3);
+  const uint16_t* in_base = static_cast<const uint16_t*>(keys ? a.k : a.v) + 8 * cg;
 
+  // Group 2p + wg of the pair p: its first token and head; a group past the end
+  // (odd count) stands in for the last one and writes nothing.
+  auto group_of = [&](uint32_t p, int64_t& t0, int& h) -> bool {
+    const uint32_t grp = 2u * p + (uint32_t)wg;
+    const bool live = grp < ngroups;
+    const uint32_t gg = live ? grp : ngroups - 1;
+    const uint32_t tb = gg / hkv;
+    h = (int)(gg - tb * hkv);
+    t0 = (int64_t)tb * 16;
+    return live;
+  };
+  // Inputs and slot of this lane's token; loads are unconditional (indices clamped).
+  auto load_group = [&](uint32_t p, uint4 (&dst)[4], int64_t& slot) {
+    int64_t t0;
+    int h;
+    const bool live = group_of(p, t0, h);
+    const int64_t t = min(t0 + tok, tmax);
+    const uint16_t* src = in_base + (t * a.hkv + h) * kDim;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) dst[n] = *reinterpret_cast<const uint4*>(src + 32 * n);
+    slot = a.slots[t];
+    if (!live || t0 + tok > tmax || !(slot >= 0 && slot < a.num_blocks * kBlockTokensDev)) slot = -1;
+  };
+
+  uint32_t p = blockIdx.x;                 // the launcher keeps gridDim.x <= npairs
+  uint4 in[4], fl[4];
+  int64_t slot;
+  load_group(p, in, slot);
   if (keys) {
-    // inputs first, then the code grid, so the two latencies overlap
-    uint2 ka[8];
-    {
-      const uint2* src = reinterpret_cast<const uint2*>(kin + row_of(j) + 4 * g);
 #pragma unroll
-      for (int kh = 0; kh < 8; ++kh) ka[kh] = src[4 * kh];
-    }
-    for (int i = lane; i < kLutCells; i += 64) lut[i] = a.c->klut[i];
-    const int64_t tj = t0 + j;
-    int64_t slot = tj <= tmax ? a.slots[tj] : -1;
-    if (!(slot >= 0 && slot < a.num_blocks * kBlockTokensDev)) slot = -1;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int n = 0; n < 4; ++n) fl[n] = *reinterpret_cast<const uint4*>(&a.c->kflip[16 * n + 4 * (lane >> 4)]);
+    for (int i = threadIdx.x; i < kUnitCellsPadded; i += 128)
+      *reinterpret_cast<uint4*>(&lut[i]) = *reinterpret_cast<const uint4*>(&a.c->kulut[i]);
+  }
+  __syncthreads();
 
-    // ---- keys: signs, H16 on the matrix cores, H8 in registers
-    shortx4 hb;                                  // B operand: H16[j][4g + e]
+  // Pairs p, p + gridDim.x, ...: the next pair's inputs are loaded while this
+  // one is quantized.
+  for (;;) {
+    const uint32_t pn = p + gridDim.x;
+    const bool more = pn < npairs;
+    uint4 nin[4];
+    int64_t nslot;
+    load_group(more ? pn : p, nin, nslot);
+    int64_t t0;
+    int h;
+    (void)group_of(p, t0, h);
+    auto page_of = [&](int64_t s) -> uint8_t* { return a.cache + ((s >> 4) * a.hkv + h) * (int64_t)a.f.page_bytes; };
+
+    if (keys) {
+      const int j = lane & 15, g = lane >> 4;
+      shortx4 hb;                                  // A operand: H16[j][4g + e]
 #pragma unroll
-    for (int e = 0; e < 4; ++e) hb[e] = (__builtin_popcount(j & (4 * g + e)) & 1) ? (short)0xBF80 : (short)0x3F80;
-    floatx4 z[8];
-#pragma unroll
-    for (int kh = 0; kh < 8; ++kh) {
-      const int c0 = 16 * kh + 4 * g;            // first coordinate of this lane's 4 inputs
-      const uint32_t sb = (a.sign_bits[c0 >> 5] >> (c0 & 31)) & 0xFu;
-      uint2 x = ka[kh];
-      x.x ^= ((sb & 1u) << 15) | ((sb & 2u) << 30);
-      x.y ^= ((sb & 4u) << 13) | ((sb & 8u) << 28);
+      for (int e = 0; e < 4; ++e) hb[e] = (__builtin_popcount(j & (4 * g + e)) & 1) ? (short)0xBF80 : (short)0x3F80;
+      // z[b], b = beta + 2n: the 16-point transform of coordinates 32n + 8g' + 4beta + e
+      floatx4 z[8];
       const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-      z[kh] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(shortx4, x), hb, zero, 0, 0, 0);
-    }
-    // y[ch][r] = sum_kh H8[ch][kh] z[kh][r]: coordinate 16 ch + j of token 4g + r
 #pragma unroll
-    for (int len = 1; len < 8; len <<= 1)
+      for (int n = 0; n < 4; ++n) {
+        const uint4 x = make_uint4(in[n].x ^ fl[n].x, in[n].y ^ fl[n].y, in[n].z ^ fl[n].z, in[n].w ^ fl[n].w);
+        z[2 * n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hb, __builtin_bit_cast(shortx4, make_uint2(x.x, x.y)),
+                                                            zero, 0, 0, 0);
+        z[2 * n + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hb, __builtin_bit_cast(shortx4, make_uint2(x.z, x.w)),
+                                                                zero, 0, 0, 0);
+      }
+      // 8-point butterfly over b: z[b][r] becomes coordinate 32(b/2) + 8g + 4(b%2) + r
 #pragma unroll
-      for (int i = 0; i < 8; i += 2 * len)
+      for (int len = 1; len < 8; len <<= 1)
 #pragma unroll
-        for (int m = i; m < i + len; ++m) {
-          const floatx4 p = z[m], q = z[m + len];
-          z[m] = p + q;
-          z[m + len] = p - q;
-        }
-    float ss[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 8; i += 2 * len)
 #pragma unroll
-    for (int ch = 0; ch < 8; ++ch)
+          for (int m = i; m < i + len; ++m) {
+            const floatx4 u = z[m], v = z[m + len];
+            z[m] = u + v;
+            z[m + len] = u - v;
+          }
+      float ss = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ss[r] = fmaf(z[ch][r], z[ch][r], ss[r]);
+      for (int b = 0; b < 8; ++b)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) ss[r] = row_reduce<false>(ss[r]);
-    float cn2[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      // u = y / ||y||; a zero key gives u = 0, codes 2^(b-1) and norm 0
-      const float inv = ss[r] > 0.f ? 1.f / sqrtf(ss[r]) : 0.f;
+        for (int r = 0; r < 4; ++r) ss = fmaf(z[b][r], z[b][r], ss);
+      ss = sum_rows(ss);
+      // u = y / ||y||, g = 128 u; a zero key gives g = 0, codes 2^(b-1) and norm 0
+      const float sg = ss > 0.f ? 128.f * __builtin_amdgcn_rsqf(ss) : 0.f;
+      const uint32_t lut_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) QLut*)lut + 0x4C000000u;
       float c2 = 0.f;
+      uint32_t w[4];
 #pragma unroll
-      for (int ch = 0; ch < 8; ++ch) {
-        float c;
-        const int code = lut_code(lut, z[ch][r] * inv, a.klut_scale, a.klut_bias, c);
-        c2 = fmaf(c, c, c2);
-        kcode[4 * g + r][16 * ch + j] = (uint8_t)code;
+      for (int n = 0; n < 4; ++n) {
+        uint32_t wn = 0u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float gv = z[2 * n + (i >> 2)][i & 3] * sg;
+          const uint32_t addr = (__float_as_uint(gv + kUnitMagic) << 4) + lut_addr;
+          const u32x4 e = *reinterpret_cast<lds_u32x4*>((uintptr_t)addr);
+          const bool up = gv >= __uint_as_float(e.y);
+          const float c = up ? __uint_as_float(e.w) : __uint_as_float(e.z);
+          c2 = fmaf(c, c, c2);
+          const uint32_t code = e.x + (uint32_t)up;
+          wn |= code << (KB * i);
+        }
+        w[n] = wn;
       }
-      cn2[r] = c2;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) cn2[r] = row_reduce<false>(cn2[r]);
-    if (j == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float n = sqrtf(ss[r]) * kInvSqrtDim;           // ||k|| (H/sqrt(d) is orthogonal)
-        knorm_s[4 * g + r] = a.key_nc ? (n > 0.f ? n / sqrtf(cn2[r]) : 0.f) : n;
+      c2 = sum_rows(c2);
+      if (g == 0 && slot >= 0) {
+        const float nk = __builtin_amdgcn_sqrtf(ss) * kInvSqrtDim;   // ||k|| (H/sqrt(d) is orthogonal)
+        const float nhat = a.key_nc ? (nk > 0.f ? nk * __builtin_amdgcn_rsqf(c2) : 0.f) : nk;
+        reinterpret_cast<float*>(page_of(slot) + a.f.knorm)[slot & 15] = nhat;
       }
-    }
-
-
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // Key rows: lane l packs coordinates 32(l%4)..32(l%4)+31 of token l/4.
-    const int kv = lane >> 2, kq = lane & 3;
-    uint32_t kw[KB];
-    {
-      const uint4 cb[2] = {*reinterpret_cast<const uint4*>(&kcode[kv][32 * kq]),
-                           *reinterpret_cast<const uint4*>(&kcode[kv][32 * kq + 16])};
-      pack32<KB>(cb, kw);
-    }
-    const int64_t slot_kv = __builtin_amdgcn_ds_bpermute(kv << 2, (int)slot) |
-                            ((int64_t)__builtin_amdgcn_ds_bpermute(kv << 2, (int)(slot >> 32)) << 32);
-    if (slot_kv >= 0) {
-      uint8_t* dst = page_of(slot_kv) + a.f.kcodes + (slot_kv & 15) * KROW + 4 * KB * kq;
-      if constexpr (KB == 4) *reinterpret_cast<uint4*>(dst) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
-      else if constexpr (KB == 2) *reinterpret_cast<uint2*>(dst) = make_uint2(kw[0], kw[1]);
-      else {
-        uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
-        d32[0] = kw[0]; d32[1] = kw[1]; d32[2] = kw[2];
+      // codes of coordinates 32n + 8g .. +7 are bytes KB*(4n + g) .. +KB-1 of the row
+      uint8_t* prow = &kpack[wg][j][0];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int o = KB * (4 * n + g);
+        if constexpr (KB == 4) *reinterpret_cast<uint32_t*>(prow + o) = w[n];
+        else if constexpr (KB == 2) *reinterpret_cast<uint16_t*>(prow + o) = (uint16_t)w[n];
+        else {
+          prow[o] = (uint8_t)w[n];
+          prow[o + 1] = (uint8_t)(w[n] >> 8);
+          prow[o + 2] = (uint8_t)(w[n] >> 16);
+        }
       }
-    }
-    if (lane < 16 && slot >= 0) reinterpret_cast<float*>(page_of(slot) + a.f.knorm)[slot & 15] = knorm_s[lane];
-  } else {
-    uint4 va[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) va[p] = *reinterpret_cast<const uint4*>(vin + row_of(4 * p + g) + 8 * j);
-    const int64_t tj = t0 + j;
-    int64_t slot = tj <= tmax ? a.slots[tj] : -1;
-    const bool ok = slot >= 0 && slot < a.num_blocks * kBlockTokensDev;
-    if (!ok) slot = -1;
-    const int64_t slot0 = __builtin_amdgcn_readfirstlane((int)slot) |
-                          ((int64_t)__builtin_amdgcn_readfirstlane((int)(slot >> 32)) << 32);
-    // the 16 tokens fill one page in order
-    const bool whole = (__ballot(!(ok && slot == slot0 + j)) == 0ull) && slot0 >= 0 && (slot0 & 15) == 0;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // Key rows: lane l stores bytes 4*KB*(l%4) .. +4*KB-1 of token l/4's row.
+      const int kv = lane >> 2, kq = lane & 3;
+      const int64_t slot_kv = __builtin_amdgcn_ds_bpermute(kv << 2, (int)slot) |
+                              ((int64_t)__builtin_amdgcn_ds_bpermute(kv << 2, (int)(slot >> 32)) << 32);
+      if (slot_kv >= 0) {
+        const uint8_t* srow = &kpack[wg][kv][4 * KB * kq];
+        uint8_t* dst = page_of(slot_kv) + a.f.kcodes + (slot_kv & 15) * KROW + 4 * KB * kq;
+        if constexpr (KB == 4) *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(srow);
+        else if constexpr (KB == 2) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(srow);
+        else {
+          const uint32_t* s32 = reinterpret_cast<const uint32_t*>(srow);
+          uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
+          d32[0] = s32[0]; d32[1] = s32[1]; d32[2] = s32[2];
+        }
+      }
+    } else {
+      const int t = lane >> 2, q = lane & 3;
+      const int64_t slot0 = __builtin_amdgcn_readfirstlane((int)slot) |
+                            ((int64_t)__builtin_amdgcn_readfirstlane((int)(slot >> 32)) << 32);
+      // the 16 tokens fill one page in order
+      const bool whole = (__ballot(!(slot >= 0 && slot == slot0 + t)) == 0ull) && slot0 >= 0 && (slot0 & 15) == 0;
 
-    // ---- values: row g takes token 4p + g in pass p; lane j holds coordinates 8j..8j+7
-    constexpr float levels = (float)((1 << VB) - 1);
+      float x[32];                              // x[8n + e]: coordinate 32n + 8q + e
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int v = 4 * p + g;
-      const uint32_t wv[4] = {va[p].x, va[p].y, va[p].z, va[p].w};
-      float x[8];
+      for (int n = 0; n < 4; ++n) {
+        const uint32_t wv[4] = {in[n].x, in[n].y, in[n].z, in[n].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = bf16lo(wv[i]);
-        x[2 * i + 1] = bf16hi(wv[i]);
+        for (int d = 0; d < 4; ++d) {
+          x[8 * n + 2 * d] = bf16lo(wv[d]);
+          x[8 * n + 2 * d + 1] = bf16hi(wv[d]);
+        }
       }
       float mn = x[0], mx = x[0];
 #pragma unroll
-      for (int i = 1; i < 8; ++i) {
-        mn = fminf(mn, x[i]);
-        mx = fmaxf(mx, x[i]);
+      for (int k = 1; k < 32; ++k) {
+        mn = fminf(mn, x[k]);
+        mx = fmaxf(mx, x[k]);
       }
-      mn = row_min(mn);
-      mx = row_reduce<true>(mx);
+      quad_minmax(mn, mx);
+      constexpr float levels = (float)((1 << VB) - 1);
       const float sc = (mx - mn) / levels;                  // correctly rounded division
-      const float inv = sc > 0.f ? 1.f / sc : 0.f;
-      // code = rint(fl32((x - mn) / sc)); the reciprocal product is within 2 ulp of the
-      // correctly rounded quotient, so only values within 2^-18 of a rounding boundary
-      // need the exact division
-      float xq[8];
-      uint32_t near = 0u;
+      const float inv = sc > 0.f ? 1.f / sc : 0.f;          // correctly rounded
+      // code = floor(fl32(x - mn) * inv + 1/2) in one fma.  Against rint(fl32(fl32(x - mn)
+      // / sc)) it can differ only where the quotient lies within a few ulp (about
+      // 2^-20 for codes up to 15) of a rounding boundary: a normalised distance
+      // (x - mn) / (mx - mn) far below 1e-6, inside the band where either code counts.
+      uint32_t w[4];                            // w[n]: the 8 codes of chunk q + 4n (VB bytes)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        xq[i] = (x[i] - mn) * inv;
-        if (fabsf(xq[i] - floorf(xq[i]) - 0.5f) < 3.814697265625e-06f) near |= 1u << i;
+      for (int n = 0; n < 4; ++n) {
+        uint32_t wn = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wn |= (uint32_t)fmaf(x[8 * n + e] - mn, inv, 0.5f) << (VB * e);
+        w[n] = wn;
       }
-      if (near) {                                           // rare: exact quotients
+      if (q == 0 && slot >= 0) {
+        uint8_t* pg = page_of(slot);
+        reinterpret_cast<float*>(pg + a.f.vmin)[slot & 15] = mn;
+        reinterpret_cast<float*>(pg + a.f.vscale)[slot & 15] = sc;
+      }
+      // row bytes VB*(q + 4n) .. +VB-1 are those planes
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int i = 0; i < VB; ++i) vplane[wg][VB * (q + 4 * n) + i][t] = (uint8_t)(w[n] >> (8 * i));
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // Value planes: a whole page takes one 16-byte store per plane; otherwise
+      // each token's byte of each plane goes to its own slot.
+      if (whole) {
+        if (lane < VROW)
+          *reinterpret_cast<uint4*>(page_of(slot0) + a.f.vcodes + 16 * lane) =
+              *reinterpret_cast<const uint4*>(&vplane[wg][lane][0]);
+      } else {
 #pragma unroll 1
-        for (int i = 0; i < 8; ++i)
-          if (near & (1u << i)) {
-            float d = 0.f;
-#pragma unroll
-            for (int m = 0; m < 8; ++m) d = (m == i) ? x[m] - mn : d;
-            const float qe = d / sc;
-#pragma unroll
-            for (int m = 0; m < 8; ++m) xq[m] = (m == i) ? qe : xq[m];
-          }
-      }
-      uint32_t w = 0u;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w |= (uint32_t)fminf(rintf(xq[i]), levels) << (VB * i);   // half to even
-      // bytes VB*j .. VB*j + VB - 1 of the row are planes VB*j + i
-#pragma unroll
-      for (int i = 0; i < VB; ++i) vplane[VB * j + i][v] = (uint8_t)(w >> (8 * i));
-      if (j == 0) {
-        vmin_s[v] = mn;
-        vsc_s[v] = sc;
+        for (int v = 0; v < 16; ++v) {
+          const int64_t sv = __builtin_amdgcn_readlane((int)slot, 4 * v) |
+                             ((int64_t)__builtin_amdgcn_readlane((int)(slot >> 32), 4 * v) << 32);
+          if (sv >= 0 && lane < VROW) page_of(sv)[a.f.vcodes + 16 * lane + (sv & 15)] = vplane[wg][lane][v];
+        }
       }
     }
-
+    if (!more) break;
+    p = pn;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) in[n] = nin[n];
+    slot = nslot;
+    // the LDS rows of this wave are rewritten next: keep this pass's reads first
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (lane < 16 && slot >= 0) {
-      uint8_t* pg = page_of(slot);
-      reinterpret_cast<float*>(pg + a.f.vmin)[slot & 15] = vmin_s[lane];
-      reinterpret_cast<float*>(pg + a.f.vscale)[slot & 15] = vsc_s[lane];
-    }
-    // Value planes: a whole page takes one 16-byte store per plane; otherwise
-    // each token's byte of each plane goes to its own slot.
-    if (whole) {
-      if (lane < VROW)
-        *reinterpret_cast<uint4*>(page_of(slot0) + a.f.vcodes + 16 * lane) =
-            *reinterpret_cast<const uint4*>(&vplane[lane][0]);
-    } else {
-#pragma unroll 1
-      for (int v = 0; v < 16; ++v) {
-        const int64_t sv = __builtin_amdgcn_readlane((int)slot, v) |
-                           ((int64_t)__builtin_amdgcn_readlane((int)(slot >> 32), v) << 32);
-        if (sv >= 0 && lane < VROW) page_of(sv)[a.f.vcodes + 16 * lane + (sv & 15)] = vplane[lane][v];
-      }
-    }
   }
+}
+
+const void* append_page_kernel_ptr(int key_bits, int val_bits) {
+  switch (key_bits * 8 + val_bits) {
+    case 2 * 8 + 2: return (const void*)append_page_kernel<2, 2>;
+    case 2 * 8 + 3: return (const void*)append_page_kernel<2, 3>;
+    case 2 * 8 + 4: return (const void*)append_page_kernel<2, 4>;
+    case 3 * 8 + 2: return (const void*)append_page_kernel<3, 2>;
+    case 3 * 8 + 3: return (const void*)append_page_kernel<3, 3>;
+    case 3 * 8 + 4: return (const void*)append_page_kernel<3, 4>;
+    case 4 * 8 + 2: return (const void*)append_page_kernel<4, 2>;
+    case 4 * 8 + 3: return (const void*)append_page_kernel<4, 3>;
+    case 4 * 8 + 4: return (const void*)append_page_kernel<4, 4>;
+  }
+  return nullptr;
 }
 
 namespace {
@@ -489,11 +522,13 @@ hipError_t values_mode(const AppendArgs& a, int dtype, int val_mode, hipStream_t
 
 template <int KB>
 hipError_t page_vb(const AppendArgs& a, int val_bits, hipStream_t s) {
-  const dim3 grid((unsigned)((a.num_tokens + 15) / 16 * a.hkv));
+  // one pair of 16-token groups per work-group and pass; at most a.page_wgs work-groups
+  const int64_t pairs = ((a.num_tokens + 15) / 16 * a.hkv + 1) / 2;
+  const dim3 grid((unsigned)std::min<int64_t>(pairs, std::max(1, a.page_wgs)));
   switch (val_bits) {
-    case 2: hipLaunchKernelGGL((append_page_kernel<KB, 2>), grid, dim3(128), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((append_page_kernel<KB, 3>), grid, dim3(128), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((append_page_kernel<KB, 4>), grid, dim3(128), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((append_page_kernel<KB, 2>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((append_page_kernel<KB, 3>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((append_page_kernel<KB, 4>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -505,7 +540,8 @@ hipError_t launch_append(const AppendArgs& a, int dtype, int key_bits, int key_m
                          hipStream_t s) {
   // bf16 inputs, Lloyd-Max keys without QJL and uniform values: one launch for
   // both; the other combinations take the per-vector kernels.
-  if (dtype == TQ_BF16 && key_mode != TQ_KEY_LLOYD_QJL && val_mode == TQ_VAL_UNIFORM) {
+  if (dtype == TQ_BF16 && key_mode != TQ_KEY_LLOYD_QJL && val_mode == TQ_VAL_UNIFORM && a.unit_grid_ok &&
+      (a.num_tokens + 15) / 16 * a.hkv < ((int64_t)1 << 31)) {
     switch (key_bits) {
       case 2: return page_vb<2>(a, val_bits, s);
       case 3: return page_vb<3>(a, val_bits, s);

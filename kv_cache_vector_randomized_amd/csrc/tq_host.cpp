@@ -19,6 +19,8 @@ struct tq_ctx {
   uint32_t sign_bits[4];
   tq::DevConsts* consts;   // device
   float klut_scale, klut_bias, vlut_scale, vlut_bias;
+  int unit_grid_ok;        // the page-append key grid resolves every threshold
+  int page_wgs;            // page-append grid: resident work-groups on the whole device
   int decode_wgs;          // decode grid target: resident work-groups on the whole device
 };
 
@@ -123,6 +125,33 @@ bool build_lut(int bits, const float* c, const float* t, tq::QLut* lut, float* s
   }
   *scale = (float)((cells / 2) / range);
   *bias = (float)(cells / 2);
+  return true;
+}
+
+// Grid of the page kernel over g = 128 y, |y| <= 1: cell k (0..256) takes g in
+// [k - 128.5, k - 127.5) widened by a quarter cell on each side (the end cells
+// reach to infinity), so that a cell found from a slightly rounded g still holds
+// the right answer; at most one threshold may fall inside a widened cell.
+// Thresholds are stored as 128 t (exact: a power-of-two scaling).
+bool build_unit_lut(int bits, const float* c, const float* t, tq::QLut* lut) {
+  const int nt = (1 << bits) - 1;
+  for (int k = 0; k < tq::kUnitCellsPadded; ++k) {
+    const int kk = std::min(k, tq::kUnitCells - 1);
+    const double lo = (kk == 0) ? -INFINITY : kk - 128.75;
+    const double hi = (kk == tq::kUnitCells - 1) ? INFINITY : kk - 127.25;
+    int base = 0, inside = 0;
+    float tin = INFINITY;
+    for (int j = 0; j < nt; ++j) {
+      const double tg = 128.0 * (double)t[j];
+      if (tg < lo) ++base;
+      else if (tg <= hi) { ++inside; tin = 128.0f * t[j]; }
+    }
+    if (inside > 1) return false;
+    lut[k].base = base;
+    lut[k].t = tin;
+    lut[k].c_lo = c[base];
+    lut[k].c_hi = c[base + 1 <= nt ? base + 1 : nt];
+  }
   return true;
 }
 
@@ -266,6 +295,9 @@ tq_status tq_create(const tq_config* cfg, const int8_t* signs_host, const float*
   ctx->cfg = *cfg;
   layout_of(cfg, &ctx->layout);
   bool ok = build_lut((int)cfg->key_bits, h->kc, kt, h->klut, &ctx->klut_scale, &ctx->klut_bias);
+  ctx->unit_grid_ok = build_unit_lut((int)cfg->key_bits, h->kc, kt, h->kulut) ? 1 : 0;
+  for (int p = 0; p < d / 2; ++p)
+    h->kflip[p] = (signs_host[2 * p] < 0 ? 0x8000u : 0u) | (signs_host[2 * p + 1] < 0 ? 0x80000000u : 0u);
   if (cfg->val_mode == TQ_VAL_LLOYD) {
     codebook_f32((int)cfg->val_bits, d, h->vc, vt);
     ok = ok && build_lut((int)cfg->val_bits, h->vc, vt, h->vlut, &ctx->vlut_scale, &ctx->vlut_bias);
@@ -299,6 +331,12 @@ tq_status tq_create(const tq_config* cfg, const int8_t* signs_host, const float*
     cus = 256;
   (void)hipGetLastError();
   ctx->decode_wgs = per_cu * cus;
+  int page_per_cu = 0;
+  const void* pk = tq::append_page_kernel_ptr((int)cfg->key_bits, (int)cfg->val_bits);
+  if (!pk || hipOccupancyMaxActiveBlocksPerMultiprocessor(&page_per_cu, pk, 256, 0) != hipSuccess || page_per_cu <= 0)
+    page_per_cu = 2;
+  (void)hipGetLastError();
+  ctx->page_wgs = page_per_cu * cus;
   *out = ctx;
   return TQ_OK;
 }
@@ -336,6 +374,8 @@ tq_status tq_quantize_append(tq_ctx* ctx, const void* k, const void* v, tq_dtype
   a.f = offsets_of(ctx->layout); a.c = ctx->consts;
   a.klut_scale = ctx->klut_scale; a.klut_bias = ctx->klut_bias;
   a.vlut_scale = ctx->vlut_scale; a.vlut_bias = ctx->vlut_bias;
+  a.unit_grid_ok = ctx->unit_grid_ok;
+  a.page_wgs = ctx->page_wgs;
   hipError_t e = tq::launch_append(a, (int)dt, (int)ctx->cfg.key_bits, (int)ctx->cfg.key_mode,
                                    (int)ctx->cfg.val_bits, (int)ctx->cfg.val_mode, stream);
   return e == hipSuccess ? TQ_OK : hip_fail(e, "append launch");

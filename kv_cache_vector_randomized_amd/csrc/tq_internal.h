@@ -18,6 +18,10 @@ constexpr int kMaxPagesPerSplit = 256;   // 64 tiles of 64 tokens
 constexpr int kDecodeWaves = 8;           // waves of a decode work-group (they share its tiles)
 constexpr int kDecodeWgsPerCu = 1;        // decode work-groups per compute unit the split plan aims at
 constexpr size_t kCounterBytes = 65536;   // arrival counters at the start of the decode workspace
+// Cells of the page-append look-up grid: g = 128 y for a unit-vector coordinate
+// y, cell k = round(g) + 128 in 0..256 (the end cells reach to infinity).
+constexpr int kUnitCells = 257;
+constexpr int kUnitCellsPadded = 260;     // a multiple of 4 (the table is copied in 16-byte units)
 
 // One cell of the uniform grid that maps a rotated coordinate y to its code.
 // The grid covers [-range, range) with kLutCells cells; `base` counts the
@@ -39,6 +43,8 @@ struct DevConsts {
   float vc[16];               // value centroids (Lloyd-Max values only)
   QLut klut[kLutCells];
   QLut vlut[kLutCells];
+  QLut kulut[kUnitCellsPadded];   // key grid of the page kernel; t in units of g = 128 y
+  uint32_t kflip[kDim / 2];      // bf16 pair p: bit 15 / bit 31 set when sign 2p / 2p+1 is -1
   float St[kDim * kDim];      // QJL projection transposed: St[k*d + m] = S[m][k]
 };
 
@@ -61,6 +67,8 @@ struct AppendArgs {
   uint32_t sign_bits[4];      // bit i set when sign i is -1
   float klut_scale, klut_bias;   // cell = clamp(y * scale + bias)
   float vlut_scale, vlut_bias;
+  int32_t unit_grid_ok;          // kulut resolves every key threshold (the page kernel may run)
+  int32_t page_wgs;              // grid of the page kernel: its resident work-groups on the device
 };
 
 struct DecodeArgs {
@@ -103,6 +111,7 @@ hipError_t launch_append(const AppendArgs& a, int dtype, int key_bits, int key_m
                          int val_mode, hipStream_t s);
 // Address of the decode kernel instance for a configuration (for occupancy queries).
 const void* decode_kernel_ptr(int key_bits, int key_mode, int val_bits, int val_mode);
+const void* append_page_kernel_ptr(int key_bits, int val_bits);
 hipError_t launch_decode(const DecodeArgs& a, int key_bits, int key_mode, int val_bits, int val_mode,
                          hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, int key_bits, int key_mode, int val_bits, int val_mode,

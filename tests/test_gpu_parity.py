@@ -139,8 +139,9 @@ def test_end_to_end_append_then_decode(name):
     got_cache = cache.data.cpu().numpy()
     cfg = H.oracle_config(w)
     # Codes that differ from the oracle's (the append test shows they all sit inside the
-    # boundary band).  A (sequence, q head) whose context holds such a token attends over
-    # different bytes, so it is held to a loose bound; all others to the 1e-4 bar.
+    # boundary band, where either code is allowed).  A (sequence, q head) whose context
+    # holds such a token is checked against the oracle attending over the GPU-written
+    # bytes; all others against the oracle's own cache; both to the 1e-4 bar.
     flips = 0
     dirty = set()
     seq_of = np.concatenate([np.full(int(n), b) for b, n in enumerate(lens)]) if len(slots) else np.zeros(0, int)
@@ -155,19 +156,22 @@ def test_end_to_end_append_then_decode(name):
         for b in set(seq_of[bad].tolist()):
             dirty.add((b, h))
     _, ref_out = H.oracle_decode(w, q, cache_np, lay)
+    dirty_heads = [(b, h) for b, n in enumerate(lens) for h in range(w.num_q_heads)
+                   if n and (b, h // cfg.group) in dirty]
+    ref_own = H.oracle_decode(w, q, got_cache, lay, heads=dirty_heads)[1] if dirty_heads else None
     out = out.cpu().numpy()
     checked = 0
     for b, n in enumerate(lens):
         for h in range(w.num_q_heads):
             if not n:
                 continue
-            e = H.rel_err(out[b, h], ref_out[b, h])
             if (b, h // cfg.group) in dirty:
-                assert e <= 5e-2
+                e = H.rel_err(out[b, h], ref_own[b, h])
             else:
-                assert e <= H.REL_TOL, (b, h, e)
+                e = H.rel_err(out[b, h], ref_out[b, h])
                 checked += 1
-    print(f"  tokens with a band flip: {flips}; (seq, q head) pairs held to 1e-4: {checked}")
+            assert e <= H.REL_TOL, (b, h, e)
+    print(f"  tokens with a band flip: {flips}; (seq, q head) pairs on the oracle's own bytes: {checked}")
 
 
 @pytest.mark.parametrize("name", ["toy", "gqa_decode", "long_3bit", "qjl"])
