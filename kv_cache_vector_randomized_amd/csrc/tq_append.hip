@@ -185,9 +185,9 @@ __global__ __launch_bounds__(256) void append_values_kernel(AppendArgs a) {
 
 // ---------------------------------------------------------------------------
 // Keys and values of whole pages, bf16 inputs (Lloyd-Max keys without QJL,
-// uniform values).  A work-group of 4 waves takes two groups of 16 consecutive
-// tokens of one KV head: waves 0 and 1 quantize the keys of the two groups,
-// waves 2 and 3 their values.  When a group's slots are the 16 slots of one page
+// uniform values).  A work-group of 4 waves takes pairs of groups of 16
+// consecutive tokens of one KV head: two waves quantize the keys of the two
+// groups, the other two their values, the roles swapping from pass to pass.  When a group's slots are the 16 slots of one page
 // in order (prefill), the page's value planes are assembled in LDS and written
 // with one 16-byte store per plane; otherwise every token goes to its own slot.
 //
@@ -236,23 +236,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   constexpr int VROW = 16 * VB;            // bytes of a packed value row (= planes)
   constexpr int KSTR = KROW + 16;          // LDS stride of a packed key row
   __shared__ __align__(16) QLut lut[kUnitCellsPadded];
-  __shared__ __align__(16) uint8_t kpack[2][16][KSTR];    // packed key rows [group][token]
-  __shared__ __align__(16) uint8_t vplane[2][64][16];     // value planes [group][plane][token]
+  __shared__ __align__(16) uint8_t kpack[4][16][KSTR];    // packed key rows [wave][token]
+  __shared__ __align__(16) uint8_t vplane[4][64][16];     // value planes [wave][plane][token]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool keys = wave < 2;
   const int wg = wave & 1;                 // which group of the pair
   // (the launcher keeps the group count below 2^31)
   const uint32_t hkv = (uint32_t)a.hkv;
   const uint32_t ngroups = (uint32_t)((a.num_tokens + 15) / 16) * hkv;
   const uint32_t npairs = (ngroups + 1) / 2;
   const int64_t tmax = a.num_tokens - 1;
-  // Keys: lane (j, g) = (lane % 16, lane / 16) reads chunks g + 4n of token j.
-  // Values: lane (t, q) = (lane / 4, lane % 4) reads chunks q + 4n of token t.
-  const int tok = keys ? (lane & 15) : (lane >> 2);
-  const int cg = keys ? (lane >> 4) : (lane & 3);
-  const uint16_t* in_base = static_cast<const uint16_t*>(keys ? a.k : a.v) + 8 * cg;
 
   // Group 2p + wg of the pair p: its first token and head; a group past the end
   // (odd count) stands in for the last one and writes nothing.
@@ -266,38 +260,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     return live;
   };
   // Inputs and slot of this lane's token; loads are unconditional (indices clamped).
-  auto load_group = [&](uint32_t p, uint4 (&dst)[4], int64_t& slot) {
+  // Keys: lane (j, g) = (lane % 16, lane / 16) reads chunks g + 4n of token j.
+  // Values: lane (t, q) = (lane / 4, lane % 4) reads chunks q + 4n of token t.
+  auto load_group = [&](uint32_t p, bool keys, uint4 (&dst)[4], int64_t& slot) {
     int64_t t0;
     int h;
     const bool live = group_of(p, t0, h);
+    const int tok = keys ? (lane & 15) : (lane >> 2);
+    const int cg = keys ? (lane >> 4) : (lane & 3);
     const int64_t t = min(t0 + tok, tmax);
-    const uint16_t* src = in_base + (t * a.hkv + h) * kDim;
+    const uint16_t* src = static_cast<const uint16_t*>(keys ? a.k : a.v) + (t * a.hkv + h) * kDim + 8 * cg;
 #pragma unroll
     for (int n = 0; n < 4; ++n) dst[n] = *reinterpret_cast<const uint4*>(src + 32 * n);
     slot = a.slots[t];
     if (!live || t0 + tok > tmax || !(slot >= 0 && slot < a.num_blocks * kBlockTokensDev)) slot = -1;
   };
 
+  // In pass i the waves 0, 1 (i even) or 2, 3 (i odd) quantize the keys of the
+  // pair's two groups and the other two their values, so that every SIMD gets
+  // both kinds of work.
   uint32_t p = blockIdx.x;                 // the launcher keeps gridDim.x <= npairs
-  uint4 in[4], fl[4];
+  uint32_t pass = 0;
+  uint4 in[4];
   int64_t slot;
-  load_group(p, in, slot);
-  if (keys) {
+  load_group(p, wave < 2, in, slot);
+  for (int i = threadIdx.x; i < kUnitCellsPadded; i += 256)
+    *reinterpret_cast<uint4*>(&lut[i]) = *reinterpret_cast<const uint4*>(&a.c->kulut[i]);
+  // A operands of the key rotation, one per block b = beta + 2n of the 16-point
+  // transform: H16[j][k] times the sign of coordinate 32n + 8(k/4) + 4beta + k%4
+  // (k = 4g + e), so the bf16 rows enter the MFMA as they are.
+  shortx4 hs[8];
+  {
+    const int j = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) fl[n] = *reinterpret_cast<const uint4*>(&a.c->kflip[16 * n + 4 * (lane >> 4)]);
-    for (int i = threadIdx.x; i < kUnitCellsPadded; i += 128)
-      *reinterpret_cast<uint4*>(&lut[i]) = *reinterpret_cast<const uint4*>(&a.c->kulut[i]);
+    for (int b = 0; b < 8; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int bit = 8 * g + 4 * (b & 1) + e;
+        const uint32_t neg = ((a.sign_bits[b >> 1] >> bit) ^ (uint32_t)__builtin_popcount(j & (4 * g + e))) & 1u;
+        hs[b][e] = (short)(0x3F80u | (neg << 15));
+      }
   }
   __syncthreads();
 
   // Pairs p, p + gridDim.x, ...: the next pair's inputs are loaded while this
   // one is quantized.
-  for (;;) {
+  for (;; ++pass) {
+    const bool keys = (((uint32_t)(wave >> 1) ^ pass) & 1u) == 0u;
     const uint32_t pn = p + gridDim.x;
     const bool more = pn < npairs;
     uint4 nin[4];
     int64_t nslot;
-    load_group(more ? pn : p, nin, nslot);
+    load_group(more ? pn : p, !keys, nin, nslot);
     int64_t t0;
     int h;
     (void)group_of(p, t0, h);
@@ -305,19 +319,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 
     if (keys) {
       const int j = lane & 15, g = lane >> 4;
-      shortx4 hb;                                  // A operand: H16[j][4g + e]
-#pragma unroll
-      for (int e = 0; e < 4; ++e) hb[e] = (__builtin_popcount(j & (4 * g + e)) & 1) ? (short)0xBF80 : (short)0x3F80;
-      // z[b], b = beta + 2n: the 16-point transform of coordinates 32n + 8g' + 4beta + e
+      // z[b], b = beta + 2n: the 16-point transform of the signed coordinates
+      // 32n + 8g' + 4beta + e
       floatx4 z[8];
       const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const uint4 x = make_uint4(in[n].x ^ fl[n].x, in[n].y ^ fl[n].y, in[n].z ^ fl[n].z, in[n].w ^ fl[n].w);
-        z[2 * n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hb, __builtin_bit_cast(shortx4, make_uint2(x.x, x.y)),
-                                                            zero, 0, 0, 0);
-        z[2 * n + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(hb, __builtin_bit_cast(shortx4, make_uint2(x.z, x.w)),
-                                                                zero, 0, 0, 0);
+        z[2 * n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            hs[2 * n], __builtin_bit_cast(shortx4, make_uint2(in[n].x, in[n].y)), zero, 0, 0, 0);
+        z[2 * n + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            hs[2 * n + 1], __builtin_bit_cast(shortx4, make_uint2(in[n].z, in[n].w)), zero, 0, 0, 0);
       }
       // 8-point butterfly over b: z[b][r] becomes coordinate 32(b/2) + 8g + 4(b%2) + r
 #pragma unroll
@@ -364,7 +375,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         reinterpret_cast<float*>(page_of(slot) + a.f.knorm)[slot & 15] = nhat;
       }
       // codes of coordinates 32n + 8g .. +7 are bytes KB*(4n + g) .. +KB-1 of the row
-      uint8_t* prow = &kpack[wg][j][0];
+      uint8_t* prow = &kpack[wave][j][0];
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int o = KB * (4 * n + g);
@@ -384,7 +395,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       const int64_t slot_kv = __builtin_amdgcn_ds_bpermute(kv << 2, (int)slot) |
                               ((int64_t)__builtin_amdgcn_ds_bpermute(kv << 2, (int)(slot >> 32)) << 32);
       if (slot_kv >= 0) {
-        const uint8_t* srow = &kpack[wg][kv][4 * KB * kq];
+        const uint8_t* srow = &kpack[wave][kv][4 * KB * kq];
         uint8_t* dst = page_of(slot_kv) + a.f.kcodes + (slot_kv & 15) * KROW + 4 * KB * kq;
         if constexpr (KB == 4) *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(srow);
         else if constexpr (KB == 2) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(srow);
@@ -442,7 +453,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
 #pragma unroll
       for (int n = 0; n < 4; ++n)
 #pragma unroll
-        for (int i = 0; i < VB; ++i) vplane[wg][VB * (q + 4 * n) + i][t] = (uint8_t)(w[n] >> (8 * i));
+        for (int i = 0; i < VB; ++i) vplane[wave][VB * (q + 4 * n) + i][t] = (uint8_t)(w[n] >> (8 * i));
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -451,13 +462,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
       if (whole) {
         if (lane < VROW)
           *reinterpret_cast<uint4*>(page_of(slot0) + a.f.vcodes + 16 * lane) =
-              *reinterpret_cast<const uint4*>(&vplane[wg][lane][0]);
+              *reinterpret_cast<const uint4*>(&vplane[wave][lane][0]);
       } else {
 #pragma unroll 1
         for (int v = 0; v < 16; ++v) {
           const int64_t sv = __builtin_amdgcn_readlane((int)slot, 4 * v) |
                              ((int64_t)__builtin_amdgcn_readlane((int)(slot >> 32), 4 * v) << 32);
-          if (sv >= 0 && lane < VROW) page_of(sv)[a.f.vcodes + 16 * lane + (sv & 15)] = vplane[wg][lane][v];
+          if (sv >= 0 && lane < VROW) page_of(sv)[a.f.vcodes + 16 * lane + (sv & 15)] = vplane[wave][lane][v];
         }
       }
     }

@@ -296,8 +296,6 @@ tq_status tq_create(const tq_config* cfg, const int8_t* signs_host, const float*
   layout_of(cfg, &ctx->layout);
   bool ok = build_lut((int)cfg->key_bits, h->kc, kt, h->klut, &ctx->klut_scale, &ctx->klut_bias);
   ctx->unit_grid_ok = build_unit_lut((int)cfg->key_bits, h->kc, kt, h->kulut) ? 1 : 0;
-  for (int p = 0; p < d / 2; ++p)
-    h->kflip[p] = (signs_host[2 * p] < 0 ? 0x8000u : 0u) | (signs_host[2 * p + 1] < 0 ? 0x80000000u : 0u);
   if (cfg->val_mode == TQ_VAL_LLOYD) {
     codebook_f32((int)cfg->val_bits, d, h->vc, vt);
     ok = ok && build_lut((int)cfg->val_bits, h->vc, vt, h->vlut, &ctx->vlut_scale, &ctx->vlut_bias);

@@ -44,7 +44,6 @@ struct DevConsts {
   QLut klut[kLutCells];
   QLut vlut[kLutCells];
   QLut kulut[kUnitCellsPadded];   // key grid of the page kernel; t in units of g = 128 y
-  uint32_t kflip[kDim / 2];      // bf16 pair p: bit 15 / bit 31 set when sign 2p / 2p+1 is -1
   float St[kDim * kDim];      // QJL projection transposed: St[k*d + m] = S[m][k]
 };
 
