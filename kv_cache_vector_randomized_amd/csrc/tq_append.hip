@@ -187,9 +187,10 @@ __global__ __launch_bounds__(256) void append_values_kernel(AppendArgs a) {
 // Keys and values of whole pages, bf16 inputs (Lloyd-Max keys without QJL,
 // uniform values).  A work-group of 4 waves takes pairs of groups of 16
 // consecutive tokens of one KV head: two waves quantize the keys of the two
-// groups, the other two their values, the roles swapping from pass to pass.  When a group's slots are the 16 slots of one page
-// in order (prefill), the page's value planes are assembled in LDS and written
-// with one 16-byte store per plane; otherwise every token goes to its own slot.
+// groups, the other two their values, the roles swapping from pass to pass.
+// When a group's slots are the 16 slots of one page in order (prefill), the
+// page's value planes are assembled in LDS and written with one 16-byte store
+// per plane; otherwise every token goes to its own slot.
 //
 // Rotation on the matrix cores.  Write a coordinate as 7 bits c = (c6..c0); the
 // Sylvester matrix is the product over bits of (-1)^(out_b * in_b), so it
@@ -259,31 +260,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
     t0 = (int64_t)tb * 16;
     return live;
   };
-  // Inputs and slot of this lane's token; loads are unconditional (indices clamped).
+  // Inputs and raw slot of this lane's token; loads are unconditional (indices
+  // clamped), and nothing here waits for them.
   // Keys: lane (j, g) = (lane % 16, lane / 16) reads chunks g + 4n of token j.
   // Values: lane (t, q) = (lane / 4, lane % 4) reads chunks q + 4n of token t.
-  auto load_group = [&](uint32_t p, bool keys, uint4 (&dst)[4], int64_t& slot) {
+  auto load_group = [&](uint32_t p, bool keys, uint4 (&dst)[4], int64_t& raw) {
     int64_t t0;
     int h;
-    const bool live = group_of(p, t0, h);
+    (void)group_of(p, t0, h);
     const int tok = keys ? (lane & 15) : (lane >> 2);
     const int cg = keys ? (lane >> 4) : (lane & 3);
     const int64_t t = min(t0 + tok, tmax);
     const uint16_t* src = static_cast<const uint16_t*>(keys ? a.k : a.v) + (t * a.hkv + h) * kDim + 8 * cg;
 #pragma unroll
     for (int n = 0; n < 4; ++n) dst[n] = *reinterpret_cast<const uint4*>(src + 32 * n);
-    slot = a.slots[t];
-    if (!live || t0 + tok > tmax || !(slot >= 0 && slot < a.num_blocks * kBlockTokensDev)) slot = -1;
+    raw = a.slots[t];
   };
 
   // In pass i the waves 0, 1 (i even) or 2, 3 (i odd) quantize the keys of the
   // pair's two groups and the other two their values, so that every SIMD gets
   // both kinds of work.
   uint32_t p = blockIdx.x;                 // the launcher keeps gridDim.x <= npairs
-  uint32_t pass = 0;
-  uint4 in[4];
-  int64_t slot;
-  load_group(p, wave < 2, in, slot);
+  const bool keys0 = wave < 2;             // role in even passes
+  uint4 inA[4], inB[4];
+  int64_t rawA, rawB;
+  load_group(p, keys0, inA, rawA);
   for (int i = threadIdx.x; i < kUnitCellsPadded; i += 256)
     *reinterpret_cast<uint4*>(&lut[i]) = *reinterpret_cast<const uint4*>(&a.c->kulut[i]);
   // A operands of the key rotation, one per block b = beta + 2n of the 16-point
@@ -303,184 +304,194 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   }
   __syncthreads();
 
-  // Pairs p, p + gridDim.x, ...: the next pair's inputs are loaded while this
-  // one is quantized.
-  for (;; ++pass) {
-    const bool keys = (((uint32_t)(wave >> 1) ^ pass) & 1u) == 0u;
-    const uint32_t pn = p + gridDim.x;
-    const bool more = pn < npairs;
-    uint4 nin[4];
-    int64_t nslot;
-    load_group(more ? pn : p, !keys, nin, nslot);
-    int64_t t0;
-    int h;
-    (void)group_of(p, t0, h);
-    auto page_of = [&](int64_t s) -> uint8_t* { return a.cache + ((s >> 4) * a.hkv + h) * (int64_t)a.f.page_bytes; };
+  // One pass: pair p's group wg, keys or values, from inputs `in` and raw slot
+  // `raw` (loaded one pass earlier).
+  auto run_pass = [&](uint32_t p, bool keys, const uint4 (&in)[4], int64_t raw) {
+      int64_t t0;
+      int h;
+      const bool live = group_of(p, t0, h);
+      // this lane's slot, -1 when its token or slot is out of range (or the group is)
+      const int64_t slot = (live && t0 + (keys ? (lane & 15) : (lane >> 2)) <= tmax && raw >= 0 &&
+                            raw < a.num_blocks * kBlockTokensDev) ? raw : -1;
+      auto page_of = [&](int64_t s) -> uint8_t* { return a.cache + ((s >> 4) * a.hkv + h) * (int64_t)a.f.page_bytes; };
 
-    if (keys) {
-      const int j = lane & 15, g = lane >> 4;
-      // z[b], b = beta + 2n: the 16-point transform of the signed coordinates
-      // 32n + 8g' + 4beta + e
-      floatx4 z[8];
-      const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        z[2 * n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            hs[2 * n], __builtin_bit_cast(shortx4, make_uint2(in[n].x, in[n].y)), zero, 0, 0, 0);
-        z[2 * n + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            hs[2 * n + 1], __builtin_bit_cast(shortx4, make_uint2(in[n].z, in[n].w)), zero, 0, 0, 0);
-      }
-      // 8-point butterfly over b: z[b][r] becomes coordinate 32(b/2) + 8g + 4(b%2) + r
-#pragma unroll
-      for (int len = 1; len < 8; len <<= 1)
-#pragma unroll
-        for (int i = 0; i < 8; i += 2 * len)
-#pragma unroll
-          for (int m = i; m < i + len; ++m) {
-            const floatx4 u = z[m], v = z[m + len];
-            z[m] = u + v;
-            z[m + len] = u - v;
+      if (keys) {
+        const int j = lane & 15, g = lane >> 4;
+        // z[b], b = beta + 2n: the 16-point transform of the signed coordinates
+        // 32n + 8g' + 4beta + e
+        floatx4 z[8];
+        const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          z[2 * n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              hs[2 * n], __builtin_bit_cast(shortx4, make_uint2(in[n].x, in[n].y)), zero, 0, 0, 0);
+          z[2 * n + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              hs[2 * n + 1], __builtin_bit_cast(shortx4, make_uint2(in[n].z, in[n].w)), zero, 0, 0, 0);
+        }
+        // 8-point butterfly over b: z[b][r] becomes coordinate 32(b/2) + 8g + 4(b%2) + r
+  #pragma unroll
+        for (int len = 1; len < 8; len <<= 1)
+  #pragma unroll
+          for (int i = 0; i < 8; i += 2 * len)
+  #pragma unroll
+            for (int m = i; m < i + len; ++m) {
+              const floatx4 u = z[m], v = z[m + len];
+              z[m] = u + v;
+              z[m + len] = u - v;
+            }
+        float ss = 0.f;
+  #pragma unroll
+        for (int b = 0; b < 8; ++b)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) ss = fmaf(z[b][r], z[b][r], ss);
+        ss = sum_rows(ss);
+        // u = y / ||y||, g = 128 u; a zero key gives g = 0, codes 2^(b-1) and norm 0
+        const float sg = ss > 0.f ? 128.f * __builtin_amdgcn_rsqf(ss) : 0.f;
+        const uint32_t lut_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) QLut*)lut + 0x4C000000u;
+        float c2 = 0.f;
+        uint32_t w[4];
+  #pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          uint32_t wn = 0u;
+  #pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float gv = z[2 * n + (i >> 2)][i & 3] * sg;
+            const uint32_t addr = (__float_as_uint(gv + kUnitMagic) << 4) + lut_addr;
+            const u32x4 e = *reinterpret_cast<lds_u32x4*>((uintptr_t)addr);
+            const bool up = gv >= __uint_as_float(e.y);
+            const float c = up ? __uint_as_float(e.w) : __uint_as_float(e.z);
+            c2 = fmaf(c, c, c2);
+            const uint32_t code = e.x + (uint32_t)up;
+            wn |= code << (KB * i);
           }
-      float ss = 0.f;
-#pragma unroll
-      for (int b = 0; b < 8; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ss = fmaf(z[b][r], z[b][r], ss);
-      ss = sum_rows(ss);
-      // u = y / ||y||, g = 128 u; a zero key gives g = 0, codes 2^(b-1) and norm 0
-      const float sg = ss > 0.f ? 128.f * __builtin_amdgcn_rsqf(ss) : 0.f;
-      const uint32_t lut_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) QLut*)lut + 0x4C000000u;
-      float c2 = 0.f;
-      uint32_t w[4];
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        uint32_t wn = 0u;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float gv = z[2 * n + (i >> 2)][i & 3] * sg;
-          const uint32_t addr = (__float_as_uint(gv + kUnitMagic) << 4) + lut_addr;
-          const u32x4 e = *reinterpret_cast<lds_u32x4*>((uintptr_t)addr);
-          const bool up = gv >= __uint_as_float(e.y);
-          const float c = up ? __uint_as_float(e.w) : __uint_as_float(e.z);
-          c2 = fmaf(c, c, c2);
-          const uint32_t code = e.x + (uint32_t)up;
-          wn |= code << (KB * i);
+          w[n] = wn;
         }
-        w[n] = wn;
-      }
-      c2 = sum_rows(c2);
-      if (g == 0 && slot >= 0) {
-        const float nk = __builtin_amdgcn_sqrtf(ss) * kInvSqrtDim;   // ||k|| (H/sqrt(d) is orthogonal)
-        const float nhat = a.key_nc ? (nk > 0.f ? nk * __builtin_amdgcn_rsqf(c2) : 0.f) : nk;
-        reinterpret_cast<float*>(page_of(slot) + a.f.knorm)[slot & 15] = nhat;
-      }
-      // codes of coordinates 32n + 8g .. +7 are bytes KB*(4n + g) .. +KB-1 of the row
-      uint8_t* prow = &kpack[wave][j][0];
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const int o = KB * (4 * n + g);
-        if constexpr (KB == 4) *reinterpret_cast<uint32_t*>(prow + o) = w[n];
-        else if constexpr (KB == 2) *reinterpret_cast<uint16_t*>(prow + o) = (uint16_t)w[n];
-        else {
-          prow[o] = (uint8_t)w[n];
-          prow[o + 1] = (uint8_t)(w[n] >> 8);
-          prow[o + 2] = (uint8_t)(w[n] >> 16);
+        c2 = sum_rows(c2);
+        if (g == 0 && slot >= 0) {
+          const float nk = __builtin_amdgcn_sqrtf(ss) * kInvSqrtDim;   // ||k|| (H/sqrt(d) is orthogonal)
+          const float nhat = a.key_nc ? (nk > 0.f ? nk * __builtin_amdgcn_rsqf(c2) : 0.f) : nk;
+          reinterpret_cast<float*>(page_of(slot) + a.f.knorm)[slot & 15] = nhat;
         }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // Key rows: lane l stores bytes 4*KB*(l%4) .. +4*KB-1 of token l/4's row.
-      const int kv = lane >> 2, kq = lane & 3;
-      const int64_t slot_kv = __builtin_amdgcn_ds_bpermute(kv << 2, (int)slot) |
-                              ((int64_t)__builtin_amdgcn_ds_bpermute(kv << 2, (int)(slot >> 32)) << 32);
-      if (slot_kv >= 0) {
-        const uint8_t* srow = &kpack[wave][kv][4 * KB * kq];
-        uint8_t* dst = page_of(slot_kv) + a.f.kcodes + (slot_kv & 15) * KROW + 4 * KB * kq;
-        if constexpr (KB == 4) *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(srow);
-        else if constexpr (KB == 2) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(srow);
-        else {
-          const uint32_t* s32 = reinterpret_cast<const uint32_t*>(srow);
-          uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
-          d32[0] = s32[0]; d32[1] = s32[1]; d32[2] = s32[2];
+        // codes of coordinates 32n + 8g .. +7 are bytes KB*(4n + g) .. +KB-1 of the row
+        uint8_t* prow = &kpack[wave][j][0];
+  #pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int o = KB * (4 * n + g);
+          if constexpr (KB == 4) *reinterpret_cast<uint32_t*>(prow + o) = w[n];
+          else if constexpr (KB == 2) *reinterpret_cast<uint16_t*>(prow + o) = (uint16_t)w[n];
+          else {
+            prow[o] = (uint8_t)w[n];
+            prow[o + 1] = (uint8_t)(w[n] >> 8);
+            prow[o + 2] = (uint8_t)(w[n] >> 16);
+          }
         }
-      }
-    } else {
-      const int t = lane >> 2, q = lane & 3;
-      const int64_t slot0 = __builtin_amdgcn_readfirstlane((int)slot) |
-                            ((int64_t)__builtin_amdgcn_readfirstlane((int)(slot >> 32)) << 32);
-      // the 16 tokens fill one page in order
-      const bool whole = (__ballot(!(slot >= 0 && slot == slot0 + t)) == 0ull) && slot0 >= 0 && (slot0 & 15) == 0;
-
-      float x[32];                              // x[8n + e]: coordinate 32n + 8q + e
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const uint32_t wv[4] = {in[n].x, in[n].y, in[n].z, in[n].w};
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          x[8 * n + 2 * d] = bf16lo(wv[d]);
-          x[8 * n + 2 * d + 1] = bf16hi(wv[d]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // Key rows: lane l stores bytes 4*KB*(l%4) .. +4*KB-1 of token l/4's row.
+        const int kv = lane >> 2, kq = lane & 3;
+        const int64_t slot_kv = __builtin_amdgcn_ds_bpermute(kv << 2, (int)slot) |
+                                ((int64_t)__builtin_amdgcn_ds_bpermute(kv << 2, (int)(slot >> 32)) << 32);
+        if (slot_kv >= 0) {
+          const uint8_t* srow = &kpack[wave][kv][4 * KB * kq];
+          uint8_t* dst = page_of(slot_kv) + a.f.kcodes + (slot_kv & 15) * KROW + 4 * KB * kq;
+          if constexpr (KB == 4) *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(srow);
+          else if constexpr (KB == 2) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(srow);
+          else {
+            const uint32_t* s32 = reinterpret_cast<const uint32_t*>(srow);
+            uint32_t* d32 = reinterpret_cast<uint32_t*>(dst);
+            d32[0] = s32[0]; d32[1] = s32[1]; d32[2] = s32[2];
+          }
         }
-      }
-      float mn = x[0], mx = x[0];
-#pragma unroll
-      for (int k = 1; k < 32; ++k) {
-        mn = fminf(mn, x[k]);
-        mx = fmaxf(mx, x[k]);
-      }
-      quad_minmax(mn, mx);
-      constexpr float levels = (float)((1 << VB) - 1);
-      const float sc = (mx - mn) / levels;                  // correctly rounded division
-      const float inv = sc > 0.f ? 1.f / sc : 0.f;          // correctly rounded
-      // code = floor(fl32(x - mn) * inv + 1/2) in one fma.  Against rint(fl32(fl32(x - mn)
-      // / sc)) it can differ only where the quotient lies within a few ulp (about
-      // 2^-20 for codes up to 15) of a rounding boundary: a normalised distance
-      // (x - mn) / (mx - mn) far below 1e-6, inside the band where either code counts.
-      uint32_t w[4];                            // w[n]: the 8 codes of chunk q + 4n (VB bytes)
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        uint32_t wn = 0u;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) wn |= (uint32_t)fmaf(x[8 * n + e] - mn, inv, 0.5f) << (VB * e);
-        w[n] = wn;
-      }
-      if (q == 0 && slot >= 0) {
-        uint8_t* pg = page_of(slot);
-        reinterpret_cast<float*>(pg + a.f.vmin)[slot & 15] = mn;
-        reinterpret_cast<float*>(pg + a.f.vscale)[slot & 15] = sc;
-      }
-      // row bytes VB*(q + 4n) .. +VB-1 are those planes
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-#pragma unroll
-        for (int i = 0; i < VB; ++i) vplane[wave][VB * (q + 4 * n) + i][t] = (uint8_t)(w[n] >> (8 * i));
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // Value planes: a whole page takes one 16-byte store per plane; otherwise
-      // each token's byte of each plane goes to its own slot.
-      if (whole) {
-        if (lane < VROW)
-          *reinterpret_cast<uint4*>(page_of(slot0) + a.f.vcodes + 16 * lane) =
-              *reinterpret_cast<const uint4*>(&vplane[wave][lane][0]);
       } else {
-#pragma unroll 1
-        for (int v = 0; v < 16; ++v) {
-          const int64_t sv = __builtin_amdgcn_readlane((int)slot, 4 * v) |
-                             ((int64_t)__builtin_amdgcn_readlane((int)(slot >> 32), 4 * v) << 32);
-          if (sv >= 0 && lane < VROW) page_of(sv)[a.f.vcodes + 16 * lane + (sv & 15)] = vplane[wave][lane][v];
+        const int t = lane >> 2, q = lane & 3;
+        const int64_t slot0 = __builtin_amdgcn_readfirstlane((int)slot) |
+                              ((int64_t)__builtin_amdgcn_readfirstlane((int)(slot >> 32)) << 32);
+        // the 16 tokens fill one page in order
+        const bool whole = (__ballot(!(slot >= 0 && slot == slot0 + t)) == 0ull) && slot0 >= 0 && (slot0 & 15) == 0;
+
+        float x[32];                              // x[8n + e]: coordinate 32n + 8q + e
+  #pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const uint32_t wv[4] = {in[n].x, in[n].y, in[n].z, in[n].w};
+  #pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            x[8 * n + 2 * d] = bf16lo(wv[d]);
+            x[8 * n + 2 * d + 1] = bf16hi(wv[d]);
+          }
+        }
+        float mn = x[0], mx = x[0];
+  #pragma unroll
+        for (int k = 1; k < 32; ++k) {
+          mn = fminf(mn, x[k]);
+          mx = fmaxf(mx, x[k]);
+        }
+        quad_minmax(mn, mx);
+        constexpr float levels = (float)((1 << VB) - 1);
+        const float sc = (mx - mn) / levels;                  // correctly rounded division
+        const float inv = sc > 0.f ? 1.f / sc : 0.f;          // correctly rounded
+        // code = floor(fl32(x - mn) * inv + 1/2) in one fma.  Against rint(fl32(fl32(x - mn)
+        // / sc)) it can differ only where the quotient lies within a few ulp (about
+        // 2^-20 for codes up to 15) of a rounding boundary: a normalised distance
+        // (x - mn) / (mx - mn) far below 1e-6, inside the band where either code counts.
+        uint32_t w[4];                            // w[n]: the 8 codes of chunk q + 4n (VB bytes)
+  #pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          uint32_t wn = 0u;
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) wn |= (uint32_t)fmaf(x[8 * n + e] - mn, inv, 0.5f) << (VB * e);
+          w[n] = wn;
+        }
+        if (q == 0 && slot >= 0) {
+          uint8_t* pg = page_of(slot);
+          reinterpret_cast<float*>(pg + a.f.vmin)[slot & 15] = mn;
+          reinterpret_cast<float*>(pg + a.f.vscale)[slot & 15] = sc;
+        }
+        // row bytes VB*(q + 4n) .. +VB-1 are those planes
+  #pragma unroll
+        for (int n = 0; n < 4; ++n)
+  #pragma unroll
+          for (int i = 0; i < VB; ++i) vplane[wave][VB * (q + 4 * n) + i][t] = (uint8_t)(w[n] >> (8 * i));
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // Value planes: a whole page takes one 16-byte store per plane; otherwise
+        // each token's byte of each plane goes to its own slot.
+        if (whole) {
+          if (lane < VROW)
+            *reinterpret_cast<uint4*>(page_of(slot0) + a.f.vcodes + 16 * lane) =
+                *reinterpret_cast<const uint4*>(&vplane[wave][lane][0]);
+        } else {
+  #pragma unroll 1
+          for (int v = 0; v < 16; ++v) {
+            const int64_t sv = __builtin_amdgcn_readlane((int)slot, 4 * v) |
+                               ((int64_t)__builtin_amdgcn_readlane((int)(slot >> 32), 4 * v) << 32);
+            if (sv >= 0 && lane < VROW) page_of(sv)[a.f.vcodes + 16 * lane + (sv & 15)] = vplane[wave][lane][v];
+          }
         }
       }
-    }
-    if (!more) break;
-    p = pn;
-#pragma unroll
-    for (int n = 0; n < 4; ++n) in[n] = nin[n];
-    slot = nslot;
-    // the LDS rows of this wave are rewritten next: keep this pass's reads first
+    // the LDS rows of this wave are rewritten next pass: keep this pass's reads first
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // Pairs p, p + gridDim.x, ...: the next pair's inputs are loaded while this
+  // one is quantized, into the other of two register sets (a copy of registers
+  // still being loaded would wait for the load).
+  for (;;) {
+    uint32_t pn = p + gridDim.x;
+    bool more = pn < npairs;
+    load_group(more ? pn : p, !keys0, inB, rawB);
+    run_pass(p, keys0, inA, rawA);
+    if (!more) break;
+    p = pn;
+    pn = p + gridDim.x;
+    more = pn < npairs;
+    load_group(more ? pn : p, keys0, inA, rawA);
+    run_pass(p, !keys0, inB, rawB);
+    if (!more) break;
+    p = pn;
   }
 }
 
