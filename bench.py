@@ -9,13 +9,20 @@ the paged cache, then decode attention of the 16 new queries over their 8192
 cached tokens.  Steps rotate over --layers independent caches (one per layer)
 so the 147 MB working set does not stay in the 256 MB Infinity Cache.
 
-`--workload prefill_append`: quantize-append of 131072 tokens x 8 KV heads into
-16-token pages followed by decode at batch 1 over the 131072-token context.
+Other workloads (--workload):
+  long_3bit       batch 4 x context 32768, 3-bit keys and values, same step;
+  qjl             batch 8 x context 16384, 2-bit keys + 1-bit QJL residual signs,
+                  same step;
+  prefill_append  quantize-append of 131072 tokens x 8 KV heads into 16-token
+                  pages, then decode at batch 1 over the 131072-token context.
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.  `value` is packed-KV
 GB/s: algorithmic bytes of the step (bf16 inputs read, packed rows written,
 packed rows of the attended context read, queries, outputs, tables) divided by
-the step time, with every input already resident in HBM.
+the step time, with every input already resident in HBM.  The step time comes
+from a timed region with nothing but the steps in it; a second pass over the
+same number of steps brackets the dominant kernel with HIP events on its stream
+for the roofline figure.
 """
 from __future__ import annotations
 
@@ -32,7 +39,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
-TOKEN_HEAD_BYTES = {"gqa_decode": 140, "prefill_append": 140}
+# workload -> (synthetic workload, step kind)
+MODES = {
+    "gqa_decode": ("gqa_decode", "decode"),
+    "long_3bit": ("long_3bit", "decode"),
+    "qjl": ("qjl", "decode"),
+    "prefill_append": ("prefill_append", "append"),
+}
 
 
 def log(*a):
@@ -57,10 +70,10 @@ def counter_traffic(kernel_key: str, source: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--layers", type=int, default=4, help="independent layer caches rotated over the steps")
-    ap.add_argument("--workload", default="gqa_decode", choices=["gqa_decode", "prefill_append"])
+    ap.add_argument("--workload", default="gqa_decode", choices=list(MODES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (counter calibration)")
@@ -79,13 +92,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.init()
-    w = synth.WORKLOADS[args.workload]
+    wname, kind = MODES[args.workload]
+    w = synth.WORKLOADS[wname]
     B, T, Hkv, Hq, d = w.batch, w.context, w.num_kv_heads, w.num_q_heads, w.head_dim
     cfg = tq.make_config(d, Hkv, Hq, w.key_bits, w.key_mode, w.val_bits, w.val_mode)
-    ctx = tq.Context(cfg, synth.sign_vector(w.seed))
+    S = synth.qjl_matrix(d) if w.key_mode == "lloyd_qjl" else None
+    ctx = tq.Context(cfg, synth.sign_vector(w.seed), S)
     lay = synth.paged_layout(B, [T] * B, w.seed)
     scale = 1.0 / math.sqrt(d)
-    log(f"[bench] workload={w.name} B={B} T={T} Hkv={Hkv} Hq={Hq} page_bytes={ctx.page_bytes}")
+    log(f"[bench] workload={args.workload} B={B} T={T} Hkv={Hkv} Hq={Hq} page_bytes={ctx.page_bytes}")
 
     t0 = time.time()
     k_all = synth.kv_tensor(w, B * T, "k")
@@ -108,15 +123,14 @@ def main():
     n_layers = max(1, args.layers)
     caches = [PagedKVCache(ctx, lay.num_blocks) for _ in range(n_layers)]
     stream = torch.cuda.current_stream()
+    decode_bytes = B * Hkv * T * th + B * Hq * d * 2 + B * Hq * d * 4 + lay.block_tables.nbytes + B * 4
 
-    if args.workload == "gqa_decode":
+    if kind == "decode":
         for c in caches:                               # prefill every layer (not timed)
             c.append(k_dev, v_dev, slots_all)
         torch.cuda.synchronize()
         del k_dev, v_dev
         append_bytes = B * Hkv * (2 * d * 2 + th) + B * 8
-        decode_bytes = B * Hkv * T * th + B * Hq * d * 2 + B * Hq * d * 4 + lay.block_tables.nbytes + B * 4
-        step_bytes = append_bytes + decode_bytes
         dominant, dom_bytes, dom_source = "decode_kernel", decode_bytes, "tq_decode.hip"
 
         def step(i, ev=None):
@@ -129,9 +143,7 @@ def main():
                 ev[1].record(stream)
     else:
         append_bytes = B * T * Hkv * (2 * d * 2 + th) + B * T * 8
-        decode_bytes = B * Hkv * T * th + B * Hq * d * 2 + B * Hq * d * 4 + lay.block_tables.nbytes + B * 4
-        step_bytes = append_bytes + decode_bytes
-        dominant, dom_bytes, dom_source = "append (keys + values kernels)", append_bytes, "tq_append.hip"
+        dominant, dom_bytes, dom_source = "append_page_kernel", append_bytes, "tq_append.hip"
 
         def step(i, ev=None):
             c = caches[i % n_layers]
@@ -141,6 +153,7 @@ def main():
             if ev is not None:
                 ev[1].record(stream)
             c.decode(q_dev, tables, seq_lens, T, scale, out=out)
+    step_bytes = append_bytes + decode_bytes
 
     if args.copy_calibration_mb:
         src = torch.empty(args.copy_calibration_mb << 20, dtype=torch.uint8, device="cuda")
@@ -151,22 +164,29 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    # Timed region: exactly `steps` steps, nothing else on the stream.
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i)
     stop.record(stream)
     torch.cuda.synchronize()
-    ms_total = start.elapsed_time(stop)
-    ms_step = ms_total / args.steps
+    ms_step = start.elapsed_time(stop) / args.steps
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # Second pass: the dominant kernel bracketed by events on its stream, every step.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i, evs[i])
+    torch.cuda.synchronize()
     dom_ms = [a.elapsed_time(b) for a, b in evs]
     dom_avg = statistics.mean(dom_ms)
-    value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = dom_bytes / (dom_avg * 1e-3) / 1e9
+    pct = {p: float(np.percentile(dom_ms, p)) * 1e3 for p in (10, 50, 90)}
     log(f"[bench] step {ms_step * 1e3:.1f} us; {dominant} avg {dom_avg * 1e3:.1f} us "
-        f"(p10 {np.percentile(dom_ms, 10) * 1e3:.1f}, p90 {np.percentile(dom_ms, 90) * 1e3:.1f}); "
+        f"(p10 {pct[10]:.1f}, p50 {pct[50]:.1f}, p90 {pct[90]:.1f}); "
         f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of HBM peak")
 
     cpu = None
@@ -187,10 +207,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded; bf16 N(0,1) K/V with outlier channels, N(0,1) queries)",
         "config": {
-            "workload": w.name, "batch": B, "context": T, "num_q_heads": Hq, "num_kv_heads": Hkv,
+            "workload": args.workload, "batch": B, "context": T, "num_q_heads": Hq, "num_kv_heads": Hkv,
             "head_dim": d, "key_bits": w.key_bits, "key_mode": w.key_mode, "val_bits": w.val_bits,
             "val_mode": w.val_mode, "block_tokens": 16, "layer_caches": n_layers,
-            "step": ("append 1 token/seq + decode" if w.name == "gqa_decode" else "append all tokens + decode"),
+            "step": ("append 1 token/seq + decode" if kind == "decode" else "append all tokens + decode"),
             "step_bytes": step_bytes,
         },
         "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
@@ -203,9 +223,10 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": counter_traffic(w.name + ":" + dominant, dom_source),
+            "traffic": counter_traffic(args.workload + ":" + dominant, dom_source),
             "algorithmic_bytes_per_launch": dom_bytes,
             "avg_launch_us": round(dom_avg * 1e3, 2),
+            "p10_p50_p90_us": [round(pct[10], 2), round(pct[50], 2), round(pct[90], 2)],
         },
         "cpu_baseline": cpu,
     }
@@ -214,7 +235,8 @@ def main():
 
 def cpu_baseline(w, k_all, v_all, q_np, lay, np):
     """The fp64 oracle (untuned) on a bounded sample of the same step: one sequence's
-    new-token quantize-append plus its decode attention over the whole context."""
+    new-token quantize-append plus its decode attention over its context (for the
+    prefill workload: the quantize-append of 2048 of its tokens)."""
     from oracle import tq_oracle as O
     from kv_cache_vector_randomized_amd import synth
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
@@ -222,27 +244,41 @@ def cpu_baseline(w, k_all, v_all, q_np, lay, np):
     cfg = O.Config(d, Hkv, Hq, w.key_bits, w.key_mode, w.val_bits, w.val_mode)
     signs = synth.sign_vector(w.seed)
     kcb = O.codebook(w.key_bits, d)
+    S = synth.qjl_matrix(d).astype(np.float64) if w.key_mode == "lloyd_qjl" else None
     f64 = lambda x: synth.bf16_bits_to_f32(x).astype(np.float64)
+    th = O.page_bytes(cfg) // 16
     b = 0
     slots = lay.slots(b, 0, T)
     cache = O.new_cache(cfg, lay.num_blocks)
-    t0 = time.time()
-    O.quantize_append(cfg, cache, f64(k_all[: T - 1]), f64(v_all[: T - 1]), slots[: T - 1], signs, kcb)
-    log(f"[cpu] oracle prefill of the sample sequence took {time.time() - t0:.1f}s (not timed)")
-    times = []
-    for _ in range(5):
-        t0 = time.perf_counter()
-        O.quantize_append(cfg, cache, f64(k_all[T - 1:T]), f64(v_all[T - 1:T]), slots[T - 1:T], signs, kcb)
-        O.decode_attention(cfg, f64(q_np[b:b + 1]), cache, lay.block_tables[b:b + 1], lay.seq_lens[b:b + 1],
-                           1.0 / math.sqrt(d), signs, kcb)
-        times.append(time.perf_counter() - t0)
-    sec = statistics.median(times)
-    th = O.page_bytes(cfg) // 16
-    sample_bytes = Hkv * (2 * d * 2 + th) + 8 + Hkv * T * th + Hq * d * 2 + Hq * d * 4 + lay.block_tables.shape[1] * 4 + 4
-    log(f"[cpu] oracle sample step {sec:.2f}s -> {sample_bytes / sec / 1e9:.4f} GB/s")
+    if w.name == "prefill_append":
+        n = 2048
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            O.quantize_append(cfg, cache, f64(k_all[:n]), f64(v_all[:n]), slots[:n], signs, kcb, S=S)
+            times.append(time.perf_counter() - t0)
+        sec = statistics.median(times)
+        sample_bytes = n * Hkv * (2 * d * 2 + th) + n * 8
+        sample = f"quantize-append of {n} tokens x {Hkv} kv heads, median of 3 runs, {sec:.2f} s each"
+    else:
+        t0 = time.time()
+        O.quantize_append(cfg, cache, f64(k_all[: T - 1]), f64(v_all[: T - 1]), slots[: T - 1], signs, kcb, S=S)
+        log(f"[cpu] oracle prefill of the sample sequence took {time.time() - t0:.1f}s (not timed)")
+        times = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            O.quantize_append(cfg, cache, f64(k_all[T - 1:T]), f64(v_all[T - 1:T]), slots[T - 1:T], signs, kcb, S=S)
+            O.decode_attention(cfg, f64(q_np[b:b + 1]), cache, lay.block_tables[b:b + 1], lay.seq_lens[b:b + 1],
+                               1.0 / math.sqrt(d), signs, kcb, S=S)
+            times.append(time.perf_counter() - t0)
+        sec = statistics.median(times)
+        sample_bytes = (Hkv * (2 * d * 2 + th) + 8 + Hkv * T * th + Hq * d * 2 + Hq * d * 4
+                        + lay.block_tables.shape[1] * 4 + 4)
+        sample = (f"one sequence of the step (append 1 token x {Hkv} kv heads, decode {Hq} q heads over {T} "
+                  f"tokens), median of 5 runs, {sec:.2f} s each")
+    log(f"[cpu] oracle sample {sec:.2f}s -> {sample_bytes / sec / 1e9:.4f} GB/s")
     return {"value": round(sample_bytes / sec / 1e9, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"one sequence of the step (append 1 token x {Hkv} kv heads, decode {Hq} q heads over {T} "
-                      f"tokens), median of 5 runs, {sec:.2f} s each"}
+            "sample": sample}
 
 
 if __name__ == "__main__":
