@@ -231,14 +231,17 @@ __device__ __forceinline__ float sum_rows(float v) {
   return v + __shfl_xor(v, 32);
 }
 
-template <int KB, int VB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void append_page_kernel(AppendArgs a) {
+template <int KB, int VB, bool QJL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3))) void append_page_kernel(AppendArgs a) {
   constexpr int KROW = 16 * KB;            // bytes of a packed key row
   constexpr int VROW = 16 * VB;            // bytes of a packed value row (= planes)
   constexpr int KSTR = KROW + 16;          // LDS stride of a packed key row
   __shared__ __align__(16) QLut lut[kUnitCellsPadded];
   __shared__ __align__(16) uint8_t kpack[4][16][KSTR];    // packed key rows [wave][token]
   __shared__ __align__(16) uint8_t vplane[4][64][16];     // value planes [wave][plane][token]
+  // QJL: S in the operand order of the fp32 MFMA (see the key pass)
+  __shared__ __align__(16) float sq[QJL ? kDim * kDim : 4];
+  __shared__ uint32_t sgn[QJL ? 4 : 1][16][4];              // QJL sign rows [wave][token][dword]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -287,6 +290,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   load_group(p, keys0, inA, rawA);
   for (int i = threadIdx.x; i < kUnitCellsPadded; i += 256)
     *reinterpret_cast<uint4*>(&lut[i]) = *reinterpret_cast<const uint4*>(&a.c->kulut[i]);
+  if constexpr (QJL)
+    for (int i = threadIdx.x; i < kDim * kDim / 4; i += 256)
+      *reinterpret_cast<uint4*>(&sq[4 * i]) = *reinterpret_cast<const uint4*>(&a.c->Sq[4 * i]);
   // A operands of the key rotation, one per block b = beta + 2n of the 16-point
   // transform: H16[j][k] times the sign of coordinate 32n + 8(k/4) + 4beta + k%4
   // (k = 4g + e), so the bf16 rows enter the MFMA as they are.
@@ -321,7 +327,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         // 32n + 8g' + 4beta + e
         floatx4 z[8];
         const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
+#pragma unroll
         for (int n = 0; n < 4; ++n) {
           z[2 * n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
               hs[2 * n], __builtin_bit_cast(shortx4, make_uint2(in[n].x, in[n].y)), zero, 0, 0, 0);
@@ -329,52 +335,101 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
               hs[2 * n + 1], __builtin_bit_cast(shortx4, make_uint2(in[n].z, in[n].w)), zero, 0, 0, 0);
         }
         // 8-point butterfly over b: z[b][r] becomes coordinate 32(b/2) + 8g + 4(b%2) + r
-  #pragma unroll
+#pragma unroll
         for (int len = 1; len < 8; len <<= 1)
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 8; i += 2 * len)
-  #pragma unroll
+#pragma unroll
             for (int m = i; m < i + len; ++m) {
               const floatx4 u = z[m], v = z[m + len];
               z[m] = u + v;
               z[m + len] = u - v;
             }
         float ss = 0.f;
-  #pragma unroll
+#pragma unroll
         for (int b = 0; b < 8; ++b)
-  #pragma unroll
+#pragma unroll
           for (int r = 0; r < 4; ++r) ss = fmaf(z[b][r], z[b][r], ss);
         ss = sum_rows(ss);
         // u = y / ||y||, g = 128 u; a zero key gives g = 0, codes 2^(b-1) and norm 0
         const float sg = ss > 0.f ? 128.f * __builtin_amdgcn_rsqf(ss) : 0.f;
         const uint32_t lut_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) QLut*)lut + 0x4C000000u;
+        // QJL: the residual in the rotated frame, times sqrt(d): z - ||z|| C[code]
+        const float nz = QJL ? __builtin_amdgcn_sqrtf(ss) : 0.f;
         float c2 = 0.f;
         uint32_t w[4];
-  #pragma unroll
+#pragma unroll
         for (int n = 0; n < 4; ++n) {
           uint32_t wn = 0u;
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 8; ++i) {
             const float gv = z[2 * n + (i >> 2)][i & 3] * sg;
             const uint32_t addr = (__float_as_uint(gv + kUnitMagic) << 4) + lut_addr;
             const u32x4 e = *reinterpret_cast<lds_u32x4*>((uintptr_t)addr);
             const bool up = gv >= __uint_as_float(e.y);
             const float c = up ? __uint_as_float(e.w) : __uint_as_float(e.z);
-            c2 = fmaf(c, c, c2);
+            if constexpr (QJL) z[2 * n + (i >> 2)][i & 3] = fmaf(-nz, c, z[2 * n + (i >> 2)][i & 3]);
+            else c2 = fmaf(c, c, c2);
             const uint32_t code = e.x + (uint32_t)up;
             wn |= code << (KB * i);
           }
           w[n] = wn;
         }
-        c2 = sum_rows(c2);
+        if constexpr (!QJL) c2 = sum_rows(c2);
         if (g == 0 && slot >= 0) {
           const float nk = __builtin_amdgcn_sqrtf(ss) * kInvSqrtDim;   // ||k|| (H/sqrt(d) is orthogonal)
-          const float nhat = a.key_nc ? (nk > 0.f ? nk * __builtin_amdgcn_rsqf(c2) : 0.f) : nk;
+          const float nhat = (!QJL && a.key_nc) ? (nk > 0.f ? nk * __builtin_amdgcn_rsqf(c2) : 0.f) : nk;
           reinterpret_cast<float*>(page_of(slot) + a.f.knorm)[slot & 15] = nhat;
+        }
+        if constexpr (QJL) {
+          // p = S r~ on the fp32 16x16x4 MFMA: rows = 16 rows of S (tile mt), columns =
+          // the 16 tokens, K step s = 8n + 4beta + r takes from lane (j, g) its own
+          // residual coordinate 32n + 8g + 4beta + r, so the B operand is this
+          // lane's register; sq holds, for lane l and steps 4q..4q+3 of tile mt,
+          // S[16mt + l%16][32(q/2) + 8(l/16) + 4(q%2) + e] at ((8mt + q) * 64 + l) * 4 + e.
+          float rr = 0.f;
+#pragma unroll
+          for (int b = 0; b < 8; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rr = fmaf(z[b][r], z[b][r], rr);
+          rr = sum_rows(rr);
+          // Sign rows of the wave's 16 tokens, assembled in LDS with OR: bit
+          // 16mt + 4g + r of token j comes from lane (j, g).
+          uint32_t* srow = &sgn[wave][j][0];
+          srow[g] = 0u;
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll 1
+          for (int mt = 0; mt < 8; ++mt) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const float4 av = *reinterpret_cast<const float4*>(&sq[((8 * mt + q) * 64 + lane) * 4]);
+              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, z[q][0], acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, z[q][1], acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, z[q][2], acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, z[q][3], acc, 0, 0, 0);
+            }
+            // lane (j, g) holds p[16mt + 4g + r] of token j: sign bit 1 for p >= 0
+            uint32_t nib = 0u;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) nib |= (acc[r] >= 0.f ? 1u : 0u) << r;
+            atomicOr(&srow[mt >> 1], nib << (16 * (mt & 1) + 4 * g));
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          if (slot >= 0) {
+            uint8_t* pg = page_of(slot);
+            // lane g stores dword g of token j's sign row
+            reinterpret_cast<uint32_t*>(pg + a.f.ksigns + 16 * (slot & 15))[g] = srow[g];
+            if (g == 0) reinterpret_cast<float*>(pg + a.f.kres)[slot & 15] = __builtin_amdgcn_sqrtf(rr) * kInvSqrtDim;
+          }
         }
         // codes of coordinates 32n + 8g .. +7 are bytes KB*(4n + g) .. +KB-1 of the row
         uint8_t* prow = &kpack[wave][j][0];
-  #pragma unroll
+#pragma unroll
         for (int n = 0; n < 4; ++n) {
           const int o = KB * (4 * n + g);
           if constexpr (KB == 4) *reinterpret_cast<uint32_t*>(prow + o) = w[n];
@@ -411,17 +466,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         const bool whole = (__ballot(!(slot >= 0 && slot == slot0 + t)) == 0ull) && slot0 >= 0 && (slot0 & 15) == 0;
 
         float x[32];                              // x[8n + e]: coordinate 32n + 8q + e
-  #pragma unroll
+#pragma unroll
         for (int n = 0; n < 4; ++n) {
           const uint32_t wv[4] = {in[n].x, in[n].y, in[n].z, in[n].w};
-  #pragma unroll
+#pragma unroll
           for (int d = 0; d < 4; ++d) {
             x[8 * n + 2 * d] = bf16lo(wv[d]);
             x[8 * n + 2 * d + 1] = bf16hi(wv[d]);
           }
         }
         float mn = x[0], mx = x[0];
-  #pragma unroll
+#pragma unroll
         for (int k = 1; k < 32; ++k) {
           mn = fminf(mn, x[k]);
           mx = fmaxf(mx, x[k]);
@@ -435,10 +490,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
         // 2^-20 for codes up to 15) of a rounding boundary: a normalised distance
         // (x - mn) / (mx - mn) far below 1e-6, inside the band where either code counts.
         uint32_t w[4];                            // w[n]: the 8 codes of chunk q + 4n (VB bytes)
-  #pragma unroll
+#pragma unroll
         for (int n = 0; n < 4; ++n) {
           uint32_t wn = 0u;
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 8; ++e) wn |= (uint32_t)fmaf(x[8 * n + e] - mn, inv, 0.5f) << (VB * e);
           w[n] = wn;
         }
@@ -448,9 +503,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
           reinterpret_cast<float*>(pg + a.f.vscale)[slot & 15] = sc;
         }
         // row bytes VB*(q + 4n) .. +VB-1 are those planes
-  #pragma unroll
+#pragma unroll
         for (int n = 0; n < 4; ++n)
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < VB; ++i) vplane[wave][VB * (q + 4 * n) + i][t] = (uint8_t)(w[n] >> (8 * i));
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -462,7 +517,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
             *reinterpret_cast<uint4*>(page_of(slot0) + a.f.vcodes + 16 * lane) =
                 *reinterpret_cast<const uint4*>(&vplane[wave][lane][0]);
         } else {
-  #pragma unroll 1
+#pragma unroll 1
           for (int v = 0; v < 16; ++v) {
             const int64_t sv = __builtin_amdgcn_readlane((int)slot, 4 * v) |
                                ((int64_t)__builtin_amdgcn_readlane((int)(slot >> 32), 4 * v) << 32);
@@ -495,19 +550,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void a
   }
 }
 
-const void* append_page_kernel_ptr(int key_bits, int val_bits) {
+namespace {
+template <bool QJL>
+const void* page_ptr(int key_bits, int val_bits) {
   switch (key_bits * 8 + val_bits) {
-    case 2 * 8 + 2: return (const void*)append_page_kernel<2, 2>;
-    case 2 * 8 + 3: return (const void*)append_page_kernel<2, 3>;
-    case 2 * 8 + 4: return (const void*)append_page_kernel<2, 4>;
-    case 3 * 8 + 2: return (const void*)append_page_kernel<3, 2>;
-    case 3 * 8 + 3: return (const void*)append_page_kernel<3, 3>;
-    case 3 * 8 + 4: return (const void*)append_page_kernel<3, 4>;
-    case 4 * 8 + 2: return (const void*)append_page_kernel<4, 2>;
-    case 4 * 8 + 3: return (const void*)append_page_kernel<4, 3>;
-    case 4 * 8 + 4: return (const void*)append_page_kernel<4, 4>;
+    case 2 * 8 + 2: return (const void*)append_page_kernel<2, 2, QJL>;
+    case 2 * 8 + 3: return (const void*)append_page_kernel<2, 3, QJL>;
+    case 2 * 8 + 4: return (const void*)append_page_kernel<2, 4, QJL>;
+    case 3 * 8 + 2: return (const void*)append_page_kernel<3, 2, QJL>;
+    case 3 * 8 + 3: return (const void*)append_page_kernel<3, 3, QJL>;
+    case 3 * 8 + 4: return (const void*)append_page_kernel<3, 4, QJL>;
+    case 4 * 8 + 2: return (const void*)append_page_kernel<4, 2, QJL>;
+    case 4 * 8 + 3: return (const void*)append_page_kernel<4, 3, QJL>;
+    case 4 * 8 + 4: return (const void*)append_page_kernel<4, 4, QJL>;
   }
   return nullptr;
+}
+}  // namespace
+
+const void* append_page_kernel_ptr(int key_bits, int val_bits, bool qjl) {
+  return qjl ? page_ptr<true>(key_bits, val_bits) : page_ptr<false>(key_bits, val_bits);
 }
 
 namespace {
@@ -542,15 +604,15 @@ hipError_t values_mode(const AppendArgs& a, int dtype, int val_mode, hipStream_t
   return val_mode == TQ_VAL_LLOYD ? values_for_dtype<VB, true>(a, dtype, s) : values_for_dtype<VB, false>(a, dtype, s);
 }
 
-template <int KB>
+template <int KB, bool QJL>
 hipError_t page_vb(const AppendArgs& a, int val_bits, hipStream_t s) {
   // one pair of 16-token groups per work-group and pass; at most a.page_wgs work-groups
   const int64_t pairs = ((a.num_tokens + 15) / 16 * a.hkv + 1) / 2;
   const dim3 grid((unsigned)std::min<int64_t>(pairs, std::max(1, a.page_wgs)));
   switch (val_bits) {
-    case 2: hipLaunchKernelGGL((append_page_kernel<KB, 2>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((append_page_kernel<KB, 3>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((append_page_kernel<KB, 4>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((append_page_kernel<KB, 2, QJL>), grid, dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((append_page_kernel<KB, 3, QJL>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((append_page_kernel<KB, 4, QJL>), grid, dim3(256), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -560,14 +622,15 @@ hipError_t page_vb(const AppendArgs& a, int val_bits, hipStream_t s) {
 
 hipError_t launch_append(const AppendArgs& a, int dtype, int key_bits, int key_mode, int val_bits, int val_mode,
                          hipStream_t s) {
-  // bf16 inputs, Lloyd-Max keys without QJL and uniform values: one launch for
-  // both; the other combinations take the per-vector kernels.
-  if (dtype == TQ_BF16 && key_mode != TQ_KEY_LLOYD_QJL && val_mode == TQ_VAL_UNIFORM && a.unit_grid_ok &&
+  // bf16 inputs and uniform values: one launch for keys and values; the other
+  // combinations take the per-vector kernels.
+  if (dtype == TQ_BF16 && val_mode == TQ_VAL_UNIFORM && a.unit_grid_ok &&
       (a.num_tokens + 15) / 16 * a.hkv < ((int64_t)1 << 31)) {
+    const bool qjl = key_mode == TQ_KEY_LLOYD_QJL;
     switch (key_bits) {
-      case 2: return page_vb<2>(a, val_bits, s);
-      case 3: return page_vb<3>(a, val_bits, s);
-      case 4: return page_vb<4>(a, val_bits, s);
+      case 2: return qjl ? page_vb<2, true>(a, val_bits, s) : page_vb<2, false>(a, val_bits, s);
+      case 3: return qjl ? page_vb<3, true>(a, val_bits, s) : page_vb<3, false>(a, val_bits, s);
+      case 4: return qjl ? page_vb<4, true>(a, val_bits, s) : page_vb<4, false>(a, val_bits, s);
     }
     return hipErrorInvalidValue;
   }

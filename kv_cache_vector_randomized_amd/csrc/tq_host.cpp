@@ -301,9 +301,16 @@ tq_status tq_create(const tq_config* cfg, const int8_t* signs_host, const float*
     ok = ok && build_lut((int)cfg->val_bits, h->vc, vt, h->vlut, &ctx->vlut_scale, &ctx->vlut_bias);
   }
   if (!ok) { delete h; delete ctx; return fail(TQ_ERR_UNSUPPORTED, "codebook thresholds too dense for the look-up grid"); }
-  if (cfg->key_mode == TQ_KEY_LLOYD_QJL)
+  if (cfg->key_mode == TQ_KEY_LLOYD_QJL) {
     for (int m = 0; m < d; ++m)
       for (int k = 0; k < d; ++k) h->St[k * d + m] = S_host[m * d + k];
+    for (int mt = 0; mt < 8; ++mt)
+      for (int q = 0; q < 8; ++q)
+        for (int l = 0; l < 64; ++l)
+          for (int e = 0; e < 4; ++e)
+            h->Sq[((8 * mt + q) * 64 + l) * 4 + e] =
+                S_host[(16 * mt + l % 16) * d + 32 * (q / 2) + 8 * (l / 16) + 4 * (q % 2) + e];
+  }
   for (int i = 0; i < 4; ++i) ctx->sign_bits[i] = 0;
   for (int i = 0; i < d; ++i)
     if (signs_host[i] < 0) ctx->sign_bits[i >> 5] |= 1u << (i & 31);
@@ -330,7 +337,8 @@ tq_status tq_create(const tq_config* cfg, const int8_t* signs_host, const float*
   (void)hipGetLastError();
   ctx->decode_wgs = per_cu * cus;
   int page_per_cu = 0;
-  const void* pk = tq::append_page_kernel_ptr((int)cfg->key_bits, (int)cfg->val_bits);
+  const void* pk = tq::append_page_kernel_ptr((int)cfg->key_bits, (int)cfg->val_bits,
+                                              cfg->key_mode == TQ_KEY_LLOYD_QJL);
   if (!pk || hipOccupancyMaxActiveBlocksPerMultiprocessor(&page_per_cu, pk, 256, 0) != hipSuccess || page_per_cu <= 0)
     page_per_cu = 2;
   (void)hipGetLastError();

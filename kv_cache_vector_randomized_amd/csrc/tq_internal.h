@@ -45,6 +45,10 @@ struct DevConsts {
   QLut vlut[kLutCells];
   QLut kulut[kUnitCellsPadded];   // key grid of the page kernel; t in units of g = 128 y
   float St[kDim * kDim];      // QJL projection transposed: St[k*d + m] = S[m][k]
+  // QJL projection in the page kernel's MFMA operand order: for tile mt (rows
+  // 16mt..16mt+15), step group q and lane l, the 4 values
+  // S[16mt + l%16][32(q/2) + 8(l/16) + 4(q%2) + e] at ((8mt + q) * 64 + l) * 4 + e.
+  float Sq[kDim * kDim];
 };
 
 struct FieldOffsets {
@@ -110,7 +114,7 @@ hipError_t launch_append(const AppendArgs& a, int dtype, int key_bits, int key_m
                          int val_mode, hipStream_t s);
 // Address of the decode kernel instance for a configuration (for occupancy queries).
 const void* decode_kernel_ptr(int key_bits, int key_mode, int val_bits, int val_mode);
-const void* append_page_kernel_ptr(int key_bits, int val_bits);
+const void* append_page_kernel_ptr(int key_bits, int val_bits, bool qjl);
 hipError_t launch_decode(const DecodeArgs& a, int key_bits, int key_mode, int val_bits, int val_mode,
                          hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, int key_bits, int key_mode, int val_bits, int val_mode,
