@@ -225,6 +225,12 @@ __device__ __forceinline__ void quad_minmax(float& mn, float& mx) {
       : "+v"(mn), "+v"(mx));
 }
 
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ floatx4 mfma_f16x32(const uint4& a, const uint4& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c, 0, 0,
+                                                0);
+}
+
 // Sum over the lanes j, j+16, j+32, j+48.
 __device__ __forceinline__ float sum_rows(float v) {
   v += __shfl_xor(v, 16);
@@ -239,8 +245,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
   __shared__ __align__(16) QLut lut[kUnitCellsPadded];
   __shared__ __align__(16) uint8_t kpack[4][16][KSTR];    // packed key rows [wave][token]
   __shared__ __align__(16) uint8_t vplane[4][64][16];     // value planes [wave][plane][token]
-  // QJL: S in the operand order of the fp32 MFMA (see the key pass)
-  __shared__ __align__(16) float sq[QJL ? kDim * kDim : 4];
+  // QJL: the f16 terms of S in the operand order of the MFMA (see the key pass)
+  __shared__ __align__(16) uint32_t sq[QJL ? kDim * kDim : 4];
   __shared__ uint32_t sgn[QJL ? 4 : 1][16][4];              // QJL sign rows [wave][token][dword]
 
   const int lane = threadIdx.x & 63;
@@ -292,7 +298,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
     *reinterpret_cast<uint4*>(&lut[i]) = *reinterpret_cast<const uint4*>(&a.c->kulut[i]);
   if constexpr (QJL)
     for (int i = threadIdx.x; i < kDim * kDim / 4; i += 256)
-      *reinterpret_cast<uint4*>(&sq[4 * i]) = *reinterpret_cast<const uint4*>(&a.c->Sq[4 * i]);
+      *reinterpret_cast<uint4*>(&sq[4 * i]) = *reinterpret_cast<const uint4*>(&a.c->Sh[4 * i]);
   // A operands of the key rotation, one per block b = beta + 2n of the 16-point
   // transform: H16[j][k] times the sign of coordinate 32n + 8(k/4) + 4beta + k%4
   // (k = 4g + e), so the bf16 rows enter the MFMA as they are.
@@ -382,17 +388,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
           reinterpret_cast<float*>(page_of(slot) + a.f.knorm)[slot & 15] = nhat;
         }
         if constexpr (QJL) {
-          // p = S r~ on the fp32 16x16x4 MFMA: rows = 16 rows of S (tile mt), columns =
-          // the 16 tokens, K step s = 8n + 4beta + r takes from lane (j, g) its own
-          // residual coordinate 32n + 8g + 4beta + r, so the B operand is this
-          // lane's register; sq holds, for lane l and steps 4q..4q+3 of tile mt,
-          // S[16mt + l%16][32(q/2) + 8(l/16) + 4(q%2) + e] at ((8mt + q) * 64 + l) * 4 + e.
+          // p = S r~ on the f16 16x16x32 MFMA, each side split into two f16 terms
+          // (r~ scaled by a power of two per token: signs do not change):
+          // p = S_hi r_hi + S_hi r_lo + S_lo r_hi, the dropped S_lo r_lo and the
+          // terms' own rounding below 2^-22 |S_i| |r~| each (Cauchy-Schwarz), far
+          // inside the 1e-6 band of the sign decision.  Rows = 16 rows of S (tile
+          // mt), columns = the 16 tokens, K step n = coordinates 32n + 8g + e of
+          // lane (j, g): the lane's own registers are its B operand.
           float rr = 0.f;
 #pragma unroll
           for (int b = 0; b < 8; ++b)
 #pragma unroll
             for (int r = 0; r < 4; ++r) rr = fmaf(z[b][r], z[b][r], rr);
           rr = sum_rows(rr);
+          // |r~_i| <= ||z|| (1 + max |C|) < 2^(e+1) with ||z|| in [2^(e-1), 2^e)
+          const float rs = ldexpf(1.f, 13 - __builtin_amdgcn_frexp_expf(nz));
+          uint4 rh[4], rl[4];
+#pragma unroll
+          for (int n = 0; n < 4; ++n) {
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int p2 = 0; p2 < 4; ++p2) {
+              const float v0 = z[2 * n + (p2 >> 1)][2 * (p2 & 1)] * rs;
+              const float v1 = z[2 * n + (p2 >> 1)][2 * (p2 & 1) + 1] * rs;
+              const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
+              const _Float16 l0 = (_Float16)(v0 - (float)h0), l1 = (_Float16)(v1 - (float)h1);
+              hw[p2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+              lw[p2] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+            }
+            rh[n] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            rl[n] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+          }
           // Sign rows of the wave's 16 tokens, assembled in LDS with OR: bit
           // 16mt + 4g + r of token j comes from lane (j, g).
           uint32_t* srow = &sgn[wave][j][0];
@@ -404,12 +430,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
           for (int mt = 0; mt < 8; ++mt) {
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              const float4 av = *reinterpret_cast<const float4*>(&sq[((8 * mt + q) * 64 + lane) * 4]);
-              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, z[q][0], acc, 0, 0, 0);
-              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, z[q][1], acc, 0, 0, 0);
-              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, z[q][2], acc, 0, 0, 0);
-              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, z[q][3], acc, 0, 0, 0);
+            for (int n = 0; n < 4; ++n) {
+              const uint4 sh = *reinterpret_cast<const uint4*>(&sq[(((0 * 8 + mt) * 4 + n) * 64 + lane) * 4]);
+              const uint4 sl = *reinterpret_cast<const uint4*>(&sq[(((1 * 8 + mt) * 4 + n) * 64 + lane) * 4]);
+              acc = mfma_f16x32(sl, rh[n], acc);
+              acc = mfma_f16x32(sh, rl[n], acc);
+              acc = mfma_f16x32(sh, rh[n], acc);
             }
             // lane (j, g) holds p[16mt + 4g + r] of token j: sign bit 1 for p >= 0
             uint32_t nib = 0u;

@@ -305,11 +305,18 @@ tq_status tq_create(const tq_config* cfg, const int8_t* signs_host, const float*
     for (int m = 0; m < d; ++m)
       for (int k = 0; k < d; ++k) h->St[k * d + m] = S_host[m * d + k];
     for (int mt = 0; mt < 8; ++mt)
-      for (int q = 0; q < 8; ++q)
+      for (int n = 0; n < 4; ++n)
         for (int l = 0; l < 64; ++l)
-          for (int e = 0; e < 4; ++e)
-            h->Sq[((8 * mt + q) * 64 + l) * 4 + e] =
-                S_host[(16 * mt + l % 16) * d + 32 * (q / 2) + 8 * (l / 16) + 4 * (q % 2) + e];
+          for (int e = 0; e < 8; ++e) {
+            const float x = S_host[(16 * mt + l % 16) * d + 32 * n + 8 * (l / 16) + e];
+            const _Float16 hi = (_Float16)x;
+            const _Float16 lo = (_Float16)(x - (float)hi);
+            const uint32_t sh = 16u * (uint32_t)(e & 1);
+            const size_t w = ((size_t)((0 * 8 + mt) * 4 + n) * 64 + l) * 4 + e / 2;
+            const size_t w_lo = ((size_t)((1 * 8 + mt) * 4 + n) * 64 + l) * 4 + e / 2;
+            h->Sh[w] |= (uint32_t)__builtin_bit_cast(uint16_t, hi) << sh;
+            h->Sh[w_lo] |= (uint32_t)__builtin_bit_cast(uint16_t, lo) << sh;
+          }
   }
   for (int i = 0; i < 4; ++i) ctx->sign_bits[i] = 0;
   for (int i = 0; i < d; ++i)

@@ -45,10 +45,12 @@ struct DevConsts {
   QLut vlut[kLutCells];
   QLut kulut[kUnitCellsPadded];   // key grid of the page kernel; t in units of g = 128 y
   float St[kDim * kDim];      // QJL projection transposed: St[k*d + m] = S[m][k]
-  // QJL projection in the page kernel's MFMA operand order: for tile mt (rows
-  // 16mt..16mt+15), step group q and lane l, the 4 values
-  // S[16mt + l%16][32(q/2) + 8(l/16) + 4(q%2) + e] at ((8mt + q) * 64 + l) * 4 + e.
-  float Sq[kDim * kDim];
+  // QJL projection for the page kernel's f16 MFMA: S = S_hi + S_lo (f16 terms,
+  // S_lo the f16 rounding of S - S_hi).  For term t, row tile mt (rows
+  // 16mt..16mt+15), K step n and lane l, the 8 halves S_t[16mt + l%16][32n +
+  // 8(l/16) + e], e = 0..7, two per word (even e low), at words
+  // (((t * 8 + mt) * 4 + n) * 64 + l) * 4 .. + 3.
+  uint32_t Sh[2 * kDim * kDim / 2];
 };
 
 struct FieldOffsets {
