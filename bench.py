@@ -6,8 +6,9 @@ Default workload (GQA decode, Llama-8B-like shape): batch 16, 32 query heads,
 corrected norm, values 4-bit uniform with fp32 min/scale.  One step = quantize
 and append the new token of every sequence (K and V, 16 x 8 token-heads) into
 the paged cache, then decode attention of the 16 new queries over their 8192
-cached tokens.  Steps rotate over --layers independent caches (one per layer)
-so the 147 MB working set does not stay in the 256 MB Infinity Cache.
+cached tokens, in one launch (tq_append_decode; --separate: tq_quantize_append
+then tq_decode_attention).  Steps rotate over --layers independent caches (one
+per layer) so the 147 MB working set does not stay in the 256 MB Infinity Cache.
 
 Other workloads (--workload):
   long_3bit       batch 4 x context 32768, 3-bit keys and values, same step;
@@ -75,6 +76,8 @@ def main():
     ap.add_argument("--layers", type=int, default=4, help="independent layer caches rotated over the steps")
     ap.add_argument("--workload", default="gqa_decode", choices=list(MODES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="decode workloads: append and decode as two launches instead of one")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -131,16 +134,29 @@ def main():
         torch.cuda.synchronize()
         del k_dev, v_dev
         append_bytes = B * Hkv * (2 * d * 2 + th) + B * 8
-        dominant, dom_bytes, dom_source = "decode_kernel", decode_bytes, "tq_decode.hip"
+        if args.separate:
+            dominant, dom_bytes, dom_source = "decode_kernel", decode_bytes, "tq_decode.hip"
 
-        def step(i, ev=None):
-            c = caches[i % n_layers]
-            c.append(k_new, v_new, slots_new)
-            if ev is not None:
-                ev[0].record(stream)
-            c.decode(q_dev, tables, seq_lens, T, scale, out=out)
-            if ev is not None:
-                ev[1].record(stream)
+            def step(i, ev=None):
+                c = caches[i % n_layers]
+                c.append(k_new, v_new, slots_new)
+                if ev is not None:
+                    ev[0].record(stream)
+                c.decode(q_dev, tables, seq_lens, T, scale, out=out)
+                if ev is not None:
+                    ev[1].record(stream)
+        else:
+            # one launch: the decode kernel also quantizes and stores the new tokens
+            # (their slots are those of position T-1 in the block tables)
+            dominant, dom_bytes, dom_source = "decode_kernel (fused append)", decode_bytes + append_bytes, "tq_decode.hip"
+
+            def step(i, ev=None):
+                c = caches[i % n_layers]
+                if ev is not None:
+                    ev[0].record(stream)
+                c.append_decode(k_new, v_new, q_dev, tables, seq_lens, T, scale, out=out)
+                if ev is not None:
+                    ev[1].record(stream)
     else:
         append_bytes = B * T * Hkv * (2 * d * 2 + th) + B * T * 8
         dominant, dom_bytes, dom_source = "append_page_kernel", append_bytes, "tq_append.hip"
@@ -210,7 +226,8 @@ def main():
             "workload": args.workload, "batch": B, "context": T, "num_q_heads": Hq, "num_kv_heads": Hkv,
             "head_dim": d, "key_bits": w.key_bits, "key_mode": w.key_mode, "val_bits": w.val_bits,
             "val_mode": w.val_mode, "block_tokens": 16, "layer_caches": n_layers,
-            "step": ("append 1 token/seq + decode" if kind == "decode" else "append all tokens + decode"),
+            "step": ("append 1 token/seq + decode" + (" (two launches)" if args.separate else " (one launch)")
+                     if kind == "decode" else "append all tokens + decode"),
             "step_bytes": step_bytes,
         },
         "hbm_fraction": round(value / HBM_PEAK_GBS, 4),

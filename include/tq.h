@@ -191,6 +191,27 @@ tq_status tq_decode_attention(tq_ctx* ctx, const void* q, tq_dtype dt, const voi
                               int32_t batch, int32_t max_seq_len, float softmax_scale, float* out,
                               float* logits_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* One decode step in one launch: store the new token of every sequence, then
+ * attend over the context including it (turboquant-vllm write-up, "Incremental
+ * dequantization": each step handles only the one new token; "Bugs Nobody Else
+ * Has Found": the attention is fused over the compressed cache).  The result
+ * equals tq_quantize_append of the new tokens followed by tq_decode_attention,
+ * up to the decision band and the fp32 summation order.
+ *   k_new, v_new: device [batch][num_kv_heads][head_dim], dtype dt (the query's).
+ *                 The new token of sequence b is position seq_lens[b] - 1: it is
+ *                 written to slot block_tables[b][(seq_lens[b]-1)/16]*16 +
+ *                 (seq_lens[b]-1)%16 (nothing is written, and the position is
+ *                 attended as stored, when that block is outside [0, num_blocks);
+ *                 a sequence of length 0 takes no new token).
+ *   cache:        device, written at those slots only.
+ *   all other arguments as for tq_decode_attention.
+ * Uniform values only (TQ_ERR_UNSUPPORTED for Lloyd-Max values). */
+tq_status tq_append_decode(tq_ctx* ctx, const void* k_new, const void* v_new, const void* q, tq_dtype dt,
+                           void* cache, int64_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float softmax_scale,
+                           float* out, float* logits_out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 /* Reconstruct stored tokens in the original basis (stage 1 only for QJL keys):
  *   k_hat = norm * R^T C[code];  v_hat = min + scale * code  (or as keys).
  *   slots: device int64 [n]; k_out, v_out: device fp32 [n][num_kv_heads][head_dim].

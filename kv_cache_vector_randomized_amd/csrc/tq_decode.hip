@@ -303,6 +303,115 @@ __device__ __forceinline__ int limb4(const uint4& x, uint32_t sh) {
   return (int)(b0 | (b1 << 8) | (b2 << 16) | (b3 << 24));
 }
 
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Bits 0..15 of e to the even and of o to the odd bit positions of a word.
+__device__ __forceinline__ uint32_t interleave16(uint32_t e, uint32_t o) {
+  auto spread = [](uint32_t x) {
+    x &= 0xFFFFu;
+    x = (x | (x << 8)) & 0x00FF00FFu;
+    x = (x | (x << 4)) & 0x0F0F0F0Fu;
+    x = (x | (x << 2)) & 0x33333333u;
+    return (x | (x << 1)) & 0x55555555u;
+  };
+  return spread(e) | (spread(o) << 1);
+}
+
+// Byte p of the LSB-first bit stream of 128 codes of B bits held one per byte.
+template <int B>
+__device__ __forceinline__ uint32_t stream_byte(const uint8_t* codes, int p) {
+  uint32_t v = 0u;
+  for (int i = (8 * p) / B; i < kDim && B * i < 8 * p + 8; ++i) {
+    const int sh = B * i - 8 * p;
+    const uint32_t c = codes[i];
+    v |= sh >= 0 ? (c << sh) : (c >> -sh);
+  }
+  return v & 0xFFu;
+}
+
+// Fused append (one wave): quantize the new token (lane l holds its coordinates
+// 2l, 2l+1 of the key k0, k1 and the value v0, v1) as the append kernels do (rotation, codes through the key grid, fp32 norm with the
+// optional correction, QJL signs and residual norm, uniform values) and write its
+// fields into slot `so` of `page`.  Lane l works on coordinates 2l, 2l+1 and
+// returns their key centroids (c0, c1), the stored norm, the QJL residual norm and
+// the signs (+1/-1) of rows 2l, 2l+1 of S r'; the dequantized value row goes to
+// vhat.  codes / rbuf are LDS scratch of the wave.
+template <int KB, bool QJL, int VB>
+__device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, float v0, float v1, int lane,
+                                   uint8_t* page, int so, uint8_t (&codes)[2][kDim], float* vhat, float* rbuf,
+                                   float& c0, float& c1, float& nhat, float& rho, float& sgn0, float& sgn1) {
+  // keys: z = H(s * k), then codes of u = z / ||z||
+  float x0 = k0 * a.c->signs[2 * lane], x1 = k1 * a.c->signs[2 * lane + 1];
+  {
+    const float s0 = x0 + x1, d0 = x0 - x1;
+    x0 = s0;
+    x1 = d0;
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const float p0 = __shfl_xor(x0, m), p1 = __shfl_xor(x1, m);
+    const bool upper = (lane & m) != 0;
+    x0 = upper ? p0 - x0 : x0 + p0;
+    x1 = upper ? p1 - x1 : x1 + p1;
+  }
+  const float ss = wave_sum(fmaf(x0, x0, x1 * x1));
+  const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;     // a zero key gives codes 2^(b-1)
+  const int kc0 = lut_code(a.c->klut, x0 * inv, a.klut_scale, a.klut_bias, c0);
+  const int kc1 = lut_code(a.c->klut, x1 * inv, a.klut_scale, a.klut_bias, c1);
+  const float nk = sqrtf(ss) * kInvSqrtDim;               // ||k||
+  const float c2 = wave_sum(fmaf(c0, c0, c1 * c1));
+  nhat = (!QJL && a.key_nc) ? (nk > 0.f ? nk / sqrtf(c2) : 0.f) : nk;
+  rho = 0.f;
+  sgn0 = sgn1 = 1.f;
+  if constexpr (QJL) {
+    // residual in the rotated frame r' = H(s*k)/sqrt(d) - ||k|| C[code], and S r'
+    const float r0 = fmaf(-nk, c0, x0 * kInvSqrtDim), r1 = fmaf(-nk, c1, x1 * kInvSqrtDim);
+    rho = sqrtf(wave_sum(fmaf(r0, r0, r1 * r1)));
+    rbuf[2 * lane] = r0;
+    rbuf[2 * lane + 1] = r1;
+    wave_sync_lds();
+    float p0 = 0.f, p1 = 0.f;
+#pragma unroll 8
+    for (int k = 0; k < kDim; ++k) {
+      const float2 sv = *reinterpret_cast<const float2*>(&a.c->St[k * kDim + 2 * lane]);
+      p0 = fmaf(sv.x, rbuf[k], p0);
+      p1 = fmaf(sv.y, rbuf[k], p1);
+    }
+    sgn0 = p0 >= 0.f ? 1.f : -1.f;
+    sgn1 = p1 >= 0.f ? 1.f : -1.f;
+    const uint64_t em = __ballot(p0 >= 0.f), om = __ballot(p1 >= 0.f);
+    if (lane < 4)
+      reinterpret_cast<uint32_t*>(page + a.f.ksigns + 16 * so)[lane] =
+          interleave16((uint32_t)(em >> (16 * lane)), (uint32_t)(om >> (16 * lane)));
+  }
+  // uniform values, as the append kernel: codes floor(fl32(x - mn) / sc + 1/2)
+  const float mn = -wave_max(-fminf(v0, v1));
+  const float mx = wave_max(fmaxf(v0, v1));
+  constexpr float levels = (float)((1 << VB) - 1);
+  const float sc = (mx - mn) / levels;
+  const float vinv = sc > 0.f ? 1.f / sc : 0.f;
+  const uint32_t vc0 = (uint32_t)fmaf(v0 - mn, vinv, 0.5f), vc1 = (uint32_t)fmaf(v1 - mn, vinv, 0.5f);
+  vhat[2 * lane] = fmaf(sc, (float)vc0, mn);
+  vhat[2 * lane + 1] = fmaf(sc, (float)vc1, mn);
+  codes[0][2 * lane] = (uint8_t)kc0;
+  codes[0][2 * lane + 1] = (uint8_t)kc1;
+  codes[1][2 * lane] = (uint8_t)vc0;
+  codes[1][2 * lane + 1] = (uint8_t)vc1;
+  wave_sync_lds();
+  if (lane < 16 * KB) page[a.f.kcodes + so * 16 * KB + lane] = (uint8_t)stream_byte<KB>(codes[0], lane);
+  if (lane < 16 * VB) page[a.f.vcodes + 16 * lane + so] = (uint8_t)stream_byte<VB>(codes[1], lane);
+  if (lane == 0) {
+    reinterpret_cast<float*>(page + a.f.knorm)[so] = nhat;
+    reinterpret_cast<float*>(page + a.f.vmin)[so] = mn;
+    reinterpret_cast<float*>(page + a.f.vscale)[so] = sc;
+    if constexpr (QJL) reinterpret_cast<float*>(page + a.f.kres)[so] = rho;
+  }
+}
+
 template <int KB, bool QJL, int VB, bool VLM>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -332,6 +441,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   // tiles are handed to the waves one at a time, so every wave may need any of them.
   __shared__ int blk_lds[kMaxPagesPerSplit];
   __shared__ unsigned tile_ctr;
+  // Fused append: fp32 rotated query rows and QJL projections of the heads, the
+  // new token's codes, dequantized value row and QJL residual.
+  __shared__ __align__(16) float qf[VLM ? 1 : 4][kDim];
+  __shared__ __align__(16) float pf[QJL ? 4 : 1][kDim];
+  __shared__ __align__(16) uint8_t nt_codes[VLM ? 1 : 2][kDim];
+  __shared__ __align__(16) float nt_vhat[VLM ? 1 : kDim];
+  __shared__ __align__(16) float nt_r[QJL ? kDim : 1];
 
   const int G = a.group;
   int seq_len = a.seq_lens[b];
@@ -341,10 +457,19 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   // sequence's tiles (at most 64).
   const int tile_begin = (int)((uint32_t)(split * a.tiles_total) / (uint32_t)a.splits);
   const int tile_end = (int)((uint32_t)((split + 1) * a.tiles_total) / (uint32_t)a.splits);
-  const int tok_end = min(seq_len, tile_end * 64);
   const int64_t head_stride = a.f.page_bytes;
   const int64_t blk_stride = head_stride * a.hkv;
   const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
+  // Fused append: position seq_len - 1 is the new token (when its block exists); it
+  // is left out of the tiles and enters through the work-group whose split holds it.
+  int new_blk = -1;
+  if (!VLM && a.k_new != nullptr && seq_len > 0) {
+    const int raw = table[(seq_len - 1) >> 4];
+    new_blk = (raw >= 0 && (int64_t)raw < a.num_blocks) ? raw : -1;
+  }
+  const bool has_new = new_blk >= 0;
+  const bool own_new = has_new && ((seq_len - 1) >> 6) >= tile_begin && ((seq_len - 1) >> 6) < tile_end;
+  const int tok_end = min(seq_len - (has_new ? 1 : 0), tile_end * 64);
   uint32_t (&wt)[4][68] = wT[wave];
 
   // ---- Prologue.  The constants the shared tables need are fetched first (the
@@ -467,6 +592,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     *reinterpret_cast<uint2*>(&qd[wave][2][2 * lane]) = make_uint2(f16bits(m0) * 0x10001u, f16bits(m1) * 0x10001u);
     *reinterpret_cast<uint2*>(&qd[wave][3][2 * lane]) = make_uint2(0u, 0u);
     if (lane == 0) qexp[wave] = s1;
+    if constexpr (!VLM) *reinterpret_cast<float2*>(&qf[wave][2 * lane]) = make_float2(x0, x1);
     if constexpr (QJL) {
       // p'' = coef * S q''  (coef = sqrt(pi/2)/m): lane computes rows 2*lane, 2*lane+1
       q_sh[wave][2 * lane] = x0;
@@ -482,6 +608,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
       }
       acc0 *= a.qjl_coef;
       acc1 *= a.qjl_coef;
+      *reinterpret_cast<float2*>(&pf[wave][2 * lane]) = make_float2(acc0, acc1);
       const float pm = wave_max(fmaxf(fabsf(acc0), fabsf(acc1)));
       const int sp = pm > 0.f ? 15 - __builtin_amdgcn_frexp_expf(pm) : 0;
       split_f16(ldexpf(acc0, sp), h0, l0, m0);
@@ -491,6 +618,23 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
       pt[wave][2][lane] = f16bits(m0) | (f16bits(m1) << 16);
       pt[wave][3][lane] = 0u;
       if (lane == 0) pexp[wave] = sp;
+    }
+  }
+  // Fused append: the new token's key and value pairs of this lane, loaded before
+  // the barrier; wave kMaxGroup quantizes them after it, so no other wave waits.
+  float nt_k0 = 0.f, nt_k1 = 0.f, nt_v0 = 0.f, nt_v1 = 0.f;
+  if constexpr (!VLM) {
+    if (own_new && wave == kMaxGroup) {
+      const int64_t e0 = ((int64_t)b * a.hkv + kvh) * kDim + 2 * lane;
+      if (a.q_dtype != TQ_BF16) {
+        const float2 kk = *reinterpret_cast<const float2*>(static_cast<const float*>(a.k_new) + e0);
+        const float2 vv = *reinterpret_cast<const float2*>(static_cast<const float*>(a.v_new) + e0);
+        nt_k0 = kk.x; nt_k1 = kk.y; nt_v0 = vv.x; nt_v1 = vv.y;
+      } else {
+        const uint32_t kw = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.k_new) + e0);
+        const uint32_t vw = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.v_new) + e0);
+        nt_k0 = bf16lo(kw); nt_k1 = bf16hi(kw); nt_v0 = bf16lo(vw); nt_v1 = bf16hi(vw);
+      }
     }
   }
   __syncthreads();
@@ -512,6 +656,33 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   // Lloyd-Max values: rows = heads, columns = coordinates 2*lane, 2*lane+1.
   floatx4 O0 = {0.f, 0.f, 0.f, 0.f}, O1 = O0, O2 = O0, O3 = O0;
   const int vsh = (VB == 2) ? 4 * (lane & 1) : (VB == 3) ? ((6 * lane) & 7) : 0;
+  if constexpr (!VLM) {
+    if (own_new && wave == kMaxGroup) {
+      float nt_c0, nt_c1, nt_nhat, nt_rho, nt_s0, nt_s1;
+      uint8_t* page = const_cast<uint8_t*>(a.cache) + (int64_t)new_blk * blk_stride + kvh * head_stride;
+      new_token_quantize<KB, QJL, VB>(a, nt_k0, nt_k1, nt_v0, nt_v1, lane, page, (seq_len - 1) & 15, nt_codes,
+                                      nt_vhat, nt_r, nt_c0, nt_c1, nt_nhat, nt_rho, nt_s0, nt_s1);
+      // the new token's base-2 logit for each head, then the wave's softmax state
+      // starts from it (weight 1 at its own max)
+      float ell[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        ell[h] = wave_sum(fmaf(qf[h][2 * lane], nt_c0, qf[h][2 * lane + 1] * nt_c1)) * nt_nhat;
+        if constexpr (QJL) ell[h] = fmaf(wave_sum(fmaf(pf[h][2 * lane], nt_s0, pf[h][2 * lane + 1] * nt_s1)), nt_rho, ell[h]);
+      }
+      const float my = grp == 0 ? ell[0] : grp == 1 ? ell[1] : grp == 2 ? ell[2] : ell[3];
+      if (grp < G) {
+        m_run = my;
+        l_lane = j16 == 0 ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) O[m] = nt_vhat[8 * j16 + m];
+      }
+      if (a.logits != nullptr && lane < G) {
+        const float mine = lane == 0 ? ell[0] : lane == 1 ? ell[1] : lane == 2 ? ell[2] : ell[3];
+        a.logits[((int64_t)b * a.hq + (int64_t)kvh * G + lane) * a.max_seq + seq_len - 1] = mine * kLn2;
+      }
+    }
+  }
 
   while (have) {
     // The next tile of the work-group's range for this wave (handed out in order).

@@ -402,10 +402,13 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t max_s
          (size_t)batch * ctx->cfg.num_kv_heads * splits * tq::kMaxGroup * (2 + tq::kDim) * sizeof(float);
 }
 
-tq_status tq_decode_attention(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cache, int64_t num_blocks,
-                              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
-                              int32_t batch, int32_t max_seq_len, float softmax_scale, float* out,
-                              float* logits_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+tq_status decode_common(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cache, int64_t num_blocks,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                        int32_t batch, int32_t max_seq_len, float softmax_scale, float* out, float* logits_out,
+                        void* workspace, size_t workspace_bytes, const void* k_new, const void* v_new,
+                        hipStream_t stream) {
   if (!ctx) return fail(TQ_ERR_INVALID_ARG, "ctx is null");
   if (dt != TQ_F32 && dt != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad dtype %d", (int)dt);
   if (batch < 0 || max_seq_len < 0 || max_blocks_per_seq < 0 || num_blocks < 0)
@@ -419,6 +422,12 @@ tq_status tq_decode_attention(tq_ctx* ctx, const void* q, tq_dtype dt, const voi
     return fail(TQ_ERR_INVALID_ARG, "null device pointer");
   if (!aligned(cache, 16) || !aligned(workspace, 16) || !aligned(q, 4) || !aligned(out, 4))
     return fail(TQ_ERR_INVALID_ARG, "misaligned pointer (cache/workspace need 16 bytes)");
+  if (k_new != nullptr) {
+    if (!v_new) return fail(TQ_ERR_INVALID_ARG, "v_new is null");
+    if (!aligned(k_new, 4) || !aligned(v_new, 4)) return fail(TQ_ERR_INVALID_ARG, "misaligned k_new / v_new");
+    if (ctx->cfg.val_mode == TQ_VAL_LLOYD)
+      return fail(TQ_ERR_UNSUPPORTED, "the fused append takes uniform values only");
+  }
   const size_t need = tq_decode_workspace_bytes(ctx, batch, max_seq_len);
   if (workspace_bytes < need)
     return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
@@ -436,10 +445,33 @@ tq_status tq_decode_attention(tq_ctx* ctx, const void* q, tq_dtype dt, const voi
   if ((int64_t)(a.splits + 1) * a.tiles_total >= ((int64_t)1 << 31))
     return fail(TQ_ERR_UNSUPPORTED, "max_seq_len too large");
   a.f = offsets_of(ctx->layout); a.c = ctx->consts;
+  a.k_new = k_new; a.v_new = v_new;
+  a.key_nc = ctx->cfg.key_mode == TQ_KEY_LLOYD_NC;
+  a.klut_scale = ctx->klut_scale; a.klut_bias = ctx->klut_bias;
   hipError_t e = tq::launch_decode(a, (int)ctx->cfg.key_bits, (int)ctx->cfg.key_mode, (int)ctx->cfg.val_bits,
                                    (int)ctx->cfg.val_mode, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return TQ_OK;
+}
+
+}  // namespace
+
+tq_status tq_decode_attention(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cache, int64_t num_blocks,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                              int32_t batch, int32_t max_seq_len, float softmax_scale, float* out,
+                              float* logits_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_common(ctx, q, dt, cache, num_blocks, block_tables, max_blocks_per_seq, seq_lens, batch, max_seq_len,
+                       softmax_scale, out, logits_out, workspace, workspace_bytes, nullptr, nullptr, stream);
+}
+
+tq_status tq_append_decode(tq_ctx* ctx, const void* k_new, const void* v_new, const void* q, tq_dtype dt,
+                           void* cache, int64_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float softmax_scale,
+                           float* out, float* logits_out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  if (!k_new) return fail(TQ_ERR_INVALID_ARG, "k_new is null");
+  return decode_common(ctx, q, dt, cache, num_blocks, block_tables, max_blocks_per_seq, seq_lens, batch, max_seq_len,
+                       softmax_scale, out, logits_out, workspace, workspace_bytes, k_new, v_new, stream);
 }
 
 tq_status tq_dequantize(tq_ctx* ctx, const void* cache, int64_t num_blocks, const int64_t* slots, int64_t n,

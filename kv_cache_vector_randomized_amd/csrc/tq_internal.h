@@ -95,6 +95,12 @@ struct DecodeArgs {
   int32_t tiles_total;        // 64-token tiles of the longest sequence, split evenly
   FieldOffsets f;
   const DevConsts* c;
+  // Fused append: the new token of sequence b ([batch][hkv][128], dtype q_dtype) is
+  // position seq_lens[b] - 1; null for a plain decode.
+  const void* k_new;
+  const void* v_new;
+  int32_t key_nc;             // 1: corrected key norm
+  float klut_scale, klut_bias;
 };
 
 

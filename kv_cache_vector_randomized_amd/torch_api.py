@@ -60,6 +60,26 @@ class PagedKVCache:
                                   ws.numel(), logits_out=logits, stream=stream)
         return out
 
+    def append_decode(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, block_tables: torch.Tensor,
+                      seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float,
+                      out: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+        """Store the new token k_new, v_new [B, Hkv, d] of every sequence at position
+        seq_lens[b] - 1, then attend q [B, Hq, d] over the context including it."""
+        assert q.is_contiguous() and k_new.is_contiguous() and v_new.is_contiguous()
+        assert k_new.dtype == q.dtype and v_new.dtype == q.dtype and k_new.shape == v_new.shape
+        assert k_new.shape[0] == q.shape[0]
+        assert block_tables.dtype == torch.int32 and seq_lens.dtype == torch.int32
+        assert block_tables.is_contiguous() and seq_lens.is_contiguous()
+        B = q.shape[0]
+        if out is None:
+            out = torch.empty((B, q.shape[1], q.shape[2]), dtype=torch.float32, device=q.device)
+        ws = self.workspace(B, max_seq_len)
+        self.ctx.append_decode(k_new, v_new, q, _dtype_code(q), self.data, self.num_blocks, block_tables,
+                               block_tables.shape[1], seq_lens, B, max_seq_len, softmax_scale, out, ws, ws.numel(),
+                               logits_out=logits, stream=stream)
+        return out
+
     def dequantize(self, slots: torch.Tensor, stream=None):
         """Reconstruct (k_hat, v_hat) [n, Hkv, d] fp32 for int64 slots [n]."""
         n = slots.shape[0]

@@ -28,7 +28,8 @@ VAL_MODES = {"uniform": 0, "lloyd": 1}
 # Every entry point declared in include/tq.h.
 EXPORTS = ("tq_abi_version", "tq_validate_config", "tq_layout_for_config", "tq_codebook", "tq_create",
            "tq_destroy", "tq_layout_query", "tq_quantize_append", "tq_decode_workspace_bytes",
-           "tq_decode_attention", "tq_dequantize", "tq_status_string", "tq_last_error_message")
+           "tq_decode_attention", "tq_append_decode", "tq_dequantize", "tq_status_string",
+           "tq_last_error_message")
 
 
 class TQError(RuntimeError):
@@ -74,6 +75,8 @@ def library() -> ctypes.CDLL:
         "tq_quantize_append": (ctypes.c_int, [P, P, P, ctypes.c_int, I64, P, P, I64, P]),
         "tq_decode_workspace_bytes": (SZ, [P, I32, I32]),
         "tq_decode_attention": (ctypes.c_int, [P, P, ctypes.c_int, P, I64, P, I32, P, I32, I32, F32, P, P, P, SZ, P]),
+        "tq_append_decode": (ctypes.c_int, [P, P, P, P, ctypes.c_int, P, I64, P, I32, P, I32, I32, F32, P, P, P,
+                                            SZ, P]),
         "tq_dequantize": (ctypes.c_int, [P, P, I64, P, I64, P, P, P]),
         "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tq_last_error_message": (ctypes.c_char_p, []),
@@ -188,6 +191,15 @@ class Context:
                                              max_blocks_per_seq, _ptr(seq_lens), batch, max_seq_len,
                                              float(softmax_scale), _ptr(out), _ptr(logits_out), _ptr(workspace),
                                              workspace_bytes, _stream(stream)))
+
+    def append_decode(self, k_new, v_new, q, dtype: int, cache, num_blocks: int, block_tables,
+                      max_blocks_per_seq: int, seq_lens, batch: int, max_seq_len: int, softmax_scale: float, out,
+                      workspace, workspace_bytes: int, logits_out=None, stream=None):
+        """tq_append_decode (asynchronous on `stream`)."""
+        _check(library().tq_append_decode(self._h, _ptr(k_new), _ptr(v_new), _ptr(q), dtype, _ptr(cache), num_blocks,
+                                          _ptr(block_tables), max_blocks_per_seq, _ptr(seq_lens), batch,
+                                          max_seq_len, float(softmax_scale), _ptr(out), _ptr(logits_out),
+                                          _ptr(workspace), workspace_bytes, _stream(stream)))
 
     def dequantize(self, cache, num_blocks: int, slots, n: int, k_out, v_out, stream=None):
         """tq_dequantize (asynchronous on `stream`)."""

@@ -1,0 +1,150 @@
+"""GPU parity of the fused one-launch decode step (tq_append_decode): the new token
+of every sequence is quantized into its slot, then attended together with the
+stored context.
+
+* the new tokens' fields against the oracle's quantization of them (codes
+  bit-exact outside the 1e-6 band, scalars to their rounding tolerance);
+* logits and outputs against the oracle attending over the cache bytes the GPU
+  wrote (1e-4 relative per (sequence, q head) vector);
+* the bytes of every other slot are untouched, and a sequence of length 0 takes
+  no new token.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from kv_cache_vector_randomized_amd import synth
+from oracle import tq_oracle as O
+from tests import gpu_helpers as H
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+# workload -> sequence lengths after the step (ragged; 1 = only the new token; 0 = none)
+CASES = {
+    "gqa_decode": [1000, 17, 0, 129, 1, 64, 65],
+    "long_3bit": [777, 64, 5],
+    "qjl": [513, 100, 16],
+    "prefill_append": [300],
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_append_decode_matches_oracle(name):
+    from kv_cache_vector_randomized_amd.torch_api import PagedKVCache
+    w = synth.WORKLOADS[name]
+    print(f"[append_decode] {name}", flush=True)
+    lens = np.asarray(CASES[name], np.int64)
+    B = len(lens)
+    cfg = H.oracle_config(w)
+    lay = synth.paged_layout(B, lens, 41)
+    k = synth.kv_tensor(w, int(lens.sum()), "k", 41)
+    v = synth.kv_tensor(w, int(lens.sum()), "v", 41)
+    q = synth.query_tensor(w, B, 41)
+    start = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    # stored context: every position but the last of each sequence
+    ctx_rows = np.concatenate([start[b] + np.arange(max(int(lens[b]) - 1, 0)) for b in range(B)]).astype(np.int64)
+    ctx_slots = np.concatenate([lay.slots(b, 0, max(int(lens[b]) - 1, 0)) for b in range(B)])
+    cache_np = np.full((lay.num_blocks, cfg.num_kv_heads, O.page_bytes(cfg)), 0xA5, np.uint8)
+    if len(ctx_rows):
+        O.write_tokens(cfg, cache_np, ctx_slots, H.oracle_quantize(w, k[ctx_rows], v[ctx_rows]))
+    # new tokens: the last position of each sequence (zeros for an empty one)
+    has_new = lens > 0
+    new_rows = np.where(has_new, start + lens - 1, 0)
+    k_new = k[new_rows].copy()
+    v_new = v[new_rows].copy()
+    k_new[~has_new] = 0
+    v_new[~has_new] = 0
+    new_slots = np.array([lay.slots(b, int(lens[b]) - 1, int(lens[b]))[0] if has_new[b] else -1 for b in range(B)])
+
+    ctx = H.make_context(w)
+    cache = PagedKVCache(ctx, lay.num_blocks)
+    cache.data.copy_(torch.from_numpy(cache_np))
+    max_seq = int(max(lens.max(), 1))
+    logits = torch.full((B, w.num_q_heads, max_seq), float("nan"), device="cuda")
+    out = cache.append_decode(H.upload(k_new, w, torch), H.upload(v_new, w, torch), H.upload(q, w, torch),
+                              torch.from_numpy(lay.block_tables).cuda(), torch.from_numpy(lay.seq_lens).cuda(),
+                              max_seq, 1.0 / math.sqrt(w.head_dim), logits=logits)
+    torch.cuda.synchronize()
+    got = cache.data.cpu().numpy()
+    out = out.cpu().numpy().astype(np.float64)
+    logits = logits.cpu().numpy().astype(np.float64)
+
+    # only the new slots changed
+    changed = got != cache_np
+    allowed = H.written_mask(cfg, got.shape, new_slots[has_new])
+    assert not np.any(changed & ~allowed), "bytes outside the new tokens' rows changed"
+    # the new tokens' fields
+    report = {}
+    if has_new.any():
+        qz = H.oracle_quantize(w, k_new[has_new], v_new[has_new])
+        H.compare_append(w, got, new_slots[has_new], qz, report)
+    print(f"  new tokens: {report}")
+    # attention over the GPU-written bytes
+    ref_logits, ref_out = H.oracle_decode(w, q, got, lay)
+    worst = 0.0
+    for b in range(B):
+        for h in range(w.num_q_heads):
+            if lens[b] == 0:
+                assert np.all(out[b, h] == 0)
+                continue
+            el = H.rel_err(logits[b, h, :lens[b]], ref_logits[(b, h)])
+            eo = H.rel_err(out[b, h], ref_out[b, h])
+            worst = max(worst, el, eo)
+            assert el <= H.REL_TOL and eo <= H.REL_TOL, (b, h, el, eo)
+    print(f"  worst relative error {worst:.3e}")
+
+
+def test_append_decode_equals_two_launches():
+    """The fused step and tq_quantize_append + tq_decode_attention agree (same
+    shapes, same bytes of context)."""
+    from kv_cache_vector_randomized_amd.torch_api import PagedKVCache
+    w = synth.WORKLOADS["gqa_decode"]
+    lens = np.array([300, 45, 1], np.int64)
+    B = len(lens)
+    lay = synth.paged_layout(B, lens, 43)
+    total = int(lens.sum())
+    k = synth.kv_tensor(w, total, "k", 43)
+    v = synth.kv_tensor(w, total, "v", 43)
+    q = synth.query_tensor(w, B, 43)
+    start = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    ctx_rows = np.concatenate([start[b] + np.arange(int(lens[b]) - 1) for b in range(B)]).astype(np.int64)
+    ctx_slots = np.concatenate([lay.slots(b, 0, int(lens[b]) - 1) for b in range(B)])
+    new_rows = start + lens - 1
+    new_slots = np.array([lay.slots(b, int(lens[b]) - 1, int(lens[b]))[0] for b in range(B)])
+    ctx = H.make_context(w)
+    tables = torch.from_numpy(lay.block_tables).cuda()
+    seq = torch.from_numpy(lay.seq_lens).cuda()
+    scale = 1.0 / math.sqrt(w.head_dim)
+    outs = []
+    for fused in (True, False):
+        cache = PagedKVCache(ctx, lay.num_blocks, fill=0)
+        cache.append(H.upload(k[ctx_rows], w, torch), H.upload(v[ctx_rows], w, torch),
+                     torch.from_numpy(ctx_slots).cuda())
+        kn, vn, qd = H.upload(k[new_rows], w, torch), H.upload(v[new_rows], w, torch), H.upload(q, w, torch)
+        if fused:
+            out = cache.append_decode(kn, vn, qd, tables, seq, int(lens.max()), scale)
+        else:
+            cache.append(kn, vn, torch.from_numpy(new_slots).cuda())
+            out = cache.decode(qd, tables, seq, int(lens.max()), scale)
+        torch.cuda.synchronize()
+        outs.append((out.cpu().numpy().astype(np.float64), cache.data.cpu().numpy()))
+    (o1, c1), (o2, c2) = outs
+    cfg = H.oracle_config(w)
+    for h in range(cfg.num_kv_heads):
+        a = O.read_tokens(cfg, c1, new_slots, h)
+        r = O.read_tokens(cfg, c2, new_slots, h)
+        # codes agree up to the decision band; scalars up to rounding
+        assert np.mean(a["kcodes"] == r["kcodes"]) > 0.999
+        assert np.mean(a["vcodes"] == r["vcodes"]) > 0.999
+    worst = max(H.rel_err(o1[b, hq], o2[b, hq]) for b in range(B) for hq in range(w.num_q_heads))
+    assert worst <= H.REL_TOL, worst
+    print(f"  fused vs two launches: worst relative difference {worst:.2e}")
