@@ -15,7 +15,9 @@ Other workloads (--workload):
   qjl             batch 8 x context 16384, 2-bit keys + 1-bit QJL residual signs,
                   same step;
   prefill_append  quantize-append of 131072 tokens x 8 KV heads into 16-token
-                  pages, then decode at batch 1 over the 131072-token context.
+                  pages, then decode at batch 1 over the 131072-token context;
+  qjl_build       the qjl workload's whole cache (8 x 16384 tokens x 8 KV heads)
+                  quantized and appended in one step, then its decode.
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.  `value` is packed-KV
 GB/s: algorithmic bytes of the step (bf16 inputs read, packed rows written,
@@ -46,6 +48,7 @@ MODES = {
     "long_3bit": ("long_3bit", "decode"),
     "qjl": ("qjl", "decode"),
     "prefill_append": ("prefill_append", "append"),
+    "qjl_build": ("qjl", "append"),
 }
 
 
@@ -207,7 +210,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, k_all, v_all, q_np, lay, np)
+        cpu = cpu_baseline(w, kind, k_all, v_all, q_np, lay, np)
 
     rec = {
         "metric": "packed-KV GB/s (% HBM peak) for quantize-append and decode attention",
@@ -250,10 +253,10 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(w, k_all, v_all, q_np, lay, np):
+def cpu_baseline(w, kind, k_all, v_all, q_np, lay, np):
     """The fp64 oracle (untuned) on a bounded sample of the same step: one sequence's
     new-token quantize-append plus its decode attention over its context (for the
-    prefill workload: the quantize-append of 2048 of its tokens)."""
+    append workloads: the quantize-append of 2048 of the step's tokens)."""
     from oracle import tq_oracle as O
     from kv_cache_vector_randomized_amd import synth
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
@@ -267,7 +270,7 @@ def cpu_baseline(w, k_all, v_all, q_np, lay, np):
     b = 0
     slots = lay.slots(b, 0, T)
     cache = O.new_cache(cfg, lay.num_blocks)
-    if w.name == "prefill_append":
+    if kind == "append":
         n = 2048
         times = []
         for _ in range(3):
