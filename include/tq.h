@@ -212,6 +212,26 @@ tq_status tq_append_decode(tq_ctx* ctx, const void* k_new, const void* v_new, co
                            float* out, float* logits_out, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* Copy whole blocks between the cache and host memory, bytes unchanged (qiita
+ * LMCache article: the transfer side moves the packed slots without
+ * interpreting them, and a save/restore round trip must reproduce the bytes and
+ * leave other regions untouched).  A block is the num_kv_heads pages of one
+ * block id: num_kv_heads * page_bytes contiguous bytes (tq_layout describes the
+ * format, TQ_FORMAT_VERSION its version).
+ *   block_ids: device int32 [n]; ids outside [0, num_blocks) are skipped (their
+ *              host range is left as it was).
+ *   host_dst / host_src: host memory pinned and mapped for the device (e.g.
+ *              hipHostMalloc), 16-byte aligned, n * num_kv_heads * page_bytes
+ *              bytes: block block_ids[i] <-> bytes [i * block_bytes, (i+1) *
+ *              block_bytes).  The GPU reads or writes it directly over the host
+ *              link; the caller synchronizes the stream before touching it.
+ *   cache:     offload reads it; restore writes only the listed blocks.
+ * Two ids equal in one restore race (the caller must not do that). */
+tq_status tq_offload_blocks(tq_ctx* ctx, const void* cache, int64_t num_blocks, const int32_t* block_ids, int64_t n,
+                            void* host_dst, hipStream_t stream);
+tq_status tq_restore_blocks(tq_ctx* ctx, const void* host_src, const int32_t* block_ids, int64_t n, void* cache,
+                            int64_t num_blocks, hipStream_t stream);
+
 /* Reconstruct stored tokens in the original basis (stage 1 only for QJL keys):
  *   k_hat = norm * R^T C[code];  v_hat = min + scale * code  (or as keys).
  *   slots: device int64 [n]; k_out, v_out: device fp32 [n][num_kv_heads][head_dim].

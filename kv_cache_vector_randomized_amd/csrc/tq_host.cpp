@@ -474,6 +474,44 @@ tq_status tq_append_decode(tq_ctx* ctx, const void* k_new, const void* v_new, co
                        softmax_scale, out, logits_out, workspace, workspace_bytes, k_new, v_new, stream);
 }
 
+namespace {
+
+tq_status transfer(tq_ctx* ctx, bool to_host, void* cache, int64_t num_blocks, const int32_t* block_ids, int64_t n,
+                   void* host, hipStream_t stream) {
+  if (!ctx) return fail(TQ_ERR_INVALID_ARG, "ctx is null");
+  if (n < 0 || num_blocks < 0) return fail(TQ_ERR_INVALID_ARG, "negative size");
+  if (n == 0) return TQ_OK;
+  if (!cache || !block_ids || !host) return fail(TQ_ERR_INVALID_ARG, "null pointer");
+  if (!aligned(cache, 16) || !aligned(host, 16) || !aligned(block_ids, 4))
+    return fail(TQ_ERR_INVALID_ARG, "cache and host buffer must be 16-byte aligned");
+  const int64_t block_bytes = (int64_t)ctx->layout.page_bytes * ctx->cfg.num_kv_heads;
+  if (n > ((int64_t)1 << 40) / block_bytes) return fail(TQ_ERR_UNSUPPORTED, "n too large");
+  DeviceGuard g(ctx->device);
+  // The kernel touches the host buffer through its device mapping: refuse memory
+  // that is not pinned host memory mapped for the device.
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, host) != hipSuccess || attr.type != hipMemoryTypeHost ||
+      attr.devicePointer == nullptr) {
+    (void)hipGetLastError();
+    return fail(TQ_ERR_INVALID_ARG, "host buffer is not pinned host memory mapped for the device");
+  }
+  hipError_t e = tq::launch_transfer(to_host, cache, attr.devicePointer, block_ids, n, num_blocks, block_bytes,
+                                     ctx->decode_wgs * 4, stream);
+  return e == hipSuccess ? TQ_OK : hip_fail(e, "transfer launch");
+}
+
+}  // namespace
+
+tq_status tq_offload_blocks(tq_ctx* ctx, const void* cache, int64_t num_blocks, const int32_t* block_ids, int64_t n,
+                            void* host_dst, hipStream_t stream) {
+  return transfer(ctx, true, const_cast<void*>(cache), num_blocks, block_ids, n, host_dst, stream);
+}
+
+tq_status tq_restore_blocks(tq_ctx* ctx, const void* host_src, const int32_t* block_ids, int64_t n, void* cache,
+                            int64_t num_blocks, hipStream_t stream) {
+  return transfer(ctx, false, cache, num_blocks, block_ids, n, const_cast<void*>(host_src), stream);
+}
+
 tq_status tq_dequantize(tq_ctx* ctx, const void* cache, int64_t num_blocks, const int64_t* slots, int64_t n,
                         float* k_out, float* v_out, hipStream_t stream) {
   if (!ctx) return fail(TQ_ERR_INVALID_ARG, "ctx is null");

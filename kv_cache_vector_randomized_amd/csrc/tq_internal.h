@@ -125,6 +125,8 @@ const void* decode_kernel_ptr(int key_bits, int key_mode, int val_bits, int val_
 const void* append_page_kernel_ptr(int key_bits, int val_bits, bool qjl);
 hipError_t launch_decode(const DecodeArgs& a, int key_bits, int key_mode, int val_bits, int val_mode,
                          hipStream_t s);
+hipError_t launch_transfer(bool to_host, void* cache, void* host, const int32_t* block_ids, int64_t n,
+                           int64_t num_blocks, int64_t block_bytes, int grid, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, int key_bits, int key_mode, int val_bits, int val_mode,
                           hipStream_t s);
 

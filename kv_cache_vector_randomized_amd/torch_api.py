@@ -80,6 +80,23 @@ class PagedKVCache:
                                logits_out=logits, stream=stream)
         return out
 
+    @property
+    def block_bytes(self) -> int:
+        return self.ctx.cfg.num_kv_heads * self.ctx.page_bytes
+
+    def offload_blocks(self, block_ids: torch.Tensor, host: torch.Tensor, stream=None) -> None:
+        """Copy blocks block_ids (device int32 [n]) into pinned host memory `host`
+        (uint8, at least n * block_bytes): block i of the list at [i*block_bytes, ...)."""
+        assert block_ids.dtype == torch.int32 and block_ids.is_contiguous() and block_ids.is_cuda
+        assert host.is_pinned() and host.dtype == torch.uint8 and host.numel() >= block_ids.numel() * self.block_bytes
+        self.ctx.offload_blocks(self.data, self.num_blocks, block_ids, block_ids.numel(), host, stream)
+
+    def restore_blocks(self, host: torch.Tensor, block_ids: torch.Tensor, stream=None) -> None:
+        """Copy the blocks saved in pinned host memory `host` back to block_ids."""
+        assert block_ids.dtype == torch.int32 and block_ids.is_contiguous() and block_ids.is_cuda
+        assert host.is_pinned() and host.dtype == torch.uint8 and host.numel() >= block_ids.numel() * self.block_bytes
+        self.ctx.restore_blocks(host, block_ids, block_ids.numel(), self.data, self.num_blocks, stream)
+
     def dequantize(self, slots: torch.Tensor, stream=None):
         """Reconstruct (k_hat, v_hat) [n, Hkv, d] fp32 for int64 slots [n]."""
         n = slots.shape[0]

@@ -28,8 +28,8 @@ VAL_MODES = {"uniform": 0, "lloyd": 1}
 # Every entry point declared in include/tq.h.
 EXPORTS = ("tq_abi_version", "tq_validate_config", "tq_layout_for_config", "tq_codebook", "tq_create",
            "tq_destroy", "tq_layout_query", "tq_quantize_append", "tq_decode_workspace_bytes",
-           "tq_decode_attention", "tq_append_decode", "tq_dequantize", "tq_status_string",
-           "tq_last_error_message")
+           "tq_decode_attention", "tq_append_decode", "tq_offload_blocks", "tq_restore_blocks", "tq_dequantize",
+           "tq_status_string", "tq_last_error_message")
 
 
 class TQError(RuntimeError):
@@ -77,6 +77,8 @@ def library() -> ctypes.CDLL:
         "tq_decode_attention": (ctypes.c_int, [P, P, ctypes.c_int, P, I64, P, I32, P, I32, I32, F32, P, P, P, SZ, P]),
         "tq_append_decode": (ctypes.c_int, [P, P, P, P, ctypes.c_int, P, I64, P, I32, P, I32, I32, F32, P, P, P,
                                             SZ, P]),
+        "tq_offload_blocks": (ctypes.c_int, [P, P, I64, P, I64, P, P]),
+        "tq_restore_blocks": (ctypes.c_int, [P, P, P, I64, P, I64, P]),
         "tq_dequantize": (ctypes.c_int, [P, P, I64, P, I64, P, P, P]),
         "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tq_last_error_message": (ctypes.c_char_p, []),
@@ -200,6 +202,16 @@ class Context:
                                           _ptr(block_tables), max_blocks_per_seq, _ptr(seq_lens), batch,
                                           max_seq_len, float(softmax_scale), _ptr(out), _ptr(logits_out),
                                           _ptr(workspace), workspace_bytes, _stream(stream)))
+
+    def offload_blocks(self, cache, num_blocks: int, block_ids, n: int, host_dst, stream=None):
+        """tq_offload_blocks (asynchronous on `stream`)."""
+        _check(library().tq_offload_blocks(self._h, _ptr(cache), num_blocks, _ptr(block_ids), n, _ptr(host_dst),
+                                           _stream(stream)))
+
+    def restore_blocks(self, host_src, block_ids, n: int, cache, num_blocks: int, stream=None):
+        """tq_restore_blocks (asynchronous on `stream`)."""
+        _check(library().tq_restore_blocks(self._h, _ptr(host_src), _ptr(block_ids), n, _ptr(cache), num_blocks,
+                                           _stream(stream)))
 
     def dequantize(self, cache, num_blocks: int, slots, n: int, k_out, v_out, stream=None):
         """tq_dequantize (asynchronous on `stream`)."""
