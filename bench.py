@@ -17,7 +17,11 @@ Other workloads (--workload):
   prefill_append  quantize-append of 131072 tokens x 8 KV heads into 16-token
                   pages, then decode at batch 1 over the 131072-token context;
   qjl_build       the qjl workload's whole cache (8 x 16384 tokens x 8 KV heads)
-                  quantized and appended in one step, then its decode.
+                  quantized and appended in one step, then its decode;
+  dequant_layer   the prefill_append cache (131072 tokens x 8 KV heads)
+                  reconstructed into a bf16 buffer (--dequant-f32: fp32) in one
+                  tq_dequantize_rows call: the whole-cache reconstruction that
+                  incremental dequantization replaces by one token per step.
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.  `value` is packed-KV
 GB/s: algorithmic bytes of the step (bf16 inputs read, packed rows written,
@@ -49,6 +53,7 @@ MODES = {
     "qjl": ("qjl", "decode"),
     "prefill_append": ("prefill_append", "append"),
     "qjl_build": ("qjl", "append"),
+    "dequant_layer": ("prefill_append", "dequant"),
 }
 
 
@@ -81,6 +86,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="decode workloads: append and decode as two launches instead of one")
+    ap.add_argument("--dequant-f32", action="store_true", help="dequant_layer: fp32 output instead of bf16")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -160,6 +166,26 @@ def main():
                 c.append_decode(k_new, v_new, q_dev, tables, seq_lens, T, scale, out=out)
                 if ev is not None:
                     ev[1].record(stream)
+    elif kind == "dequant":
+        for c in caches:                               # fill every layer (not timed)
+            c.append(k_dev, v_dev, slots_all)
+        torch.cuda.synchronize()
+        del k_dev, v_dev
+        odt = torch.float32 if args.dequant_f32 else torch.bfloat16
+        eb = 4 if args.dequant_f32 else 2
+        kbuf = torch.empty((B * T, Hkv, d), dtype=odt, device="cuda")
+        vbuf = torch.empty_like(kbuf)
+        append_bytes = 0
+        decode_bytes = B * T * Hkv * (th + 2 * d * eb) + B * T * 8
+        dominant, dom_bytes, dom_source = "dequant_kernel", decode_bytes, "tq_dequant.hip"
+
+        def step(i, ev=None):
+            c = caches[i % n_layers]
+            if ev is not None:
+                ev[0].record(stream)
+            c.dequantize_rows(slots_all, None, kbuf, vbuf)
+            if ev is not None:
+                ev[1].record(stream)
     else:
         append_bytes = B * T * Hkv * (2 * d * 2 + th) + B * T * 8
         dominant, dom_bytes, dom_source = "append_page_kernel", append_bytes, "tq_append.hip"
@@ -230,7 +256,8 @@ def main():
             "head_dim": d, "key_bits": w.key_bits, "key_mode": w.key_mode, "val_bits": w.val_bits,
             "val_mode": w.val_mode, "block_tokens": 16, "layer_caches": n_layers,
             "step": ("append 1 token/seq + decode" + (" (two launches)" if args.separate else " (one launch)")
-                     if kind == "decode" else "append all tokens + decode"),
+                     if kind == "decode" else "append all tokens + decode" if kind == "append" else
+                     "reconstruct every stored token into a " + ("fp32" if args.dequant_f32 else "bf16") + " buffer"),
             "step_bytes": step_bytes,
         },
         "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
@@ -270,7 +297,20 @@ def cpu_baseline(w, kind, k_all, v_all, q_np, lay, np):
     b = 0
     slots = lay.slots(b, 0, T)
     cache = O.new_cache(cfg, lay.num_blocks)
-    if kind == "append":
+    if kind == "dequant":
+        n = 8192
+        O.quantize_append(cfg, cache, f64(k_all[:n]), f64(v_all[:n]), slots[:n], signs, kcb, S=S)
+        vcb = O.codebook(w.val_bits, d) if w.val_mode == "lloyd" else None
+        times = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            for h in range(Hkv):
+                O.dequantize_slots(cfg, cache, slots[:n], h, signs, kcb, vcb)
+            times.append(time.perf_counter() - t0)
+        sec = statistics.median(times)
+        sample_bytes = n * Hkv * (th + 2 * d * 2) + n * 8
+        sample = f"reconstruction of {n} tokens x {Hkv} kv heads (bf16-sized output), median of 5 runs, {sec:.2f} s each"
+    elif kind == "append":
         n = 2048
         times = []
         for _ in range(3):

@@ -232,12 +232,29 @@ tq_status tq_offload_blocks(tq_ctx* ctx, const void* cache, int64_t num_blocks, 
 tq_status tq_restore_blocks(tq_ctx* ctx, const void* host_src, const int32_t* block_ids, int64_t n, void* cache,
                             int64_t num_blocks, hipStream_t stream);
 
-/* Reconstruct stored tokens in the original basis (stage 1 only for QJL keys):
- *   k_hat = norm * R^T C[code];  v_hat = min + scale * code  (or as keys).
- *   slots: device int64 [n]; k_out, v_out: device fp32 [n][num_kv_heads][head_dim].
- *   Slots outside [0, num_blocks*16) give zero rows. */
+/* Reconstruct stored tokens in the original basis (issoh.co.jp "TurboQuantとは？…",
+ * 第1段: the rotation is orthogonal, so its inverse is diag(s) H / sqrt(d); stage 1
+ * only for QJL keys):
+ *   k_hat = norm * R^T C[code];  v_hat = min + scale * code  (Lloyd-Max values: as keys).
+ *   slots: device int64 [n]; k_out, v_out: device fp32 [n][num_kv_heads][head_dim],
+ *   16-byte aligned.  Slots outside [0, num_blocks*16) give zero rows. */
 tq_status tq_dequantize(tq_ctx* ctx, const void* cache, int64_t num_blocks, const int64_t* slots, int64_t n,
                         float* k_out, float* v_out, hipStream_t stream);
+
+/* Incremental dequantization (turboquant-vllm write-up, "Incremental
+ * dequantization": rather than reconstructing the whole cache at every step, a
+ * step reconstructs only its new tokens and appends them to a running buffer):
+ * entry i reconstructs the token at slots[i] into row rows[i] of k_buf / v_buf.
+ *   slots:   device int64 [n]; a slot outside [0, num_blocks*16) gives a zero row.
+ *   rows:    device int64 [n], or NULL for rows[i] = i.  Rows outside
+ *            [0, buf_rows) are skipped; rows not listed are left as they were.
+ *            Two entries naming one row race (the caller must not do that).
+ *   k_buf, v_buf: device [buf_rows][num_kv_heads][head_dim] of out_dt (TQ_F32,
+ *            or TQ_BF16 rounded to nearest even), 16-byte aligned; caller-owned.
+ * tq_dequantize is this call with rows = NULL, buf_rows = n and TQ_F32. */
+tq_status tq_dequantize_rows(tq_ctx* ctx, const void* cache, int64_t num_blocks, const int64_t* slots, int64_t n,
+                             const int64_t* rows, void* k_buf, void* v_buf, int64_t buf_rows, tq_dtype out_dt,
+                             hipStream_t stream);
 
 const char* tq_status_string(tq_status s);
 const char* tq_last_error_message(void);

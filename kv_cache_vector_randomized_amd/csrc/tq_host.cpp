@@ -512,23 +512,33 @@ tq_status tq_restore_blocks(tq_ctx* ctx, const void* host_src, const int32_t* bl
   return transfer(ctx, false, cache, num_blocks, block_ids, n, const_cast<void*>(host_src), stream);
 }
 
-tq_status tq_dequantize(tq_ctx* ctx, const void* cache, int64_t num_blocks, const int64_t* slots, int64_t n,
-                        float* k_out, float* v_out, hipStream_t stream) {
+tq_status tq_dequantize_rows(tq_ctx* ctx, const void* cache, int64_t num_blocks, const int64_t* slots, int64_t n,
+                             const int64_t* rows, void* k_buf, void* v_buf, int64_t buf_rows, tq_dtype out_dt,
+                             hipStream_t stream) {
   if (!ctx) return fail(TQ_ERR_INVALID_ARG, "ctx is null");
-  if (n < 0 || num_blocks < 0) return fail(TQ_ERR_INVALID_ARG, "negative size");
-  if (n == 0) return TQ_OK;
-  if (!cache || !slots || !k_out || !v_out) return fail(TQ_ERR_INVALID_ARG, "null device pointer");
-  if (!aligned(cache, 16) || !aligned(k_out, 16) || !aligned(v_out, 16))
-    return fail(TQ_ERR_INVALID_ARG, "cache and outputs must be 16-byte aligned");
+  if (n < 0 || num_blocks < 0 || buf_rows < 0) return fail(TQ_ERR_INVALID_ARG, "negative size");
+  if (out_dt != TQ_F32 && out_dt != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "output dtype must be TQ_F32 or TQ_BF16");
+  if (n == 0 || buf_rows == 0) return TQ_OK;
+  if (!cache || !slots || !k_buf || !v_buf) return fail(TQ_ERR_INVALID_ARG, "null device pointer");
+  if (!aligned(cache, 16) || !aligned(k_buf, 16) || !aligned(v_buf, 16) || !aligned(slots, 8) ||
+      (rows && !aligned(rows, 8)))
+    return fail(TQ_ERR_INVALID_ARG, "cache and buffers must be 16-byte aligned, slots and rows 8-byte aligned");
+  if ((n + 15) / 16 * (int64_t)ctx->cfg.num_kv_heads >= (int64_t(1) << 32))
+    return fail(TQ_ERR_INVALID_ARG, "n too large for one launch (below 2^36 / num_kv_heads entries)");
   DeviceGuard g(ctx->device);
   tq::DequantArgs a;
   for (int i = 0; i < 4; ++i) a.sign_bits[i] = ctx->sign_bits[i];
-  a.cache = (const uint8_t*)cache; a.num_blocks = num_blocks; a.slots = slots; a.n = n;
-  a.hkv = (int32_t)ctx->cfg.num_kv_heads; a.k_out = k_out; a.v_out = v_out;
+  a.cache = (const uint8_t*)cache; a.num_blocks = num_blocks; a.slots = slots; a.rows = rows; a.n = n;
+  a.buf_rows = buf_rows; a.hkv = (int32_t)ctx->cfg.num_kv_heads; a.k_out = k_buf; a.v_out = v_buf;
   a.f = offsets_of(ctx->layout); a.c = ctx->consts;
-  hipError_t e = tq::launch_dequant(a, (int)ctx->cfg.key_bits, (int)ctx->cfg.key_mode, (int)ctx->cfg.val_bits,
-                                    (int)ctx->cfg.val_mode, stream);
+  hipError_t e = tq::launch_dequant(a, (int)ctx->cfg.key_bits, (int)ctx->cfg.val_bits, (int)ctx->cfg.val_mode,
+                                    out_dt == TQ_BF16, stream);
   return e == hipSuccess ? TQ_OK : hip_fail(e, "dequantize launch");
+}
+
+tq_status tq_dequantize(tq_ctx* ctx, const void* cache, int64_t num_blocks, const int64_t* slots, int64_t n,
+                        float* k_out, float* v_out, hipStream_t stream) {
+  return tq_dequantize_rows(ctx, cache, num_blocks, slots, n, nullptr, k_out, v_out, n, TQ_F32, stream);
 }
 
 }  // extern "C"

@@ -109,10 +109,12 @@ struct DequantArgs {
   const uint8_t* cache;
   int64_t num_blocks;
   const int64_t* slots;
+  const int64_t* rows;   // output row of entry i (nullptr: row i)
   int64_t n;
+  int64_t buf_rows;      // rows of k_out / v_out; other rows are skipped
   int32_t hkv;
-  float* k_out;
-  float* v_out;
+  void* k_out;           // fp32 or bf16 [buf_rows][hkv][kDim]
+  void* v_out;
   FieldOffsets f;
   const DevConsts* c;
 };
@@ -127,7 +129,7 @@ hipError_t launch_decode(const DecodeArgs& a, int key_bits, int key_mode, int va
                          hipStream_t s);
 hipError_t launch_transfer(bool to_host, void* cache, void* host, const int32_t* block_ids, int64_t n,
                            int64_t num_blocks, int64_t block_bytes, int grid, hipStream_t s);
-hipError_t launch_dequant(const DequantArgs& a, int key_bits, int key_mode, int val_bits, int val_mode,
+hipError_t launch_dequant(const DequantArgs& a, int key_bits, int val_bits, int val_mode, bool bf16_out,
                           hipStream_t s);
 
 }  // namespace tq

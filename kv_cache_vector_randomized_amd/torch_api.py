@@ -106,6 +106,18 @@ class PagedKVCache:
         self.ctx.dequantize(self.data, self.num_blocks, slots, n, k, v, stream)
         return k, v
 
+    def dequantize_rows(self, slots: torch.Tensor, rows: Optional[torch.Tensor], k_buf: torch.Tensor,
+                        v_buf: torch.Tensor, stream=None) -> None:
+        """Reconstruct the tokens at int64 `slots` [n] into rows `rows` [n] (None: row i) of
+        the running buffers k_buf, v_buf [rows, Hkv, d] (fp32 or bf16)."""
+        assert slots.dtype == torch.int64 and slots.is_contiguous() and slots.is_cuda
+        assert rows is None or (rows.dtype == torch.int64 and rows.is_contiguous() and rows.numel() == slots.numel())
+        shape = (self.ctx.cfg.num_kv_heads, self.ctx.cfg.head_dim)
+        assert k_buf.shape[1:] == shape and v_buf.shape == k_buf.shape and k_buf.dtype == v_buf.dtype
+        assert k_buf.is_contiguous() and v_buf.is_contiguous()
+        self.ctx.dequantize_rows(self.data, self.num_blocks, slots, slots.numel(), rows, k_buf, v_buf,
+                                 k_buf.shape[0], _dtype_code(k_buf), stream)
+
 
 def bf16_from_bits(bits: np.ndarray, device="cuda") -> torch.Tensor:
     """Upload bf16 bit patterns (uint16) as a torch.bfloat16 tensor."""

@@ -29,7 +29,7 @@ VAL_MODES = {"uniform": 0, "lloyd": 1}
 EXPORTS = ("tq_abi_version", "tq_validate_config", "tq_layout_for_config", "tq_codebook", "tq_create",
            "tq_destroy", "tq_layout_query", "tq_quantize_append", "tq_decode_workspace_bytes",
            "tq_decode_attention", "tq_append_decode", "tq_offload_blocks", "tq_restore_blocks", "tq_dequantize",
-           "tq_status_string", "tq_last_error_message")
+           "tq_dequantize_rows", "tq_status_string", "tq_last_error_message")
 
 
 class TQError(RuntimeError):
@@ -80,6 +80,7 @@ def library() -> ctypes.CDLL:
         "tq_offload_blocks": (ctypes.c_int, [P, P, I64, P, I64, P, P]),
         "tq_restore_blocks": (ctypes.c_int, [P, P, P, I64, P, I64, P]),
         "tq_dequantize": (ctypes.c_int, [P, P, I64, P, I64, P, P, P]),
+        "tq_dequantize_rows": (ctypes.c_int, [P, P, I64, P, I64, P, P, P, I64, ctypes.c_int, P]),
         "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tq_last_error_message": (ctypes.c_char_p, []),
     }
@@ -217,3 +218,9 @@ class Context:
         """tq_dequantize (asynchronous on `stream`)."""
         _check(library().tq_dequantize(self._h, _ptr(cache), num_blocks, _ptr(slots), n, _ptr(k_out), _ptr(v_out),
                                        _stream(stream)))
+
+    def dequantize_rows(self, cache, num_blocks: int, slots, n: int, rows, k_buf, v_buf, buf_rows: int, out_dtype: int,
+                        stream=None):
+        """tq_dequantize_rows (asynchronous on `stream`); rows may be None (row i)."""
+        _check(library().tq_dequantize_rows(self._h, _ptr(cache), num_blocks, _ptr(slots), n, _ptr(rows),
+                                            _ptr(k_buf), _ptr(v_buf), buf_rows, out_dtype, _stream(stream)))

@@ -62,6 +62,23 @@ def test_null_config_and_context():
     assert b"ctx" in lib.tq_last_error_message() or lib.tq_last_error_message()
 
 
+def test_every_call_refuses_a_null_context():
+    """Argument errors come back synchronously as TQ_ERR_INVALID_ARG (no GPU is touched)."""
+    lib = tq.library()
+    calls = {
+        "tq_decode_attention": (None, None, 1, None, 1, None, 1, None, 1, 1, 1.0, None, None, None, 0, None),
+        "tq_append_decode": (None, None, None, None, 1, None, 1, None, 1, None, 1, 1, 1.0, None, None, None, 0, None),
+        "tq_offload_blocks": (None, None, 1, None, 1, None, None),
+        "tq_restore_blocks": (None, None, None, 1, None, 1, None),
+        "tq_dequantize": (None, None, 1, None, 1, None, None, None),
+        "tq_dequantize_rows": (None, None, 1, None, 1, None, None, None, 1, tq.TQ_BF16, None),
+        "tq_layout_query": (None, None),
+    }
+    for name, args in calls.items():
+        assert getattr(lib, name)(*args) == tq.TQ_ERR_INVALID_ARG, name
+        assert b"null" in lib.tq_last_error_message(), name
+
+
 @pytest.mark.parametrize("kb,km,vb,vm", [(4, "lloyd", 4, "lloyd"), (4, "lloyd_nc", 4, "uniform"),
                                          (3, "lloyd_nc", 3, "uniform"), (2, "lloyd_qjl", 4, "uniform"),
                                          (2, "lloyd", 2, "uniform"), (3, "lloyd_qjl", 3, "lloyd")])
