@@ -18,6 +18,10 @@ Other workloads (--workload):
                   pages, then decode at batch 1 over the 131072-token context;
   qjl_build       the qjl workload's whole cache (8 x 16384 tokens x 8 KV heads)
                   quantized and appended in one step, then its decode;
+  k3v4_nc         the GQA shape with 3-bit corrected keys and 4-bit values (an
+                  asymmetric serving preset), same step;
+  k3qjl_v2        batch 8 x context 16384, 3-bit keys + 1-bit QJL residual signs,
+                  2-bit values (a second asymmetric preset), same step;
   dequant_layer   the prefill_append cache (131072 tokens x 8 KV heads)
                   reconstructed into a bf16 buffer (--dequant-f32: fp32) in one
                   tq_dequantize_rows call: the whole-cache reconstruction that
@@ -54,6 +58,8 @@ MODES = {
     "prefill_append": ("prefill_append", "append"),
     "qjl_build": ("qjl", "append"),
     "dequant_layer": ("prefill_append", "dequant"),
+    "k3v4_nc": ("k3v4_nc", "decode"),
+    "k3qjl_v2": ("k3qjl_v2", "decode"),
 }
 
 

@@ -52,7 +52,7 @@ class Workload:
     seed: int
 
 
-# The five workloads.  Sizes are the full ones; tests shrink batch/context with
+# The workloads.  Sizes are the full ones; tests shrink batch/context with
 # `shrink()` while keeping the recipe.
 WORKLOADS = {
     "toy": Workload("toy", 128, 1, 1, 1, 4096, 4, "lloyd", 4, "lloyd", "f32",
@@ -65,6 +65,12 @@ WORKLOADS = {
                                "5% of channels per KV head Student-t nu=4", 4),
     "qjl": Workload("qjl", 128, 8, 32, 8, 16384, 2, "lloyd_qjl", 4, "uniform", "bf16",
                     "none", 5),
+    # asymmetric presets: 3-bit corrected keys with 4-bit values (the serving
+    # engine's k3v4_nc), and 3-bit keys + 1-bit QJL residual with 2-bit values
+    "k3v4_nc": Workload("k3v4_nc", 128, 8, 32, 16, 8192, 3, "lloyd_nc", 4, "uniform", "bf16",
+                        "2% of channels per KV head x8", 6),
+    "k3qjl_v2": Workload("k3qjl_v2", 128, 8, 32, 8, 16384, 3, "lloyd_qjl", 2, "uniform", "bf16",
+                         "none", 7),
 }
 
 
@@ -101,7 +107,7 @@ def kv_tensor(w: Workload, num_tokens: int, which: str, seed_offset: int = 0) ->
     chan_rng = np.random.Generator(np.random.PCG64([w.seed, 7]))
     if w.name == "toy":
         x[:, :, [3, 17, 64, 100]] *= np.float32(10.0)
-    elif w.name == "gqa_decode":
+    elif w.name in ("gqa_decode", "k3v4_nc"):
         ch = _outlier_channels(chan_rng, hk, d, int(round(0.02 * d)))
         for h in range(hk):
             x[:, h, ch[h]] *= np.float32(8.0)

@@ -27,6 +27,8 @@ CASES = {
     "long_3bit": [777, 64, 5],
     "qjl": [513, 100, 16],
     "prefill_append": [300],
+    "k3v4_nc": [200, 1, 64],
+    "k3qjl_v2": [129, 30],
 }
 
 
