@@ -31,6 +31,9 @@ Readings taken where the pages are silent (each is listed in the design notes):
   R12 bit order: LSB-first stream per vector (generalises [P4]'s nibble order).
   R13 QJL: residual in the rotated frame, m = d rows, sign(0) -> bit 1.
   R14 GQA: q head h reads kv head h // (Hq/Hkv); softmax scale supplied by caller.
+  R24 FP8 keys ([P1] preset table: the k8v4 preset stores keys in FP8, 2.6x):
+      OCP E4M3 of each raw key coordinate (no rotation, no per-token scale),
+      nearest value with ties to the even code, magnitudes above 448 saturate.
 
 Parity unpinned (no page fixes them; pinned only to their stated definitions):
   the norm-correction definition (R5), the value scheme of the toy and QJL
@@ -175,6 +178,8 @@ def quantize_keys(k: np.ndarray, signs: np.ndarray, cb: Codebook, mode: str,
     [P3 QJL section] 1-bit signs of a Gaussian projection of the residual.
     mode: "lloyd" (plain norm), "lloyd_nc" (corrected norm), "lloyd_qjl" (plain + QJL).
     """
+    if mode == "fp8":
+        return quantize_keys_fp8(k)
     k = np.asarray(k, dtype=np.float64)
     R = rotation_matrix(signs)
     n = np.sqrt((k * k).sum(axis=-1))
@@ -210,6 +215,49 @@ def dequantize_keys(codes: np.ndarray, norm: np.ndarray, signs: np.ndarray, cb: 
     """Stage-1 reconstruction in the original basis: k_hat = norm * R^T C[code]."""
     R = rotation_matrix(signs)
     return np.asarray(norm, dtype=np.float64)[..., None] * (cb.centroids[codes] @ R)
+
+
+# ----------------------------------------------------------------------------
+# FP8 keys  [P1 preset table: one serving preset keeps the keys in FP8 and the
+# values in 4 bits]  (R24)
+# ----------------------------------------------------------------------------
+FP8_MAX = 448.0
+
+
+def fp8_e4m3_value(code) -> np.ndarray:
+    """Value of E4M3 bytes: sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
+    exponent 0 holds the subnormals m * 2^-9; there are no infinities and
+    S.1111.111 is NaN."""
+    code = np.asarray(code, dtype=np.int64)
+    sign = np.where(code & 0x80, -1.0, 1.0)
+    e = (code >> 3) & 0xF
+    m = code & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where((code & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def quantize_fp8_e4m3(x) -> np.ndarray:
+    """E4M3 code of each value: the nearest finite value, ties to the even code
+    (even mantissa), magnitudes above 448 saturating to 448; the sign bit is
+    kept, so -0 and negatives that round to zero give 0x80."""
+    x = np.asarray(x, dtype=np.float64)
+    mags = fp8_e4m3_value(np.arange(0x7F))           # codes 0..126, increasing
+    a = np.minimum(np.abs(x), FP8_MAX)
+    hi = np.minimum(np.searchsorted(mags, a, side="left"), 0x7E)   # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    return code | np.where(np.signbit(x), 0x80, 0)
+
+
+def quantize_keys_fp8(k: np.ndarray) -> KeyCodes:
+    """FP8 keys: codes are the E4M3 bytes of the coordinates; nothing else is
+    stored (norm 1 stands for 'no scale').  The decision is exact on both sides,
+    so there is no boundary band (inf)."""
+    k = np.asarray(k, dtype=np.float64)
+    return KeyCodes(codes=quantize_fp8_e4m3(k), norm=np.ones(k.shape[:-1]), y=k,
+                    band=np.full(k.shape, np.inf))
 
 
 # ----------------------------------------------------------------------------
@@ -277,7 +325,7 @@ def unpack_codes(packed: np.ndarray, bits: int, n: int) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # Paged cache format (format version 1).  A page holds 16 tokens of one KV head;
 # fields are stored one after another, each holding one row per token slot:
-#   key codes, key norm (f32), [QJL sign bits, QJL residual norm (f32)],
+#   key codes, key norm (f32; absent for FP8 keys), [QJL sign bits, QJL residual norm (f32)],
 #   value codes, value min or value norm (f32), [value scale (f32)].
 # Every field is slot-major (row of slot s at field + s * row_bytes) except the
 # value codes, which are plane-major: byte p of slot s's row sits at
@@ -291,7 +339,7 @@ class Config:
     num_kv_heads: int
     num_q_heads: int
     key_bits: int
-    key_mode: str       # "lloyd" | "lloyd_nc" | "lloyd_qjl"
+    key_mode: str       # "lloyd" | "lloyd_nc" | "lloyd_qjl" | "fp8" (key_bits 8)
     val_bits: int
     val_mode: str       # "uniform" | "lloyd"
 
@@ -303,7 +351,9 @@ class Config:
 def page_fields(cfg: Config) -> Dict[str, Tuple[int, int]]:
     """Byte offset and per-token row size of every field inside one page."""
     d = cfg.head_dim
-    rows = [("kcodes", d * cfg.key_bits // 8), ("knorm", 4)]
+    rows = [("kcodes", d * cfg.key_bits // 8)]
+    if cfg.key_mode != "fp8":
+        rows += [("knorm", 4)]
     if cfg.key_mode == "lloyd_qjl":
         rows += [("ksigns", d // 8), ("kres", 4)]
     rows += [("vcodes", d * cfg.val_bits // 8)]
@@ -361,9 +411,10 @@ def write_tokens(cfg: Config, cache: np.ndarray, slots: np.ndarray, qz: Quantize
     blk, off = slots // BLOCK_TOKENS, slots % BLOCK_TOKENS
     rows = {
         "kcodes": pack_codes(qz.key.codes, cfg.key_bits),
-        "knorm": _f32_bytes(qz.key.norm),
         "vcodes": pack_codes(qz.val_codes, cfg.val_bits),
     }
+    if cfg.key_mode != "fp8":
+        rows["knorm"] = _f32_bytes(qz.key.norm)
     if cfg.key_mode == "lloyd_qjl":
         rows["ksigns"] = pack_codes(qz.key.qjl_bits, 1)
         rows["kres"] = _f32_bytes(qz.key.qjl_norm)
@@ -422,7 +473,10 @@ def dequantize_slots(cfg: Config, cache, slots, head: int, signs, kcb: Codebook,
                      vcb: Optional[Codebook]) -> Tuple[np.ndarray, np.ndarray, Dict[str, np.ndarray]]:
     """k_hat (stage 1) and v_hat [n, d] in the original basis for the given slots of one head."""
     f = read_tokens(cfg, cache, slots, head)
-    k_hat = dequantize_keys(f["kcodes"], f["knorm"], signs, kcb)
+    if cfg.key_mode == "fp8":
+        k_hat = fp8_e4m3_value(f["kcodes"])
+    else:
+        k_hat = dequantize_keys(f["kcodes"], f["knorm"], signs, kcb)
     if cfg.val_mode == "uniform":
         v_hat = dequantize_values_uniform(f["vcodes"], f["vmin"], f["vscale"])
     else:
