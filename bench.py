@@ -22,6 +22,8 @@ Other workloads (--workload):
                   asymmetric serving preset), same step;
   k3qjl_v2        batch 8 x context 16384, 3-bit keys + 1-bit QJL residual signs,
                   2-bit values (a second asymmetric preset), same step;
+  k8v4            the GQA shape with FP8 (E4M3) keys and 4-bit values (the
+                  preset table's k8v4), same step;
   dequant_layer   the prefill_append cache (131072 tokens x 8 KV heads)
                   reconstructed into a bf16 buffer (--dequant-f32: fp32) in one
                   tq_dequantize_rows call: the whole-cache reconstruction that
@@ -60,6 +62,7 @@ MODES = {
     "dequant_layer": ("prefill_append", "dequant"),
     "k3v4_nc": ("k3v4_nc", "decode"),
     "k3qjl_v2": ("k3qjl_v2", "decode"),
+    "k8v4": ("k8v4", "decode"),
 }
 
 
@@ -296,7 +299,7 @@ def cpu_baseline(w, kind, k_all, v_all, q_np, lay, np):
     T, Hkv, Hq, d = w.context, w.num_kv_heads, w.num_q_heads, w.head_dim
     cfg = O.Config(d, Hkv, Hq, w.key_bits, w.key_mode, w.val_bits, w.val_mode)
     signs = synth.sign_vector(w.seed)
-    kcb = O.codebook(w.key_bits, d)
+    kcb = O.codebook(w.key_bits, d) if w.key_mode != "fp8" else None   # FP8 keys have no codebook
     S = synth.qjl_matrix(d).astype(np.float64) if w.key_mode == "lloyd_qjl" else None
     f64 = lambda x: synth.bf16_bits_to_f32(x).astype(np.float64)
     th = O.page_bytes(cfg) // 16

@@ -40,8 +40,10 @@
  *   Inside a page the fields follow one another, each holding one row per slot;
  *   rows are slot-major (row of slot s at field + s*row_bytes) except the value
  *   codes (see below):
- *     key codes   d*key_bits/8 bytes per row, LSB-first bit stream
- *     key norm    fp32 (plain: ||k||; corrected: ||k|| / ||C[code]||)
+ *     key codes   d*key_bits/8 bytes per row, LSB-first bit stream (FP8 keys:
+ *                 the d E4M3 bytes of the coordinates, coordinate i at byte i)
+ *     key norm    fp32 (plain: ||k||; corrected: ||k|| / ||C[code]||); absent
+ *                 for FP8 keys
  *     [QJL only]  sign bits d/8 bytes per row (bit i = 1 if (S r)_i >= 0), then
  *                 residual norm fp32
  *     value codes d*val_bits/8 bytes per row, LSB-first bit stream, stored
@@ -80,7 +82,13 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
 typedef enum {
   TQ_KEY_LLOYD = 0,      /* stage 1, stored norm = ||k||                          */
   TQ_KEY_LLOYD_NC = 1,   /* stage 1, stored norm = ||k|| / ||C[code]|| (`_nc`)     */
-  TQ_KEY_LLOYD_QJL = 2   /* stage 1 (plain norm) + 1-bit QJL residual signs        */
+  TQ_KEY_LLOYD_QJL = 2,  /* stage 1 (plain norm) + 1-bit QJL residual signs        */
+  TQ_KEY_FP8 = 3         /* FP8 keys (issoh.co.jp "TurboQuantとは？…", preset table:
+                            one serving preset keeps keys in FP8, values in 4 bits):
+                            each coordinate of the raw key as an OCP E4M3 byte,
+                            nearest value with ties to even, magnitudes above 448
+                            saturate; no rotation, no per-token scalar.  Needs
+                            key_bits 8 and uniform values.                        */
 } tq_key_mode;
 
 typedef enum {
@@ -93,7 +101,7 @@ typedef struct {
   uint32_t head_dim;      /* d; the library supports 128                           */
   uint32_t num_kv_heads;  /* Hkv >= 1                                               */
   uint32_t num_q_heads;   /* Hq, a multiple of Hkv; Hq/Hkv must be 1, 2 or 4        */
-  uint32_t key_bits;      /* 2, 3 or 4                                              */
+  uint32_t key_bits;      /* 2, 3 or 4 (Lloyd-Max modes); 8 (TQ_KEY_FP8)             */
   uint32_t key_mode;      /* tq_key_mode                                            */
   uint32_t val_bits;      /* 2, 3 or 4                                              */
   uint32_t val_mode;      /* tq_val_mode                                            */

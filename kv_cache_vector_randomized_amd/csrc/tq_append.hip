@@ -184,6 +184,70 @@ __global__ __launch_bounds__(256) void append_values_kernel(AppendArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// FP8 keys with uniform values (issoh.co.jp "TurboQuantとは？…", preset table:
+// keys in FP8, values in 4 bits).  A wave takes one (token, head) row at a time
+// (rows handed out grid-stride); lane l holds coordinates 2l and 2l+1.  The key
+// bytes form one 128-byte row; the values follow the per-vector kernel above
+// (same min, scale and rounding), their codes gathered through LDS into the
+// page's byte planes.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_reduce_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+template <int VB, bool BF16>
+__global__ __launch_bounds__(256) void append_fp8_kernel(AppendArgs a) {
+  __shared__ __align__(16) uint8_t vcodes[4][kDim];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t rows = a.num_tokens * a.hkv;
+  const int64_t step = (int64_t)gridDim.x * 4;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < rows; r += step) {   // uniform over the wave
+    const int64_t t = r / a.hkv;
+    const int h = (int)(r - t * a.hkv);
+    const int64_t slot = a.slots[t];
+    if (slot < 0 || slot >= a.num_blocks * kBlockTokensDev) continue;
+    uint8_t* page = a.cache + ((slot >> 4) * a.hkv + h) * (int64_t)a.f.page_bytes;
+    const int so = (int)(slot & 15);
+    float k0, k1, v0, v1;
+    if constexpr (BF16) {
+      const uint32_t kw = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.k) + r * kDim)[lane];
+      const uint32_t vw = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.v) + r * kDim)[lane];
+      k0 = bf16lo(kw); k1 = bf16hi(kw); v0 = bf16lo(vw); v1 = bf16hi(vw);
+    } else {
+      const float2 kk = reinterpret_cast<const float2*>(static_cast<const float*>(a.k) + r * kDim)[lane];
+      const float2 vv = reinterpret_cast<const float2*>(static_cast<const float*>(a.v) + r * kDim)[lane];
+      k0 = kk.x; k1 = kk.y; v0 = vv.x; v1 = vv.y;
+    }
+    *reinterpret_cast<uint16_t*>(page + a.f.kcodes + so * kDim + 2 * lane) =
+        (uint16_t)(fp8_e4m3(k0) | (fp8_e4m3(k1) << 8));
+    const float mn = -wave_reduce_max(-fminf(v0, v1));
+    const float mx = wave_reduce_max(fmaxf(v0, v1));
+    constexpr float levels = (float)((1 << VB) - 1);
+    const float sc = (mx - mn) / levels;               // correctly rounded division
+    const float inv = sc > 0.f ? 1.f / sc : 0.f;
+    float xv[2] = {v0, v1};
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      // as the per-vector kernel: rint of the correctly rounded quotient, taken
+      // exactly when the reciprocal product lies within 2^-18 of a boundary
+      const float d = xv[e] - mn;
+      float xq = d * inv;
+      if (fabsf(xq - floorf(xq) - 0.5f) < 3.814697265625e-06f) xq = d / sc;
+      vcodes[wave][2 * lane + e] = (uint8_t)fminf(rintf(xq), levels);
+    }
+    wave_sync_lds();
+    if (lane < 16 * VB) page[a.f.vcodes + 16 * lane + so] = (uint8_t)stream_byte<VB>(vcodes[wave], lane);
+    if (lane == 0) {
+      reinterpret_cast<float*>(page + a.f.vmin)[so] = mn;
+      reinterpret_cast<float*>(page + a.f.vscale)[so] = sc;
+    }
+    wave_sync_lds();   // the codes are read before the next row overwrites them
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Keys and values of whole pages, bf16 inputs (Lloyd-Max keys without QJL,
 // uniform values).  A work-group of 4 waves takes pairs of groups of 16
 // consecutive tokens of one KV head: two waves quantize the keys of the two
@@ -648,6 +712,21 @@ hipError_t page_vb(const AppendArgs& a, int val_bits, hipStream_t s) {
 
 hipError_t launch_append(const AppendArgs& a, int dtype, int key_bits, int key_mode, int val_bits, int val_mode,
                          hipStream_t s) {
+  if (key_mode == TQ_KEY_FP8) {
+    if (key_bits != 8 || val_mode != TQ_VAL_UNIFORM) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)std::min<int64_t>((a.num_tokens * a.hkv + 3) / 4, 8192));
+    const bool bf = dtype == TQ_BF16;
+    switch (val_bits) {
+      case 2: if (bf) hipLaunchKernelGGL((append_fp8_kernel<2, true>), grid, dim3(256), 0, s, a);
+              else hipLaunchKernelGGL((append_fp8_kernel<2, false>), grid, dim3(256), 0, s, a); break;
+      case 3: if (bf) hipLaunchKernelGGL((append_fp8_kernel<3, true>), grid, dim3(256), 0, s, a);
+              else hipLaunchKernelGGL((append_fp8_kernel<3, false>), grid, dim3(256), 0, s, a); break;
+      case 4: if (bf) hipLaunchKernelGGL((append_fp8_kernel<4, true>), grid, dim3(256), 0, s, a);
+              else hipLaunchKernelGGL((append_fp8_kernel<4, false>), grid, dim3(256), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   // bf16 inputs and uniform values: one launch for keys and values; the other
   // combinations take the per-vector kernels.
   if (dtype == TQ_BF16 && val_mode == TQ_VAL_UNIFORM && a.unit_grid_ok &&

@@ -44,11 +44,6 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 __device__ __forceinline__ void store_agent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -152,7 +147,11 @@ __device__ __forceinline__ void load_key_codes(KeyTile<KB, QJL>& r, const Decode
   for (int pg = 0; pg < 4; ++pg) {
     const uint8_t* page = a.cache + page_offset(tp.b[pg], kvh, blk_stride, head_stride);
     const uint8_t* row = page + a.f.kcodes + j * (16 * KB) + g * (4 * KB);
-    if constexpr (KB == 4) {
+    if constexpr (KB == 8) {   // FP8 keys: 32 bytes
+      const uint4 u = reinterpret_cast<const uint4*>(row)[0], w = reinterpret_cast<const uint4*>(row)[1];
+      r.kc[pg][0] = u.x; r.kc[pg][1] = u.y; r.kc[pg][2] = u.z; r.kc[pg][3] = u.w;
+      r.kc[pg][4] = w.x; r.kc[pg][5] = w.y; r.kc[pg][6] = w.z; r.kc[pg][7] = w.w;
+    } else if constexpr (KB == 4) {
       const uint4 u = *reinterpret_cast<const uint4*>(row);
       r.kc[pg][0] = u.x; r.kc[pg][1] = u.y; r.kc[pg][2] = u.z; r.kc[pg][3] = u.w;
     } else if constexpr (KB == 2) {
@@ -174,7 +173,7 @@ __device__ __forceinline__ void load_key_scalars(KeyTile<KB, QJL>& r, const Deco
 #pragma unroll
   for (int pg = 0; pg < 4; ++pg) {
     const uint8_t* page = a.cache + page_offset(tp.b[pg], kvh, blk_stride, head_stride);
-    r.knorm[pg] = reinterpret_cast<const float*>(page + a.f.knorm)[j];
+    r.knorm[pg] = KB == 8 ? 1.f : reinterpret_cast<const float*>(page + a.f.knorm)[j];   // FP8: no norm
     r.va[pg] = reinterpret_cast<const float*>(page + a.f.vmin)[j];
     r.vb[pg] = VLM ? 0.f : reinterpret_cast<const float*>(page + a.f.vscale)[j];
     r.kres[pg] = QJL ? reinterpret_cast<const float*>(page + a.f.kres)[j] : 0.f;
@@ -199,9 +198,27 @@ __device__ __forceinline__ void load_value_group(uint4 (&vq)[VB], const DecodeAr
 // match (see qd below).
 template <int KB>
 struct KeyTable {
-  static constexpr int kEntries = KB == 3 ? 64 : 256;
-  static constexpr int kWords = KB == 2 ? 4 : 2;
+  static constexpr int kEntries = KB == 8 ? 1 : KB == 3 ? 64 : 256;   // FP8 keys need none
+  static constexpr int kWords = KB == 8 ? 1 : KB == 2 ? 4 : 2;
 };
+
+// FP8 keys: B operand of the logits MFMA for coordinates 32g + 8*KAP .. +7 of this
+// lane's chunk: the E4M3 bytes converted to f16 (every finite E4M3 value is an
+// f16 normal number, so both conversions are exact).
+template <int KAP>
+__device__ __forceinline__ uint4 fp8_key_operand(const uint32_t (&kc)[8]) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t x = kc[2 * KAP + i];
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(x, false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(x, true);
+    w[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo.x, lo.y));
+    w[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi.x, hi.y));
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
 
 // B operand of the logits MFMA for coordinates 32g + 4*KAP .. 32g + 4*KAP + 3 of
 // this lane's chunk (K = coordinate x term, 8 halves).
@@ -321,18 +338,6 @@ __device__ __forceinline__ uint32_t interleave16(uint32_t e, uint32_t o) {
   return spread(e) | (spread(o) << 1);
 }
 
-// Byte p of the LSB-first bit stream of 128 codes of B bits held one per byte.
-template <int B>
-__device__ __forceinline__ uint32_t stream_byte(const uint8_t* codes, int p) {
-  uint32_t v = 0u;
-  for (int i = (8 * p) / B; i < kDim && B * i < 8 * p + 8; ++i) {
-    const int sh = B * i - 8 * p;
-    const uint32_t c = codes[i];
-    v |= sh >= 0 ? (c << sh) : (c >> -sh);
-  }
-  return v & 0xFFu;
-}
-
 // Fused append (one wave): quantize the new token (lane l holds its coordinates
 // 2l, 2l+1 of the key k0, k1 and the value v0, v1) as the append kernels do (rotation, codes through the key grid, fp32 norm with the
 // optional correction, QJL signs and residual norm, uniform values) and write its
@@ -344,6 +349,19 @@ template <int KB, bool QJL, int VB>
 __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, float v0, float v1, int lane,
                                    uint8_t* page, int so, uint8_t (&codes)[2][kDim], float* vhat, float* rbuf,
                                    float& c0, float& c1, float& nhat, float& rho, float& sgn0, float& sgn1) {
+  rho = 0.f;
+  sgn0 = sgn1 = 1.f;
+  int kc0 = 0, kc1 = 0;
+  if constexpr (KB == 8) {
+    // FP8 keys: the E4M3 bytes of the coordinates, their values for the logit
+    const uint32_t b0 = fp8_e4m3(k0), b1 = fp8_e4m3(k1);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 cv = __builtin_amdgcn_cvt_pk_f32_fp8(b0 | (b1 << 8), false);
+    c0 = cv.x;
+    c1 = cv.y;
+    nhat = 1.f;
+    *reinterpret_cast<uint16_t*>(page + a.f.kcodes + so * kDim + 2 * lane) = (uint16_t)(b0 | (b1 << 8));
+  } else {
   // keys: z = H(s * k), then codes of u = z / ||z||
   float x0 = k0 * a.c->signs[2 * lane], x1 = k1 * a.c->signs[2 * lane + 1];
   {
@@ -360,13 +378,11 @@ __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, floa
   }
   const float ss = wave_sum(fmaf(x0, x0, x1 * x1));
   const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;     // a zero key gives codes 2^(b-1)
-  const int kc0 = lut_code(a.c->klut, x0 * inv, a.klut_scale, a.klut_bias, c0);
-  const int kc1 = lut_code(a.c->klut, x1 * inv, a.klut_scale, a.klut_bias, c1);
+  kc0 = lut_code(a.c->klut, x0 * inv, a.klut_scale, a.klut_bias, c0);
+  kc1 = lut_code(a.c->klut, x1 * inv, a.klut_scale, a.klut_bias, c1);
   const float nk = sqrtf(ss) * kInvSqrtDim;               // ||k||
   const float c2 = wave_sum(fmaf(c0, c0, c1 * c1));
   nhat = (!QJL && a.key_nc) ? (nk > 0.f ? nk / sqrtf(c2) : 0.f) : nk;
-  rho = 0.f;
-  sgn0 = sgn1 = 1.f;
   if constexpr (QJL) {
     // residual in the rotated frame r' = H(s*k)/sqrt(d) - ||k|| C[code], and S r'
     const float r0 = fmaf(-nk, c0, x0 * kInvSqrtDim), r1 = fmaf(-nk, c1, x1 * kInvSqrtDim);
@@ -388,6 +404,7 @@ __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, floa
       reinterpret_cast<uint32_t*>(page + a.f.ksigns + 16 * so)[lane] =
           interleave16((uint32_t)(em >> (16 * lane)), (uint32_t)(om >> (16 * lane)));
   }
+  }
   // uniform values, as the append kernel: codes floor(fl32(x - mn) / sc + 1/2)
   const float mn = -wave_max(-fminf(v0, v1));
   const float mx = wave_max(fmaxf(v0, v1));
@@ -402,10 +419,10 @@ __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, floa
   codes[1][2 * lane] = (uint8_t)vc0;
   codes[1][2 * lane + 1] = (uint8_t)vc1;
   wave_sync_lds();
-  if (lane < 16 * KB) page[a.f.kcodes + so * 16 * KB + lane] = (uint8_t)stream_byte<KB>(codes[0], lane);
+  if (KB != 8 && lane < 16 * KB) page[a.f.kcodes + so * 16 * KB + lane] = (uint8_t)stream_byte<KB>(codes[0], lane);
   if (lane < 16 * VB) page[a.f.vcodes + 16 * lane + so] = (uint8_t)stream_byte<VB>(codes[1], lane);
   if (lane == 0) {
-    reinterpret_cast<float*>(page + a.f.knorm)[so] = nhat;
+    if (KB != 8) reinterpret_cast<float*>(page + a.f.knorm)[so] = nhat;
     reinterpret_cast<float*>(page + a.f.vmin)[so] = mn;
     reinterpret_cast<float*>(page + a.f.vscale)[so] = sc;
     if constexpr (QJL) reinterpret_cast<float*>(page + a.f.kres)[so] = rho;
@@ -478,9 +495,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   // wave) is loaded before the query is rotated, so that its latency overlaps the
   // rotation, the tables and the barrier.  Block-table reads do not wait for the
   // sequence length: entries past the end are dropped once it is known.
-  const float kc_top = a.c->kc[(1 << KB) - 1];
+  constexpr bool FP8 = KB == 8;   // FP8 keys: no rotation, no codebook, no norm
+  const float kc_top = FP8 ? 1.f : a.c->kc[((1 << KB) - 1) & 15];
   float kc_e[KB == 2 ? 4 : 2];
-  {
+  if constexpr (!FP8) {
     const int ent = tid & (KeyTable<KB>::kEntries - 1);
 #pragma unroll
     for (int i = 0; i < (KB == 2 ? 4 : 2); ++i) kc_e[i] = a.c->kc[(ent >> (KB * i)) & ((1 << KB) - 1)];
@@ -540,8 +558,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
 
   // Key centroid table: C * 2^s2 with 2^s2 bringing the largest |C| (the last,
   // the codebook being symmetric) into [2^14, 2^15).
-  const int s2 = 15 - __builtin_amdgcn_frexp_expf(kc_top);
-  if (tid < KeyTable<KB>::kEntries) {
+  const int s2 = FP8 ? 0 : 15 - __builtin_amdgcn_frexp_expf(kc_top);
+  if (!FP8 && tid < KeyTable<KB>::kEntries) {
     uint32_t* e = &ktab[tid * Tab::kWords];
 #pragma unroll
     for (int i = 0; i < (KB == 2 ? 4 : 2); ++i) {
@@ -567,18 +585,22 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     float qx0 = f32 ? __uint_as_float(qw0) : bf16lo(qw0);
     float qx1 = f32 ? __uint_as_float(qw1) : bf16hi(qw0);
     if (wave >= G) qx0 = qx1 = 0.f;
-    float x0 = qx0 * sg0, x1 = qx1 * sg1;
-    const float s0 = x0 + x1, d0 = x0 - x1;
-    x0 = s0;
-    x1 = d0;
+    float x0 = qx0, x1 = qx1;
+    if constexpr (!FP8) {
+      x0 *= sg0;
+      x1 *= sg1;
+      const float s0 = x0 + x1, d0 = x0 - x1;
+      x0 = s0;
+      x1 = d0;
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const float p0 = __shfl_xor(x0, m), p1 = __shfl_xor(x1, m);
-      const bool upper = (lane & m) != 0;
-      x0 = upper ? p0 - x0 : x0 + p0;
-      x1 = upper ? p1 - x1 : x1 + p1;
+      for (int m = 1; m < 64; m <<= 1) {
+        const float p0 = __shfl_xor(x0, m), p1 = __shfl_xor(x1, m);
+        const bool upper = (lane & m) != 0;
+        x0 = upper ? p0 - x0 : x0 + p0;
+        x1 = upper ? p1 - x1 : x1 + p1;
+      }
     }
-    const float f = a.scale * kInvSqrtDim * kLog2e;
+    const float f = a.scale * (FP8 ? 1.f : kInvSqrtDim) * kLog2e;
     x0 *= f;
     x1 *= f;
     // f16 terms of q'' * 2^s1, 2^s1 bringing the head's largest |q''| into [2^14, 2^15)
@@ -587,10 +609,18 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     float h0, l0, m0, h1, l1, m1;
     split_f16(ldexpf(x0, s1), h0, l0, m0);
     split_f16(ldexpf(x1, s1), h1, l1, m1);
-    *reinterpret_cast<uint2*>(&qd[wave][0][2 * lane]) = make_uint2(f16bits(h0) * 0x10001u, f16bits(h1) * 0x10001u);
-    *reinterpret_cast<uint2*>(&qd[wave][1][2 * lane]) = make_uint2(f16bits(l0) * 0x10001u, f16bits(l1) * 0x10001u);
-    *reinterpret_cast<uint2*>(&qd[wave][2][2 * lane]) = make_uint2(f16bits(m0) * 0x10001u, f16bits(m1) * 0x10001u);
-    *reinterpret_cast<uint2*>(&qd[wave][3][2 * lane]) = make_uint2(0u, 0u);
+    if constexpr (FP8) {
+      // FP8 keys take one f16 term each: the query terms are not duplicated
+      qd[wave][0][lane] = f16bits(h0) | (f16bits(h1) << 16);
+      qd[wave][1][lane] = f16bits(l0) | (f16bits(l1) << 16);
+      qd[wave][2][lane] = f16bits(m0) | (f16bits(m1) << 16);
+      qd[wave][3][lane] = 0u;
+    } else {
+      *reinterpret_cast<uint2*>(&qd[wave][0][2 * lane]) = make_uint2(f16bits(h0) * 0x10001u, f16bits(h1) * 0x10001u);
+      *reinterpret_cast<uint2*>(&qd[wave][1][2 * lane]) = make_uint2(f16bits(l0) * 0x10001u, f16bits(l1) * 0x10001u);
+      *reinterpret_cast<uint2*>(&qd[wave][2][2 * lane]) = make_uint2(f16bits(m0) * 0x10001u, f16bits(m1) * 0x10001u);
+      *reinterpret_cast<uint2*>(&qd[wave][3][2 * lane]) = make_uint2(0u, 0u);
+    }
     if (lane == 0) qexp[wave] = s1;
     if constexpr (!VLM) *reinterpret_cast<float2*>(&qf[wave][2 * lane]) = make_float2(x0, x1);
     if constexpr (QJL) {
@@ -641,7 +671,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
 
   // A operands of the logits MFMA: row lane%16 = (head (lane/4)%4, term lane%4),
   // coordinates 32g + 4*kap + (0..3), each twice (g = lane/16).
-  const uint32_t* qa_src = &qd[(lane >> 2) & 3][lane & 3][32 * grp];
+  const uint32_t* qa_src = &qd[(lane >> 2) & 3][lane & 3][(FP8 ? 16 : 32) * grp];
   // base-2 logit of head grp = D * 2^-(s1 + s2) * norm (and the QJL part: D2 * 2^-sp * residual norm)
   const float lscale = ldexpf(1.f, -(qexp[grp] + s2));
   const float pscale = QJL ? ldexpf(1.f, -pexp[grp]) : 0.f;
@@ -716,7 +746,20 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     _Pragma("unroll") for (int pg = 0; pg < 4; ++pg)                        \
         D[pg] = mfma_f16(qa, key_operand<KB, KAP>(cur.kc[pg], ktab_p), D[pg]); \
   }
-    TQ_KAP(0) TQ_KAP(1) TQ_KAP(2) TQ_KAP(3) TQ_KAP(4) TQ_KAP(5) TQ_KAP(6) TQ_KAP(7)
+    if constexpr (FP8) {
+#pragma unroll
+      for (int kap = 0; kap < 4; ++kap) {
+        const uint4 qa = *reinterpret_cast<const uint4*>(qa_src + 4 * kap);
+#pragma unroll
+        for (int pg = 0; pg < 4; ++pg) {
+          const uint4 kb = kap == 0 ? fp8_key_operand<0>(cur.kc[pg]) : kap == 1 ? fp8_key_operand<1>(cur.kc[pg])
+                         : kap == 2 ? fp8_key_operand<2>(cur.kc[pg]) : fp8_key_operand<3>(cur.kc[pg]);
+          D[pg] = mfma_f16(qa, kb, D[pg]);
+        }
+      }
+    } else {
+      TQ_KAP(0) TQ_KAP(1) TQ_KAP(2) TQ_KAP(3) TQ_KAP(4) TQ_KAP(5) TQ_KAP(6) TQ_KAP(7)
+    }
 #undef TQ_KAP
     if constexpr (QJL) {
 #pragma unroll
@@ -981,8 +1024,12 @@ namespace {
 template <int KB, bool QJL, int VB>
 hipError_t decode_v(const DecodeArgs& a, int val_mode, hipStream_t s) {
   const dim3 grid((unsigned)a.splits, (unsigned)a.hkv, (unsigned)a.batch);
-  if (val_mode == TQ_VAL_LLOYD) hipLaunchKernelGGL((decode_kernel<KB, QJL, VB, true>), grid, dim3(64 * kDecodeWaves), 0, s, a);
-  else hipLaunchKernelGGL((decode_kernel<KB, QJL, VB, false>), grid, dim3(64 * kDecodeWaves), 0, s, a);
+  if (val_mode == TQ_VAL_LLOYD) {
+    if constexpr (KB == 8) return hipErrorInvalidValue;   // FP8 keys pair with uniform values
+    else hipLaunchKernelGGL((decode_kernel<KB, QJL, VB, true>), grid, dim3(64 * kDecodeWaves), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<KB, QJL, VB, false>), grid, dim3(64 * kDecodeWaves), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -999,18 +1046,28 @@ hipError_t decode_vb(const DecodeArgs& a, int val_bits, int val_mode, hipStream_
 template <int KB, bool QJL>
 const void* kernel_vb(int val_bits, int val_mode) {
   const bool lm = val_mode == TQ_VAL_LLOYD;
+  if constexpr (KB == 8) {
+    switch (val_bits) {
+      case 2: return (const void*)decode_kernel<8, false, 2, false>;
+      case 3: return (const void*)decode_kernel<8, false, 3, false>;
+      case 4: return (const void*)decode_kernel<8, false, 4, false>;
+    }
+    return nullptr;
+  } else {
   switch (val_bits) {
     case 2: return lm ? (const void*)decode_kernel<KB, QJL, 2, true> : (const void*)decode_kernel<KB, QJL, 2, false>;
     case 3: return lm ? (const void*)decode_kernel<KB, QJL, 3, true> : (const void*)decode_kernel<KB, QJL, 3, false>;
     case 4: return lm ? (const void*)decode_kernel<KB, QJL, 4, true> : (const void*)decode_kernel<KB, QJL, 4, false>;
   }
   return nullptr;
+  }
 }
 
 }  // namespace
 
 const void* decode_kernel_ptr(int key_bits, int key_mode, int val_bits, int val_mode) {
   const bool qjl = key_mode == TQ_KEY_LLOYD_QJL;
+  if (key_mode == TQ_KEY_FP8) return key_bits == 8 && val_mode == TQ_VAL_UNIFORM ? kernel_vb<8, false>(val_bits, val_mode) : nullptr;
   switch (key_bits) {
     case 2: return qjl ? kernel_vb<2, true>(val_bits, val_mode) : kernel_vb<2, false>(val_bits, val_mode);
     case 3: return qjl ? kernel_vb<3, true>(val_bits, val_mode) : kernel_vb<3, false>(val_bits, val_mode);
@@ -1022,6 +1079,8 @@ const void* decode_kernel_ptr(int key_bits, int key_mode, int val_bits, int val_
 hipError_t launch_decode(const DecodeArgs& a, int key_bits, int key_mode, int val_bits, int val_mode,
                          hipStream_t s) {
   const bool qjl = key_mode == TQ_KEY_LLOYD_QJL;
+  if (key_mode == TQ_KEY_FP8)
+    return key_bits == 8 && val_mode == TQ_VAL_UNIFORM ? decode_vb<8, false>(a, val_bits, val_mode, s) : hipErrorInvalidValue;
   switch (key_bits) {
     case 2: return qjl ? decode_vb<2, true>(a, val_bits, val_mode, s) : decode_vb<2, false>(a, val_bits, val_mode, s);
     case 3: return qjl ? decode_vb<3, true>(a, val_bits, val_mode, s) : decode_vb<3, false>(a, val_bits, val_mode, s);

@@ -27,7 +27,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kStageBytes = 2560;   // the largest page (4-bit QJL keys, 4-bit uniform values)
+constexpr int kStageBytes = kMaxPageBytes;   // the largest page (FP8 keys, 4-bit uniform values)
+constexpr int kStageLoads = (kStageBytes + 1023) / 1024;   // 16-byte loads per lane to stage a page
 // groups of 16 list entries per wave (measured: one for fp32 output, two for bf16)
 template <bool BF16OUT>
 constexpr int groups_per_wave() { return BF16OUT ? 2 : 1; }
@@ -97,14 +98,17 @@ struct Group {
   static constexpr int kBit(int p, int m) { return B * (8 * G * m + G * p); }
   static constexpr bool kWide = B != 3;                  // aligned 1-, 2- or 4-byte word
   static constexpr int kBytes = B == 3 ? (G == 8 ? 3 : 2) : B * G / 8;
-  static constexpr int kRawKey = kWide ? 1 : kBytes;     // raw registers per key group
+  static constexpr int kRawKey = B == 8 ? G / 4 : kWide ? 1 : kBytes;   // raw registers per key group
 };
 
 template <int B, int G>
 __device__ __forceinline__ void load_key_group(const uint8_t* krow, int p, int m, uint32_t* raw) {
   constexpr int n = Group<B, G>::kBytes;
   const int q = Group<B, G>::kBit(p, m) >> 3;
-  if constexpr (Group<B, G>::kWide) {
+  if constexpr (B == 8) {   // FP8 keys: G bytes, dword-aligned
+#pragma unroll
+    for (int i = 0; i < G / 4; ++i) raw[i] = reinterpret_cast<const uint32_t*>(krow + q)[i];
+  } else if constexpr (Group<B, G>::kWide) {
     if constexpr (n == 4) raw[0] = *reinterpret_cast<const uint32_t*>(krow + q);
     else if constexpr (n == 2) raw[0] = *reinterpret_cast<const uint16_t*>(krow + q);
     else raw[0] = krow[q];
@@ -223,7 +227,7 @@ __device__ __forceinline__ void load_raw(const uint8_t* pg, const FieldOffsets& 
     load_key_group<KB, G>(pg + f.kcodes + so * (KB * 16), p, m, r.k[m]);
     load_value_group<VB, G>(pg + f.vcodes + so, p, m, r.v[m]);
   }
-  r.knrm = reinterpret_cast<const float*>(pg + f.knorm)[so];
+  r.knrm = KB == 8 ? 1.f : reinterpret_cast<const float*>(pg + f.knorm)[so];
   r.vmn = reinterpret_cast<const float*>(pg + f.vmin)[so];
   r.vsc = VLM ? 0.f : reinterpret_cast<const float*>(pg + f.vscale)[so];
 }
@@ -233,14 +237,28 @@ __device__ __forceinline__ void load_raw(const uint8_t* pg, const FieldOffsets& 
 template <int KB, int VB, int G, bool VLM, bool BF16OUT>
 __device__ __forceinline__ void finish(const DequantArgs& a, const Raw<KB, VB, G>& r, bool ok, int64_t rw, uint32_t h,
                                        const float* ktbl, const float* vtbl, uint32_t sgn, int lane, int p) {
-  uint32_t kw[16 / G], vw[16 / G];
+  uint32_t vw[16 / G];
 #pragma unroll
-  for (int m = 0; m < 16 / G; ++m) {
-    kw[m] = group_word<KB, G, Group<KB, G>::kWide>(r.k[m], p, m);
-    vw[m] = group_word<VB, G, false>(r.v[m], p, m);
-  }
+  for (int m = 0; m < 16 / G; ++m) vw[m] = group_word<VB, G, false>(r.v[m], p, m);
   float xk[16], xv[16];
-  lloyd_part<KB, G>(kw, ktbl, ok ? r.knrm * kInvSqrtDim : 0.f, sgn, lane, xk);
+  if constexpr (KB == 8) {
+    // FP8 keys: the E4M3 values themselves (exact conversions), no rotation
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int m = 0; m < 16 / G; ++m)
+#pragma unroll
+      for (int i = 0; i < G / 4; ++i) {
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(r.k[m][i], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(r.k[m][i], true);
+        float* y = xk + G * m + 4 * i;
+        y[0] = ok ? lo.x : 0.f; y[1] = ok ? lo.y : 0.f; y[2] = ok ? hi.x : 0.f; y[3] = ok ? hi.y : 0.f;
+      }
+  } else {
+    uint32_t kw[16 / G];
+#pragma unroll
+    for (int m = 0; m < 16 / G; ++m) kw[m] = group_word<KB, G, Group<KB, G>::kWide>(r.k[m], p, m);
+    lloyd_part<KB, G>(kw, ktbl, ok ? r.knrm * kInvSqrtDim : 0.f, sgn, lane, xk);
+  }
   if constexpr (VLM) {
     lloyd_part<VB, G>(vw, vtbl, ok ? r.vmn * kInvSqrtDim : 0.f, sgn, lane, xv);
   } else {
@@ -261,8 +279,8 @@ __device__ __forceinline__ void finish(const DequantArgs& a, const Raw<KB, VB, G
 
 // A wave's entries form kGroups groups of 16.  A group that is one whole page in
 // slot order (the usual case when a whole sequence is reconstructed) is read
-// with three 16-byte loads per lane, all issued at the start, and staged in
-// LDS; any other group is read entry by entry.
+// with kStageLoads 16-byte loads per lane, all issued at the start, and staged
+// in LDS; any other group is read entry by entry.
 template <int KB, int VB, bool VLM, bool BF16OUT>
 __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   __shared__ __align__(16) float ktbl[table_floats<KB>()];
@@ -297,7 +315,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   // Whole-page groups: slot of entry first + 16g + j in lane j (and j + 16, ...).
   bool whole[kGroups];
   const uint8_t* gpage[kGroups];
-  u32x4 st[kGroups][3];
+  u32x4 st[kGroups][kStageLoads];
   int64_t sl[kGroups], wrow[kGroups][2];
   bool in[kGroups];
 #pragma unroll
@@ -325,7 +343,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   for (int g = 0; g < kGroups; ++g) {
     if (whole[g]) {
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
+      for (int k = 0; k < kStageLoads; ++k) {
         const uint32_t off = 16u * (lane + 64 * k);
         if (off < pb) st[g][k] = *reinterpret_cast<const u32x4*>(gpage[g] + off);
       }
@@ -337,7 +355,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   for (int g = 0; g < kGroups; ++g) {
     if (whole[g]) {
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
+      for (int k = 0; k < kStageLoads; ++k) {
         const uint32_t off = 16u * (lane + 64 * k);
         if (off < pb) *reinterpret_cast<u32x4*>(stage[wave][g] + off) = st[g][k];
       }
@@ -377,7 +395,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
 
 namespace {
 
-static_assert(sizeof(DevConsts) >= 4096, "invalid slots read a page's worth of the constant block");
+static_assert(sizeof(DevConsts) >= kMaxPageBytes, "invalid slots read a page's worth of the constant block");
 
 template <int KB, int VB>
 hipError_t dequant_launch(const DequantArgs& a, bool lm, bool bf16, hipStream_t s) {
@@ -385,7 +403,8 @@ hipError_t dequant_launch(const DequantArgs& a, bool lm, bool bf16, hipStream_t 
   const int64_t items = (a.n + per_wave - 1) / per_wave * a.hkv;
   const dim3 grid((unsigned)((items + 3) / 4));
   if (lm) {
-    if (bf16) hipLaunchKernelGGL((dequant_kernel<KB, VB, true, true>), grid, dim3(256), 0, s, a);
+    if constexpr (KB == 8) return hipErrorInvalidValue;   // FP8 keys pair with uniform values
+    else if (bf16) hipLaunchKernelGGL((dequant_kernel<KB, VB, true, true>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((dequant_kernel<KB, VB, true, false>), grid, dim3(256), 0, s, a);
   } else {
     if (bf16) hipLaunchKernelGGL((dequant_kernel<KB, VB, false, true>), grid, dim3(256), 0, s, a);
@@ -410,6 +429,7 @@ hipError_t launch_dequant(const DequantArgs& a, int key_bits, int val_bits, int 
                           hipStream_t s) {
   const bool lm = val_mode == TQ_VAL_LLOYD;
   switch (key_bits) {
+    case 8: return lm ? hipErrorInvalidValue : dequant_vb<8>(a, val_bits, false, bf16_out, s);   // FP8 keys
     case 2: return dequant_vb<2>(a, val_bits, lm, bf16_out, s);
     case 3: return dequant_vb<3>(a, val_bits, lm, bf16_out, s);
     case 4: return dequant_vb<4>(a, val_bits, lm, bf16_out, s);

@@ -149,4 +149,40 @@ __device__ __forceinline__ float lloyd_codes(float (&x)[kDim], const uint32_t (&
   return n;
 }
 
+// Make a wave's LDS writes visible to the wave's later LDS reads.
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Byte p of the LSB-first bit stream of 128 codes of B bits held one per byte.
+template <int B>
+__device__ __forceinline__ uint32_t stream_byte(const uint8_t* codes, int p) {
+  uint32_t v = 0u;
+  for (int i = (8 * p) / B; i < kDim && B * i < 8 * p + 8; ++i) {
+    const int sh = B * i - 8 * p;
+    const uint32_t c = codes[i];
+    v |= sh >= 0 ? (c << sh) : (c >> -sh);
+  }
+  return v & 0xFFu;
+}
+
+// E4M3 byte of x (FP8 keys): the nearest finite value with ties to the even
+// code, magnitudes above 448 saturating to 448, the sign bit kept.  Every step is
+// exact (power-of-two scalings, rint of an exactly scaled value).
+__device__ __forceinline__ uint32_t fp8_e4m3(float x) {
+  const uint32_t sgn = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.f);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)rintf(a * 512.f);   // subnormals: multiples of 2^-9 (8 = the smallest normal)
+  } else {
+    const int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;   // floor(log2 a), -6..8
+    const uint32_t m = (uint32_t)rintf(ldexpf(a, 3 - e));           // 8..16; 16 carries
+    code = (uint32_t)(8 * (e + 7)) + m - 8u;
+  }
+  return code | sgn;
+}
+
 }  // namespace tq

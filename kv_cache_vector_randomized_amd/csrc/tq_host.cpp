@@ -162,7 +162,11 @@ tq_status layout_of(const tq_config* c, tq_layout* L) {
   const size_t none = (size_t)-1;
   size_t off = 0;
   L->off_kcodes = off; L->row_kcodes = d * c->key_bits / 8; off += T * L->row_kcodes;
-  L->off_knorm = off; off += T * 4;
+  if (c->key_mode == TQ_KEY_FP8) {
+    L->off_knorm = none;
+  } else {
+    L->off_knorm = off; off += T * 4;
+  }
   if (c->key_mode == TQ_KEY_LLOYD_QJL) {
     L->off_ksigns = off; L->row_ksigns = d / 8; off += T * L->row_ksigns;
     L->off_kresid = off; off += T * 4;
@@ -174,6 +178,7 @@ tq_status layout_of(const tq_config* c, tq_layout* L) {
   if (c->val_mode == TQ_VAL_UNIFORM) { L->off_vscale = off; off += T * 4; } else L->off_vscale = none;
   L->page_bytes = off;
   L->token_head_bytes = off / T;
+  if (off > (size_t)tq::kMaxPageBytes) return fail(TQ_ERR_UNSUPPORTED, "page of %zu bytes exceeds %d", off, tq::kMaxPageBytes);
   return TQ_OK;
 }
 
@@ -181,7 +186,7 @@ tq::FieldOffsets offsets_of(const tq_layout& L) {
   tq::FieldOffsets f;
   f.page_bytes = (uint32_t)L.page_bytes;
   f.kcodes = (uint32_t)L.off_kcodes;
-  f.knorm = (uint32_t)L.off_knorm;
+  f.knorm = L.off_knorm == (size_t)-1 ? 0u : (uint32_t)L.off_knorm;
   f.ksigns = L.off_ksigns == (size_t)-1 ? 0u : (uint32_t)L.off_ksigns;
   f.kres = L.off_kresid == (size_t)-1 ? 0u : (uint32_t)L.off_kresid;
   f.vcodes = (uint32_t)L.off_vcodes;
@@ -246,12 +251,17 @@ tq_status tq_validate_config(const tq_config* c) {
   if (c->num_kv_heads == 0 || c->num_q_heads == 0 || c->num_q_heads % c->num_kv_heads)
     return fail(TQ_ERR_INVALID_ARG, "num_q_heads (%u) must be a positive multiple of num_kv_heads (%u)",
                 c->num_q_heads, c->num_kv_heads);
-  if (c->key_mode > TQ_KEY_LLOYD_QJL) return fail(TQ_ERR_INVALID_ARG, "bad key_mode %u", c->key_mode);
+  if (c->key_mode > TQ_KEY_FP8) return fail(TQ_ERR_INVALID_ARG, "bad key_mode %u", c->key_mode);
   if (c->val_mode > TQ_VAL_LLOYD) return fail(TQ_ERR_INVALID_ARG, "bad val_mode %u", c->val_mode);
   if (c->key_bits < 1 || c->key_bits > 8) return fail(TQ_ERR_INVALID_ARG, "key_bits %u out of [1, 8]", c->key_bits);
   if (c->val_bits < 1 || c->val_bits > 8) return fail(TQ_ERR_INVALID_ARG, "val_bits %u out of [1, 8]", c->val_bits);
   if (c->head_dim != (uint32_t)tq::kDim) return fail(TQ_ERR_UNSUPPORTED, "head_dim %u: kernels are built for 128", c->head_dim);
-  if (c->key_bits < 2 || c->key_bits > 4) return fail(TQ_ERR_UNSUPPORTED, "key_bits %u: supported 2..4", c->key_bits);
+  if (c->key_mode == TQ_KEY_FP8) {
+    if (c->key_bits != 8) return fail(TQ_ERR_INVALID_ARG, "FP8 keys take key_bits 8 (got %u)", c->key_bits);
+    if (c->val_mode != TQ_VAL_UNIFORM) return fail(TQ_ERR_UNSUPPORTED, "FP8 keys are built with uniform values only");
+  } else if (c->key_bits < 2 || c->key_bits > 4) {
+    return fail(TQ_ERR_UNSUPPORTED, "key_bits %u: supported 2..4 (8 with FP8 keys)", c->key_bits);
+  }
   if (c->val_bits < 2 || c->val_bits > 4) return fail(TQ_ERR_UNSUPPORTED, "val_bits %u: supported 2..4", c->val_bits);
   const uint32_t g = c->num_q_heads / c->num_kv_heads;
   if (g != 1 && g != 2 && g != 4) return fail(TQ_ERR_UNSUPPORTED, "group size %u: supported 1, 2, 4", g);
@@ -289,13 +299,14 @@ tq_status tq_create(const tq_config* cfg, const int8_t* signs_host, const float*
   std::memset(h, 0, sizeof *h);
   for (int i = 0; i < d; ++i) h->signs[i] = (float)signs_host[i];
   float kt[15] = {0}, vt[15] = {0};
-  codebook_f32((int)cfg->key_bits, d, h->kc, kt);
+  const bool fp8 = cfg->key_mode == TQ_KEY_FP8;   // no key codebook
+  if (!fp8) codebook_f32((int)cfg->key_bits, d, h->kc, kt);
   tq_ctx* ctx = new (std::nothrow) tq_ctx();
   if (!ctx) { delete h; return fail(TQ_ERR_OUT_OF_MEMORY, "host allocation failed"); }
   ctx->cfg = *cfg;
-  layout_of(cfg, &ctx->layout);
-  bool ok = build_lut((int)cfg->key_bits, h->kc, kt, h->klut, &ctx->klut_scale, &ctx->klut_bias);
-  ctx->unit_grid_ok = build_unit_lut((int)cfg->key_bits, h->kc, kt, h->kulut) ? 1 : 0;
+  if ((s = layout_of(cfg, &ctx->layout)) != TQ_OK) { delete h; delete ctx; return s; }
+  bool ok = fp8 || build_lut((int)cfg->key_bits, h->kc, kt, h->klut, &ctx->klut_scale, &ctx->klut_bias);
+  ctx->unit_grid_ok = (!fp8 && build_unit_lut((int)cfg->key_bits, h->kc, kt, h->kulut)) ? 1 : 0;
   if (cfg->val_mode == TQ_VAL_LLOYD) {
     codebook_f32((int)cfg->val_bits, d, h->vc, vt);
     ok = ok && build_lut((int)cfg->val_bits, h->vc, vt, h->vlut, &ctx->vlut_scale, &ctx->vlut_bias);

@@ -16,7 +16,8 @@ constexpr int kMaxGroup = 4;       // q heads per kv head handled by one work-gr
 constexpr int kBlockTokensDev = TQ_BLOCK_TOKENS;
 constexpr int kMaxPagesPerSplit = 256;   // 64 tiles of 64 tokens
 constexpr int kDecodeWaves = 8;           // waves of a decode work-group (they share its tiles)
-constexpr int kDecodeWgsPerCu = 1;        // decode work-groups per compute unit the split plan aims at
+constexpr int kDecodeWgsPerCu = 1;
+constexpr int kMaxPageBytes = 3200;      // largest page of any supported format (FP8 keys, 4-bit uniform values)        // decode work-groups per compute unit the split plan aims at
 constexpr size_t kCounterBytes = 65536;   // arrival counters at the start of the decode workspace
 // Cells of the page-append look-up grid: g = 128 y for a unit-vector coordinate
 // y, cell k = round(g) + 128 in 0..256 (the end cells reach to infinity).

@@ -44,7 +44,7 @@ class Workload:
     batch: int
     context: int            # tokens attended per sequence in the decode step
     key_bits: int
-    key_mode: str           # "lloyd" | "lloyd_nc" | "lloyd_qjl"
+    key_mode: str           # "lloyd" | "lloyd_nc" | "lloyd_qjl" | "fp8"
     val_bits: int
     val_mode: str           # "uniform" | "lloyd"
     dtype: str              # "f32" | "bf16"
@@ -71,6 +71,9 @@ WORKLOADS = {
                         "2% of channels per KV head x8", 6),
     "k3qjl_v2": Workload("k3qjl_v2", 128, 8, 32, 8, 16384, 3, "lloyd_qjl", 2, "uniform", "bf16",
                          "none", 7),
+    # FP8 (E4M3) keys with 4-bit uniform values (the serving engine's k8v4)
+    "k8v4": Workload("k8v4", 128, 8, 32, 16, 8192, 8, "fp8", 4, "uniform", "bf16",
+                     "2% of channels per KV head x8", 8),
 }
 
 
@@ -107,7 +110,7 @@ def kv_tensor(w: Workload, num_tokens: int, which: str, seed_offset: int = 0) ->
     chan_rng = np.random.Generator(np.random.PCG64([w.seed, 7]))
     if w.name == "toy":
         x[:, :, [3, 17, 64, 100]] *= np.float32(10.0)
-    elif w.name in ("gqa_decode", "k3v4_nc"):
+    elif w.name in ("gqa_decode", "k3v4_nc", "k8v4"):
         ch = _outlier_channels(chan_rng, hk, d, int(round(0.02 * d)))
         for h in range(hk):
             x[:, h, ch[h]] *= np.float32(8.0)

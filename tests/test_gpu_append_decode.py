@@ -29,6 +29,7 @@ CASES = {
     "prefill_append": [300],
     "k3v4_nc": [200, 1, 64],
     "k3qjl_v2": [129, 30],
+    "k8v4": [333, 1, 16, 0],
 }
 
 

@@ -48,6 +48,10 @@ def test_status_strings():
     (dict(val_mode=2), tq.TQ_ERR_INVALID_ARG),
     (dict(block_tokens=32), tq.TQ_ERR_INVALID_ARG),
     (dict(abi_version=2), tq.TQ_ERR_INVALID_ARG),
+    (dict(key_bits=8, key_mode="fp8"), tq.TQ_OK),
+    (dict(key_bits=4, key_mode="fp8"), tq.TQ_ERR_INVALID_ARG),
+    (dict(key_bits=8, key_mode="fp8", val_mode="lloyd"), tq.TQ_ERR_UNSUPPORTED),
+    (dict(key_mode=4), tq.TQ_ERR_INVALID_ARG),
 ])
 def test_validate_config(kw, expect):
     assert tq.validate_config(tq.make_config(**kw)) == expect
@@ -81,7 +85,8 @@ def test_every_call_refuses_a_null_context():
 
 @pytest.mark.parametrize("kb,km,vb,vm", [(4, "lloyd", 4, "lloyd"), (4, "lloyd_nc", 4, "uniform"),
                                          (3, "lloyd_nc", 3, "uniform"), (2, "lloyd_qjl", 4, "uniform"),
-                                         (2, "lloyd", 2, "uniform"), (3, "lloyd_qjl", 3, "lloyd")])
+                                         (2, "lloyd", 2, "uniform"), (3, "lloyd_qjl", 3, "lloyd"),
+                                         (8, "fp8", 4, "uniform"), (8, "fp8", 3, "uniform")])
 def test_layout_matches_format(kb, km, vb, vm):
     lay = tq.layout_for_config(tq.make_config(128, 8, 32, kb, km, vb, vm)).as_dict()
     f = O.page_fields(O.Config(128, 8, 32, kb, km, vb, vm))
@@ -90,7 +95,7 @@ def test_layout_matches_format(kb, km, vb, vm):
     assert lay["page_bytes"] == O.page_bytes(O.Config(128, 8, 32, kb, km, vb, vm))
     assert lay["token_head_bytes"] * 16 == lay["page_bytes"]
     assert (lay["off_kcodes"], lay["row_kcodes"]) == f["kcodes"]
-    assert lay["off_knorm"] == f["knorm"][0]
+    assert lay["off_knorm"] == (f["knorm"][0] if km != "fp8" else none)
     assert (lay["off_vcodes"], lay["row_vcodes"]) == f["vcodes"]
     if km == "lloyd_qjl":
         assert (lay["off_ksigns"], lay["row_ksigns"]) == f["ksigns"]
