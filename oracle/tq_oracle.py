@@ -110,7 +110,11 @@ def lloyd_max_standard_normal(bits: int, tol: float = 1e-15, max_iter: int = 2_0
     for i in range(k):
         a, b = edges[i], edges[i + 1]
         c[i] = (_phi(a) - (0.0 if np.isinf(b) else _phi(b))) / (_upper_tail(a)[0] - _upper_tail(b)[0])
-    for _ in range(max_iter):
+    # With many levels the alternation converges slowly (its error contracts by
+    # about 1 - O(1/k^2) per round); from 5 bits on a bounded number of rounds is
+    # followed by Newton's method on the same fixpoint equations.
+    rounds = max_iter if bits <= 4 else 2000
+    for _ in range(rounds):
         t = np.concatenate([[0.0], 0.5 * (c[:-1] + c[1:]), [np.inf]])
         upper = _upper_tail(t)
         dens = _phi(t[:-1]) - _phi(t[1:])          # phi(inf) = 0
@@ -119,10 +123,42 @@ def lloyd_max_standard_normal(bits: int, tol: float = 1e-15, max_iter: int = 2_0
         c = c_new
         if step < tol:
             break
+    if bits > 4:
+        c = _lloyd_newton(c, tol)
     pos_t = 0.5 * (c[:-1] + c[1:])
     centroids = np.concatenate([-c[::-1], c])
     thresholds = np.concatenate([-pos_t[::-1], [0.0], pos_t])
     return centroids, thresholds
+
+
+def _lloyd_newton(c: np.ndarray, tol: float, max_steps: int = 60) -> np.ndarray:
+    """Newton's method on G(c) = c - m(c) = 0 for the positive centroids c, where
+    m_i is the mean of N(0,1) on the cell (a_i, b_i) whose edges are the midpoints
+    a_i = (c_{i-1} + c_i)/2 (a_0 = 0) and b_i = (c_i + c_{i+1})/2 (last b = inf).
+    The mean of a cell moves with its edges as dm/da = phi(a)(m - a)/P and
+    dm/db = phi(b)(b - m)/P (P = the cell's mass), so the Jacobian of G is
+    tridiagonal."""
+    k = c.shape[0]
+    for _ in range(max_steps):
+        t = np.concatenate([[0.0], 0.5 * (c[:-1] + c[1:]), [np.inf]])
+        a, b = t[:-1], t[1:]
+        upper = _upper_tail(t)
+        P = upper[:-1] - upper[1:]
+        m = (_phi(a) - _phi(b)) / P
+        G = c - m
+        dA = _phi(a) * (m - a) / P
+        dA[0] = 0.0                                 # a_0 = 0 does not move
+        dB = np.where(np.isinf(b), 0.0, _phi(np.where(np.isinf(b), 0.0, b)) * (b - m) / P)
+        J = np.zeros((k, k))
+        idx = np.arange(k)
+        J[idx, idx] = 1.0 - 0.5 * dA - 0.5 * dB
+        J[idx[1:], idx[1:] - 1] = -0.5 * dA[1:]
+        J[idx[:-1], idx[:-1] + 1] = -0.5 * dB[:-1]
+        delta = np.linalg.solve(J, G)
+        c = c - delta
+        if np.max(np.abs(delta)) < tol:
+            break
+    return c
 
 
 @dataclasses.dataclass(frozen=True)
