@@ -24,6 +24,8 @@ Other workloads (--workload):
                   2-bit values (a second asymmetric preset), same step;
   k8v4            the GQA shape with FP8 (E4M3) keys and 4-bit values (the
                   preset table's k8v4), same step;
+  turbo8v3        the GQA shape with 8-bit Lloyd-Max keys (corrected norm) and
+                  3-bit values (an on-device default named on the pages), same step;
   dequant_layer   the prefill_append cache (131072 tokens x 8 KV heads)
                   reconstructed into a bf16 buffer (--dequant-f32: fp32) in one
                   tq_dequantize_rows call: the whole-cache reconstruction that
@@ -63,6 +65,7 @@ MODES = {
     "k3v4_nc": ("k3v4_nc", "decode"),
     "k3qjl_v2": ("k3qjl_v2", "decode"),
     "k8v4": ("k8v4", "decode"),
+    "turbo8v3": ("turbo8v3", "decode"),
 }
 
 

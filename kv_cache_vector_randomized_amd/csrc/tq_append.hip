@@ -23,10 +23,17 @@ namespace tq {
 // ---------------------------------------------------------------------------
 template <int KB, bool QJL, bool BF16>
 __global__ __launch_bounds__(256) void append_keys_kernel(AppendArgs a) {
-  __shared__ QLut lut[kLutCells];
+  constexpr bool WIDE = KB == 8;   // 8-bit codes: binary search over the thresholds instead of the grid
+  __shared__ QLut lut[WIDE ? 1 : kLutCells];
+  __shared__ float kt8[WIDE ? 256 : 1], kc8[WIDE ? 256 : 1];
   __shared__ float rbuf[QJL ? 4 : 1][QJL ? 64 : 1][QJL ? 33 : 1];
   __shared__ uint32_t sbits[QJL ? 4 : 1][QJL ? 64 : 1][4];
-  for (int i = threadIdx.x; i < kLutCells; i += blockDim.x) lut[i] = a.c->klut[i];
+  if constexpr (WIDE) {
+    kt8[threadIdx.x] = a.c->kt[threadIdx.x];   // blockDim.x == 256
+    kc8[threadIdx.x] = a.c->kc[threadIdx.x];
+  } else {
+    for (int i = threadIdx.x; i < kLutCells; i += blockDim.x) lut[i] = a.c->klut[i];
+  }
   __syncthreads();
 
   const int64_t th = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -48,7 +55,7 @@ __global__ __launch_bounds__(256) void append_keys_kernel(AppendArgs a) {
   uint32_t w[KB * 4];
   float cn2;
   float cres[QJL ? kDim : 1];
-  const float n = lloyd_codes<KB, QJL>(x, sb, lut, a.klut_scale, a.klut_bias, w, cn2, cres);
+  const float n = lloyd_codes<KB, QJL>(x, sb, lut, a.klut_scale, a.klut_bias, w, cn2, cres, kt8, kc8);
   const float nhat = (a.key_nc && !QJL) ? n / sqrtf(cn2) : n;
 
   uint8_t* page = nullptr;
@@ -741,6 +748,7 @@ hipError_t launch_append(const AppendArgs& a, int dtype, int key_bits, int key_m
   }
   hipError_t e;
   switch (key_bits) {
+    case 8: e = keys_for_dtype<8, false>(a, dtype, s); break;   // 8-bit Lloyd-Max keys (no QJL)
     case 2: e = keys_mode<2>(a, dtype, key_mode, s); break;
     case 3: e = keys_mode<3>(a, dtype, key_mode, s); break;
     case 4: e = keys_mode<4>(a, dtype, key_mode, s); break;

@@ -147,7 +147,7 @@ __device__ __forceinline__ void load_key_codes(KeyTile<KB, QJL>& r, const Decode
   for (int pg = 0; pg < 4; ++pg) {
     const uint8_t* page = a.cache + page_offset(tp.b[pg], kvh, blk_stride, head_stride);
     const uint8_t* row = page + a.f.kcodes + j * (16 * KB) + g * (4 * KB);
-    if constexpr (KB == 8) {   // FP8 keys: 32 bytes
+    if constexpr (KB == 8) {   // 8-bit codes or FP8 keys: 32 bytes
       const uint4 u = reinterpret_cast<const uint4*>(row)[0], w = reinterpret_cast<const uint4*>(row)[1];
       r.kc[pg][0] = u.x; r.kc[pg][1] = u.y; r.kc[pg][2] = u.z; r.kc[pg][3] = u.w;
       r.kc[pg][4] = w.x; r.kc[pg][5] = w.y; r.kc[pg][6] = w.z; r.kc[pg][7] = w.w;
@@ -166,14 +166,14 @@ __device__ __forceinline__ void load_key_codes(KeyTile<KB, QJL>& r, const Decode
   }
 }
 
-template <int KB, bool QJL, bool VLM>
+template <int KB, bool QJL, bool VLM, bool FP8>
 __device__ __forceinline__ void load_key_scalars(KeyTile<KB, QJL>& r, const DecodeArgs& a, const TilePages& tp,
                                                  int kvh, int lane, int64_t blk_stride, int64_t head_stride) {
   const int j = lane & 15;
 #pragma unroll
   for (int pg = 0; pg < 4; ++pg) {
     const uint8_t* page = a.cache + page_offset(tp.b[pg], kvh, blk_stride, head_stride);
-    r.knorm[pg] = KB == 8 ? 1.f : reinterpret_cast<const float*>(page + a.f.knorm)[j];   // FP8: no norm
+    r.knorm[pg] = FP8 ? 1.f : reinterpret_cast<const float*>(page + a.f.knorm)[j];   // FP8: no norm
     r.va[pg] = reinterpret_cast<const float*>(page + a.f.vmin)[j];
     r.vb[pg] = VLM ? 0.f : reinterpret_cast<const float*>(page + a.f.vscale)[j];
     r.kres[pg] = QJL ? reinterpret_cast<const float*>(page + a.f.kres)[j] : 0.f;
@@ -196,10 +196,11 @@ __device__ __forceinline__ void load_value_group(uint4 (&vq)[VB], const DecodeAr
 // each code in coordinate order, hi first.  Interleaving the terms along K lets
 // one MFMA add both terms of the centroid: the query terms are duplicated to
 // match (see qd below).
-template <int KB>
+template <int KB, bool FP8>
 struct KeyTable {
-  static constexpr int kEntries = KB == 8 ? 1 : KB == 3 ? 64 : 256;   // FP8 keys need none
-  static constexpr int kWords = KB == 8 ? 1 : KB == 2 ? 4 : 2;
+  static constexpr int kEntries = FP8 ? 1 : KB == 3 ? 64 : 256;   // FP8 keys need none
+  static constexpr int kWords = FP8 || KB == 8 ? 1 : KB == 2 ? 4 : 2;
+  static constexpr int kCodes = KB == 2 ? 4 : KB == 8 ? 1 : 2;     // codes per entry (per byte of codes)
 };
 
 // FP8 keys: B operand of the logits MFMA for coordinates 32g + 8*KAP .. +7 of this
@@ -225,7 +226,10 @@ __device__ __forceinline__ uint4 fp8_key_operand(const uint32_t (&kc)[8]) {
 template <int KB, int KAP>
 __device__ __forceinline__ uint4 key_operand(const uint32_t (&kc)[KB], const uint32_t* tab) {
   const char* t = reinterpret_cast<const char*>(tab);
-  if constexpr (KB == 4) {
+  if constexpr (KB == 8) {   // one code per byte, one word per code
+    const uint32_t x = kc[KAP];
+    return make_uint4(tab[x & 0xFFu], tab[(x >> 8) & 0xFFu], tab[(x >> 16) & 0xFFu], tab[x >> 24]);
+  } else if constexpr (KB == 4) {
     const uint32_t x = kc[KAP >> 1];
     const uint2 e0 = *reinterpret_cast<const uint2*>(t + byte_shl<3, 2 * (KAP & 1)>(x));
     const uint2 e1 = *reinterpret_cast<const uint2*>(t + byte_shl<3, 2 * (KAP & 1) + 1>(x));
@@ -345,14 +349,14 @@ __device__ __forceinline__ uint32_t interleave16(uint32_t e, uint32_t o) {
 // returns their key centroids (c0, c1), the stored norm, the QJL residual norm and
 // the signs (+1/-1) of rows 2l, 2l+1 of S r'; the dequantized value row goes to
 // vhat.  codes / rbuf are LDS scratch of the wave.
-template <int KB, bool QJL, int VB>
+template <int KB, bool QJL, int VB, bool FP8>
 __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, float v0, float v1, int lane,
                                    uint8_t* page, int so, uint8_t (&codes)[2][kDim], float* vhat, float* rbuf,
                                    float& c0, float& c1, float& nhat, float& rho, float& sgn0, float& sgn1) {
   rho = 0.f;
   sgn0 = sgn1 = 1.f;
   int kc0 = 0, kc1 = 0;
-  if constexpr (KB == 8) {
+  if constexpr (FP8) {
     // FP8 keys: the E4M3 bytes of the coordinates, their values for the logit
     const uint32_t b0 = fp8_e4m3(k0), b1 = fp8_e4m3(k1);
     typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -378,8 +382,13 @@ __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, floa
   }
   const float ss = wave_sum(fmaf(x0, x0, x1 * x1));
   const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;     // a zero key gives codes 2^(b-1)
-  kc0 = lut_code(a.c->klut, x0 * inv, a.klut_scale, a.klut_bias, c0);
-  kc1 = lut_code(a.c->klut, x1 * inv, a.klut_scale, a.klut_bias, c1);
+  if constexpr (KB == 8) {
+    kc0 = code_bsearch8(a.c->kt, a.c->kc, x0 * inv, c0);
+    kc1 = code_bsearch8(a.c->kt, a.c->kc, x1 * inv, c1);
+  } else {
+    kc0 = lut_code(a.c->klut, x0 * inv, a.klut_scale, a.klut_bias, c0);
+    kc1 = lut_code(a.c->klut, x1 * inv, a.klut_scale, a.klut_bias, c1);
+  }
   const float nk = sqrtf(ss) * kInvSqrtDim;               // ||k||
   const float c2 = wave_sum(fmaf(c0, c0, c1 * c1));
   nhat = (!QJL && a.key_nc) ? (nk > 0.f ? nk / sqrtf(c2) : 0.f) : nk;
@@ -419,23 +428,35 @@ __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, floa
   codes[1][2 * lane] = (uint8_t)vc0;
   codes[1][2 * lane + 1] = (uint8_t)vc1;
   wave_sync_lds();
-  if (KB != 8 && lane < 16 * KB) page[a.f.kcodes + so * 16 * KB + lane] = (uint8_t)stream_byte<KB>(codes[0], lane);
+  if constexpr (KB == 8) {
+    // 8-bit codes (and FP8 above): one byte per coordinate, the lane's two bytes
+    if (!FP8) *reinterpret_cast<uint16_t*>(page + a.f.kcodes + so * kDim + 2 * lane) = (uint16_t)(kc0 | (kc1 << 8));
+  } else if (lane < 16 * KB) {
+    page[a.f.kcodes + so * 16 * KB + lane] = (uint8_t)stream_byte<KB>(codes[0], lane);
+  }
   if (lane < 16 * VB) page[a.f.vcodes + 16 * lane + so] = (uint8_t)stream_byte<VB>(codes[1], lane);
   if (lane == 0) {
-    if (KB != 8) reinterpret_cast<float*>(page + a.f.knorm)[so] = nhat;
+    if (!FP8) reinterpret_cast<float*>(page + a.f.knorm)[so] = nhat;
     reinterpret_cast<float*>(page + a.f.vmin)[so] = mn;
     reinterpret_cast<float*>(page + a.f.vscale)[so] = sc;
     if constexpr (QJL) reinterpret_cast<float*>(page + a.f.kres)[so] = rho;
   }
 }
 
-template <int KB, bool QJL, int VB, bool VLM>
+// Key formats of the kernel (template parameter KM).
+constexpr int kKmLloyd = 0;   // Lloyd-Max codes with a stored norm (plain or corrected)
+constexpr int kKmQjl = 1;     // Lloyd-Max codes + QJL residual signs and norm
+constexpr int kKmFp8 = 2;     // E4M3 bytes of the raw key (KB = 8)
+
+template <int KB, int KM, int VB, bool VLM>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
+  constexpr bool QJL = KM == kKmQjl;
+  constexpr bool FP8 = KM == kKmFp8;   // FP8 keys: no rotation, no codebook, no norm
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j16 = lane & 15, grp = lane >> 4;   // column (token of a page) and row group (head) of the lane
 
-  using Tab = KeyTable<KB>;
+  using Tab = KeyTable<KB, FP8>;
   // Shared by the 4 waves: the f16 terms of the rotated query rows ([head][term]
   // [coordinate], each half duplicated into both halves of a word to meet the
   // two centroid terms; the 4th term is zero) and of their QJL projections
@@ -495,13 +516,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   // wave) is loaded before the query is rotated, so that its latency overlaps the
   // rotation, the tables and the barrier.  Block-table reads do not wait for the
   // sequence length: entries past the end are dropped once it is known.
-  constexpr bool FP8 = KB == 8;   // FP8 keys: no rotation, no codebook, no norm
-  const float kc_top = FP8 ? 1.f : a.c->kc[((1 << KB) - 1) & 15];
-  float kc_e[KB == 2 ? 4 : 2];
+  const float kc_top = FP8 ? 1.f : a.c->kc[(1 << KB) - 1];
+  float kc_e[Tab::kCodes];
   if constexpr (!FP8) {
-    const int ent = tid & (KeyTable<KB>::kEntries - 1);
+    const int ent = tid & (Tab::kEntries - 1);
 #pragma unroll
-    for (int i = 0; i < (KB == 2 ? 4 : 2); ++i) kc_e[i] = a.c->kc[(ent >> (KB * i)) & ((1 << KB) - 1)];
+    for (int i = 0; i < Tab::kCodes; ++i) kc_e[i] = a.c->kc[(ent >> (KB * i)) & ((1 << KB) - 1)];
   }
   // Loads of the prologue are unconditional (heads >= G read head 0 and are
   // zeroed, a wave without a tile reads block 0): conditional loads would make
@@ -552,17 +572,17 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   uint4 vp[VB == 3 ? 8 : 4];     // Lloyd-Max values: byte planes of coordinates 2*lane, 2*lane+1
   uint4 vq[VB];                  // uniform values: the planes of coordinates 8j..8j+7 of page lane/16
   load_key_codes<KB, QJL>(nx, a, tp, kvh, lane, blk_stride, head_stride);
-  load_key_scalars<KB, QJL, VLM>(nx, a, tp, kvh, lane, blk_stride, head_stride);
+  load_key_scalars<KB, QJL, VLM, FP8>(nx, a, tp, kvh, lane, blk_stride, head_stride);
   if constexpr (VLM) load_value_planes<VB>(vp, a, tp, kvh, lane, blk_stride, head_stride);
   else load_value_group<VB>(vq, a, vblk, kvh, lane, blk_stride, head_stride);
 
   // Key centroid table: C * 2^s2 with 2^s2 bringing the largest |C| (the last,
   // the codebook being symmetric) into [2^14, 2^15).
   const int s2 = FP8 ? 0 : 15 - __builtin_amdgcn_frexp_expf(kc_top);
-  if (!FP8 && tid < KeyTable<KB>::kEntries) {
+  if (!FP8 && tid < Tab::kEntries) {
     uint32_t* e = &ktab[tid * Tab::kWords];
 #pragma unroll
-    for (int i = 0; i < (KB == 2 ? 4 : 2); ++i) {
+    for (int i = 0; i < Tab::kCodes; ++i) {
       float hi, lo, unused;
       split_f16(ldexpf(kc_e[i], s2), hi, lo, unused);
       e[i] = f16bits(hi) | (f16bits(lo) << 16);
@@ -690,7 +710,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     if (own_new && wave == kMaxGroup) {
       float nt_c0, nt_c1, nt_nhat, nt_rho, nt_s0, nt_s1;
       uint8_t* page = const_cast<uint8_t*>(a.cache) + (int64_t)new_blk * blk_stride + kvh * head_stride;
-      new_token_quantize<KB, QJL, VB>(a, nt_k0, nt_k1, nt_v0, nt_v1, lane, page, (seq_len - 1) & 15, nt_codes,
+      new_token_quantize<KB, QJL, VB, FP8>(a, nt_k0, nt_k1, nt_v0, nt_v1, lane, page, (seq_len - 1) & 15, nt_codes,
                                       nt_vhat, nt_r, nt_c0, nt_c1, nt_nhat, nt_rho, nt_s0, nt_s1);
       // the new token's base-2 logit for each head, then the wave's softmax state
       // starts from it (weight 1 at its own max)
@@ -829,7 +849,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
       l_lane += pr[pg];
       if (!VLM) s_lane = fmaf(pr[pg], va[pg], s_lane);
     }
-    load_key_scalars<KB, QJL, VLM>(nx, a, tpn, kvh, lane, blk_stride, head_stride);
+    load_key_scalars<KB, QJL, VLM, FP8>(nx, a, tpn, kvh, lane, blk_stride, head_stride);
     if constexpr (VLM) {
 #pragma unroll
       for (int pg = 0; pg < 4; ++pg) wt[grp][16 * pg + j16] = __float_as_uint(pr[pg] * va[pg]);
@@ -1021,45 +1041,46 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
 
 namespace {
 
-template <int KB, bool QJL, int VB>
+template <int KB, int KM, int VB>
 hipError_t decode_v(const DecodeArgs& a, int val_mode, hipStream_t s) {
   const dim3 grid((unsigned)a.splits, (unsigned)a.hkv, (unsigned)a.batch);
   if (val_mode == TQ_VAL_LLOYD) {
-    if constexpr (KB == 8) return hipErrorInvalidValue;   // FP8 keys pair with uniform values
-    else hipLaunchKernelGGL((decode_kernel<KB, QJL, VB, true>), grid, dim3(64 * kDecodeWaves), 0, s, a);
+    if constexpr (KB == 8) return hipErrorInvalidValue;   // 8-bit and FP8 keys pair with uniform values
+    else hipLaunchKernelGGL((decode_kernel<KB, KM, VB, true>), grid, dim3(64 * kDecodeWaves), 0, s, a);
   } else {
-    hipLaunchKernelGGL((decode_kernel<KB, QJL, VB, false>), grid, dim3(64 * kDecodeWaves), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<KB, KM, VB, false>), grid, dim3(64 * kDecodeWaves), 0, s, a);
   }
   return hipGetLastError();
 }
 
-template <int KB, bool QJL>
+template <int KB, int KM>
 hipError_t decode_vb(const DecodeArgs& a, int val_bits, int val_mode, hipStream_t s) {
   switch (val_bits) {
-    case 2: return decode_v<KB, QJL, 2>(a, val_mode, s);
-    case 3: return decode_v<KB, QJL, 3>(a, val_mode, s);
-    case 4: return decode_v<KB, QJL, 4>(a, val_mode, s);
+    case 2: return decode_v<KB, KM, 2>(a, val_mode, s);
+    case 3: return decode_v<KB, KM, 3>(a, val_mode, s);
+    case 4: return decode_v<KB, KM, 4>(a, val_mode, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <int KB, bool QJL>
+template <int KB, int KM>
 const void* kernel_vb(int val_bits, int val_mode) {
   const bool lm = val_mode == TQ_VAL_LLOYD;
   if constexpr (KB == 8) {
+    if (lm) return nullptr;
     switch (val_bits) {
-      case 2: return (const void*)decode_kernel<8, false, 2, false>;
-      case 3: return (const void*)decode_kernel<8, false, 3, false>;
-      case 4: return (const void*)decode_kernel<8, false, 4, false>;
+      case 2: return (const void*)decode_kernel<8, KM, 2, false>;
+      case 3: return (const void*)decode_kernel<8, KM, 3, false>;
+      case 4: return (const void*)decode_kernel<8, KM, 4, false>;
     }
     return nullptr;
   } else {
-  switch (val_bits) {
-    case 2: return lm ? (const void*)decode_kernel<KB, QJL, 2, true> : (const void*)decode_kernel<KB, QJL, 2, false>;
-    case 3: return lm ? (const void*)decode_kernel<KB, QJL, 3, true> : (const void*)decode_kernel<KB, QJL, 3, false>;
-    case 4: return lm ? (const void*)decode_kernel<KB, QJL, 4, true> : (const void*)decode_kernel<KB, QJL, 4, false>;
-  }
-  return nullptr;
+    switch (val_bits) {
+      case 2: return lm ? (const void*)decode_kernel<KB, KM, 2, true> : (const void*)decode_kernel<KB, KM, 2, false>;
+      case 3: return lm ? (const void*)decode_kernel<KB, KM, 3, true> : (const void*)decode_kernel<KB, KM, 3, false>;
+      case 4: return lm ? (const void*)decode_kernel<KB, KM, 4, true> : (const void*)decode_kernel<KB, KM, 4, false>;
+    }
+    return nullptr;
   }
 }
 
@@ -1067,11 +1088,13 @@ const void* kernel_vb(int val_bits, int val_mode) {
 
 const void* decode_kernel_ptr(int key_bits, int key_mode, int val_bits, int val_mode) {
   const bool qjl = key_mode == TQ_KEY_LLOYD_QJL;
-  if (key_mode == TQ_KEY_FP8) return key_bits == 8 && val_mode == TQ_VAL_UNIFORM ? kernel_vb<8, false>(val_bits, val_mode) : nullptr;
   switch (key_bits) {
-    case 2: return qjl ? kernel_vb<2, true>(val_bits, val_mode) : kernel_vb<2, false>(val_bits, val_mode);
-    case 3: return qjl ? kernel_vb<3, true>(val_bits, val_mode) : kernel_vb<3, false>(val_bits, val_mode);
-    case 4: return qjl ? kernel_vb<4, true>(val_bits, val_mode) : kernel_vb<4, false>(val_bits, val_mode);
+    case 8:
+      if (qjl) return nullptr;
+      return key_mode == TQ_KEY_FP8 ? kernel_vb<8, kKmFp8>(val_bits, val_mode) : kernel_vb<8, kKmLloyd>(val_bits, val_mode);
+    case 2: return qjl ? kernel_vb<2, kKmQjl>(val_bits, val_mode) : kernel_vb<2, kKmLloyd>(val_bits, val_mode);
+    case 3: return qjl ? kernel_vb<3, kKmQjl>(val_bits, val_mode) : kernel_vb<3, kKmLloyd>(val_bits, val_mode);
+    case 4: return qjl ? kernel_vb<4, kKmQjl>(val_bits, val_mode) : kernel_vb<4, kKmLloyd>(val_bits, val_mode);
   }
   return nullptr;
 }
@@ -1079,12 +1102,15 @@ const void* decode_kernel_ptr(int key_bits, int key_mode, int val_bits, int val_
 hipError_t launch_decode(const DecodeArgs& a, int key_bits, int key_mode, int val_bits, int val_mode,
                          hipStream_t s) {
   const bool qjl = key_mode == TQ_KEY_LLOYD_QJL;
-  if (key_mode == TQ_KEY_FP8)
-    return key_bits == 8 && val_mode == TQ_VAL_UNIFORM ? decode_vb<8, false>(a, val_bits, val_mode, s) : hipErrorInvalidValue;
+  if (key_mode == TQ_KEY_FP8 && key_bits != 8) return hipErrorInvalidValue;
   switch (key_bits) {
-    case 2: return qjl ? decode_vb<2, true>(a, val_bits, val_mode, s) : decode_vb<2, false>(a, val_bits, val_mode, s);
-    case 3: return qjl ? decode_vb<3, true>(a, val_bits, val_mode, s) : decode_vb<3, false>(a, val_bits, val_mode, s);
-    case 4: return qjl ? decode_vb<4, true>(a, val_bits, val_mode, s) : decode_vb<4, false>(a, val_bits, val_mode, s);
+    case 8:
+      if (qjl) return hipErrorInvalidValue;
+      return key_mode == TQ_KEY_FP8 ? decode_vb<8, kKmFp8>(a, val_bits, val_mode, s)
+                                    : decode_vb<8, kKmLloyd>(a, val_bits, val_mode, s);
+    case 2: return qjl ? decode_vb<2, kKmQjl>(a, val_bits, val_mode, s) : decode_vb<2, kKmLloyd>(a, val_bits, val_mode, s);
+    case 3: return qjl ? decode_vb<3, kKmQjl>(a, val_bits, val_mode, s) : decode_vb<3, kKmLloyd>(a, val_bits, val_mode, s);
+    case 4: return qjl ? decode_vb<4, kKmQjl>(a, val_bits, val_mode, s) : decode_vb<4, kKmLloyd>(a, val_bits, val_mode, s);
   }
   return hipErrorInvalidValue;
 }

@@ -158,13 +158,16 @@ __device__ __forceinline__ void table_lookup(const float* tbl, uint32_t w, float
   }
 }
 
-// Table entries: B = 4: 256 float pairs; B = 2: 256 float quads; B = 3: 8 floats.
+// Table entries: B = 4: 256 float pairs; B = 2: 256 float quads; B = 3: 8 floats;
+// B = 8: 256 floats (one code per byte, read straight from the raw words).
 template <int B>
-constexpr int table_floats() { return B == 4 ? 512 : (B == 2 ? 1024 : 8); }
+constexpr int table_floats() { return B == 8 ? 256 : B == 4 ? 512 : (B == 2 ? 1024 : 8); }
 
 template <int B>
 __device__ __forceinline__ void build_table(float* tbl, const float* c, int tid) {
-  if constexpr (B == 4) {
+  if constexpr (B == 8) {
+    tbl[tid] = c[tid];   // 256 threads, one code each
+  } else if constexpr (B == 4) {
     tbl[2 * tid] = c[tid & 15];
     tbl[2 * tid + 1] = c[tid >> 4];
   } else if constexpr (B == 2) {
@@ -200,14 +203,18 @@ __device__ __forceinline__ void store_part(void* buf, int64_t elem, int p, const
 
 // x = scale * s (.) H C[code] for one Lloyd-Max row from its group words; sgn
 // bit i = sign to apply to value i (the rotation's sign of its coordinate times rho).
+__device__ __forceinline__ void rotate_scale(float (&x)[16], float scale, uint32_t sgn, int lane) {
+  wht_part(x, lane);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) x[e] = __uint_as_float(__float_as_uint(x[e] * scale) ^ (((sgn >> e) & 1u) << 31));
+}
+
 template <int B, int G>
 __device__ __forceinline__ void lloyd_part(const uint32_t* words, const float* tbl, float scale, uint32_t sgn,
                                            int lane, float (&x)[16]) {
 #pragma unroll
   for (int m = 0; m < 16 / G; ++m) table_lookup<B, G>(tbl, words[m], x + G * m);
-  wht_part(x, lane);
-#pragma unroll
-  for (int e = 0; e < 16; ++e) x[e] = __uint_as_float(__float_as_uint(x[e] * scale) ^ (((sgn >> e) & 1u) << 31));
+  rotate_scale(x, scale, sgn, lane);
 }
 
 // Raw fields of one list entry: key and value group bytes (or words) and scalars.
@@ -219,7 +226,7 @@ struct Raw {
 };
 
 // Read the fields of slot `so` of a page (in global memory or staged in LDS).
-template <int KB, int VB, int G, bool VLM>
+template <int KB, int VB, int G, bool VLM, bool FP8>
 __device__ __forceinline__ void load_raw(const uint8_t* pg, const FieldOffsets& f, int so, int p,
                                          Raw<KB, VB, G>& r) {
 #pragma unroll
@@ -227,21 +234,21 @@ __device__ __forceinline__ void load_raw(const uint8_t* pg, const FieldOffsets& 
     load_key_group<KB, G>(pg + f.kcodes + so * (KB * 16), p, m, r.k[m]);
     load_value_group<VB, G>(pg + f.vcodes + so, p, m, r.v[m]);
   }
-  r.knrm = KB == 8 ? 1.f : reinterpret_cast<const float*>(pg + f.knorm)[so];
+  r.knrm = FP8 ? 1.f : reinterpret_cast<const float*>(pg + f.knorm)[so];
   r.vmn = reinterpret_cast<const float*>(pg + f.vmin)[so];
   r.vsc = VLM ? 0.f : reinterpret_cast<const float*>(pg + f.vscale)[so];
 }
 
 // Reconstruct one entry from its raw fields (ok = 0 gives zeros) and store it to
 // row rw when rw is inside the buffer.
-template <int KB, int VB, int G, bool VLM, bool BF16OUT>
+template <int KB, int VB, int G, bool VLM, bool BF16OUT, bool FP8>
 __device__ __forceinline__ void finish(const DequantArgs& a, const Raw<KB, VB, G>& r, bool ok, int64_t rw, uint32_t h,
                                        const float* ktbl, const float* vtbl, uint32_t sgn, int lane, int p) {
   uint32_t vw[16 / G];
 #pragma unroll
   for (int m = 0; m < 16 / G; ++m) vw[m] = group_word<VB, G, false>(r.v[m], p, m);
   float xk[16], xv[16];
-  if constexpr (KB == 8) {
+  if constexpr (FP8) {
     // FP8 keys: the E4M3 values themselves (exact conversions), no rotation
     typedef float f32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
@@ -253,6 +260,15 @@ __device__ __forceinline__ void finish(const DequantArgs& a, const Raw<KB, VB, G
         float* y = xk + G * m + 4 * i;
         y[0] = ok ? lo.x : 0.f; y[1] = ok ? lo.y : 0.f; y[2] = ok ? hi.x : 0.f; y[3] = ok ? hi.y : 0.f;
       }
+  } else if constexpr (KB == 8) {
+    // 8-bit codes: one table read per byte of the raw words, then the rotation
+#pragma unroll
+    for (int m = 0; m < 16 / G; ++m)
+#pragma unroll
+      for (int i = 0; i < G / 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xk[G * m + 4 * i + e] = ktbl[(r.k[m][i] >> (8 * e)) & 0xFFu];
+    rotate_scale(xk, ok ? r.knrm * kInvSqrtDim : 0.f, sgn, lane);
   } else {
     uint32_t kw[16 / G];
 #pragma unroll
@@ -281,14 +297,14 @@ __device__ __forceinline__ void finish(const DequantArgs& a, const Raw<KB, VB, G
 // slot order (the usual case when a whole sequence is reconstructed) is read
 // with kStageLoads 16-byte loads per lane, all issued at the start, and staged
 // in LDS; any other group is read entry by entry.
-template <int KB, int VB, bool VLM, bool BF16OUT>
+template <int KB, int VB, bool VLM, bool BF16OUT, bool FP8>
 __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
   __shared__ __align__(16) float ktbl[table_floats<KB>()];
   __shared__ __align__(16) float vtbl[VLM ? table_floats<VB>() : 1];
   constexpr int kGroups = groups_per_wave<BF16OUT>();
   __shared__ __align__(16) uint8_t stage[4][kGroups][kStageBytes];   // a page per group
   const int tid = threadIdx.x;
-  build_table<KB>(ktbl, a.c->kc, tid);
+  if constexpr (!FP8) build_table<KB>(ktbl, a.c->kc, tid);
   if constexpr (VLM) build_table<VB>(vtbl, a.c->vc, tid);
   __syncthreads();
   constexpr int G = BF16OUT ? 8 : 4;   // consecutive coordinates per group
@@ -370,9 +386,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
       const uint8_t* sp = stage[wave][g];
       Raw<KB, VB, G> r[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) load_raw<KB, VB, G, VLM>(sp, a.f, 8 * j + t, p, r[j]);
+      for (int j = 0; j < 2; ++j) load_raw<KB, VB, G, VLM, FP8>(sp, a.f, 8 * j + t, p, r[j]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) finish<KB, VB, G, VLM, BF16OUT>(a, r[j], true, wrow[g][j], h, ktbl, vtbl, sgn, lane, p);
+      for (int j = 0; j < 2; ++j) finish<KB, VB, G, VLM, BF16OUT, FP8>(a, r[j], true, wrow[g][j], h, ktbl, vtbl, sgn, lane, p);
     } else {
       Raw<KB, VB, G> r[2];
       bool ok[2];
@@ -385,10 +401,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
         // an entry without a valid slot reads the (in-bounds) constant block and is zeroed
         const uint32_t pg = (uint32_t)(slot >> 4) * (uint32_t)a.hkv + h;   // < 2^32 for any cache in memory
         const uint8_t* pgp = ok[j] ? a.cache + (uint64_t)pg * pb : reinterpret_cast<const uint8_t*>(a.c);
-        load_raw<KB, VB, G, VLM>(pgp, a.f, ok[j] ? (int)(slot & 15) : 0, p, r[j]);
+        load_raw<KB, VB, G, VLM, FP8>(pgp, a.f, ok[j] ? (int)(slot & 15) : 0, p, r[j]);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) finish<KB, VB, G, VLM, BF16OUT>(a, r[j], ok[j], wrow[g][j], h, ktbl, vtbl, sgn, lane, p);
+      for (int j = 0; j < 2; ++j) finish<KB, VB, G, VLM, BF16OUT, FP8>(a, r[j], ok[j], wrow[g][j], h, ktbl, vtbl, sgn, lane, p);
     }
   }
 }
@@ -397,42 +413,44 @@ namespace {
 
 static_assert(sizeof(DevConsts) >= kMaxPageBytes, "invalid slots read a page's worth of the constant block");
 
-template <int KB, int VB>
+template <int KB, int VB, bool FP8>
 hipError_t dequant_launch(const DequantArgs& a, bool lm, bool bf16, hipStream_t s) {
   const int per_wave = 16 * (bf16 ? groups_per_wave<true>() : groups_per_wave<false>());
   const int64_t items = (a.n + per_wave - 1) / per_wave * a.hkv;
   const dim3 grid((unsigned)((items + 3) / 4));
   if (lm) {
-    if constexpr (KB == 8) return hipErrorInvalidValue;   // FP8 keys pair with uniform values
-    else if (bf16) hipLaunchKernelGGL((dequant_kernel<KB, VB, true, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((dequant_kernel<KB, VB, true, false>), grid, dim3(256), 0, s, a);
+    if constexpr (KB == 8) return hipErrorInvalidValue;   // 8-bit and FP8 keys pair with uniform values
+    else if (bf16) hipLaunchKernelGGL((dequant_kernel<KB, VB, true, true, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((dequant_kernel<KB, VB, true, false, false>), grid, dim3(256), 0, s, a);
   } else {
-    if (bf16) hipLaunchKernelGGL((dequant_kernel<KB, VB, false, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((dequant_kernel<KB, VB, false, false>), grid, dim3(256), 0, s, a);
+    if (bf16) hipLaunchKernelGGL((dequant_kernel<KB, VB, false, true, FP8>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((dequant_kernel<KB, VB, false, false, FP8>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
 
-template <int KB>
+template <int KB, bool FP8>
 hipError_t dequant_vb(const DequantArgs& a, int val_bits, bool lm, bool bf16, hipStream_t s) {
   switch (val_bits) {
-    case 2: return dequant_launch<KB, 2>(a, lm, bf16, s);
-    case 3: return dequant_launch<KB, 3>(a, lm, bf16, s);
-    case 4: return dequant_launch<KB, 4>(a, lm, bf16, s);
+    case 2: return dequant_launch<KB, 2, FP8>(a, lm, bf16, s);
+    case 3: return dequant_launch<KB, 3, FP8>(a, lm, bf16, s);
+    case 4: return dequant_launch<KB, 4, FP8>(a, lm, bf16, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_dequant(const DequantArgs& a, int key_bits, int val_bits, int val_mode, bool bf16_out,
+hipError_t launch_dequant(const DequantArgs& a, int key_bits, int key_mode, int val_bits, int val_mode, bool bf16_out,
                           hipStream_t s) {
   const bool lm = val_mode == TQ_VAL_LLOYD;
   switch (key_bits) {
-    case 8: return lm ? hipErrorInvalidValue : dequant_vb<8>(a, val_bits, false, bf16_out, s);   // FP8 keys
-    case 2: return dequant_vb<2>(a, val_bits, lm, bf16_out, s);
-    case 3: return dequant_vb<3>(a, val_bits, lm, bf16_out, s);
-    case 4: return dequant_vb<4>(a, val_bits, lm, bf16_out, s);
+    case 8:
+      return key_mode == TQ_KEY_FP8 ? dequant_vb<8, true>(a, val_bits, lm, bf16_out, s)
+                                    : dequant_vb<8, false>(a, val_bits, lm, bf16_out, s);
+    case 2: return dequant_vb<2, false>(a, val_bits, lm, bf16_out, s);
+    case 3: return dequant_vb<3, false>(a, val_bits, lm, bf16_out, s);
+    case 4: return dequant_vb<4, false>(a, val_bits, lm, bf16_out, s);
   }
   return hipErrorInvalidValue;
 }

@@ -76,6 +76,18 @@ __device__ __forceinline__ int lut_code(const QLut* lut, float y, float sc, floa
   return e.base + (up ? 1 : 0);
 }
 
+// 8-bit codes: code = #{j : t_j <= y} by binary search over the 255 ascending
+// thresholds (each step keeps the count of thresholds known to be <= y); also
+// returns C[code].
+__device__ __forceinline__ int code_bsearch8(const float* t, const float* c, float y, float& cv) {
+  int n = 0;
+#pragma unroll
+  for (int step = 128; step >= 1; step >>= 1)
+    if (t[n + step - 1] <= y) n += step;
+  cv = c[n];
+  return n;
+}
+
 // Put code i (B bits) into an LSB-first bit stream held in 32-bit words.
 template <int B>
 __device__ __forceinline__ void put_code(uint32_t (&w)[B * 4], int i, uint32_t code) {
@@ -129,7 +141,7 @@ __device__ __forceinline__ void apply_signs(float (&x)[kDim], const uint32_t (&s
 template <int B, bool KEEP_C>
 __device__ __forceinline__ float lloyd_codes(float (&x)[kDim], const uint32_t (&sb)[4], const QLut* lut,
                                              float lsc, float lbi, uint32_t (&w)[B * 4], float& cn2,
-                                             float* cvals) {
+                                             float* cvals, const float* t8 = nullptr, const float* c8 = nullptr) {
   apply_signs(x, sb);
   const float n = sqrtf(sum_squares(x));
   wht128(x);
@@ -140,7 +152,7 @@ __device__ __forceinline__ float lloyd_codes(float (&x)[kDim], const uint32_t (&
 #pragma unroll
   for (int i = 0; i < kDim; ++i) {
     float c;
-    const int code = lut_code(lut, x[i] * inv, lsc, lbi, c);
+    const int code = B == 8 ? code_bsearch8(t8, c8, x[i] * inv, c) : lut_code(lut, x[i] * inv, lsc, lbi, c);
     put_code<B>(w, i, (uint32_t)code);
     if (i & 1) a1 = fmaf(c, c, a1); else a0 = fmaf(c, c, a0);
     if (KEEP_C) cvals[i] = c;

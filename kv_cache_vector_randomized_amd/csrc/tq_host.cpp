@@ -62,7 +62,11 @@ void lloyd_max_std(int bits, std::vector<double>& centroids, std::vector<double>
   std::vector<long double> c(half);       // positive centroids, ascending
   for (int i = 0; i < half; ++i) c[i] = (i + 0.5L) * 3.0L / half;
   std::vector<long double> t(half + 1);
-  for (int it = 0; it < 200000; ++it) {
+  // With many levels the alternation contracts its error only by about
+  // 1 - O(1/k^2) per round: from 5 bits on, a bounded number of rounds is followed
+  // by Newton's method on the same equations (below).
+  const int rounds = bits <= 4 ? 200000 : 2000;
+  for (int it = 0; it < rounds; ++it) {
     t[0] = 0.0L;
     t[half] = std::numeric_limits<long double>::infinity();
     for (int i = 1; i < half; ++i) t[i] = 0.5L * (c[i - 1] + c[i]);
@@ -75,6 +79,40 @@ void lloyd_max_std(int bits, std::vector<double>& centroids, std::vector<double>
       c[i] = nc;
     }
     if (moved < 1e-17L) break;
+  }
+  if (bits > 4) {
+    // Newton on G(c) = c - m(c): the mean of a cell moves with its edges as
+    // dm/da = phi(a)(m - a)/P and dm/db = phi(b)(b - m)/P, and the edges are the
+    // midpoints of neighbouring centroids, so the Jacobian is tridiagonal
+    // (solved by elimination down the diagonal).
+    std::vector<long double> lo(half), di(half), up(half), g(half);
+    for (int step = 0; step < 60; ++step) {
+      long double worst = 0.0L;
+      for (int i = 0; i < half; ++i) {
+        const long double a = i == 0 ? 0.0L : 0.5L * (c[i - 1] + c[i]);
+        const bool last = i == half - 1;
+        const long double b = last ? std::numeric_limits<long double>::infinity() : 0.5L * (c[i] + c[i + 1]);
+        const long double P = ntail(a) - ntail(b);
+        const long double m = (npdf(a) - (last ? 0.0L : npdf(b))) / P;
+        const long double dA = i == 0 ? 0.0L : npdf(a) * (m - a) / P;
+        const long double dB = last ? 0.0L : npdf(b) * (b - m) / P;
+        g[i] = c[i] - m;
+        di[i] = 1.0L - 0.5L * dA - 0.5L * dB;
+        lo[i] = -0.5L * dA;
+        up[i] = -0.5L * dB;
+      }
+      for (int i = 1; i < half; ++i) {   // forward elimination
+        const long double f = lo[i] / di[i - 1];
+        di[i] -= f * up[i - 1];
+        g[i] -= f * g[i - 1];
+      }
+      for (int i = half - 1; i >= 0; --i) {   // back substitution: g becomes the step
+        g[i] = (g[i] - (i + 1 < half ? up[i] * g[i + 1] : 0.0L)) / di[i];
+        c[i] -= g[i];
+        worst = std::fmax(worst, std::fabs(g[i]));
+      }
+      if (worst < 1e-17L) break;
+    }
   }
   centroids.assign(levels, 0.0);
   thresholds.assign(levels - 1, 0.0);
@@ -259,8 +297,10 @@ tq_status tq_validate_config(const tq_config* c) {
   if (c->key_mode == TQ_KEY_FP8) {
     if (c->key_bits != 8) return fail(TQ_ERR_INVALID_ARG, "FP8 keys take key_bits 8 (got %u)", c->key_bits);
     if (c->val_mode != TQ_VAL_UNIFORM) return fail(TQ_ERR_UNSUPPORTED, "FP8 keys are built with uniform values only");
+  } else if (c->key_bits == 8) {
+    if (c->key_mode == TQ_KEY_LLOYD_QJL) return fail(TQ_ERR_UNSUPPORTED, "8-bit keys take no QJL residual");
   } else if (c->key_bits < 2 || c->key_bits > 4) {
-    return fail(TQ_ERR_UNSUPPORTED, "key_bits %u: supported 2..4 (8 with FP8 keys)", c->key_bits);
+    return fail(TQ_ERR_UNSUPPORTED, "key_bits %u: supported 2..4 and 8", c->key_bits);
   }
   if (c->val_bits < 2 || c->val_bits > 4) return fail(TQ_ERR_UNSUPPORTED, "val_bits %u: supported 2..4", c->val_bits);
   const uint32_t g = c->num_q_heads / c->num_kv_heads;
@@ -298,15 +338,17 @@ tq_status tq_create(const tq_config* cfg, const int8_t* signs_host, const float*
   if (!h) return fail(TQ_ERR_OUT_OF_MEMORY, "host allocation failed");
   std::memset(h, 0, sizeof *h);
   for (int i = 0; i < d; ++i) h->signs[i] = (float)signs_host[i];
-  float kt[15] = {0}, vt[15] = {0};
+  float vt[15] = {0};
   const bool fp8 = cfg->key_mode == TQ_KEY_FP8;   // no key codebook
-  if (!fp8) codebook_f32((int)cfg->key_bits, d, h->kc, kt);
+  const bool wide = cfg->key_bits > 4;            // 8-bit codes: a binary search over h->kt, no grid
+  if (!fp8) codebook_f32((int)cfg->key_bits, d, h->kc, h->kt);
+  const float* kt = h->kt;
   tq_ctx* ctx = new (std::nothrow) tq_ctx();
   if (!ctx) { delete h; return fail(TQ_ERR_OUT_OF_MEMORY, "host allocation failed"); }
   ctx->cfg = *cfg;
   if ((s = layout_of(cfg, &ctx->layout)) != TQ_OK) { delete h; delete ctx; return s; }
-  bool ok = fp8 || build_lut((int)cfg->key_bits, h->kc, kt, h->klut, &ctx->klut_scale, &ctx->klut_bias);
-  ctx->unit_grid_ok = (!fp8 && build_unit_lut((int)cfg->key_bits, h->kc, kt, h->kulut)) ? 1 : 0;
+  bool ok = fp8 || wide || build_lut((int)cfg->key_bits, h->kc, kt, h->klut, &ctx->klut_scale, &ctx->klut_bias);
+  ctx->unit_grid_ok = (!fp8 && !wide && build_unit_lut((int)cfg->key_bits, h->kc, kt, h->kulut)) ? 1 : 0;
   if (cfg->val_mode == TQ_VAL_LLOYD) {
     codebook_f32((int)cfg->val_bits, d, h->vc, vt);
     ok = ok && build_lut((int)cfg->val_bits, h->vc, vt, h->vlut, &ctx->vlut_scale, &ctx->vlut_bias);
@@ -542,7 +584,7 @@ tq_status tq_dequantize_rows(tq_ctx* ctx, const void* cache, int64_t num_blocks,
   a.cache = (const uint8_t*)cache; a.num_blocks = num_blocks; a.slots = slots; a.rows = rows; a.n = n;
   a.buf_rows = buf_rows; a.hkv = (int32_t)ctx->cfg.num_kv_heads; a.k_out = k_buf; a.v_out = v_buf;
   a.f = offsets_of(ctx->layout); a.c = ctx->consts;
-  hipError_t e = tq::launch_dequant(a, (int)ctx->cfg.key_bits, (int)ctx->cfg.val_bits, (int)ctx->cfg.val_mode,
+  hipError_t e = tq::launch_dequant(a, (int)ctx->cfg.key_bits, (int)ctx->cfg.key_mode, (int)ctx->cfg.val_bits, (int)ctx->cfg.val_mode,
                                     out_dt == TQ_BF16, stream);
   return e == hipSuccess ? TQ_OK : hip_fail(e, "dequantize launch");
 }

@@ -40,7 +40,8 @@ struct QLut {
 // Constants of one context, stored in one device allocation.
 struct DevConsts {
   float signs[kDim];          // +-1 of the rotation
-  float kc[16];               // key centroids (fp32), 2^key_bits used
+  float kc[256];              // key centroids (fp32), 2^key_bits used
+  float kt[256];              // key thresholds (fp32), 2^key_bits - 1 used (8-bit keys search them)
   float vc[16];               // value centroids (Lloyd-Max values only)
   QLut klut[kLutCells];
   QLut vlut[kLutCells];
@@ -130,7 +131,7 @@ hipError_t launch_decode(const DecodeArgs& a, int key_bits, int key_mode, int va
                          hipStream_t s);
 hipError_t launch_transfer(bool to_host, void* cache, void* host, const int32_t* block_ids, int64_t n,
                            int64_t num_blocks, int64_t block_bytes, int grid, hipStream_t s);
-hipError_t launch_dequant(const DequantArgs& a, int key_bits, int val_bits, int val_mode, bool bf16_out,
+hipError_t launch_dequant(const DequantArgs& a, int key_bits, int key_mode, int val_bits, int val_mode, bool bf16_out,
                           hipStream_t s);
 
 }  // namespace tq

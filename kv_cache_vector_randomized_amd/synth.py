@@ -74,6 +74,9 @@ WORKLOADS = {
     # FP8 (E4M3) keys with 4-bit uniform values (the serving engine's k8v4)
     "k8v4": Workload("k8v4", 128, 8, 32, 16, 8192, 8, "fp8", 4, "uniform", "bf16",
                      "2% of channels per KV head x8", 8),
+    # 8-bit Lloyd-Max keys (corrected norm) with 3-bit uniform values (the MLX default turbo8v3)
+    "turbo8v3": Workload("turbo8v3", 128, 8, 32, 16, 8192, 8, "lloyd_nc", 3, "uniform", "bf16",
+                         "2% of channels per KV head x8", 9),
 }
 
 
@@ -110,7 +113,7 @@ def kv_tensor(w: Workload, num_tokens: int, which: str, seed_offset: int = 0) ->
     chan_rng = np.random.Generator(np.random.PCG64([w.seed, 7]))
     if w.name == "toy":
         x[:, :, [3, 17, 64, 100]] *= np.float32(10.0)
-    elif w.name in ("gqa_decode", "k3v4_nc", "k8v4"):
+    elif w.name in ("gqa_decode", "k3v4_nc", "k8v4", "turbo8v3"):
         ch = _outlier_channels(chan_rng, hk, d, int(round(0.02 * d)))
         for h in range(hk):
             x[:, h, ch[h]] *= np.float32(8.0)

@@ -30,6 +30,7 @@ CASES = {
     "k3v4_nc": [200, 1, 64],
     "k3qjl_v2": [129, 30],
     "k8v4": [333, 1, 16, 0],
+    "turbo8v3": [200, 17],
 }
 
 

@@ -42,7 +42,8 @@ def test_status_strings():
     (dict(head_dim=96), tq.TQ_ERR_INVALID_ARG),
     (dict(head_dim=64), tq.TQ_ERR_UNSUPPORTED),
     (dict(key_bits=0), tq.TQ_ERR_INVALID_ARG),
-    (dict(key_bits=8), tq.TQ_ERR_UNSUPPORTED),
+    (dict(key_bits=8), tq.TQ_OK),                    # 8-bit Lloyd-Max keys
+    (dict(key_bits=5), tq.TQ_ERR_UNSUPPORTED),
     (dict(val_bits=1), tq.TQ_ERR_UNSUPPORTED),
     (dict(key_mode=3), tq.TQ_ERR_INVALID_ARG),
     (dict(val_mode=2), tq.TQ_ERR_INVALID_ARG),
@@ -52,6 +53,9 @@ def test_status_strings():
     (dict(key_bits=4, key_mode="fp8"), tq.TQ_ERR_INVALID_ARG),
     (dict(key_bits=8, key_mode="fp8", val_mode="lloyd"), tq.TQ_ERR_UNSUPPORTED),
     (dict(key_mode=4), tq.TQ_ERR_INVALID_ARG),
+    (dict(key_bits=8, key_mode="lloyd_nc", val_bits=3), tq.TQ_OK),
+    (dict(key_bits=8, key_mode="lloyd_qjl"), tq.TQ_ERR_UNSUPPORTED),
+    (dict(key_bits=6), tq.TQ_ERR_UNSUPPORTED),
 ])
 def test_validate_config(kw, expect):
     assert tq.validate_config(tq.make_config(**kw)) == expect
@@ -86,7 +90,8 @@ def test_every_call_refuses_a_null_context():
 @pytest.mark.parametrize("kb,km,vb,vm", [(4, "lloyd", 4, "lloyd"), (4, "lloyd_nc", 4, "uniform"),
                                          (3, "lloyd_nc", 3, "uniform"), (2, "lloyd_qjl", 4, "uniform"),
                                          (2, "lloyd", 2, "uniform"), (3, "lloyd_qjl", 3, "lloyd"),
-                                         (8, "fp8", 4, "uniform"), (8, "fp8", 3, "uniform")])
+                                         (8, "fp8", 4, "uniform"), (8, "fp8", 3, "uniform"),
+                                         (8, "lloyd_nc", 3, "uniform")])
 def test_layout_matches_format(kb, km, vb, vm):
     lay = tq.layout_for_config(tq.make_config(128, 8, 32, kb, km, vb, vm)).as_dict()
     f = O.page_fields(O.Config(128, 8, 32, kb, km, vb, vm))
@@ -108,7 +113,7 @@ def test_layout_matches_format(kb, km, vb, vm):
         assert lay["off_vmin"] == f["vnorm"][0] and lay["off_vscale"] == none
 
 
-@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 8])
 def test_library_codebook_equals_oracle_rounded(bits):
     """The library solves Lloyd-Max on its own (C++, long double); its fp32 tables must be the
     fp32 rounding of the oracle's fp64 solution (at most 1 ulp apart)."""
