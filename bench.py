@@ -295,7 +295,8 @@ def main():
 def cpu_baseline(w, kind, k_all, v_all, q_np, lay, np):
     """The fp64 oracle (untuned) on a bounded sample of the same step: one sequence's
     new-token quantize-append plus its decode attention over its context (for the
-    append workloads: the quantize-append of 2048 of the step's tokens)."""
+    append workloads: the quantize-append of 16384 of the step's tokens;
+    dequant_layer: the reconstruction of 8192 tokens)."""
     from oracle import tq_oracle as O
     from kv_cache_vector_randomized_amd import synth
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
@@ -323,7 +324,7 @@ def cpu_baseline(w, kind, k_all, v_all, q_np, lay, np):
         sample_bytes = n * Hkv * (th + 2 * d * 2) + n * 8
         sample = f"reconstruction of {n} tokens x {Hkv} kv heads (bf16-sized output), median of 5 runs, {sec:.2f} s each"
     elif kind == "append":
-        n = 2048
+        n = 16384
         times = []
         for _ in range(3):
             t0 = time.perf_counter()
@@ -337,7 +338,7 @@ def cpu_baseline(w, kind, k_all, v_all, q_np, lay, np):
         O.quantize_append(cfg, cache, f64(k_all[: T - 1]), f64(v_all[: T - 1]), slots[: T - 1], signs, kcb, S=S)
         log(f"[cpu] oracle prefill of the sample sequence took {time.time() - t0:.1f}s (not timed)")
         times = []
-        for _ in range(5):
+        for _ in range(25):
             t0 = time.perf_counter()
             O.quantize_append(cfg, cache, f64(k_all[T - 1:T]), f64(v_all[T - 1:T]), slots[T - 1:T], signs, kcb, S=S)
             O.decode_attention(cfg, f64(q_np[b:b + 1]), cache, lay.block_tables[b:b + 1], lay.seq_lens[b:b + 1],
@@ -347,7 +348,7 @@ def cpu_baseline(w, kind, k_all, v_all, q_np, lay, np):
         sample_bytes = (Hkv * (2 * d * 2 + th) + 8 + Hkv * T * th + Hq * d * 2 + Hq * d * 4
                         + lay.block_tables.shape[1] * 4 + 4)
         sample = (f"one sequence of the step (append 1 token x {Hkv} kv heads, decode {Hq} q heads over {T} "
-                  f"tokens), median of 5 runs, {sec:.2f} s each")
+                  f"tokens), median of 25 runs, {sec:.2f} s each")
     log(f"[cpu] oracle sample {sec:.2f}s -> {sample_bytes / sec / 1e9:.4f} GB/s")
     return {"value": round(sample_bytes / sec / 1e9, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": sample}
