@@ -31,6 +31,12 @@ Readings taken where the pages are silent (each is listed in the design notes):
   R12 bit order: LSB-first stream per vector (generalises [P4]'s nibble order).
   R13 QJL: residual in the rotated frame, m = d rows, sign(0) -> bit 1.
   R14 GQA: q head h reads kv head h // (Hq/Hkv); softmax scale supplied by caller.
+  R26 PolarQuant keys ([P3] PolarQuant section): after the stage-1 rotation the
+      vector goes through the recursive polar transform (pairs -> radius and
+      angle, radii paired again, down to one radius and d-1 angles); every angle
+      takes a b-bit uniform grid over its range (level 1: [-pi, pi), higher
+      levels: [0, pi/2]) with cell-centre reconstruction; the radius is fp32
+      (R7).  Stream order of the 128 slots: subtree-major (R27).
   R24 FP8 keys ([P1] preset table: the k8v4 preset stores keys in FP8, 2.6x):
       OCP E4M3 of each raw key coordinate (no rotation, no per-token scale),
       nearest value with ties to the even code, magnitudes above 448 saturate.
@@ -216,6 +222,8 @@ def quantize_keys(k: np.ndarray, signs: np.ndarray, cb: Codebook, mode: str,
     """
     if mode == "fp8":
         return quantize_keys_fp8(k)
+    if mode == "polar":
+        return quantize_keys_polar(k, signs, cb.bits)
     k = np.asarray(k, dtype=np.float64)
     R = rotation_matrix(signs)
     n = np.sqrt((k * k).sum(axis=-1))
@@ -297,6 +305,121 @@ def quantize_keys_fp8(k: np.ndarray) -> KeyCodes:
 
 
 # ----------------------------------------------------------------------------
+# PolarQuant keys  [P3 PolarQuant section: recursive polar transform, one
+# radius and d-1 angles, angles on a uniform grid with no per-block constants]
+# (R26, R27)
+# ----------------------------------------------------------------------------
+def polar_slot_map(d: int = 128):
+    """(level, node) stored in each of the d code slots; (0, 0) is padding.
+
+    Quarter g of the coordinates (32g .. 32g+31 at d = 128) owns slots 32g..32g+31:
+    its 16 level-1 angles, 8 level-2, 4 level-3, 2 level-4 and 1 level-5 angle,
+    in node order; slot 32g+31 holds the root (g = 0), the two level-6 angles
+    (g = 1, 2) or padding (g = 3)."""
+    assert d == 128
+    slots = []
+    for g in range(4):
+        for level, count in ((1, 16), (2, 8), (3, 4), (4, 2), (5, 1)):
+            slots += [(level, count * g + i) for i in range(count)]
+        slots.append({0: (7, 0), 1: (6, 0), 2: (6, 1), 3: (0, 0)}[g])
+    return slots
+
+
+def polar_forward(y: np.ndarray):
+    """Recursive polar transform of y[..., d]: angles per level (level 1: atan2 of
+    coordinate pairs; level l > 1: atan2 of pairs of level l-1 radii) and the
+    final radius ||y||."""
+    rho = np.asarray(y, dtype=np.float64)
+    angles = {}
+    level = 1
+    while rho.shape[-1] > 1:
+        a, b = rho[..., 0::2], rho[..., 1::2]
+        angles[level] = np.arctan2(b, a)
+        rho = np.hypot(a, b)
+        level += 1
+    return angles, rho[..., 0]
+
+
+def polar_inverse(angles: dict, radius) -> np.ndarray:
+    """Inverse transform: top down, a node of radius r and angle t gives its
+    children r cos t and r sin t."""
+    rho = np.asarray(radius, dtype=np.float64)[..., None]
+    for level in sorted(angles, reverse=True):
+        t = angles[level]
+        rho = np.stack([rho * np.cos(t), rho * np.sin(t)], axis=-1).reshape(t.shape[:-1] + (2 * t.shape[-1],))
+    return rho
+
+
+def polar_grid(level: int, bits: int):
+    """(lowest edge, cell width) of the uniform angle grid of a level."""
+    return (-math.pi, 2 * math.pi / (1 << bits)) if level == 1 else (0.0, (math.pi / 2) / (1 << bits))
+
+
+def polar_codes(theta: np.ndarray, level: int, bits: int):
+    """Cell index of each angle (level 1 wraps around: pi is -pi) and its distance to
+    the nearest cell edge (the decision boundaries)."""
+    lo, w = polar_grid(level, bits)
+    x = (theta - lo) / w
+    if level == 1:
+        code = np.floor(x).astype(np.int64) % (1 << bits)
+        band = np.abs(x - np.rint(x)) * w
+    else:
+        code = np.clip(np.floor(x), 0, (1 << bits) - 1).astype(np.int64)
+        inner = np.clip(np.rint(x), 1, (1 << bits) - 1)      # edges between cells
+        band = np.abs(x - inner) * w
+    return code, band
+
+
+def polar_angle(code, level: int, bits: int) -> np.ndarray:
+    lo, w = polar_grid(level, bits)
+    return lo + (np.asarray(code, dtype=np.float64) + 0.5) * w
+
+
+def quantize_keys_polar(k: np.ndarray, signs: np.ndarray, bits: int) -> KeyCodes:
+    """PolarQuant keys: y = R k, polar transform of y, b-bit angle codes in slot
+    order; stored scalar = fp32 radius (= ||k||).  An angle whose pair has zero
+    radius is undefined and counted in the band."""
+    k = np.asarray(k, dtype=np.float64)
+    y = k @ rotation_matrix(signs).T
+    angles, radius = polar_forward(y)
+    # radii below each angle (to flag undefined angles)
+    rho = y
+    node_r = {}
+    level = 1
+    while rho.shape[-1] > 1:
+        a, b = rho[..., 0::2], rho[..., 1::2]
+        rho = np.hypot(a, b)
+        node_r[level] = rho
+        level += 1
+    slots = polar_slot_map(k.shape[-1])
+    codes = np.zeros(k.shape, dtype=np.int64)
+    band = np.full(k.shape, np.inf)
+    for i, (level, node) in enumerate(slots):
+        if level == 0:
+            continue
+        c, bd = polar_codes(angles[level][..., node], level, bits)
+        codes[..., i] = c
+        band[..., i] = np.where(node_r[level][..., node] > 0, bd, 0.0)
+    return KeyCodes(codes=codes, norm=fl32(radius), y=y, band=band)
+
+
+def dequantize_keys_polar(codes: np.ndarray, norm, signs: np.ndarray, bits: int) -> np.ndarray:
+    """k_hat = R^T y_hat, y_hat the inverse polar transform of the cell-centre angles
+    and the stored radius."""
+    codes = np.asarray(codes, dtype=np.int64)
+    d = codes.shape[-1]
+    slots = polar_slot_map(d)
+    angles = {}
+    for level in range(1, 8):
+        angles[level] = np.zeros(codes.shape[:-1] + (d >> level,))
+    for i, (level, node) in enumerate(slots):
+        if level:
+            angles[level][..., node] = polar_angle(codes[..., i], level, bits)
+    y_hat = polar_inverse(angles, norm)
+    return y_hat @ rotation_matrix(signs)
+
+
+# ----------------------------------------------------------------------------
 # Values  [P1 stage 2: stage 1 paired with uniform quantization of values]
 # ----------------------------------------------------------------------------
 @dataclasses.dataclass
@@ -375,7 +498,7 @@ class Config:
     num_kv_heads: int
     num_q_heads: int
     key_bits: int
-    key_mode: str       # "lloyd" | "lloyd_nc" | "lloyd_qjl" | "fp8" (key_bits 8)
+    key_mode: str       # "lloyd" | "lloyd_nc" | "lloyd_qjl" | "fp8" (key_bits 8) | "polar"
     val_bits: int
     val_mode: str       # "uniform" | "lloyd"
 
@@ -511,6 +634,8 @@ def dequantize_slots(cfg: Config, cache, slots, head: int, signs, kcb: Codebook,
     f = read_tokens(cfg, cache, slots, head)
     if cfg.key_mode == "fp8":
         k_hat = fp8_e4m3_value(f["kcodes"])
+    elif cfg.key_mode == "polar":
+        k_hat = dequantize_keys_polar(f["kcodes"], f["knorm"], signs, cfg.key_bits)
     else:
         k_hat = dequantize_keys(f["kcodes"], f["knorm"], signs, kcb)
     if cfg.val_mode == "uniform":
