@@ -83,12 +83,25 @@ typedef enum {
   TQ_KEY_LLOYD = 0,      /* stage 1, stored norm = ||k||                          */
   TQ_KEY_LLOYD_NC = 1,   /* stage 1, stored norm = ||k|| / ||C[code]|| (`_nc`)     */
   TQ_KEY_LLOYD_QJL = 2,  /* stage 1 (plain norm) + 1-bit QJL residual signs        */
-  TQ_KEY_FP8 = 3         /* FP8 keys (issoh.co.jp "TurboQuantとは？…", preset table:
+  TQ_KEY_FP8 = 3,        /* FP8 keys (issoh.co.jp "TurboQuantとは？…", preset table:
                             one serving preset keeps keys in FP8, values in 4 bits):
                             each coordinate of the raw key as an OCP E4M3 byte,
                             nearest value with ties to even, magnitudes above 448
                             saturate; no rotation, no per-token scalar.  Needs
                             key_bits 8 and uniform values.                        */
+  TQ_KEY_POLAR = 4       /* PolarQuant keys (lilting.ch TurboQuant article,
+                            PolarQuant section): after the stage-1 rotation, the
+                            recursive polar transform (coordinate pairs, then pairs
+                            of radii, down to one radius and d-1 angles); each
+                            angle a key_bits-bit cell of a uniform grid (level 1
+                            over [-pi, pi), higher levels over [0, pi/2]),
+                            reconstructed at the cell centre; the radius (= ||k||)
+                            in the key norm field.  Codes fill the d slots
+                            subtree-major: quarter g of the coordinates owns slots
+                            32g..32g+31 (its level 1..5 angles in node order; slot
+                            31 holds the root, slots 63 and 95 the two level-6
+                            angles, slot 127 is zero).  Uniform values only; not
+                            taken by tq_append_decode.                            */
 } tq_key_mode;
 
 typedef enum {

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libtq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["tq_host.cpp", "tq_append.hip", "tq_decode.hip", "tq_dequant.hip", "tq_transfer.hip"]
+SOURCES = ["tq_host.cpp", "tq_append.hip", "tq_decode.hip", "tq_dequant.hip", "tq_transfer.hip", "tq_polar.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -719,6 +719,17 @@ hipError_t page_vb(const AppendArgs& a, int val_bits, hipStream_t s) {
 
 hipError_t launch_append(const AppendArgs& a, int dtype, int key_bits, int key_mode, int val_bits, int val_mode,
                          hipStream_t s) {
+  if (key_mode == TQ_KEY_POLAR) {
+    if (val_mode != TQ_VAL_UNIFORM) return hipErrorInvalidValue;
+    const hipError_t e = launch_polar_keys(a, dtype, key_bits, s);
+    if (e != hipSuccess) return e;
+    switch (val_bits) {
+      case 2: return values_mode<2>(a, dtype, val_mode, s);
+      case 3: return values_mode<3>(a, dtype, val_mode, s);
+      case 4: return values_mode<4>(a, dtype, val_mode, s);
+    }
+    return hipErrorInvalidValue;
+  }
   if (key_mode == TQ_KEY_FP8) {
     if (key_bits != 8 || val_mode != TQ_VAL_UNIFORM) return hipErrorInvalidValue;
     const dim3 grid((unsigned)std::min<int64_t>((a.num_tokens * a.hkv + 3) / 4, 8192));

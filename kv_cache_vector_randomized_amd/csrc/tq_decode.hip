@@ -447,11 +447,43 @@ __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, floa
 constexpr int kKmLloyd = 0;   // Lloyd-Max codes with a stored norm (plain or corrected)
 constexpr int kKmQjl = 1;     // Lloyd-Max codes + QJL residual signs and norm
 constexpr int kKmFp8 = 2;     // E4M3 bytes of the raw key (KB = 8)
+constexpr int kKmPolar = 3;   // PolarQuant angle codes (subtree-major) and the radius
+
+// PolarQuant keys: the 32 coordinates 32g..32g+31 of one token (g = lane / 16) as
+// unit-radius leaf factors, rebuilt top down from the quarter's angle codes
+// (slots 0..30 of the lane's chunk), the root angle and the quarter's level-6
+// angle (cos and sin tables t1: level 1, tu: higher levels, in LDS).
+template <int KB>
+__device__ __forceinline__ void polar_leaves(const uint32_t (&kc)[KB], uint32_t root, uint32_t l6, int g,
+                                             const float2* t1, const float2* tu, float (&f)[32]) {
+  const float2 r7 = tu[root], r6 = tu[l6];
+  float v[16];
+  v[0] = ((g >> 1) ? r7.y : r7.x) * ((g & 1) ? r6.y : r6.x);
+  // levels 5, 4, 3, 2: 1, 2, 4, 8 angles at slots 30, 28, 24, 16
+#pragma unroll
+  for (int lv = 5, n = 1, base = 30; lv >= 2; --lv, n <<= 1, base -= n) {   // bases 30, 28, 24, 16
+#pragma unroll
+    for (int i = n - 1; i >= 0; --i) {
+      const float2 cs = tu[get_code<KB>(kc, base + i)];
+      const float r = v[i];
+      v[2 * i] = r * cs.x;
+      v[2 * i + 1] = r * cs.y;
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const float2 cs = t1[get_code<KB>(kc, p)];
+    f[2 * p] = v[p] * cs.x;
+    f[2 * p + 1] = v[p] * cs.y;
+  }
+}
 
 template <int KB, int KM, int VB, bool VLM>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a) {
   constexpr bool QJL = KM == kKmQjl;
   constexpr bool FP8 = KM == kKmFp8;   // FP8 keys: no rotation, no codebook, no norm
+  constexpr bool POLAR = KM == kKmPolar;   // PolarQuant keys: leaf factors from the angles, radius as norm
+  __shared__ float2 ptab[POLAR ? 32 : 1];  // (cos, sin) per code: level 1 at [0, 16), higher levels at [16, 32)
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j16 = lane & 15, grp = lane >> 4;   // column (token of a page) and row group (head) of the lane
@@ -516,9 +548,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   // wave) is loaded before the query is rotated, so that its latency overlaps the
   // rotation, the tables and the barrier.  Block-table reads do not wait for the
   // sequence length: entries past the end are dropped once it is known.
-  const float kc_top = FP8 ? 1.f : a.c->kc[(1 << KB) - 1];
+  const float kc_top = (FP8 || POLAR) ? 1.f : a.c->kc[(1 << KB) - 1];
   float kc_e[Tab::kCodes];
-  if constexpr (!FP8) {
+  if constexpr (!FP8 && !POLAR) {
     const int ent = tid & (Tab::kEntries - 1);
 #pragma unroll
     for (int i = 0; i < Tab::kCodes; ++i) kc_e[i] = a.c->kc[(ent >> (KB * i)) & ((1 << KB) - 1)];
@@ -578,8 +610,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
 
   // Key centroid table: C * 2^s2 with 2^s2 bringing the largest |C| (the last,
   // the codebook being symmetric) into [2^14, 2^15).
-  const int s2 = FP8 ? 0 : 15 - __builtin_amdgcn_frexp_expf(kc_top);
-  if (!FP8 && tid < Tab::kEntries) {
+  // (PolarQuant: leaf factors are in [-1, 1], scaled by 2^14)
+  const int s2 = FP8 ? 0 : POLAR ? 14 : 15 - __builtin_amdgcn_frexp_expf(kc_top);
+  if constexpr (POLAR) {
+    if (tid < 32) ptab[tid] = tid < 16 ? make_float2(a.c->pcs1[2 * tid], a.c->pcs1[2 * tid + 1])
+                                       : make_float2(a.c->pcsU[2 * tid - 32], a.c->pcsU[2 * tid - 31]);
+  }
+  if (!FP8 && !POLAR && tid < Tab::kEntries) {
     uint32_t* e = &ktab[tid * Tab::kWords];
 #pragma unroll
     for (int i = 0; i < Tab::kCodes; ++i) {
@@ -775,6 +812,29 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
           const uint4 kb = kap == 0 ? fp8_key_operand<0>(cur.kc[pg]) : kap == 1 ? fp8_key_operand<1>(cur.kc[pg])
                          : kap == 2 ? fp8_key_operand<2>(cur.kc[pg]) : fp8_key_operand<3>(cur.kc[pg]);
           D[pg] = mfma_f16(qa, kb, D[pg]);
+        }
+      }
+    } else if constexpr (POLAR) {
+      // slot 31 of each quarter: the root (quarter 0) and the level-6 angles (quarters 1, 2)
+#pragma unroll
+      for (int pg = 0; pg < 4; ++pg) {
+        const uint32_t c31 = cur.kc[pg][KB - 1] >> (32 - KB);
+        const uint32_t root = (uint32_t)__shfl((int)c31, j16);
+        const uint32_t l6 = (uint32_t)__shfl((int)c31, j16 + 16 * (1 + (grp >> 1)));
+        float f[32];
+        polar_leaves<KB>(cur.kc[pg], root, l6, grp, ptab, ptab + 16, f);
+#pragma unroll
+        for (int kap = 0; kap < 8; ++kap) {
+          uint32_t wv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = f[4 * kap + e] * 16384.f;
+            const _Float16 hi = (_Float16)x;
+            const _Float16 lo = (_Float16)(x - (float)hi);
+            wv[e] = (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
+          }
+          const uint4 qa = *reinterpret_cast<const uint4*>(qa_src + 4 * kap);
+          D[pg] = mfma_f16(qa, make_uint4(wv[0], wv[1], wv[2], wv[3]), D[pg]);
         }
       }
     } else {
@@ -1045,7 +1105,7 @@ template <int KB, int KM, int VB>
 hipError_t decode_v(const DecodeArgs& a, int val_mode, hipStream_t s) {
   const dim3 grid((unsigned)a.splits, (unsigned)a.hkv, (unsigned)a.batch);
   if (val_mode == TQ_VAL_LLOYD) {
-    if constexpr (KB == 8) return hipErrorInvalidValue;   // 8-bit and FP8 keys pair with uniform values
+    if constexpr (KB == 8 || KM == kKmPolar) return hipErrorInvalidValue;   // these pair with uniform values
     else hipLaunchKernelGGL((decode_kernel<KB, KM, VB, true>), grid, dim3(64 * kDecodeWaves), 0, s, a);
   } else {
     hipLaunchKernelGGL((decode_kernel<KB, KM, VB, false>), grid, dim3(64 * kDecodeWaves), 0, s, a);
@@ -1066,12 +1126,12 @@ hipError_t decode_vb(const DecodeArgs& a, int val_bits, int val_mode, hipStream_
 template <int KB, int KM>
 const void* kernel_vb(int val_bits, int val_mode) {
   const bool lm = val_mode == TQ_VAL_LLOYD;
-  if constexpr (KB == 8) {
+  if constexpr (KB == 8 || KM == kKmPolar) {
     if (lm) return nullptr;
     switch (val_bits) {
-      case 2: return (const void*)decode_kernel<8, KM, 2, false>;
-      case 3: return (const void*)decode_kernel<8, KM, 3, false>;
-      case 4: return (const void*)decode_kernel<8, KM, 4, false>;
+      case 2: return (const void*)decode_kernel<KB, KM, 2, false>;
+      case 3: return (const void*)decode_kernel<KB, KM, 3, false>;
+      case 4: return (const void*)decode_kernel<KB, KM, 4, false>;
     }
     return nullptr;
   } else {
@@ -1088,6 +1148,14 @@ const void* kernel_vb(int val_bits, int val_mode) {
 
 const void* decode_kernel_ptr(int key_bits, int key_mode, int val_bits, int val_mode) {
   const bool qjl = key_mode == TQ_KEY_LLOYD_QJL;
+  if (key_mode == TQ_KEY_POLAR) {
+    switch (key_bits) {
+      case 2: return kernel_vb<2, kKmPolar>(val_bits, val_mode);
+      case 3: return kernel_vb<3, kKmPolar>(val_bits, val_mode);
+      case 4: return kernel_vb<4, kKmPolar>(val_bits, val_mode);
+    }
+    return nullptr;
+  }
   switch (key_bits) {
     case 8:
       if (qjl) return nullptr;
@@ -1103,6 +1171,14 @@ hipError_t launch_decode(const DecodeArgs& a, int key_bits, int key_mode, int va
                          hipStream_t s) {
   const bool qjl = key_mode == TQ_KEY_LLOYD_QJL;
   if (key_mode == TQ_KEY_FP8 && key_bits != 8) return hipErrorInvalidValue;
+  if (key_mode == TQ_KEY_POLAR) {
+    switch (key_bits) {
+      case 2: return decode_vb<2, kKmPolar>(a, val_bits, val_mode, s);
+      case 3: return decode_vb<3, kKmPolar>(a, val_bits, val_mode, s);
+      case 4: return decode_vb<4, kKmPolar>(a, val_bits, val_mode, s);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (key_bits) {
     case 8:
       if (qjl) return hipErrorInvalidValue;

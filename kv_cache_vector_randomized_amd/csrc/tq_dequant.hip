@@ -444,6 +444,7 @@ hipError_t dequant_vb(const DequantArgs& a, int val_bits, bool lm, bool bf16, hi
 hipError_t launch_dequant(const DequantArgs& a, int key_bits, int key_mode, int val_bits, int val_mode, bool bf16_out,
                           hipStream_t s) {
   const bool lm = val_mode == TQ_VAL_LLOYD;
+  if (key_mode == TQ_KEY_POLAR) return lm ? hipErrorInvalidValue : launch_polar_dequant(a, key_bits, val_bits, bf16_out, s);
   switch (key_bits) {
     case 8:
       return key_mode == TQ_KEY_FP8 ? dequant_vb<8, true>(a, val_bits, lm, bf16_out, s)

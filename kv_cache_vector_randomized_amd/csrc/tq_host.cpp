@@ -289,7 +289,7 @@ tq_status tq_validate_config(const tq_config* c) {
   if (c->num_kv_heads == 0 || c->num_q_heads == 0 || c->num_q_heads % c->num_kv_heads)
     return fail(TQ_ERR_INVALID_ARG, "num_q_heads (%u) must be a positive multiple of num_kv_heads (%u)",
                 c->num_q_heads, c->num_kv_heads);
-  if (c->key_mode > TQ_KEY_FP8) return fail(TQ_ERR_INVALID_ARG, "bad key_mode %u", c->key_mode);
+  if (c->key_mode > TQ_KEY_POLAR) return fail(TQ_ERR_INVALID_ARG, "bad key_mode %u", c->key_mode);
   if (c->val_mode > TQ_VAL_LLOYD) return fail(TQ_ERR_INVALID_ARG, "bad val_mode %u", c->val_mode);
   if (c->key_bits < 1 || c->key_bits > 8) return fail(TQ_ERR_INVALID_ARG, "key_bits %u out of [1, 8]", c->key_bits);
   if (c->val_bits < 1 || c->val_bits > 8) return fail(TQ_ERR_INVALID_ARG, "val_bits %u out of [1, 8]", c->val_bits);
@@ -297,6 +297,9 @@ tq_status tq_validate_config(const tq_config* c) {
   if (c->key_mode == TQ_KEY_FP8) {
     if (c->key_bits != 8) return fail(TQ_ERR_INVALID_ARG, "FP8 keys take key_bits 8 (got %u)", c->key_bits);
     if (c->val_mode != TQ_VAL_UNIFORM) return fail(TQ_ERR_UNSUPPORTED, "FP8 keys are built with uniform values only");
+  } else if (c->key_mode == TQ_KEY_POLAR) {
+    if (c->key_bits < 2 || c->key_bits > 4) return fail(TQ_ERR_UNSUPPORTED, "PolarQuant keys take 2..4 bits per angle");
+    if (c->val_mode != TQ_VAL_UNIFORM) return fail(TQ_ERR_UNSUPPORTED, "PolarQuant keys are built with uniform values only");
   } else if (c->key_bits == 8) {
     if (c->key_mode == TQ_KEY_LLOYD_QJL) return fail(TQ_ERR_UNSUPPORTED, "8-bit keys take no QJL residual");
   } else if (c->key_bits < 2 || c->key_bits > 4) {
@@ -340,15 +343,26 @@ tq_status tq_create(const tq_config* cfg, const int8_t* signs_host, const float*
   for (int i = 0; i < d; ++i) h->signs[i] = (float)signs_host[i];
   float vt[15] = {0};
   const bool fp8 = cfg->key_mode == TQ_KEY_FP8;   // no key codebook
+  const bool polar = cfg->key_mode == TQ_KEY_POLAR;
   const bool wide = cfg->key_bits > 4;            // 8-bit codes: a binary search over h->kt, no grid
-  if (!fp8) codebook_f32((int)cfg->key_bits, d, h->kc, h->kt);
+  if (!fp8 && !polar) codebook_f32((int)cfg->key_bits, d, h->kc, h->kt);
+  if (polar) {
+    // cell centres of the angle grids: level 1 over [-pi, pi), levels >= 2 over [0, pi/2]
+    const double pi = std::acos(-1.0);
+    const int n = 1 << cfg->key_bits;
+    for (int c = 0; c < n; ++c) {
+      const double t1 = -pi + (c + 0.5) * (2 * pi / n), tu = (c + 0.5) * (0.5 * pi / n);
+      h->pcs1[2 * c] = (float)std::cos(t1); h->pcs1[2 * c + 1] = (float)std::sin(t1);
+      h->pcsU[2 * c] = (float)std::cos(tu); h->pcsU[2 * c + 1] = (float)std::sin(tu);
+    }
+  }
   const float* kt = h->kt;
   tq_ctx* ctx = new (std::nothrow) tq_ctx();
   if (!ctx) { delete h; return fail(TQ_ERR_OUT_OF_MEMORY, "host allocation failed"); }
   ctx->cfg = *cfg;
   if ((s = layout_of(cfg, &ctx->layout)) != TQ_OK) { delete h; delete ctx; return s; }
-  bool ok = fp8 || wide || build_lut((int)cfg->key_bits, h->kc, kt, h->klut, &ctx->klut_scale, &ctx->klut_bias);
-  ctx->unit_grid_ok = (!fp8 && !wide && build_unit_lut((int)cfg->key_bits, h->kc, kt, h->kulut)) ? 1 : 0;
+  bool ok = fp8 || polar || wide || build_lut((int)cfg->key_bits, h->kc, kt, h->klut, &ctx->klut_scale, &ctx->klut_bias);
+  ctx->unit_grid_ok = (!fp8 && !polar && !wide && build_unit_lut((int)cfg->key_bits, h->kc, kt, h->kulut)) ? 1 : 0;
   if (cfg->val_mode == TQ_VAL_LLOYD) {
     codebook_f32((int)cfg->val_bits, d, h->vc, vt);
     ok = ok && build_lut((int)cfg->val_bits, h->vc, vt, h->vlut, &ctx->vlut_scale, &ctx->vlut_bias);
@@ -480,6 +494,8 @@ tq_status decode_common(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cac
     if (!aligned(k_new, 4) || !aligned(v_new, 4)) return fail(TQ_ERR_INVALID_ARG, "misaligned k_new / v_new");
     if (ctx->cfg.val_mode == TQ_VAL_LLOYD)
       return fail(TQ_ERR_UNSUPPORTED, "the fused append takes uniform values only");
+    if (ctx->cfg.key_mode == TQ_KEY_POLAR)
+      return fail(TQ_ERR_UNSUPPORTED, "the fused append does not take PolarQuant keys");
   }
   const size_t need = tq_decode_workspace_bytes(ctx, batch, max_seq_len);
   if (workspace_bytes < need)

@@ -42,6 +42,8 @@ struct DevConsts {
   float signs[kDim];          // +-1 of the rotation
   float kc[256];              // key centroids (fp32), 2^key_bits used
   float kt[256];              // key thresholds (fp32), 2^key_bits - 1 used (8-bit keys search them)
+  float pcs1[32];             // PolarQuant: (cos, sin) of the level-1 cell centres, per code
+  float pcsU[32];             // PolarQuant: (cos, sin) of the level >= 2 cell centres, per code
   float vc[16];               // value centroids (Lloyd-Max values only)
   QLut klut[kLutCells];
   QLut vlut[kLutCells];
@@ -131,6 +133,8 @@ hipError_t launch_decode(const DecodeArgs& a, int key_bits, int key_mode, int va
                          hipStream_t s);
 hipError_t launch_transfer(bool to_host, void* cache, void* host, const int32_t* block_ids, int64_t n,
                            int64_t num_blocks, int64_t block_bytes, int grid, hipStream_t s);
+hipError_t launch_polar_keys(const AppendArgs& a, int dtype, int key_bits, hipStream_t s);
+hipError_t launch_polar_dequant(const DequantArgs& a, int key_bits, int val_bits, bool bf16_out, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, int key_bits, int key_mode, int val_bits, int val_mode, bool bf16_out,
                           hipStream_t s);
 

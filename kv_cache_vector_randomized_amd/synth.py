@@ -44,7 +44,7 @@ class Workload:
     batch: int
     context: int            # tokens attended per sequence in the decode step
     key_bits: int
-    key_mode: str           # "lloyd" | "lloyd_nc" | "lloyd_qjl" | "fp8"
+    key_mode: str           # "lloyd" | "lloyd_nc" | "lloyd_qjl" | "fp8" | "polar"
     val_bits: int
     val_mode: str           # "uniform" | "lloyd"
     dtype: str              # "f32" | "bf16"
@@ -77,6 +77,9 @@ WORKLOADS = {
     # 8-bit Lloyd-Max keys (corrected norm) with 3-bit uniform values (the MLX default turbo8v3)
     "turbo8v3": Workload("turbo8v3", 128, 8, 32, 16, 8192, 8, "lloyd_nc", 3, "uniform", "bf16",
                          "2% of channels per KV head x8", 9),
+    # PolarQuant keys (3-bit angles, fp32 radius) with 4-bit uniform values
+    "polar3": Workload("polar3", 128, 8, 32, 16, 8192, 3, "polar", 4, "uniform", "bf16",
+                       "2% of channels per KV head x8", 10),
 }
 
 
@@ -113,7 +116,7 @@ def kv_tensor(w: Workload, num_tokens: int, which: str, seed_offset: int = 0) ->
     chan_rng = np.random.Generator(np.random.PCG64([w.seed, 7]))
     if w.name == "toy":
         x[:, :, [3, 17, 64, 100]] *= np.float32(10.0)
-    elif w.name in ("gqa_decode", "k3v4_nc", "k8v4", "turbo8v3"):
+    elif w.name in ("gqa_decode", "k3v4_nc", "k8v4", "turbo8v3", "polar3"):
         ch = _outlier_channels(chan_rng, hk, d, int(round(0.02 * d)))
         for h in range(hk):
             x[:, h, ch[h]] *= np.float32(8.0)

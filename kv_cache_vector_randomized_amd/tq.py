@@ -22,7 +22,7 @@ BLOCK_TOKENS = 16
 
 TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE_TOO_SMALL, TQ_ERR_HIP, TQ_ERR_OUT_OF_MEMORY = range(6)
 TQ_F32, TQ_BF16 = 0, 1
-KEY_MODES = {"lloyd": 0, "lloyd_nc": 1, "lloyd_qjl": 2, "fp8": 3}
+KEY_MODES = {"lloyd": 0, "lloyd_nc": 1, "lloyd_qjl": 2, "fp8": 3, "polar": 4}
 VAL_MODES = {"uniform": 0, "lloyd": 1}
 
 # Every entry point declared in include/tq.h.

@@ -79,7 +79,10 @@ def compare_append(w, gpu_cache: np.ndarray, slots, qz: O.Quantized, report: dic
         band = qz.key.band[:, h] < BAND
         diff = kc != kref
         assert not np.any(diff & ~band), f"key code mismatch outside the band (head {h})"
-        assert np.all(np.abs(kc - kref) <= 1)
+        if cfg.key_mode == "polar":     # level-1 angles wrap around: neighbours modulo 2^b
+            assert np.all(np.isin((kc - kref) % (1 << cfg.key_bits), [0, 1, (1 << cfg.key_bits) - 1]))
+        else:
+            assert np.all(np.abs(kc - kref) <= 1)
         report["key_band"] = report.get("key_band", 0) + int(band.sum())
         report["key_band_flips"] = report.get("key_band_flips", 0) + int(diff.sum())
         clean = ~diff.any(axis=1)

@@ -107,6 +107,20 @@ def test_append_decode_matches_oracle(name):
     print(f"  worst relative error {worst:.3e}")
 
 
+def test_append_decode_refuses_polar_keys():
+    """The one-launch step does not take PolarQuant keys: refused before any launch."""
+    from kv_cache_vector_randomized_amd import tq
+    from kv_cache_vector_randomized_amd.torch_api import PagedKVCache
+    w = synth.WORKLOADS["polar3"]
+    lay = synth.paged_layout(1, [20], 45)
+    cache = PagedKVCache(H.make_context(w), lay.num_blocks, fill=0)
+    z = torch.zeros((1, w.num_kv_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((1, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(tq.TQError):
+        cache.append_decode(z, z, q, torch.from_numpy(lay.block_tables).cuda(), torch.from_numpy(lay.seq_lens).cuda(),
+                            20, 1.0 / math.sqrt(w.head_dim))
+
+
 def test_append_decode_equals_two_launches():
     """The fused step and tq_quantize_append + tq_decode_attention agree (same
     shapes, same bytes of context)."""

@@ -43,7 +43,8 @@ def _dense_attention(q, kbuf, vbuf, base, n, group, scale):
     return out
 
 
-@pytest.mark.parametrize("name", ["toy", "gqa_decode", "long_3bit", "qjl", "k3v4_nc", "k3qjl_v2", "k8v4", "turbo8v3"])
+@pytest.mark.parametrize("name", ["toy", "gqa_decode", "long_3bit", "qjl", "k3v4_nc", "k3qjl_v2", "k8v4", "turbo8v3",
+                                  "polar3"])
 def test_incremental_buffer_equals_full_dequantize(name):
     from kv_cache_vector_randomized_amd.torch_api import PagedKVCache
     w = synth.WORKLOADS[name]

@@ -28,6 +28,7 @@ CASES = {
     "k3qjl_v2": [400, 0, 33],
     "k8v4": [500, 31, 0, 64],
     "turbo8v3": [300, 0, 47],
+    "polar3": [400, 33, 0],
 }
 
 
@@ -125,7 +126,8 @@ def test_decode_matches_oracle_on_identical_bytes(name):
     print(f"  worst relative error {worst:.3e}")
 
 
-@pytest.mark.parametrize("name", ["toy", "gqa_decode", "long_3bit", "qjl", "k3v4_nc", "k3qjl_v2", "k8v4", "turbo8v3"])
+@pytest.mark.parametrize("name", ["toy", "gqa_decode", "long_3bit", "qjl", "k3v4_nc", "k3qjl_v2", "k8v4", "turbo8v3",
+                                  "polar3"])
 def test_end_to_end_append_then_decode(name):
     """GPU append then GPU decode vs the oracle end to end (its own codes)."""
     w = synth.WORKLOADS[name]
@@ -178,7 +180,8 @@ def test_end_to_end_append_then_decode(name):
     print(f"  tokens with a band flip: {flips}; (seq, q head) pairs on the oracle's own bytes: {checked}")
 
 
-@pytest.mark.parametrize("name", ["toy", "gqa_decode", "long_3bit", "qjl", "k3v4_nc", "k3qjl_v2", "k8v4", "turbo8v3"])
+@pytest.mark.parametrize("name", ["toy", "gqa_decode", "long_3bit", "qjl", "k3v4_nc", "k3qjl_v2", "k8v4", "turbo8v3",
+                                  "polar3"])
 def test_dequantize_matches_oracle(name):
     w = synth.WORKLOADS[name]
     lens = [70, 33] if w.batch > 1 else [70]

@@ -44,6 +44,9 @@ def test_status_strings():
     (dict(key_bits=0), tq.TQ_ERR_INVALID_ARG),
     (dict(key_bits=8), tq.TQ_OK),                    # 8-bit Lloyd-Max keys
     (dict(key_bits=5), tq.TQ_ERR_UNSUPPORTED),
+    (dict(key_bits=3, key_mode="polar"), tq.TQ_OK),
+    (dict(key_bits=8, key_mode="polar"), tq.TQ_ERR_UNSUPPORTED),
+    (dict(key_bits=3, key_mode="polar", val_mode="lloyd"), tq.TQ_ERR_UNSUPPORTED),
     (dict(val_bits=1), tq.TQ_ERR_UNSUPPORTED),
     (dict(key_mode=3), tq.TQ_ERR_INVALID_ARG),
     (dict(val_mode=2), tq.TQ_ERR_INVALID_ARG),
@@ -52,7 +55,7 @@ def test_status_strings():
     (dict(key_bits=8, key_mode="fp8"), tq.TQ_OK),
     (dict(key_bits=4, key_mode="fp8"), tq.TQ_ERR_INVALID_ARG),
     (dict(key_bits=8, key_mode="fp8", val_mode="lloyd"), tq.TQ_ERR_UNSUPPORTED),
-    (dict(key_mode=4), tq.TQ_ERR_INVALID_ARG),
+    (dict(key_mode=5), tq.TQ_ERR_INVALID_ARG),
     (dict(key_bits=8, key_mode="lloyd_nc", val_bits=3), tq.TQ_OK),
     (dict(key_bits=8, key_mode="lloyd_qjl"), tq.TQ_ERR_UNSUPPORTED),
     (dict(key_bits=6), tq.TQ_ERR_UNSUPPORTED),
@@ -91,7 +94,7 @@ def test_every_call_refuses_a_null_context():
                                          (3, "lloyd_nc", 3, "uniform"), (2, "lloyd_qjl", 4, "uniform"),
                                          (2, "lloyd", 2, "uniform"), (3, "lloyd_qjl", 3, "lloyd"),
                                          (8, "fp8", 4, "uniform"), (8, "fp8", 3, "uniform"),
-                                         (8, "lloyd_nc", 3, "uniform")])
+                                         (8, "lloyd_nc", 3, "uniform"), (3, "polar", 4, "uniform")])
 def test_layout_matches_format(kb, km, vb, vm):
     lay = tq.layout_for_config(tq.make_config(128, 8, 32, kb, km, vb, vm)).as_dict()
     f = O.page_fields(O.Config(128, 8, 32, kb, km, vb, vm))
