@@ -39,9 +39,13 @@ Prints ONE JSON line on stdout; diagnostics go to stderr.  `value` is packed-KV
 GB/s: algorithmic bytes of the step (bf16 inputs read, packed rows written,
 packed rows of the attended context read, queries, outputs, tables) divided by
 the step time, with every input already resident in HBM.  The step time comes
-from a timed region with nothing but the steps in it; a second pass over the
-same number of steps brackets the dominant kernel with HIP events on its stream
-for the roofline figure.
+from a timed region with nothing but the steps in it: the steps are captured in a
+HIP graph and replayed (--eager: launched one by one from Python, which leaves the
+GPU waiting on the host between short kernels).  For the roofline figure a
+second pass runs the dominant kernel alone the same number of times back to
+back (graph-replayed likewise) between one pair of HIP events on its stream; a
+third pass, eager, brackets each step's dominant launch with its own events for
+the spread of single launches.
 """
 from __future__ import annotations
 
@@ -96,14 +100,16 @@ def counter_traffic(kernel_key: str, source: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=4, help="independent layer caches rotated over the steps")
     ap.add_argument("--workload", default="gqa_decode", choices=list(MODES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="decode workloads: append and decode as two launches instead of one")
     ap.add_argument("--dequant-f32", action="store_true", help="dequant_layer: fp32 output instead of bf16")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step from Python instead of replaying a HIP graph of the steps")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -173,6 +179,9 @@ def main():
                 c.decode(q_dev, tables, seq_lens, T, scale, out=out)
                 if ev is not None:
                     ev[1].record(stream)
+
+            def dom(i):
+                caches[i % n_layers].decode(q_dev, tables, seq_lens, T, scale, out=out)
         else:
             # one launch: the decode kernel also quantizes and stores the new tokens
             # (their slots are those of position T-1 in the block tables)
@@ -185,6 +194,9 @@ def main():
                 c.append_decode(k_new, v_new, q_dev, tables, seq_lens, T, scale, out=out)
                 if ev is not None:
                     ev[1].record(stream)
+
+            def dom(i):
+                caches[i % n_layers].append_decode(k_new, v_new, q_dev, tables, seq_lens, T, scale, out=out)
     elif kind == "dequant":
         for c in caches:                               # fill every layer (not timed)
             c.append(k_dev, v_dev, slots_all)
@@ -205,6 +217,9 @@ def main():
             c.dequantize_rows(slots_all, None, kbuf, vbuf)
             if ev is not None:
                 ev[1].record(stream)
+
+        def dom(i):
+            caches[i % n_layers].dequantize_rows(slots_all, None, kbuf, vbuf)
     else:
         append_bytes = B * T * Hkv * (2 * d * 2 + th) + B * T * 8
         dominant, dom_bytes, dom_source = "append_page_kernel", append_bytes, "tq_append.hip"
@@ -217,6 +232,9 @@ def main():
             if ev is not None:
                 ev[1].record(stream)
             c.decode(q_dev, tables, seq_lens, T, scale, out=out)
+
+        def dom(i):
+            caches[i % n_layers].append(k_dev, v_dev, slots_all)
     step_bytes = append_bytes + decode_bytes
 
     if args.copy_calibration_mb:
@@ -229,24 +247,45 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    def timed(fn, base):
+        """Milliseconds of `steps` calls of fn between one pair of events on the stream.
+        With a graph (the default) the calls are captured once, replayed once untimed
+        (the graph's upload), then replayed in the timed region: the GPU then runs the
+        launches back to back instead of waiting on the Python side between them."""
+        a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if args.eager:
+            torch.cuda.synchronize()
+            a_ev.record(stream)
+            for i in range(args.steps):
+                fn(base + i)
+            b_ev.record(stream)
+        else:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(args.steps):
+                    fn(base + i)
+            g.replay()
+            torch.cuda.synchronize()
+            a_ev.record(stream)
+            g.replay()
+            b_ev.record(stream)
+        torch.cuda.synchronize()
+        return a_ev.elapsed_time(b_ev)
+
     # Timed region: exactly `steps` steps, nothing else on the stream.
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / args.steps
+    ms_step = timed(step, args.warmup) / args.steps
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
-    # Second pass: the dominant kernel bracketed by events on its stream, every step.
+    # Second pass: the dominant kernel alone, `steps` launches back to back between
+    # one pair of events on its stream (per-launch event pairs add their own gaps).
+    dom_avg = timed(dom, args.warmup + args.steps) / args.steps
+    # Third pass: every step with the dominant kernel bracketed by its own events,
+    # for the spread of single launches (these include the events' own overhead).
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.steps):
-        step(args.warmup + args.steps + i, evs[i])
+        step(args.warmup + 2 * args.steps + i, evs[i])
     torch.cuda.synchronize()
     dom_ms = [a.elapsed_time(b) for a, b in evs]
-    dom_avg = statistics.mean(dom_ms)
     achieved = dom_bytes / (dom_avg * 1e-3) / 1e9
     pct = {p: float(np.percentile(dom_ms, p)) * 1e3 for p in (10, 50, 90)}
     log(f"[bench] step {ms_step * 1e3:.1f} us; {dominant} avg {dom_avg * 1e3:.1f} us "
@@ -295,6 +334,7 @@ def main():
             "p10_p50_p90_us": [round(pct[10], 2), round(pct[50], 2), round(pct[90], 2)],
         },
         "cpu_baseline": cpu,
+        "launch": "eager" if args.eager else "hip graph of the timed steps (replayed once untimed first)",
     }
     print(json.dumps(rec), flush=True)
 
