@@ -708,20 +708,23 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     }
   }
   // Fused append: the new token's key and value pairs of this lane, loaded before
-  // the barrier; wave kMaxGroup quantizes them after it, so no other wave waits.
-  float nt_k0 = 0.f, nt_k1 = 0.f, nt_v0 = 0.f, nt_v1 = 0.f;
+  // the barrier as raw words (bf16: one word, fp32: two; the second re-reads the
+  // first for bf16) and converted only where wave kMaxGroup quantizes them after
+  // it.  A use here would wait for every earlier load, this wave's first tile
+  // included, and hold the barrier for the whole work-group.
+  uint32_t nt_kw0 = 0u, nt_kw1 = 0u, nt_vw0 = 0u, nt_vw1 = 0u;
   if constexpr (!VLM) {
     if (own_new && wave == kMaxGroup) {
+      const bool f32 = a.q_dtype != TQ_BF16;
       const int64_t e0 = ((int64_t)b * a.hkv + kvh) * kDim + 2 * lane;
-      if (a.q_dtype != TQ_BF16) {
-        const float2 kk = *reinterpret_cast<const float2*>(static_cast<const float*>(a.k_new) + e0);
-        const float2 vv = *reinterpret_cast<const float2*>(static_cast<const float*>(a.v_new) + e0);
-        nt_k0 = kk.x; nt_k1 = kk.y; nt_v0 = vv.x; nt_v1 = vv.y;
-      } else {
-        const uint32_t kw = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.k_new) + e0);
-        const uint32_t vw = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.v_new) + e0);
-        nt_k0 = bf16lo(kw); nt_k1 = bf16hi(kw); nt_v0 = bf16lo(vw); nt_v1 = bf16hi(vw);
-      }
+      const uint32_t* kp = f32 ? reinterpret_cast<const uint32_t*>(static_cast<const float*>(a.k_new) + e0)
+                               : reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.k_new) + e0);
+      const uint32_t* vp = f32 ? reinterpret_cast<const uint32_t*>(static_cast<const float*>(a.v_new) + e0)
+                               : reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.v_new) + e0);
+      nt_kw0 = kp[0];
+      nt_kw1 = kp[f32 ? 1 : 0];
+      nt_vw0 = vp[0];
+      nt_vw1 = vp[f32 ? 1 : 0];
     }
   }
   __syncthreads();
@@ -745,6 +748,11 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   const int vsh = (VB == 2) ? 4 * (lane & 1) : (VB == 3) ? ((6 * lane) & 7) : 0;
   if constexpr (!VLM) {
     if (own_new && wave == kMaxGroup) {
+      const bool f32 = a.q_dtype != TQ_BF16;
+      const float nt_k0 = f32 ? __uint_as_float(nt_kw0) : bf16lo(nt_kw0);
+      const float nt_k1 = f32 ? __uint_as_float(nt_kw1) : bf16hi(nt_kw0);
+      const float nt_v0 = f32 ? __uint_as_float(nt_vw0) : bf16lo(nt_vw0);
+      const float nt_v1 = f32 ? __uint_as_float(nt_vw1) : bf16hi(nt_vw0);
       float nt_c0, nt_c1, nt_nhat, nt_rho, nt_s0, nt_s1;
       uint8_t* page = const_cast<uint8_t*>(a.cache) + (int64_t)new_blk * blk_stride + kvh * head_stride;
       new_token_quantize<KB, QJL, VB, FP8>(a, nt_k0, nt_k1, nt_v0, nt_v1, lane, page, (seq_len - 1) & 15, nt_codes,
