@@ -497,17 +497,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll 1
+#pragma unroll 2
           for (int mt = 0; mt < 8; ++mt) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            // the three products in separate accumulators: three MFMA chains instead of one
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = acc, acc2 = acc;
 #pragma unroll
             for (int n = 0; n < 4; ++n) {
               const uint4 sh = *reinterpret_cast<const uint4*>(&sq[(((0 * 8 + mt) * 4 + n) * 64 + lane) * 4]);
               const uint4 sl = *reinterpret_cast<const uint4*>(&sq[(((1 * 8 + mt) * 4 + n) * 64 + lane) * 4]);
-              acc = mfma_f16x32(sl, rh[n], acc);
-              acc = mfma_f16x32(sh, rl[n], acc);
+              acc1 = mfma_f16x32(sl, rh[n], acc1);
+              acc2 = mfma_f16x32(sh, rl[n], acc2);
               acc = mfma_f16x32(sh, rh[n], acc);
             }
+            acc = acc + (acc1 + acc2);
             // lane (j, g) holds p[16mt + 4g + r] of token j: sign bit 1 for p >= 0
             uint32_t nib = 0u;
 #pragma unroll
