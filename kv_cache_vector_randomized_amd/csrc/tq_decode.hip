@@ -613,7 +613,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   // (PolarQuant: leaf factors are in [-1, 1], scaled by 2^14)
   const int s2 = FP8 ? 0 : POLAR ? 14 : 15 - __builtin_amdgcn_frexp_expf(kc_top);
   if constexpr (POLAR) {
-    if (tid < 32) ptab[tid] = tid < 16 ? make_float2(a.c->pcs1[2 * tid], a.c->pcs1[2 * tid + 1])
+    // (level 1 also carries the 2^14 scale of the MFMA operand, so the leaves come out scaled)
+    if (tid < 32) ptab[tid] = tid < 16 ? make_float2(16384.f * a.c->pcs1[2 * tid], 16384.f * a.c->pcs1[2 * tid + 1])
                                        : make_float2(a.c->pcsU[2 * tid - 32], a.c->pcsU[2 * tid - 31]);
   }
   if (!FP8 && !POLAR && tid < Tab::kEntries) {
@@ -836,10 +837,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
           uint32_t wv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float x = f[4 * kap + e] * 16384.f;
-            const _Float16 hi = (_Float16)x;
-            const _Float16 lo = (_Float16)(x - (float)hi);
-            wv[e] = (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
+            // x = hi + lo: hi keeps x's top 11 significant bits (an f16 value for
+            // |x| >= 2^-14), lo = x - hi exactly, both packed toward zero in one
+            // instruction (lo loses at most 2^-10 of itself: |error| < 2^-20 |x|)
+            const float x = f[4 * kap + e];
+            const float hi = __uint_as_float(__float_as_uint(x) & 0xFFFFE000u);
+            wv[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi, x - hi));
           }
           const uint4 qa = *reinterpret_cast<const uint4*>(qa_src + 4 * kap);
           D[pg] = mfma_f16(qa, make_uint4(wv[0], wv[1], wv[2], wv[3]), D[pg]);
