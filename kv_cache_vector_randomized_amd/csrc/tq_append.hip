@@ -723,6 +723,7 @@ hipError_t launch_append(const AppendArgs& a, int dtype, int key_bits, int key_m
                          hipStream_t s) {
   if (key_mode == TQ_KEY_POLAR) {
     if (val_mode != TQ_VAL_UNIFORM) return hipErrorInvalidValue;
+    if (a.num_tokens * a.hkv <= kPolarWaveRows) return launch_polar_append_rows(a, dtype, key_bits, val_bits, s);
     const hipError_t e = launch_polar_keys(a, dtype, key_bits, s);
     if (e != hipSuccess) return e;
     switch (val_bits) {

@@ -134,6 +134,9 @@ hipError_t launch_decode(const DecodeArgs& a, int key_bits, int key_mode, int va
 hipError_t launch_transfer(bool to_host, void* cache, void* host, const int32_t* block_ids, int64_t n,
                            int64_t num_blocks, int64_t block_bytes, int grid, hipStream_t s);
 hipError_t launch_polar_keys(const AppendArgs& a, int dtype, int key_bits, hipStream_t s);
+// PolarQuant keys and uniform values of few rows in one launch (one wave per row)
+constexpr int64_t kPolarWaveRows = 32768;
+hipError_t launch_polar_append_rows(const AppendArgs& a, int dtype, int key_bits, int val_bits, hipStream_t s);
 hipError_t launch_polar_dequant(const DequantArgs& a, int key_bits, int val_bits, bool bf16_out, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, int key_bits, int key_mode, int val_bits, int val_mode, bool bf16_out,
                           hipStream_t s);

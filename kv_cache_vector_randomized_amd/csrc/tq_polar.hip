@@ -18,6 +18,8 @@
 // the decode kernel (key format kKmPolar).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "tq_device.h"
 
 namespace tq {
@@ -45,6 +47,12 @@ __device__ __forceinline__ uint32_t polar_code(float theta, bool level1) {
   }
   const float x = theta * ((float)(1 << B) / (0.5f * kPi));
   return (uint32_t)fminf(floorf(x), (float)((1 << B) - 1));
+}
+
+__device__ __forceinline__ float wave_max_xor(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
 }
 
 }  // namespace
@@ -84,6 +92,94 @@ __global__ __launch_bounds__(256) void append_polar_kernel(AppendArgs a) {
   const int so = (int)(slot & 15);
   store_words<KB>(page + a.f.kcodes + so * (KB * 16), w);
   reinterpret_cast<float*>(page + a.f.knorm)[so] = x[0];
+}
+
+// ---------------------------------------------------------------------------
+// Append of few rows (a decode step's new tokens): one wave per (token, head)
+// row, keys and values together; lane l holds coordinates 2l and 2l+1 of both.
+// The rotation is the butterfly across lanes.  Node n of tree level L sits in
+// lane n 2^(L-1), its second child one exchange of 2^(L-2) lanes away.  Every
+// value is computed with the same operations, in the same order, as in the
+// one-lane-per-row kernels, so the bytes are the same.  Codes gather in LDS at
+// their slots and leave as the packed row's bytes.  Values: the per-vector
+// uniform rule (min, correctly rounded scale, codes) of the values kernel.
+// ---------------------------------------------------------------------------
+template <int KB, int VB, bool BF16>
+__global__ __launch_bounds__(256) void append_polar_wave_kernel(AppendArgs a) {
+  __shared__ __align__(16) uint8_t kcod[4][kDim];
+  __shared__ __align__(16) uint8_t vcod[4][kDim];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t rows = a.num_tokens * a.hkv;
+  const int64_t step = (int64_t)gridDim.x * 4;
+  // sign word and bit of coordinates 2l, 2l+1
+  const int sw = lane >> 4;
+  const uint32_t sbits = sw == 0 ? a.sign_bits[0] : sw == 1 ? a.sign_bits[1] : sw == 2 ? a.sign_bits[2] : a.sign_bits[3];
+  const uint32_t sg0 = ((sbits >> (2 * (lane & 15))) & 1u) << 31, sg1 = ((sbits >> (2 * (lane & 15) + 1)) & 1u) << 31;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < rows; r += step) {   // uniform over the wave
+    const int64_t t = r / a.hkv;
+    const int h = (int)(r - t * a.hkv);
+    const int64_t slot = a.slots[t];
+    if (slot < 0 || slot >= a.num_blocks * kBlockTokensDev) continue;
+    uint8_t* page = a.cache + ((slot >> 4) * a.hkv + h) * (int64_t)a.f.page_bytes;
+    const int so = (int)(slot & 15);
+    float k0, k1, v0, v1;
+    if constexpr (BF16) {
+      const uint32_t kw = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.k) + r * kDim)[lane];
+      const uint32_t vw = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.v) + r * kDim)[lane];
+      k0 = bf16lo(kw); k1 = bf16hi(kw); v0 = bf16lo(vw); v1 = bf16hi(vw);
+    } else {
+      const float2 kk = reinterpret_cast<const float2*>(static_cast<const float*>(a.k) + r * kDim)[lane];
+      const float2 vv = reinterpret_cast<const float2*>(static_cast<const float*>(a.v) + r * kDim)[lane];
+      k0 = kk.x; k1 = kk.y; v0 = vv.x; v1 = vv.y;
+    }
+    // keys: signs, the 128-point butterfly (coordinate bit 0 in the lane, bits
+    // 1..6 across lanes 1..32 apart), 1/sqrt(d)
+    k0 = __uint_as_float(__float_as_uint(k0) ^ sg0);
+    k1 = __uint_as_float(__float_as_uint(k1) ^ sg1);
+    float y0 = k0 + k1, y1 = k0 - k1;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const float p0 = __shfl_xor(y0, m), p1 = __shfl_xor(y1, m);
+      const bool up = (lane & m) != 0;
+      y0 = up ? p0 - y0 : y0 + p0;
+      y1 = up ? p1 - y1 : y1 + p1;
+    }
+    y0 *= kInvSqrtDim;
+    y1 *= kInvSqrtDim;
+    if (lane == 0) kcod[wave][kDim - 1] = 0;                 // the unused slot
+    kcod[wave][polar_slot(1, lane)] = (uint8_t)polar_code<KB>(atan2f(y1, y0), true);
+    float rad = sqrtf(fmaf(y0, y0, y1 * y1));
+#pragma unroll
+    for (int lv = 2; lv <= 7; ++lv) {
+      const float u = rad, v = __shfl_xor(rad, 1 << (lv - 2));
+      if ((lane & ((1 << (lv - 1)) - 1)) == 0)
+        kcod[wave][polar_slot(lv, lane >> (lv - 1))] = (uint8_t)polar_code<KB>(atan2f(v, u), false);
+      rad = sqrtf(fmaf(u, u, v * v));
+    }
+    // values: per-vector min and correctly rounded scale
+    const float mn = -wave_max_xor(-fminf(v0, v1));
+    const float mx = wave_max_xor(fmaxf(v0, v1));
+    constexpr float levels = (float)((1 << VB) - 1);
+    const float sc = (mx - mn) / levels;
+    const float inv = sc > 0.f ? 1.f / sc : 0.f;
+    const float xv[2] = {v0, v1};
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float d = xv[e] - mn;
+      float xq = d * inv;
+      if (fabsf(xq - floorf(xq) - 0.5f) < 3.814697265625e-06f) xq = d / sc;
+      vcod[wave][2 * lane + e] = (uint8_t)fminf(rintf(xq), levels);
+    }
+    wave_sync_lds();
+    if (lane < 16 * KB) page[a.f.kcodes + so * (KB * 16) + lane] = (uint8_t)stream_byte<KB>(kcod[wave], lane);
+    if (lane < 16 * VB) page[a.f.vcodes + 16 * lane + so] = (uint8_t)stream_byte<VB>(vcod[wave], lane);
+    if (lane == 0) {
+      reinterpret_cast<float*>(page + a.f.knorm)[so] = rad;   // the root radius: ||y||
+      reinterpret_cast<float*>(page + a.f.vmin)[so] = mn;
+      reinterpret_cast<float*>(page + a.f.vscale)[so] = sc;
+    }
+    wave_sync_lds();   // the codes are read before the next row overwrites them
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -195,6 +291,37 @@ hipError_t launch_polar_keys(const AppendArgs& a, int dtype, int key_bits, hipSt
     case 2: return polar_keys<2>(a, dtype, s);
     case 3: return polar_keys<3>(a, dtype, s);
     case 4: return polar_keys<4>(a, dtype, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+namespace {
+
+template <int KB, int VB>
+hipError_t polar_wave(const AppendArgs& a, int dtype, hipStream_t s) {
+  const dim3 grid((unsigned)std::min<int64_t>((a.num_tokens * a.hkv + 3) / 4, 8192));
+  if (dtype == TQ_BF16) hipLaunchKernelGGL((append_polar_wave_kernel<KB, VB, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((append_polar_wave_kernel<KB, VB, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int KB>
+hipError_t polar_wave_vb(const AppendArgs& a, int dtype, int val_bits, hipStream_t s) {
+  switch (val_bits) {
+    case 2: return polar_wave<KB, 2>(a, dtype, s);
+    case 3: return polar_wave<KB, 3>(a, dtype, s);
+    case 4: return polar_wave<KB, 4>(a, dtype, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_polar_append_rows(const AppendArgs& a, int dtype, int key_bits, int val_bits, hipStream_t s) {
+  switch (key_bits) {
+    case 2: return polar_wave_vb<2>(a, dtype, val_bits, s);
+    case 3: return polar_wave_vb<3>(a, dtype, val_bits, s);
+    case 4: return polar_wave_vb<4>(a, dtype, val_bits, s);
   }
   return hipErrorInvalidValue;
 }
