@@ -27,9 +27,8 @@ Other workloads (--workload):
   turbo8v3        the GQA shape with 8-bit Lloyd-Max keys (corrected norm) and
                   3-bit values (an on-device default named on the pages), same step;
   polar3          the GQA shape with PolarQuant keys (3-bit angles of the
-                  recursive polar transform, fp32 radius) and 4-bit values; the
-                  one-launch step does not take them, so append and decode are
-                  two launches;
+                  recursive polar transform, fp32 radius) and 4-bit values, same
+                  step;
   dequant_layer   the prefill_append cache (131072 tokens x 8 KV heads)
                   reconstructed into a bf16 buffer (--dequant-f32: fp32) in one
                   tq_dequantize_rows call: the whole-cache reconstruction that
@@ -128,8 +127,6 @@ def main():
         sys.exit(1)
     torch.cuda.init()
     wname, kind = MODES[args.workload]
-    if wname == "polar3":
-        args.separate = True     # the one-launch step does not take PolarQuant keys
     w = synth.WORKLOADS[wname]
     B, T, Hkv, Hq, d = w.batch, w.context, w.num_kv_heads, w.num_q_heads, w.head_dim
     cfg = tq.make_config(d, Hkv, Hq, w.key_bits, w.key_mode, w.val_bits, w.val_mode)

@@ -100,8 +100,7 @@ typedef enum {
                             subtree-major: quarter g of the coordinates owns slots
                             32g..32g+31 (its level 1..5 angles in node order; slot
                             31 holds the root, slots 63 and 95 the two level-6
-                            angles, slot 127 is zero).  Uniform values only; not
-                            taken by tq_append_decode.                            */
+                            angles, slot 127 is zero).  Uniform values only.     */
 } tq_key_mode;
 
 typedef enum {

@@ -349,7 +349,7 @@ __device__ __forceinline__ uint32_t interleave16(uint32_t e, uint32_t o) {
 // returns their key centroids (c0, c1), the stored norm, the QJL residual norm and
 // the signs (+1/-1) of rows 2l, 2l+1 of S r'; the dequantized value row goes to
 // vhat.  codes / rbuf are LDS scratch of the wave.
-template <int KB, bool QJL, int VB, bool FP8>
+template <int KB, bool QJL, int VB, bool FP8, bool POLAR>
 __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, float v0, float v1, int lane,
                                    uint8_t* page, int so, uint8_t (&codes)[2][kDim], float* vhat, float* rbuf,
                                    float& c0, float& c1, float& nhat, float& rho, float& sgn0, float& sgn1) {
@@ -380,6 +380,34 @@ __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, floa
     x0 = upper ? p0 - x0 : x0 + p0;
     x1 = upper ? p1 - x1 : x1 + p1;
   }
+  if constexpr (POLAR) {
+    // PolarQuant: the tree over y = z / sqrt(d) across the wave as in the append
+    // (node n of level L in lane n 2^(L-1)), each angle's cell index at its slot;
+    // the root radius is the norm.  For the logit: the unit leaves of this lane's
+    // coordinates, products of the cell centres' cos / sin along the path, top down.
+    const float y0 = x0 * kInvSqrtDim, y1 = x1 * kInvSqrtDim;
+    if (lane == 0) codes[0][kDim - 1] = 0;                   // the unused slot
+    codes[0][polar_slot(1, lane)] = (uint8_t)polar_code<KB>(atan2f(y1, y0), true);
+    float rad = sqrtf(fmaf(y0, y0, y1 * y1));
+#pragma unroll
+    for (int lv = 2; lv <= 7; ++lv) {
+      const float u = rad, v = __shfl_xor(rad, 1 << (lv - 2));
+      if ((lane & ((1 << (lv - 1)) - 1)) == 0)
+        codes[0][polar_slot(lv, lane >> (lv - 1))] = (uint8_t)polar_code<KB>(atan2f(v, u), false);
+      rad = sqrtf(fmaf(u, u, v * v));
+    }
+    nhat = __shfl(rad, 0);
+    wave_sync_lds();
+    float pf = 1.f;
+#pragma unroll
+    for (int lv = 7; lv >= 2; --lv) {
+      const uint32_t cd = codes[0][polar_slot(lv, lane >> (lv - 1))];
+      pf *= ((lane >> (lv - 2)) & 1) ? a.c->pcsU[2 * cd + 1] : a.c->pcsU[2 * cd];
+    }
+    const uint32_t c1d = codes[0][polar_slot(1, lane)];
+    c0 = pf * a.c->pcs1[2 * c1d];
+    c1 = pf * a.c->pcs1[2 * c1d + 1];
+  } else {
   const float ss = wave_sum(fmaf(x0, x0, x1 * x1));
   const float inv = ss > 0.f ? 1.f / sqrtf(ss) : 0.f;     // a zero key gives codes 2^(b-1)
   if constexpr (KB == 8) {
@@ -414,6 +442,7 @@ __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, floa
           interleave16((uint32_t)(em >> (16 * lane)), (uint32_t)(om >> (16 * lane)));
   }
   }
+  }
   // uniform values, as the append kernel: codes floor(fl32(x - mn) / sc + 1/2)
   const float mn = -wave_max(-fminf(v0, v1));
   const float mx = wave_max(fmaxf(v0, v1));
@@ -423,8 +452,10 @@ __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, floa
   const uint32_t vc0 = (uint32_t)fmaf(v0 - mn, vinv, 0.5f), vc1 = (uint32_t)fmaf(v1 - mn, vinv, 0.5f);
   vhat[2 * lane] = fmaf(sc, (float)vc0, mn);
   vhat[2 * lane + 1] = fmaf(sc, (float)vc1, mn);
-  codes[0][2 * lane] = (uint8_t)kc0;
-  codes[0][2 * lane + 1] = (uint8_t)kc1;
+  if constexpr (!POLAR) {
+    codes[0][2 * lane] = (uint8_t)kc0;
+    codes[0][2 * lane + 1] = (uint8_t)kc1;
+  }
   codes[1][2 * lane] = (uint8_t)vc0;
   codes[1][2 * lane + 1] = (uint8_t)vc1;
   wave_sync_lds();
@@ -756,7 +787,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
       const float nt_v1 = f32 ? __uint_as_float(nt_vw1) : bf16hi(nt_vw0);
       float nt_c0, nt_c1, nt_nhat, nt_rho, nt_s0, nt_s1;
       uint8_t* page = const_cast<uint8_t*>(a.cache) + (int64_t)new_blk * blk_stride + kvh * head_stride;
-      new_token_quantize<KB, QJL, VB, FP8>(a, nt_k0, nt_k1, nt_v0, nt_v1, lane, page, (seq_len - 1) & 15, nt_codes,
+      new_token_quantize<KB, QJL, VB, FP8, POLAR>(a, nt_k0, nt_k1, nt_v0, nt_v1, lane, page, (seq_len - 1) & 15, nt_codes,
                                       nt_vhat, nt_r, nt_c0, nt_c1, nt_nhat, nt_rho, nt_s0, nt_s1);
       // the new token's base-2 logit for each head, then the wave's softmax state
       // starts from it (weight 1 at its own max)

@@ -197,4 +197,29 @@ __device__ __forceinline__ uint32_t fp8_e4m3(float x) {
   return code | sgn;
 }
 
+// PolarQuant keys (lilting.ch TurboQuant article, PolarQuant section): slot of
+// the angle of node `node` at tree level `level` in the 128-slot code row
+// (subtree-major: quarter g of the coordinates owns slots 32g..32g+31; slot 31
+// holds the root, slots 63 and 95 the two level-6 angles, slot 127 is unused),
+// and the cell index of an angle: level 1 over [-pi, pi) (pi wraps to -pi),
+// higher levels over [0, pi/2].
+constexpr int polar_slot(int level, int node) {
+  return level == 7 ? 31
+       : level == 6 ? 32 * (node + 1) + 31
+       : 32 * (node >> (5 - level)) +
+             (level == 1 ? 0 : level == 2 ? 16 : level == 3 ? 24 : level == 4 ? 28 : 30) +
+             (node & ((16 >> (level - 1)) - 1));
+}
+
+template <int B>
+__device__ __forceinline__ uint32_t polar_code(float theta, bool level1) {
+  constexpr float kPi = 3.14159265358979323846f;
+  if (level1) {
+    const float x = (theta + kPi) * ((float)(1 << B) / (2.f * kPi));
+    return (uint32_t)(int)floorf(x) & ((1u << B) - 1u);
+  }
+  const float x = theta * ((float)(1 << B) / (0.5f * kPi));
+  return (uint32_t)fminf(floorf(x), (float)((1 << B) - 1));
+}
+
 }  // namespace tq

@@ -494,8 +494,6 @@ tq_status decode_common(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cac
     if (!aligned(k_new, 4) || !aligned(v_new, 4)) return fail(TQ_ERR_INVALID_ARG, "misaligned k_new / v_new");
     if (ctx->cfg.val_mode == TQ_VAL_LLOYD)
       return fail(TQ_ERR_UNSUPPORTED, "the fused append takes uniform values only");
-    if (ctx->cfg.key_mode == TQ_KEY_POLAR)
-      return fail(TQ_ERR_UNSUPPORTED, "the fused append does not take PolarQuant keys");
   }
   const size_t need = tq_decode_workspace_bytes(ctx, batch, max_seq_len);
   if (workspace_bytes < need)

@@ -26,29 +26,6 @@ namespace tq {
 
 namespace {
 
-// Slot of level-l node n (l = 1..5) of quarter g = n >> (5 - l); the spare slots
-// hold level 6 (node h at 32(h+1) + 31) and the root (31).
-constexpr int polar_slot(int level, int node) {
-  return level == 7 ? 31
-       : level == 6 ? 32 * (node + 1) + 31
-       : 32 * (node >> (5 - level)) +
-             (level == 1 ? 0 : level == 2 ? 16 : level == 3 ? 24 : level == 4 ? 28 : 30) +
-             (node & ((16 >> (level - 1)) - 1));
-}
-
-// Cell index of an angle: level 1 over [-pi, pi) (pi wraps to -pi), higher levels
-// over [0, pi/2].
-template <int B>
-__device__ __forceinline__ uint32_t polar_code(float theta, bool level1) {
-  constexpr float kPi = 3.14159265358979323846f;
-  if (level1) {
-    const float x = (theta + kPi) * ((float)(1 << B) / (2.f * kPi));
-    return (uint32_t)(int)floorf(x) & ((1u << B) - 1u);
-  }
-  const float x = theta * ((float)(1 << B) / (0.5f * kPi));
-  return (uint32_t)fminf(floorf(x), (float)((1 << B) - 1));
-}
-
 __device__ __forceinline__ float wave_max_xor(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));

@@ -31,6 +31,7 @@ CASES = {
     "k3qjl_v2": [129, 30],
     "k8v4": [333, 1, 16, 0],
     "turbo8v3": [200, 17],
+    "polar3": [300, 1, 47, 0],
 }
 
 
@@ -105,20 +106,6 @@ def test_append_decode_matches_oracle(name):
             worst = max(worst, el, eo)
             assert el <= H.REL_TOL and eo <= H.REL_TOL, (b, h, el, eo)
     print(f"  worst relative error {worst:.3e}")
-
-
-def test_append_decode_refuses_polar_keys():
-    """The one-launch step does not take PolarQuant keys: refused before any launch."""
-    from kv_cache_vector_randomized_amd import tq
-    from kv_cache_vector_randomized_amd.torch_api import PagedKVCache
-    w = synth.WORKLOADS["polar3"]
-    lay = synth.paged_layout(1, [20], 45)
-    cache = PagedKVCache(H.make_context(w), lay.num_blocks, fill=0)
-    z = torch.zeros((1, w.num_kv_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
-    q = torch.zeros((1, w.num_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(tq.TQError):
-        cache.append_decode(z, z, q, torch.from_numpy(lay.block_tables).cuda(), torch.from_numpy(lay.seq_lens).cuda(),
-                            20, 1.0 / math.sqrt(w.head_dim))
 
 
 def test_append_decode_equals_two_launches():

@@ -1,8 +1,8 @@
 """GPU tests of HIP graph capture of the hot-path calls (a serving loop replays its
 decode step as a graph; the bench times the steps that way).
 
-One graph holds a decode step (the one-launch append-decode, or append then
-decode for key formats the fused step does not take), a plain decode, a
+One graph holds a decode step (the one-launch append-decode, or for PolarQuant
+keys also append then decode), a plain decode, a
 dequantize_rows call and a whole-batch append into a second cache.  It is
 replayed three times, with eager work (fills of the outputs, an eager decode on
 another cache) and synchronizations between the replays, and every replay is
@@ -32,11 +32,12 @@ def _cuda():
     torch.cuda.init()
 
 
-@pytest.mark.parametrize("name", ["gqa_decode", "qjl", "turbo8v3", "polar3"])
-def test_graph_replays_match_eager(name):
+@pytest.mark.parametrize("name,fused", [("gqa_decode", True), ("qjl", True), ("turbo8v3", True), ("polar3", True),
+                                        ("polar3", False)])
+def test_graph_replays_match_eager(name, fused):
     from kv_cache_vector_randomized_amd.torch_api import PagedKVCache
     w = synth.WORKLOADS[name]
-    print(f"[graph] {name}", flush=True)
+    print(f"[graph] {name} ({'one launch' if fused else 'append, then decode'})", flush=True)
     lens = np.array([300, 97, 16, 1], np.int64)
     B, T = len(lens), int(lens.max())
     lay = synth.paged_layout(B, lens, 71)
@@ -60,7 +61,6 @@ def test_graph_replays_match_eager(name):
     tables, seq_lens = dev(lay.block_tables), dev(lay.seq_lens)
     s_ctx, s_new, s_all = dev(ctx_slots), dev(new_slots), dev(all_slots)
     scale = 1.0 / math.sqrt(w.head_dim)
-    fused = w.key_mode != "polar"
     hkv, d = w.num_kv_heads, w.head_dim
 
     def make():
