@@ -2,8 +2,8 @@
 decode step as a graph; the bench times the steps that way).
 
 One graph holds a decode step (the one-launch append-decode, or for PolarQuant
-keys also append then decode), a plain decode, a
-dequantize_rows call and a whole-batch append into a second cache.  It is
+keys also append then decode), a plain decode, a dequantize_rows call and a
+whole-batch append into a second cache.  It is
 replayed three times, with eager work (fills of the outputs, an eager decode on
 another cache) and synchronizations between the replays, and every replay is
 checked against the same calls made eagerly: cache bytes and reconstructed rows
