@@ -337,10 +337,10 @@ def main():
 
 
 def cpu_baseline(w, kind, k_all, v_all, q_np, lay, np):
-    """The fp64 oracle (untuned) on a bounded sample of the same step: one sequence's
-    new-token quantize-append plus its decode attention over its context (for the
-    append workloads: the quantize-append of 16384 of the step's tokens;
-    dequant_layer: the reconstruction of 8192 tokens)."""
+    """The fp64 oracle (untuned) on a bounded sample of the same step, about 10 s of
+    CPU work: one sequence's new-token quantize-append plus its decode attention
+    over its context (for the append workloads: the quantize-append of 16384 of
+    the step's tokens; dequant_layer: the reconstruction of 16384 tokens)."""
     from oracle import tq_oracle as O
     from kv_cache_vector_randomized_amd import synth
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
@@ -355,28 +355,28 @@ def cpu_baseline(w, kind, k_all, v_all, q_np, lay, np):
     slots = lay.slots(b, 0, T)
     cache = O.new_cache(cfg, lay.num_blocks)
     if kind == "dequant":
-        n = 8192
+        n = 16384
         O.quantize_append(cfg, cache, f64(k_all[:n]), f64(v_all[:n]), slots[:n], signs, kcb, S=S)
         vcb = O.codebook(w.val_bits, d) if w.val_mode == "lloyd" else None
         times = []
-        for _ in range(5):
+        for _ in range(15):
             t0 = time.perf_counter()
             for h in range(Hkv):
                 O.dequantize_slots(cfg, cache, slots[:n], h, signs, kcb, vcb)
             times.append(time.perf_counter() - t0)
         sec = statistics.median(times)
         sample_bytes = n * Hkv * (th + 2 * d * 2) + n * 8
-        sample = f"reconstruction of {n} tokens x {Hkv} kv heads (bf16-sized output), median of 5 runs, {sec:.2f} s each"
+        sample = f"reconstruction of {n} tokens x {Hkv} kv heads (bf16-sized output), median of 15 runs, {sec:.2f} s each"
     elif kind == "append":
         n = 16384
         times = []
-        for _ in range(3):
+        for _ in range(5):
             t0 = time.perf_counter()
             O.quantize_append(cfg, cache, f64(k_all[:n]), f64(v_all[:n]), slots[:n], signs, kcb, S=S)
             times.append(time.perf_counter() - t0)
         sec = statistics.median(times)
         sample_bytes = n * Hkv * (2 * d * 2 + th) + n * 8
-        sample = f"quantize-append of {n} tokens x {Hkv} kv heads, median of 3 runs, {sec:.2f} s each"
+        sample = f"quantize-append of {n} tokens x {Hkv} kv heads, median of 5 runs, {sec:.2f} s each"
     else:
         t0 = time.time()
         O.quantize_append(cfg, cache, f64(k_all[: T - 1]), f64(v_all[: T - 1]), slots[: T - 1], signs, kcb, S=S)
