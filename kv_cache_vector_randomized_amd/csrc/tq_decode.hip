@@ -551,9 +551,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   __shared__ __align__(16) float nt_r[QJL ? kDim : 1];
 
   const int G = a.group;
-  int seq_len = a.seq_lens[b];
-  seq_len = max(0, min(seq_len, min(a.max_seq, 16 * a.max_blocks)));
-  if (a.num_blocks <= 0) seq_len = 0;     // no page exists: every block id is absent
   // Split `split` owns tiles [tile_begin, tile_end): an even share of the longest
   // sequence's tiles (at most 64).
   const int tile_begin = (int)((uint32_t)(split * a.tiles_total) / (uint32_t)a.splits);
@@ -561,24 +558,30 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   const int64_t head_stride = a.f.page_bytes;
   const int64_t blk_stride = head_stride * a.hkv;
   const int32_t* table = a.block_tables + (int64_t)b * a.max_blocks;
-  // Fused append: position seq_len - 1 is the new token (when its block exists); it
-  // is left out of the tiles and enters through the work-group whose split holds it.
-  int new_blk = -1;
-  if (!VLM && a.k_new != nullptr && seq_len > 0) {
-    const int raw = table[(seq_len - 1) >> 4];
-    new_blk = (raw >= 0 && (int64_t)raw < a.num_blocks) ? raw : -1;
-  }
-  const bool has_new = new_blk >= 0;
-  const bool own_new = has_new && ((seq_len - 1) >> 6) >= tile_begin && ((seq_len - 1) >> 6) < tile_end;
-  const int tok_end = min(seq_len - (has_new ? 1 : 0), tile_end * 64);
   uint32_t (&wt)[4][68] = wT[wave];
 
-  // ---- Prologue.  The constants the shared tables need are fetched first (the
-  // work-group barrier below then does not wait for page data), then the block
-  // ids and the query row of head `wave`; each wave's first tile (tile_begin +
-  // wave) is loaded before the query is rotated, so that its latency overlaps the
-  // rotation, the tables and the barrier.  Block-table reads do not wait for the
-  // sequence length: entries past the end are dropped once it is known.
+  // ---- Prologue.  First the block ids of the wave's first tile (tile_begin +
+  // wave) and of the range, the constants the shared tables need, the query row
+  // of head `wave`, the sequence length and the block-table entry of its last
+  // position (uniform: scalar loads), then the first tile's pages.
+  // Only the first tile's ids are waited for before the pages are requested:
+  // pages are read at every in-range block id, and which tokens count is decided
+  // once the length (and the new token's block) is known.  So the first pages
+  // are in flight after one round trip, and their latency overlaps the rest of
+  // the prologue: the tables, the query rotation and the barrier.
+  // (a table row with no entries is never read: seq_lens stands in for it)
+  const int32_t* trow = a.max_blocks > 0 ? table : a.seq_lens + b;
+  const int tmax = max(a.max_blocks - 1, 0);
+  // Loads of the prologue are unconditional (heads >= G read head 0 and are
+  // zeroed, a wave without a tile reads an in-range page): conditional loads
+  // would make the compiler wait for every earlier load before the first use of
+  // any.  The vector loads that one wait covers are issued in the order needed.
+  int t_cur = tile_begin + wave;
+  const int page_first = 4 * t_cur + (lane & 3);
+  const int raw_first = trow[min(page_first, tmax)];
+  const int e_st = min(tid, kMaxPagesPerSplit - 1);
+  const int page_st = 4 * tile_begin + e_st;
+  const int raw_st = trow[min(page_st, tmax)];
   const float kc_top = (FP8 || POLAR) ? 1.f : a.c->kc[(1 << KB) - 1];
   float kc_e[Tab::kCodes];
   if constexpr (!FP8 && !POLAR) {
@@ -586,9 +589,6 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
 #pragma unroll
     for (int i = 0; i < Tab::kCodes; ++i) kc_e[i] = a.c->kc[(ent >> (KB * i)) & ((1 << KB) - 1)];
   }
-  // Loads of the prologue are unconditional (heads >= G read head 0 and are
-  // zeroed, a wave without a tile reads block 0): conditional loads would make
-  // the compiler wait for every earlier load before the first use of any.
   // The query pair of this lane (coordinates 2*lane, 2*lane+1) is one word in
   // bf16 or two in fp32; both words are always read (the second re-reads the
   // first for bf16) so that no branch separates the load from its use.
@@ -602,42 +602,59 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     qw1 = qp[f32 ? 1 : 0];
   }
   const float sg0 = a.c->signs[2 * lane], sg1 = a.c->signs[2 * lane + 1];
-  // (a table row with no entries is never read: seq_lens stands in for it)
-  const int32_t* trow = a.max_blocks > 0 ? table : a.seq_lens + b;
-  const int tmax = max(a.max_blocks - 1, 0);
-  {
-    const int e = min(tid, kMaxPagesPerSplit - 1);
-    const int page = 4 * tile_begin + e;
-    int raw = trow[min(page, tmax)];
-    asm volatile("" : "+v"(raw));   // keep the read here, ahead of the tile loads
-    if (tid < kMaxPagesPerSplit)
-      blk_lds[e] = (e >= 4 * (tile_end - tile_begin) || page >= a.max_blocks || raw < 0 ||
-                    (int64_t)raw >= a.num_blocks || page * 16 >= tok_end)
-                       ? -1 : raw;
-  }
-  if (tid == 0) tile_ctr = kDecodeWaves;   // the first kDecodeWaves tiles go to the waves in order
-  int t_cur = tile_begin + wave;
-  bool have = t_cur < tile_end && t_cur * 64 < tok_end;
-  TilePages tp;
+  int seq_len = a.seq_lens[b];
+  seq_len = max(0, min(seq_len, min(a.max_seq, 16 * a.max_blocks)));
+  if (a.num_blocks <= 0) seq_len = 0;     // no page exists: every block id is absent
+  const int last_raw = trow[min(max(seq_len - 1, 0) >> 4, tmax)];
+  // keep the range's block ids here, read in the first tile ids' round trip:
+  // left to the scheduler, the read sinks to its use behind the page loads,
+  // and waiting for it there would wait for the pages too
+  int raw_stv = raw_st;
+  asm volatile("" : "+v"(raw_stv));
+  // the first tile's block ids as read: loads go to in-range ids (block 0 stands
+  // in for the others), validity is applied below
+  TilePages tl;
   int vblk;            // block of the page this lane reads value planes from (page lane/16)
   {
-    const int page = 4 * t_cur + (lane & 3);
-    int raw = trow[min(page, tmax)];
-    asm volatile("" : "+v"(raw));
-    const int v = (!have || page >= a.max_blocks || raw < 0 || (int64_t)raw >= a.num_blocks || page * 16 >= tok_end)
-                      ? -1 : raw;
+    const int l = (page_first >= a.max_blocks || raw_first < 0 || (int64_t)raw_first >= a.num_blocks) ? -1 : raw_first;
 #pragma unroll
-    for (int pg = 0; pg < 4; ++pg) tp.b[pg] = __builtin_amdgcn_readlane(v, pg);
-    vblk = __builtin_amdgcn_ds_bpermute(grp << 2, v);
+    for (int pg = 0; pg < 4; ++pg) tl.b[pg] = __builtin_amdgcn_readlane(l, pg);
+    // (selects, not an LDS exchange: its wait would also cover the scalar loads in flight)
+    vblk = grp == 0 ? tl.b[0] : grp == 1 ? tl.b[1] : grp == 2 ? tl.b[2] : tl.b[3];
   }
 
   KeyTile<KB, QJL> nx;
   uint4 vp[VB == 3 ? 8 : 4];     // Lloyd-Max values: byte planes of coordinates 2*lane, 2*lane+1
   uint4 vq[VB];                  // uniform values: the planes of coordinates 8j..8j+7 of page lane/16
-  load_key_codes<KB, QJL>(nx, a, tp, kvh, lane, blk_stride, head_stride);
-  load_key_scalars<KB, QJL, VLM, FP8>(nx, a, tp, kvh, lane, blk_stride, head_stride);
-  if constexpr (VLM) load_value_planes<VB>(vp, a, tp, kvh, lane, blk_stride, head_stride);
+  load_key_codes<KB, QJL>(nx, a, tl, kvh, lane, blk_stride, head_stride);
+  load_key_scalars<KB, QJL, VLM, FP8>(nx, a, tl, kvh, lane, blk_stride, head_stride);
+  if constexpr (VLM) load_value_planes<VB>(vp, a, tl, kvh, lane, blk_stride, head_stride);
   else load_value_group<VB>(vq, a, vblk, kvh, lane, blk_stride, head_stride);
+
+  // Fused append: position seq_len - 1 is the new token (when its block exists); it
+  // is left out of the tiles and enters through the work-group whose split holds it.
+  const int new_blk = (!VLM && a.k_new != nullptr && seq_len > 0 && a.max_blocks > 0 && last_raw >= 0 &&
+                       (int64_t)last_raw < a.num_blocks) ? last_raw : -1;
+  const bool has_new = new_blk >= 0;
+  const bool own_new = has_new && ((seq_len - 1) >> 6) >= tile_begin && ((seq_len - 1) >> 6) < tile_end;
+  const int tok_end = min(seq_len - (has_new ? 1 : 0), tile_end * 64);
+  // block ids of the range's pages (-1: absent or past the context), and of the
+  // first tile's, with the same rule
+  // (threads past the last entry store the same value to it: no branch for the
+  // compiler to sink the read into, behind the page loads)
+  blk_lds[e_st] = (e_st >= 4 * (tile_end - tile_begin) || page_st >= a.max_blocks || raw_stv < 0 ||
+                   (int64_t)raw_stv >= a.num_blocks || page_st * 16 >= tok_end)
+                      ? -1 : raw_stv;
+  if (tid == 0) tile_ctr = kDecodeWaves;   // the first kDecodeWaves tiles go to the waves in order
+  bool have = t_cur < tile_end && t_cur * 64 < tok_end;
+  TilePages tp;
+  {
+    const int v = (!have || page_first >= a.max_blocks || raw_first < 0 || (int64_t)raw_first >= a.num_blocks ||
+                   page_first * 16 >= tok_end)
+                      ? -1 : raw_first;
+#pragma unroll
+    for (int pg = 0; pg < 4; ++pg) tp.b[pg] = __builtin_amdgcn_readlane(v, pg);
+  }
 
   // Key centroid table: C * 2^s2 with 2^s2 bringing the largest |C| (the last,
   // the codebook being symmetric) into [2^14, 2^15).
