@@ -318,7 +318,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
   __shared__ __align__(16) uint8_t vplane[4][64][16];     // value planes [wave][plane][token]
   // QJL: the f16 terms of S in the operand order of the MFMA (see the key pass)
   __shared__ __align__(16) uint32_t sq[QJL ? kDim * kDim : 4];
-  __shared__ uint32_t sgn[QJL ? 4 : 1][16][4];              // QJL sign rows [wave][token][dword]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -490,13 +489,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
             rh[n] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
             rl[n] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
           }
-          // Sign rows of the wave's 16 tokens, assembled in LDS with OR: bit
-          // 16mt + 4g + r of token j comes from lane (j, g).
-          uint32_t* srow = &sgn[wave][j][0];
-          srow[g] = 0u;
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          // Sign rows of the wave's 16 tokens: lane (j, g) computes bits 16mt + 4g + r
+          // (mt = 0..7, r = 0..3) of token j's row, nibble mt of `mine`.
+          uint32_t mine = 0u;
 #pragma unroll 2
           for (int mt = 0; mt < 8; ++mt) {
             // the three products in separate accumulators: three MFMA chains instead of one
@@ -514,15 +509,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
             uint32_t nib = 0u;
 #pragma unroll
             for (int r = 0; r < 4; ++r) nib |= (acc[r] >= 0.f ? 1u : 0u) << r;
-            atomicOr(&srow[mt >> 1], nib << (16 * (mt & 1) + 4 * g));
+            mine |= nib << (4 * mt);
           }
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          // Dword g of token j's row (rows 32g..32g+31) takes nibbles 2g and 2g+1
+          // of each lane (j, g'), at bits 4g' + r and 16 + 4g' + r.
+          uint32_t srw = 0u;
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            const uint32_t byte = ((uint32_t)__shfl((int)mine, j + 16 * gg) >> (8 * g)) & 0xFFu;
+            srw |= ((byte & 0xFu) << (4 * gg)) | ((byte >> 4) << (16 + 4 * gg));
+          }
           if (slot >= 0) {
             uint8_t* pg = page_of(slot);
             // lane g stores dword g of token j's sign row
-            reinterpret_cast<uint32_t*>(pg + a.f.ksigns + 16 * (slot & 15))[g] = srow[g];
+            reinterpret_cast<uint32_t*>(pg + a.f.ksigns + 16 * (slot & 15))[g] = srw;
             if (g == 0) reinterpret_cast<float*>(pg + a.f.kres)[slot & 15] = __builtin_amdgcn_sqrtf(rr) * kInvSqrtDim;
           }
         }
