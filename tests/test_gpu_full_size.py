@@ -10,7 +10,11 @@ oracle computes one by one:
   of the same heads and its outputs must meet the same bar.  Tiles are handed to
   waves dynamically, so the fp32 summation order differs between launches (the
   outputs cancel, so that shows at about 1e-5); on every head the two launches
-  must agree within the oracle bar.
+  must agree within the oracle bar;
+* the one-launch step (tq_append_decode), the benchmark's default launch: the
+  cache holds positions 0..T-2 of every sequence, one launch quantizes position
+  T-1 and attends over all T; the new tokens' fields against the oracle's
+  quantization, sampled groups against the oracle over the GPU-written bytes.
 """
 import math
 
@@ -26,7 +30,9 @@ pytestmark = pytest.mark.gpu
 # workload -> (sequence, kv head) pairs whose query heads are checked
 SAMPLES = {
     "gqa_decode": [(0, 0), (7, 3), (15, 7)],
+    "long_3bit": [(0, 2), (3, 6)],
     "prefill_append": [(0, 0), (0, 5)],
+    "qjl": [(1, 1), (6, 4)],
 }
 
 
@@ -82,3 +88,39 @@ def test_full_size_append_and_decode_sampled(name):
         worst = max(worst, el, eo, eo2)
         assert el <= H.REL_TOL and eo <= H.REL_TOL and eo2 <= H.REL_TOL, (b, h, el, eo, eo2)
     print(f"  decode sample of {len(heads)} heads: worst relative error {worst:.3e}; launches differ by {drift:.2e}")
+
+
+@pytest.mark.parametrize("name", [n for n in SAMPLES if n != "prefill_append"])
+def test_full_size_one_launch_step_sampled(name):
+    from kv_cache_vector_randomized_amd.torch_api import PagedKVCache
+    w = synth.WORKLOADS[name]
+    print(f"[full size, one launch] {name}", flush=True)
+    B, T, G = w.batch, w.context, w.num_q_heads // w.num_kv_heads
+    lay = synth.paged_layout(B, [T] * B, w.seed)
+    k = synth.kv_tensor(w, B * T, "k")
+    v = synth.kv_tensor(w, B * T, "v")
+    q = synth.query_tensor(w)
+    ctx_rows = np.concatenate([b * T + np.arange(T - 1) for b in range(B)])
+    ctx_slots = np.concatenate([lay.slots(b, 0, T - 1) for b in range(B)])
+    new_rows = np.arange(B) * T + T - 1
+    new_slots = np.array([lay.slots(b, T - 1, T)[0] for b in range(B)], np.int64)
+    ctx = H.make_context(w)
+    cache = PagedKVCache(ctx, lay.num_blocks)
+    cache.append(H.upload(k[ctx_rows], w, torch), H.upload(v[ctx_rows], w, torch), torch.from_numpy(ctx_slots).cuda())
+    out = cache.append_decode(H.upload(k[new_rows], w, torch), H.upload(v[new_rows], w, torch), H.upload(q, w, torch),
+                              torch.from_numpy(lay.block_tables).cuda(), torch.from_numpy(lay.seq_lens).cuda(), T,
+                              1.0 / math.sqrt(w.head_dim))
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().astype(np.float64)
+    cache_np = cache.data.cpu().numpy()
+    report = {}
+    H.compare_append(w, cache_np, new_slots, H.oracle_quantize(w, k[new_rows], v[new_rows]), report)
+    print(f"  new tokens: {report}")
+    heads = [(b, kvh * G + i) for b, kvh in SAMPLES[name] for i in range(G)]
+    _, ref_out = H.oracle_decode(w, q, cache_np, lay, heads=heads)
+    worst = 0.0
+    for b, h in heads:
+        e = H.rel_err(out[b, h], ref_out[b, h])
+        worst = max(worst, e)
+        assert e <= H.REL_TOL, (b, h, e)
+    print(f"  one-launch step, {len(heads)} sampled heads: worst relative error {worst:.3e}")
