@@ -1,0 +1,21 @@
+"""The benchmark's CPU leg (the oracle timed on the host) runs and reports the
+agreed fields, on shrunk copies of each kind of workload (no GPU needed)."""
+import numpy as np
+import pytest
+
+import bench
+from kv_cache_vector_randomized_amd import synth
+
+
+@pytest.mark.parametrize("mode", ["gqa_decode", "qjl", "polar3", "prefill_append", "dequant_layer"])
+def test_cpu_baseline_reports_the_contract_fields(mode):
+    wname, kind = bench.MODES[mode]
+    w = synth.shrink(synth.WORKLOADS[wname], batch=2, context=48)
+    lay = synth.paged_layout(w.batch, [w.context] * w.batch, w.seed)
+    k = synth.kv_tensor(w, w.batch * w.context, "k")
+    v = synth.kv_tensor(w, w.batch * w.context, "v")
+    q = synth.query_tensor(w)
+    rec = bench.cpu_baseline(w, kind, k, v, q, lay, np)
+    assert set(rec) == {"value", "unit", "cores", "kind", "sample"}
+    assert rec["kind"] == "oracle" and rec["unit"] == "GB/s" and rec["value"] > 0 and rec["cores"] >= 1
+    assert isinstance(rec["sample"], str) and rec["sample"]
