@@ -205,7 +205,8 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t max_s
  *                 logits of valid tokens; other entries untouched) for testing.
  *   workspace:    device scratch of at least tq_decode_workspace_bytes bytes,
  *                 16-byte aligned, whose counter region is zero (see above);
- *                 batch * num_kv_heads must not exceed 16384. */
+ *                 batch * num_kv_heads must not exceed 16384 (beyond it the call
+ *                 returns TQ_ERR_UNSUPPORTED before any launch). */
 tq_status tq_decode_attention(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cache, int64_t num_blocks,
                               const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
                               int32_t batch, int32_t max_seq_len, float softmax_scale, float* out,
