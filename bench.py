@@ -244,25 +244,35 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    launch_notes = []
+
     def timed(fn, base):
         """Milliseconds of `steps` calls of fn between one pair of events on the stream.
         With a graph (the default) the calls are captured once, replayed once untimed
         (the graph's upload), then replayed in the timed region: the GPU then runs the
         launches back to back instead of waiting on the Python side between them."""
         a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        if args.eager:
+        g = None
+        if not args.eager:
+            try:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(args.steps):
+                        fn(base + i)
+                g.replay()
+                torch.cuda.synchronize()
+            except RuntimeError as e:          # timed eagerly instead, and said so in the record
+                log(f"[bench] graph capture failed ({e}); launching eagerly")
+                launch_notes.append(f"eager (graph capture failed: {e})")
+                g = None
+                torch.cuda.synchronize()
+        if g is None:
             torch.cuda.synchronize()
             a_ev.record(stream)
             for i in range(args.steps):
                 fn(base + i)
             b_ev.record(stream)
         else:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(args.steps):
-                    fn(base + i)
-            g.replay()
-            torch.cuda.synchronize()
             a_ev.record(stream)
             g.replay()
             b_ev.record(stream)
@@ -331,7 +341,8 @@ def main():
             "p10_p50_p90_us": [round(pct[10], 2), round(pct[50], 2), round(pct[90], 2)],
         },
         "cpu_baseline": cpu,
-        "launch": "eager" if args.eager else "hip graph of the timed steps (replayed once untimed first)",
+        "launch": ("eager" if args.eager else "; ".join(launch_notes) if launch_notes
+                   else "hip graph of the timed steps (replayed once untimed first)"),
     }
     print(json.dumps(rec), flush=True)
 
