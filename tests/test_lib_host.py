@@ -1,9 +1,12 @@
-"""Host-side checks of the C-ABI library (no GPU): it loads, exports every entry
-point that include/tq.h declares, validates configurations, reports the page
-layout of the format, and builds the same fp32 codebook as the oracle."""
+"""Host-side checks of the C-ABI library (no GPU): the header is plain C, the
+library loads, exports every entry point that include/tq.h declares, validates
+configurations, reports the page layout of the format, and builds the same fp32
+codebook as the oracle."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import numpy as np
 import pytest
@@ -12,6 +15,16 @@ from kv_cache_vector_randomized_amd import tq
 from oracle import tq_oracle as O
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="no C compiler")
+def test_header_is_plain_c(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "tq.h"\nint main(void) { return tq_abi_version() > 0 ? 0 : 1; }\n')
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-D__HIP_PLATFORM_AMD__",
+                        "-I" + os.path.join(ROOT, "include"), "-I/opt/rocm/include", str(src)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
 
 
 def _declared_functions():
