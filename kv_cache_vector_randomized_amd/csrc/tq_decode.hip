@@ -481,18 +481,21 @@ constexpr int kKmFp8 = 2;     // E4M3 bytes of the raw key (KB = 8)
 constexpr int kKmPolar = 3;   // PolarQuant angle codes (subtree-major) and the radius
 
 // PolarQuant keys: the 32 coordinates 32g..32g+31 of one token (g = lane / 16) as
-// unit-radius leaf factors, rebuilt top down from the quarter's angle codes
-// (slots 0..30 of the lane's chunk), the root angle and the quarter's level-6
-// angle (cos and sin tables t1: level 1, tu: higher levels, in LDS).
+// unit-radius leaf factors times 2^14, rebuilt top down from the quarter's angle
+// codes (slots 0..30 of the lane's chunk), the root angle and the quarter's
+// level-6 angle.  tu: (cos, sin) of the higher levels' cell centres; jt: for a
+// level-2 code c2 and a level-1 code c1, 2^14 cos(c2) (cos, sin)(c1) at [16 c2 + c1]
+// and 2^14 sin(c2) (cos, sin)(c1) at 256 + 16 c2 + c1, so each level-2 node's four
+// leaves take two reads and four products.  (All tables in LDS.)
 template <int KB>
 __device__ __forceinline__ void polar_leaves(const uint32_t (&kc)[KB], uint32_t root, uint32_t l6, int g,
-                                             const float2* t1, const float2* tu, float (&f)[32]) {
+                                             const float2* tu, const float2* jt, float (&f)[32]) {
   const float2 r7 = tu[root], r6 = tu[l6];
-  float v[16];
+  float v[8];
   v[0] = ((g >> 1) ? r7.y : r7.x) * ((g & 1) ? r6.y : r6.x);
-  // levels 5, 4, 3, 2: 1, 2, 4, 8 angles at slots 30, 28, 24, 16
+  // levels 5, 4, 3: 1, 2, 4 angles at slots 30, 28, 24
 #pragma unroll
-  for (int lv = 5, n = 1, base = 30; lv >= 2; --lv, n <<= 1, base -= n) {   // bases 30, 28, 24, 16
+  for (int lv = 5, n = 1, base = 30; lv >= 3; --lv, n <<= 1, base -= n) {   // bases 30, 28, 24
 #pragma unroll
     for (int i = n - 1; i >= 0; --i) {
       const float2 cs = tu[get_code<KB>(kc, base + i)];
@@ -501,11 +504,17 @@ __device__ __forceinline__ void polar_leaves(const uint32_t (&kc)[KB], uint32_t 
       v[2 * i + 1] = r * cs.y;
     }
   }
+  // levels 2 (slots 16..23) and 1 (slots 0..15) together
 #pragma unroll
-  for (int p = 0; p < 16; ++p) {
-    const float2 cs = t1[get_code<KB>(kc, p)];
-    f[2 * p] = v[p] * cs.x;
-    f[2 * p + 1] = v[p] * cs.y;
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c2 = get_code<KB>(kc, 16 + i) << 4;
+    const float2 ea = jt[c2 | get_code<KB>(kc, 2 * i)];
+    const float2 eb = jt[256 + (c2 | get_code<KB>(kc, 2 * i + 1))];
+    const float r = v[i];
+    f[4 * i] = r * ea.x;
+    f[4 * i + 1] = r * ea.y;
+    f[4 * i + 2] = r * eb.x;
+    f[4 * i + 3] = r * eb.y;
   }
 }
 
@@ -514,7 +523,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   constexpr bool QJL = KM == kKmQjl;
   constexpr bool FP8 = KM == kKmFp8;   // FP8 keys: no rotation, no codebook, no norm
   constexpr bool POLAR = KM == kKmPolar;   // PolarQuant keys: leaf factors from the angles, radius as norm
-  __shared__ float2 ptab[POLAR ? 32 : 1];  // (cos, sin) per code: level 1 at [0, 16), higher levels at [16, 32)
+  __shared__ float2 ptab[POLAR ? 16 : 1];  // (cos, sin) per code of levels 3..7
+  __shared__ float2 pjt[POLAR ? 512 : 1];  // levels 2 and 1 jointly, times 2^14 (see polar_leaves)
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j16 = lane & 15, grp = lane >> 4;   // column (token of a page) and row group (head) of the lane
@@ -661,9 +671,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   // (PolarQuant: leaf factors are in [-1, 1], scaled by 2^14)
   const int s2 = FP8 ? 0 : POLAR ? 14 : 15 - __builtin_amdgcn_frexp_expf(kc_top);
   if constexpr (POLAR) {
-    // (level 1 also carries the 2^14 scale of the MFMA operand, so the leaves come out scaled)
-    if (tid < 32) ptab[tid] = tid < 16 ? make_float2(16384.f * a.c->pcs1[2 * tid], 16384.f * a.c->pcs1[2 * tid + 1])
-                                       : make_float2(a.c->pcsU[2 * tid - 32], a.c->pcsU[2 * tid - 31]);
+    // (the joint table also carries the 2^14 scale of the MFMA operand, so the leaves come out scaled)
+    if (tid < 16) ptab[tid] = make_float2(a.c->pcsU[2 * tid], a.c->pcsU[2 * tid + 1]);
+    if (tid < 512) {
+      const int c2 = (tid >> 4) & 15, c1 = tid & 15;
+      const float h = 16384.f * a.c->pcsU[2 * c2 + (tid >> 8)];   // cos (first child) or sin (second)
+      pjt[tid] = make_float2(h * a.c->pcs1[2 * c1], h * a.c->pcs1[2 * c1 + 1]);
+    }
   }
   if (!FP8 && !POLAR && tid < Tab::kEntries) {
     uint32_t* e = &ktab[tid * Tab::kWords];
@@ -879,7 +893,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
         const uint32_t root = (uint32_t)__shfl((int)c31, j16);
         const uint32_t l6 = (uint32_t)__shfl((int)c31, j16 + 16 * (1 + (grp >> 1)));
         float f[32];
-        polar_leaves<KB>(cur.kc[pg], root, l6, grp, ptab, ptab + 16, f);
+        polar_leaves<KB>(cur.kc[pg], root, l6, grp, ptab, pjt, f);
 #pragma unroll
         for (int kap = 0; kap < 8; ++kap) {
           uint32_t wv[4];
