@@ -34,7 +34,7 @@
  *   - Pointers marked "device" must be device-accessible (hipMalloc'd) and
  *     aligned to their element size; the cache must be 16-byte aligned.
  *
- * Cache format (TQ_FORMAT_VERSION 1)
+ * Cache format (TQ_FORMAT_VERSION 2)
  *   The cache is an array [num_blocks][num_kv_heads][page_bytes] of bytes.  A page
  *   holds the 16 token slots of one block for one KV head; slot = block*16 + offset.
  *   Inside a page the fields follow one another, each holding one row per slot;
@@ -52,6 +52,8 @@
  *     Lloyd-Max values: value norm fp32
  *   Code i of a vector occupies stream bits [b*i, b*i+b); stream bit k is bit
  *   (k mod 8) of byte k/8.  All fp32 scalars are little-endian IEEE-754.
+ *   Version history: 1 stored the value codes slot-major like the other fields;
+ *   2 stores them plane-major.  A reader of transferred pages checks the version.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -65,7 +67,7 @@ extern "C" {
 #endif
 
 #define TQ_ABI_VERSION 1
-#define TQ_FORMAT_VERSION 1
+#define TQ_FORMAT_VERSION 2
 #define TQ_BLOCK_TOKENS 16
 
 typedef enum {

@@ -17,7 +17,7 @@ import numpy as np
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 
 ABI_VERSION = 1
-FORMAT_VERSION = 1
+FORMAT_VERSION = 2
 BLOCK_TOKENS = 16
 
 TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE_TOO_SMALL, TQ_ERR_HIP, TQ_ERR_OUT_OF_MEMORY = range(6)

@@ -26,8 +26,13 @@ Readings taken where the pages are silent (each is listed in the design notes):
   R2  codebook = Lloyd-Max for N(0, 1/d), solved on the positive half and mirrored.
   R5  norm correction: stored norm = ||k|| / ||C[code]||, so ||k_hat|| = ||k||.
   R6  zero key: codes = 2^(b-1), stored norm 0.
-  R11 uniform values: fp32 scale = (max-min)/(2^b-1), code = rint((v-min)/scale) in
-      fp32 (the stored precision), round half to even.
+  R11 uniform values: scale = fl32((max-min)/(2^b-1)) (the stored fp32 scale),
+      code = rint((v-min)/scale) of the exact quotient, round half to even.
+  R18 decision bands (coordinates this close to a boundary may take either code):
+      keys: min_j |y_i - t_j| with y on the unit sphere; uniform values:
+      |frac(x) - 1/2| / (2^b - 1) in [0, 1] range units; QJL signs: the cosine
+      |(S r')_i| / (||S_i|| ||r'||); PolarQuant angles: radians to the nearest
+      cell edge (level 1 wraps at +-pi).
   R12 bit order: LSB-first stream per vector (generalises [P4]'s nibble order).
   R13 QJL: residual in the rotated frame, m = d rows, sign(0) -> bit 1.
   R14 GQA: q head h reads kv head h // (Hq/Hkv); softmax scale supplied by caller.
@@ -54,7 +59,7 @@ from typing import Dict, Optional, Tuple
 import numpy as np
 
 BLOCK_TOKENS = 16
-FORMAT_VERSION = 1
+FORMAT_VERSION = 2
 
 
 # ----------------------------------------------------------------------------
@@ -433,27 +438,30 @@ class ValueCodes:
 def quantize_values_uniform(v: np.ndarray, bits: int) -> ValueCodes:
     """Per-vector uniform quantizer with fp32 min and scale (R11).
 
-    scale = (max - min) / (2^b - 1) and code = clamp(rint((v - min) / scale)), each
-    operation taken in fp32, the precision in which min and scale are stored, so
-    that the integer decision is made in the same precision as the kernel's.
-    A constant vector has scale 0 and all codes 0.  The band (distance of the
-    quotient to a rounding boundary) is measured on the fp64 quotient.
+    [P1 stage 2: stage 1 pairs with uniform quantization of the values]
+      min, max: exact (the inputs are bf16/fp32 values, so both are fp32 values);
+      scale = fl32((max - min) / (2^b - 1)), the stored fp32 scale;
+      code  = clamp(rint((v - min) / scale), 0, 2^b - 1), round half to even, the
+              quotient taken exactly (fp64 holds it to far below the band) with
+              the stored min and scale.
+    For bf16 inputs max - min is an fp32 value, and an fp64 quotient of fp32
+    values rounds to the correctly rounded fp32 quotient (53 >= 2*24 + 2 bits, so
+    the double rounding is innocuous).
+    A constant vector has scale 0 and all codes 0.  The band is the quotient's
+    distance to a rounding boundary in [0, 1] range units: |frac(x) - 1/2| / (2^b - 1).
     """
     v64 = np.asarray(v, dtype=np.float64)
-    v32 = v64.astype(np.float32)                 # inputs are bf16/fp32 values: exact
     levels = (1 << bits) - 1
-    mn = v32.min(axis=-1)
-    mx = v32.max(axis=-1)
-    sc = (mx - mn) / np.float32(levels)          # fp32, correctly rounded
-    safe = np.where(sc > 0, sc, np.float32(1.0))
-    x = (v32 - mn[..., None]) / safe[..., None]  # fp32, correctly rounded
-    x = np.where((sc > 0)[..., None], x, np.float32(0.0))
+    mn = v64.min(axis=-1)
+    mx = v64.max(axis=-1)
+    sc = fl32((mx - mn) / levels)
+    safe = np.where(sc > 0, sc, 1.0)
+    x = (v64 - mn[..., None]) / safe[..., None]
+    x = np.where((sc > 0)[..., None], x, 0.0)
     codes = np.clip(np.rint(x), 0, levels).astype(np.int64)
-    x64 = (v64 - mn[..., None].astype(np.float64)) / safe[..., None].astype(np.float64)
-    frac = x64 - np.floor(x64)
-    band = np.abs(frac - 0.5) / levels
+    band = np.abs(x - np.floor(x) - 0.5) / levels
     band = np.where((sc > 0)[..., None], band, np.inf)
-    return ValueCodes(codes=codes, vmin=mn.astype(np.float64), scale=sc.astype(np.float64), band=band)
+    return ValueCodes(codes=codes, vmin=mn, scale=sc, band=band)
 
 
 def dequantize_values_uniform(codes, vmin, scale) -> np.ndarray:
@@ -482,7 +490,7 @@ def unpack_codes(packed: np.ndarray, bits: int, n: int) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
-# Paged cache format (format version 1).  A page holds 16 tokens of one KV head;
+# Paged cache format (format version 2).  A page holds 16 tokens of one KV head;
 # fields are stored one after another, each holding one row per token slot:
 #   key codes, key norm (f32; absent for FP8 keys), [QJL sign bits, QJL residual norm (f32)],
 #   value codes, value min or value norm (f32), [value scale (f32)].

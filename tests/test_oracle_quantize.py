@@ -169,7 +169,7 @@ def test_paged_write_keeps_sentinel_and_round_trips():
     cfg = O.Config(128, 2, 8, 3, "lloyd_nc", 3, "uniform")
     rng = np.random.default_rng(5)
     k = rng.standard_normal((5, 2, 128))
-    v = rng.standard_normal((5, 2, 128))
+    v = rng.standard_normal((5, 2, 128)).astype(np.float32).astype(np.float64)   # inputs are fp32 values
     signs = synth.sign_vector(3)
     cb = O.codebook(3, 128)
     cache = O.new_cache(cfg, 4)
