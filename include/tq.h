@@ -27,8 +27,8 @@
  *     next synchronization of that stream.
  *   - The caller owns every device buffer and the stream.  The library owns only
  *     the tq_ctx (its constants live in device memory allocated by tq_create and
- *     freed by tq_destroy).  No entry point allocates device memory after
- *     tq_create.
+ *     freed by tq_destroy) and the static scratch of tq_decode_attention_noalloc.
+ *     No entry point allocates device memory after tq_create.
  *   - A tq_ctx is immutable after tq_create: calls on different streams may run
  *     concurrently as long as they write disjoint memory.
  *   - Pointers marked "device" must be device-accessible (hipMalloc'd) and
@@ -213,6 +213,27 @@ tq_status tq_decode_attention(tq_ctx* ctx, const void* q, tq_dtype dt, const voi
                               const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
                               int32_t batch, int32_t max_seq_len, float softmax_scale, float* out,
                               float* logits_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Decode attention that allocates nothing, for callers that cannot allocate
+ * device memory or hand over a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  It is tq_decode_attention
+ * with the split partials and arrival counters in a scratch array that the
+ * library keeps in device memory (TQ_STATIC_SCRATCH_BYTES bytes per GPU, held
+ * from the first tq_create on that GPU until the process ends).  Each call first
+ * zeroes the counters it uses (with a kernel on `stream`), then runs the decode.
+ * All calls on one GPU share that GPU's scratch, and it keeps the last call's
+ * contents: calls that overlap in time on one GPU (on different streams or from
+ * different threads) race and must be serialized by the caller.
+ *   Arguments as for tq_decode_attention, without the workspace.
+ *   Returns TQ_ERR_WORKSPACE_TOO_SMALL, before any launch, when
+ *   tq_decode_workspace_bytes(ctx, batch, max_seq_len) exceeds
+ *   TQ_STATIC_SCRATCH_BYTES; TQ_ERR_HIP when the scratch's device address could
+ *   not be obtained on this GPU. */
+#define TQ_STATIC_SCRATCH_BYTES (65536u + 8388608u)
+tq_status tq_decode_attention_noalloc(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cache, int64_t num_blocks,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                      float softmax_scale, float* out, float* logits_out, hipStream_t stream);
 
 /* One decode step in one launch: store the new token of every sequence, then
  * attend over the context including it (turboquant-vllm write-up, "Incremental

@@ -1240,6 +1240,27 @@ const void* decode_kernel_ptr(int key_bits, int key_mode, int val_bits, int val_
   return nullptr;
 }
 
+// Scratch of the decode entry point that allocates nothing: the arrival counters
+// (kCounterBytes) followed by the split partials, held in device memory for the
+// life of the process, one copy per GPU.  Host code reaches it only through the
+// device address that scratch_address() returns; the array's name is not a
+// device address on the host.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+hipError_t scratch_address(void** out) { return hipGetSymbolAddress(out, HIP_SYMBOL(scratch)); }
+
+// Zero n 32-bit words (a kernel rather than a memset, so the call stays safe
+// to record in a HIP graph).
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t s) {
+  const int grid = std::max(1, std::min((n + 255) / 256, 64));
+  hipLaunchKernelGGL(clear_words_kernel, dim3(grid), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int key_bits, int key_mode, int val_bits, int val_mode,
                          hipStream_t s) {
   const bool qjl = key_mode == TQ_KEY_LLOYD_QJL;

@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstring>
 #include <limits>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -43,6 +44,23 @@ tq_status hip_fail(hipError_t e, const char* what) {
 }
 
 bool is_pow2(uint32_t x) { return x && !(x & (x - 1)); }
+
+// Device address of the static decode scratch, per device (tq_decode_attention_noalloc).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// Look up the scratch address of `dev` (the current device) once; nullptr on failure.
+void* scratch_of(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (tq::scratch_address(&p) == hipSuccess) g_scratch[dev] = p;
+    else (void)hipGetLastError();
+  }
+  return g_scratch[dev];
+}
 
 // ---------------------------------------------------------------------------
 // Lloyd-Max for a Gaussian coordinate (issoh.co.jp page, stage-1 section:
@@ -417,6 +435,7 @@ tq_status tq_create(const tq_config* cfg, const int8_t* signs_host, const float*
     page_per_cu = 2;
   (void)hipGetLastError();
   ctx->page_wgs = page_per_cu * cus;
+  (void)scratch_of(ctx->device);   // set-up of the no-allocation decode's scratch on this device
   *out = ctx;
   return TQ_OK;
 }
@@ -475,7 +494,7 @@ tq_status decode_common(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cac
                         const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
                         int32_t batch, int32_t max_seq_len, float softmax_scale, float* out, float* logits_out,
                         void* workspace, size_t workspace_bytes, const void* k_new, const void* v_new,
-                        hipStream_t stream) {
+                        hipStream_t stream, bool static_scratch = false) {
   if (!ctx) return fail(TQ_ERR_INVALID_ARG, "ctx is null");
   if (dt != TQ_F32 && dt != TQ_BF16) return fail(TQ_ERR_INVALID_ARG, "bad dtype %d", (int)dt);
   if (batch < 0 || max_seq_len < 0 || max_blocks_per_seq < 0 || num_blocks < 0)
@@ -485,9 +504,9 @@ tq_status decode_common(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cac
   if (batch > 65535) return fail(TQ_ERR_UNSUPPORTED, "batch > 65535");
   if ((size_t)batch * ctx->cfg.num_kv_heads * sizeof(uint32_t) > tq::kCounterBytes)
     return fail(TQ_ERR_UNSUPPORTED, "batch * num_kv_heads > %zu", tq::kCounterBytes / sizeof(uint32_t));
-  if (!q || !cache || !block_tables || !seq_lens || !out || !workspace)
+  if (!q || !cache || !block_tables || !seq_lens || !out || (!workspace && !static_scratch))
     return fail(TQ_ERR_INVALID_ARG, "null device pointer");
-  if (!aligned(cache, 16) || !aligned(workspace, 16) || !aligned(q, 4) || !aligned(out, 4))
+  if (!aligned(cache, 16) || (!static_scratch && !aligned(workspace, 16)) || !aligned(q, 4) || !aligned(out, 4))
     return fail(TQ_ERR_INVALID_ARG, "misaligned pointer (cache/workspace need 16 bytes)");
   if (k_new != nullptr) {
     if (!v_new) return fail(TQ_ERR_INVALID_ARG, "v_new is null");
@@ -496,9 +515,18 @@ tq_status decode_common(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cac
       return fail(TQ_ERR_UNSUPPORTED, "the fused append takes uniform values only");
   }
   const size_t need = tq_decode_workspace_bytes(ctx, batch, max_seq_len);
-  if (workspace_bytes < need)
+  if (static_scratch && need > tq::kStaticScratchBytes)
+    return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "batch %d x %u kv heads up to %d tokens needs %zu bytes of scratch; "
+                "the static scratch holds %zu", batch, ctx->cfg.num_kv_heads, max_seq_len, need,
+                tq::kStaticScratchBytes);
+  if (!static_scratch && workspace_bytes < need)
     return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   DeviceGuard g(ctx->device);
+  if (static_scratch) {
+    workspace = scratch_of(ctx->device);
+    if (!workspace) return fail(TQ_ERR_HIP, "no device address for the static scratch on device %d", ctx->device);
+    workspace_bytes = tq::kStaticScratchBytes;
+  }
   tq::DecodeArgs a;
   a.q = q; a.q_dtype = (int32_t)dt; a.cache = (const uint8_t*)cache; a.num_blocks = num_blocks;
   a.block_tables = block_tables; a.max_blocks = max_blocks_per_seq; a.seq_lens = seq_lens;
@@ -515,6 +543,11 @@ tq_status decode_common(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cac
   a.k_new = k_new; a.v_new = v_new;
   a.key_nc = ctx->cfg.key_mode == TQ_KEY_LLOYD_NC;
   a.klut_scale = ctx->klut_scale; a.klut_bias = ctx->klut_bias;
+  if (static_scratch) {
+    // the shared scratch keeps the last call's contents: zero the counters this call uses
+    hipError_t ce = tq::launch_clear_words(a.counters, batch * a.hkv, stream);
+    if (ce != hipSuccess) return hip_fail(ce, "scratch clear launch");
+  }
   hipError_t e = tq::launch_decode(a, (int)ctx->cfg.key_bits, (int)ctx->cfg.key_mode, (int)ctx->cfg.val_bits,
                                    (int)ctx->cfg.val_mode, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -529,6 +562,14 @@ tq_status tq_decode_attention(tq_ctx* ctx, const void* q, tq_dtype dt, const voi
                               float* logits_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return decode_common(ctx, q, dt, cache, num_blocks, block_tables, max_blocks_per_seq, seq_lens, batch, max_seq_len,
                        softmax_scale, out, logits_out, workspace, workspace_bytes, nullptr, nullptr, stream);
+}
+
+tq_status tq_decode_attention_noalloc(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cache, int64_t num_blocks,
+                                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
+                                      float softmax_scale, float* out, float* logits_out, hipStream_t stream) {
+  return decode_common(ctx, q, dt, cache, num_blocks, block_tables, max_blocks_per_seq, seq_lens, batch, max_seq_len,
+                       softmax_scale, out, logits_out, nullptr, 0, nullptr, nullptr, stream, true);
 }
 
 tq_status tq_append_decode(tq_ctx* ctx, const void* k_new, const void* v_new, const void* q, tq_dtype dt,

@@ -16,9 +16,12 @@ constexpr int kMaxGroup = 4;       // q heads per kv head handled by one work-gr
 constexpr int kBlockTokensDev = TQ_BLOCK_TOKENS;
 constexpr int kMaxPagesPerSplit = 256;   // 64 tiles of 64 tokens
 constexpr int kDecodeWaves = 8;           // waves of a decode work-group (they share its tiles)
-constexpr int kDecodeWgsPerCu = 1;
-constexpr int kMaxPageBytes = 3200;      // largest page of any supported format (FP8 keys, 4-bit uniform values)        // decode work-groups per compute unit the split plan aims at
+constexpr int kDecodeWgsPerCu = 1;        // decode work-groups per compute unit the split plan aims at
+constexpr int kMaxPageBytes = 3200;      // largest page of any supported format (FP8 keys, 4-bit uniform values)
 constexpr size_t kCounterBytes = 65536;   // arrival counters at the start of the decode workspace
+// the static scratch of tq_decode_attention_noalloc: counters + 8 MiB of split partials
+constexpr size_t kStaticScratchBytes = kCounterBytes + ((size_t)8 << 20);
+static_assert(kStaticScratchBytes == TQ_STATIC_SCRATCH_BYTES, "tq.h states the scratch size");
 // Cells of the page-append look-up grid: g = 128 y for a unit-vector coordinate
 // y, cell k = round(g) + 128 in 0..256 (the end cells reach to infinity).
 constexpr int kUnitCells = 257;
@@ -131,6 +134,9 @@ const void* decode_kernel_ptr(int key_bits, int key_mode, int val_bits, int val_
 const void* append_page_kernel_ptr(int key_bits, int val_bits, bool qjl);
 hipError_t launch_decode(const DecodeArgs& a, int key_bits, int key_mode, int val_bits, int val_mode,
                          hipStream_t s);
+// Device address of the static decode scratch on the current device (tq_decode.hip).
+hipError_t scratch_address(void** out);
+hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t s);
 hipError_t launch_transfer(bool to_host, void* cache, void* host, const int32_t* block_ids, int64_t n,
                            int64_t num_blocks, int64_t block_bytes, int grid, hipStream_t s);
 hipError_t launch_polar_keys(const AppendArgs& a, int dtype, int key_bits, hipStream_t s);

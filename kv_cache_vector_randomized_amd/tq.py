@@ -19,6 +19,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 ABI_VERSION = 1
 FORMAT_VERSION = 2
 BLOCK_TOKENS = 16
+STATIC_SCRATCH_BYTES = 65536 + 8388608     # TQ_STATIC_SCRATCH_BYTES
 
 TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE_TOO_SMALL, TQ_ERR_HIP, TQ_ERR_OUT_OF_MEMORY = range(6)
 TQ_F32, TQ_BF16 = 0, 1
@@ -28,8 +29,8 @@ VAL_MODES = {"uniform": 0, "lloyd": 1}
 # Every entry point declared in include/tq.h.
 EXPORTS = ("tq_abi_version", "tq_validate_config", "tq_layout_for_config", "tq_codebook", "tq_create",
            "tq_destroy", "tq_layout_query", "tq_quantize_append", "tq_decode_workspace_bytes",
-           "tq_decode_attention", "tq_append_decode", "tq_offload_blocks", "tq_restore_blocks", "tq_dequantize",
-           "tq_dequantize_rows", "tq_status_string", "tq_last_error_message")
+           "tq_decode_attention", "tq_decode_attention_noalloc", "tq_append_decode", "tq_offload_blocks",
+           "tq_restore_blocks", "tq_dequantize", "tq_dequantize_rows", "tq_status_string", "tq_last_error_message")
 
 
 class TQError(RuntimeError):
@@ -75,6 +76,7 @@ def library() -> ctypes.CDLL:
         "tq_quantize_append": (ctypes.c_int, [P, P, P, ctypes.c_int, I64, P, P, I64, P]),
         "tq_decode_workspace_bytes": (SZ, [P, I32, I32]),
         "tq_decode_attention": (ctypes.c_int, [P, P, ctypes.c_int, P, I64, P, I32, P, I32, I32, F32, P, P, P, SZ, P]),
+        "tq_decode_attention_noalloc": (ctypes.c_int, [P, P, ctypes.c_int, P, I64, P, I32, P, I32, I32, F32, P, P, P]),
         "tq_append_decode": (ctypes.c_int, [P, P, P, P, ctypes.c_int, P, I64, P, I32, P, I32, I32, F32, P, P, P,
                                             SZ, P]),
         "tq_offload_blocks": (ctypes.c_int, [P, P, I64, P, I64, P, P]),
@@ -194,6 +196,15 @@ class Context:
                                              max_blocks_per_seq, _ptr(seq_lens), batch, max_seq_len,
                                              float(softmax_scale), _ptr(out), _ptr(logits_out), _ptr(workspace),
                                              workspace_bytes, _stream(stream)))
+
+    def decode_attention_noalloc(self, q, dtype: int, cache, num_blocks: int, block_tables, max_blocks_per_seq: int,
+                                 seq_lens, batch: int, max_seq_len: int, softmax_scale: float, out, logits_out=None,
+                                 stream=None):
+        """tq_decode_attention_noalloc (asynchronous on `stream`; the library's static scratch)."""
+        _check(library().tq_decode_attention_noalloc(self._h, _ptr(q), dtype, _ptr(cache), num_blocks,
+                                                     _ptr(block_tables), max_blocks_per_seq, _ptr(seq_lens), batch,
+                                                     max_seq_len, float(softmax_scale), _ptr(out), _ptr(logits_out),
+                                                     _stream(stream)))
 
     def append_decode(self, k_new, v_new, q, dtype: int, cache, num_blocks: int, block_tables,
                       max_blocks_per_seq: int, seq_lens, batch: int, max_seq_len: int, softmax_scale: float, out,
