@@ -1,21 +1,26 @@
 #!/usr/bin/env python3
 """Throughput of the TurboQuant-style KV-cache hot path on one MI355X.
 
-Default workload (GQA decode, Llama-8B-like shape): batch 16, 32 query heads,
-8 KV heads, head_dim 128, context 8192; keys 4-bit Lloyd-Max with fp32
-corrected norm, values 4-bit uniform with fp32 min/scale.  One step = quantize
-and append the new token of every sequence (K and V, 16 x 8 token-heads) into
-the paged cache, then decode attention of the 16 new queries over their 8192
-cached tokens, in one launch (tq_append_decode; --separate: tq_quantize_append
-then tq_decode_attention).  Steps rotate over --layers independent caches (one
-per layer) so the 147 MB working set does not stay in the 256 MB Infinity Cache.
+Default workload (prefill_append, the largest configuration, which exercises
+both halves of the metric): quantize and append 131072 new tokens x 8 KV heads
+x head_dim 128 of bf16 K and V (N(0,1) with 6 Student-t(4) channels per head)
+into a paged cache of 16-token blocks (keys 4-bit Lloyd-Max with fp32 corrected
+norm, values 4-bit uniform with fp32 min/scale), then decode attention at batch
+1 with 32 query heads over the whole 131072-token context.  One step = one
+tq_quantize_append + one tq_decode_attention.  Steps rotate over --layers
+independent caches (one per layer), so the 147 MB cache of a step does not stay
+in the 256 MB Infinity Cache between steps.  Both kernels get a roofline entry:
+`roofline` for the append (the dominant one) and `roofline_decode`.
 
 Other workloads (--workload):
+  gqa_decode      batch 16, 32 query heads, 8 KV heads, context 8192 (the
+                  Llama-8B-like shape), same codecs: one step = quantize and
+                  append the new token of every sequence, then decode attention
+                  of the 16 new queries over their 8192 tokens, in one launch
+                  (tq_append_decode; --separate: two launches);
   long_3bit       batch 4 x context 32768, 3-bit keys and values, same step;
   qjl             batch 8 x context 16384, 2-bit keys + 1-bit QJL residual signs,
                   same step;
-  prefill_append  quantize-append of 131072 tokens x 8 KV heads into 16-token
-                  pages, then decode at batch 1 over the 131072-token context;
   qjl_build       the qjl workload's whole cache (8 x 16384 tokens x 8 KV heads)
                   quantized and appended in one step, then its decode;
   k3v4_nc         the GQA shape with 3-bit corrected keys and 4-bit values (an
@@ -102,7 +107,7 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=4, help="independent layer caches rotated over the steps")
-    ap.add_argument("--workload", default="gqa_decode", choices=list(MODES))
+    ap.add_argument("--workload", default="prefill_append", choices=list(MODES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true",
                     help="decode workloads: append and decode as two launches instead of one")
@@ -154,6 +159,7 @@ def main():
     slots_new = slots_all[last].contiguous()
 
     th = ctx.layout.token_head_bytes
+    second = None          # a second kernel with a roofline of its own (the append workloads' decode)
     n_layers = max(1, args.layers)
     caches = [PagedKVCache(ctx, lay.num_blocks) for _ in range(n_layers)]
     stream = torch.cuda.current_stream()
@@ -220,6 +226,9 @@ def main():
     else:
         append_bytes = B * T * Hkv * (2 * d * 2 + th) + B * T * 8
         dominant, dom_bytes, dom_source = "append_page_kernel", append_bytes, "tq_append.hip"
+        for c in caches:                               # every layer holds a full cache before timing
+            c.append(k_dev, v_dev, slots_all)
+        torch.cuda.synchronize()
 
         def step(i, ev=None):
             c = caches[i % n_layers]
@@ -232,6 +241,10 @@ def main():
 
         def dom(i):
             caches[i % n_layers].append(k_dev, v_dev, slots_all)
+
+        def dom_decode(i):
+            caches[i % n_layers].decode(q_dev, tables, seq_lens, T, scale, out=out)
+        second = ("decode_kernel", decode_bytes, "tq_decode.hip", dom_decode)
     step_bytes = append_bytes + decode_bytes
 
     if args.copy_calibration_mb:
@@ -298,6 +311,16 @@ def main():
     log(f"[bench] step {ms_step * 1e3:.1f} us; {dominant} avg {dom_avg * 1e3:.1f} us "
         f"(p10 {pct[10]:.1f}, p50 {pct[50]:.1f}, p90 {pct[90]:.1f}); "
         f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of HBM peak")
+    roof2 = None
+    if second is not None:
+        name2, bytes2, source2, fn2 = second
+        avg2 = timed(fn2, args.warmup + 3 * args.steps) / args.steps
+        ach2 = bytes2 / (avg2 * 1e-3) / 1e9
+        log(f"[bench] {name2} avg {avg2 * 1e3:.1f} us; {ach2:.0f} GB/s = {ach2 / HBM_PEAK_GBS:.1%} of HBM peak")
+        roof2 = {"kernel": name2, "bound": "hbm", "achieved": round(ach2, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(ach2 / HBM_PEAK_GBS, 4),
+                 "traffic": counter_traffic(args.workload + ":" + name2, source2),
+                 "algorithmic_bytes_per_launch": bytes2, "avg_launch_us": round(avg2 * 1e3, 2)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -314,7 +337,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": {"append": "bf16 in; fp32 (append), f16x3/i8 MFMA + fp32 (decode)",
+                  "decode": "bf16 in; f16x3/i8 MFMA + fp32 (decode and new-token append)",
+                  "dequant": "fp32 (bf16 or fp32 out)"}[kind],
+        "arithmetic": ("append: bf16 inputs, rotation on the bf16 MFMA with fp32 sums, codes decided in fp32, "
+                       "stored norms from fp64 sums; decode: logits on the f16 MFMA with the query and centroids "
+                       "split into f16 terms (about 22 significant bits), value sums on the int8 MFMA with "
+                       "fixed-point weights, softmax and accumulation in fp32"),
         "data": "synthetic (seeded; bf16 N(0,1) K/V with outlier channels, N(0,1) queries)",
         "config": {
             "workload": args.workload, "batch": B, "context": T, "num_q_heads": Hq, "num_kv_heads": Hkv,
@@ -340,6 +369,7 @@ def main():
             "avg_launch_us": round(dom_avg * 1e3, 2),
             "p10_p50_p90_us": [round(pct[10], 2), round(pct[50], 2), round(pct[90], 2)],
         },
+        "roofline_decode": roof2,
         "cpu_baseline": cpu,
         "launch": ("eager" if args.eager else "; ".join(launch_notes) if launch_notes
                    else "hip graph of the timed steps (replayed once untimed first)"),
@@ -379,15 +409,22 @@ def cpu_baseline(w, kind, k_all, v_all, q_np, lay, np):
         sample_bytes = n * Hkv * (th + 2 * d * 2) + n * 8
         sample = f"reconstruction of {n} tokens x {Hkv} kv heads (bf16-sized output), median of 15 runs, {sec:.2f} s each"
     elif kind == "append":
-        n = 16384
+        # the step's two halves on the first n tokens of sequence 0: their quantize-append,
+        # then decode attention of the sequence's queries over those n tokens
+        n = min(16384, T)
+        lens_n = np.minimum(lay.seq_lens[b:b + 1], n)
         times = []
-        for _ in range(5):
+        for _ in range(3):
             t0 = time.perf_counter()
             O.quantize_append(cfg, cache, f64(k_all[:n]), f64(v_all[:n]), slots[:n], signs, kcb, S=S)
+            O.decode_attention(cfg, f64(q_np[b:b + 1]), cache, lay.block_tables[b:b + 1], lens_n,
+                               1.0 / math.sqrt(d), signs, kcb, S=S)
             times.append(time.perf_counter() - t0)
         sec = statistics.median(times)
-        sample_bytes = n * Hkv * (2 * d * 2 + th) + n * 8
-        sample = f"quantize-append of {n} tokens x {Hkv} kv heads, median of 5 runs, {sec:.2f} s each"
+        sample_bytes = (n * Hkv * (2 * d * 2 + th) + n * 8 + n * Hkv * th + Hq * d * 2 + Hq * d * 4
+                        + (n // 16) * 4 + 4)
+        sample = (f"quantize-append of {n} tokens x {Hkv} kv heads, then decode of {Hq} q heads over those {n} "
+                  f"tokens, median of 3 runs, {sec:.2f} s each")
     else:
         t0 = time.time()
         O.quantize_append(cfg, cache, f64(k_all[: T - 1]), f64(v_all[: T - 1]), slots[: T - 1], signs, kcb, S=S)

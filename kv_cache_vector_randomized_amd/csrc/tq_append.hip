@@ -53,10 +53,10 @@ __global__ __launch_bounds__(256) void append_keys_kernel(AppendArgs a) {
     for (int i = 0; i < kDim; ++i) x[i] = 0.f;
   }
   uint32_t w[KB * 4];
-  float cn2;
+  double cn2;
   float cres[QJL ? kDim : 1];
-  const float n = lloyd_codes<KB, QJL>(x, sb, lut, a.klut_scale, a.klut_bias, w, cn2, cres, kt8, kc8);
-  const float nhat = (a.key_nc && !QJL) ? n / sqrtf(cn2) : n;
+  const double n = lloyd_codes<KB, QJL>(x, sb, lut, a.klut_scale, a.klut_bias, w, cn2, cres, kt8, kc8);
+  const float nhat = stored_norm(n, cn2, a.key_nc && !QJL);
 
   uint8_t* page = nullptr;
   int so = 0;
@@ -157,9 +157,9 @@ __global__ __launch_bounds__(256) void append_values_kernel(AppendArgs a) {
   uint32_t w[VB * 4];
   if constexpr (VLM) {
     uint32_t sb[4] = {a.sign_bits[0], a.sign_bits[1], a.sign_bits[2], a.sign_bits[3]};
-    float cn2;
-    const float n = lloyd_codes<VB, false>(x, sb, lut, a.vlut_scale, a.vlut_bias, w, cn2, nullptr);
-    reinterpret_cast<float*>(page + a.f.vmin)[so] = n;
+    double cn2;
+    const double n = lloyd_codes<VB, false>(x, sb, lut, a.vlut_scale, a.vlut_bias, w, cn2, nullptr);
+    reinterpret_cast<float*>(page + a.f.vmin)[so] = (float)n;
   } else {
     float mn0 = x[0], mn1 = x[1], mx0 = x[0], mx1 = x[1];
 #pragma unroll
@@ -307,6 +307,10 @@ __device__ __forceinline__ float sum_rows(float v) {
   v += __shfl_xor(v, 16);
   return v + __shfl_xor(v, 32);
 }
+__device__ __forceinline__ double sum_rows64(double v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
 
 template <int KB, int VB, bool QJL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3))) void append_page_kernel(AppendArgs a) {
@@ -316,6 +320,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
   __shared__ __align__(16) QLut lut[kUnitCellsPadded];
   __shared__ __align__(16) uint8_t kpack[4][16][KSTR];    // packed key rows [wave][token]
   __shared__ __align__(16) uint8_t vplane[4][64][16];     // value planes [wave][plane][token]
+  // ||k||^2 (fp64) of the wave's 16 tokens, parked in LDS across the code loop
+  // (volatile: kept out of registers, where it would push the kernel into spills)
+  __shared__ volatile double knorm_lds[4][16];
+  // sum of C[code]^2 (fp64, the fp32 centroids' squares exact) of every field of a packed
+  // key row: a byte of 4-bit or 2-bit codes, 6 bits (two codes) of 3-bit codes
+  constexpr int kFieldBits = KB == 3 ? 6 : 8;
+  __shared__ double c2tab[QJL ? 1 : 1 << kFieldBits];
   // QJL: the f16 terms of S in the operand order of the MFMA (see the key pass)
   __shared__ __align__(16) uint32_t sq[QJL ? kDim * kDim : 4];
 
@@ -366,9 +377,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
   load_group(p, keys0, inA, rawA);
   for (int i = threadIdx.x; i < kUnitCellsPadded; i += 256)
     *reinterpret_cast<uint4*>(&lut[i]) = *reinterpret_cast<const uint4*>(&a.c->kulut[i]);
-  if constexpr (QJL)
+  if constexpr (QJL) {
     for (int i = threadIdx.x; i < kDim * kDim / 4; i += 256)
       *reinterpret_cast<uint4*>(&sq[4 * i]) = *reinterpret_cast<const uint4*>(&a.c->Sh[4 * i]);
+  } else {
+    for (int i = threadIdx.x; i < (1 << kFieldBits); i += 256) {
+      double t = 0.0;
+#pragma unroll
+      for (int q = 0; q < kFieldBits / KB; ++q) {
+        const double c = (double)a.c->kc[(i >> (KB * q)) & ((1 << KB) - 1)];
+        t = fma(c, c, t);
+      }
+      c2tab[i] = t;
+    }
+  }
   // A operands of the key rotation, one per block b = beta + 2n of the 16-point
   // transform: H16[j][k] times the sign of coordinate 32n + 8(k/4) + 4beta + k%4
   // (k = 4g + e), so the bf16 rows enter the MFMA as they are.
@@ -410,6 +432,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
           z[2 * n + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
               hs[2 * n + 1], __builtin_bit_cast(shortx4, make_uint2(in[n].z, in[n].w)), zero, 0, 0, 0);
         }
+        // ||k|| of the stored norm from the bf16 inputs in fp64 (squares exact), while
+        // the rotation runs on the matrix cores
+        double kk0 = 0.0, kk1 = 0.0;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const uint32_t wv[4] = {in[n].x, in[n].y, in[n].z, in[n].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kk0 = fma((double)bf16lo(wv[e]), (double)bf16lo(wv[e]), kk0);
+            kk1 = fma((double)bf16hi(wv[e]), (double)bf16hi(wv[e]), kk1);
+          }
+        }
+        const double kkt = sum_rows64(kk0 + kk1);
+        if (g == 0) knorm_lds[wave][j] = kkt;
+        __builtin_amdgcn_sched_barrier(0);     // keep the fp64 sums' registers out of the code loop
         // 8-point butterfly over b: z[b][r] becomes coordinate 32(b/2) + 8g + 4(b%2) + r
 #pragma unroll
         for (int len = 1; len < 8; len <<= 1)
@@ -421,18 +458,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
               z[m] = u + v;
               z[m + len] = u - v;
             }
-        float ss = 0.f;
-#pragma unroll
-        for (int b = 0; b < 8; ++b)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) ss = fmaf(z[b][r], z[b][r], ss);
-        ss = sum_rows(ss);
-        // u = y / ||y||, g = 128 u; a zero key gives g = 0, codes 2^(b-1) and norm 0
-        const float sg = ss > 0.f ? 128.f * __builtin_amdgcn_rsqf(ss) : 0.f;
+        // u = y / ||y||, g = 128 u = sqrt(d) z / ||k|| (||z|| = sqrt(d) ||k||); a zero key gives
+        // g = 0, codes 2^(b-1) and norm 0
+        const float kkf = (float)kkt;
+        const float sg = kkf > 0.f ? 11.313708498984761f * __builtin_amdgcn_rsqf(kkf) : 0.f;
         const uint32_t lut_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) QLut*)lut + 0x4C000000u;
-        // QJL: the residual in the rotated frame, times sqrt(d): z - ||z|| C[code]
-        const float nz = QJL ? __builtin_amdgcn_sqrtf(ss) : 0.f;
-        float c2 = 0.f;
+        // QJL: the residual in the rotated frame, times sqrt(d): z - sqrt(d) ||k|| C[code]
+        const float nz = QJL ? (float)sqrt(128.0 * kkt) : 0.f;
+        double c2 = 0.0;
         uint32_t w[4];
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
@@ -443,20 +476,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
             const uint32_t addr = (__float_as_uint(gv + kUnitMagic) << 4) + lut_addr;
             const u32x4 e = *reinterpret_cast<lds_u32x4*>((uintptr_t)addr);
             const bool up = gv >= __uint_as_float(e.y);
-            const float c = up ? __uint_as_float(e.w) : __uint_as_float(e.z);
-            if constexpr (QJL) z[2 * n + (i >> 2)][i & 3] = fmaf(-nz, c, z[2 * n + (i >> 2)][i & 3]);
-            else c2 = fmaf(c, c, c2);
+            if constexpr (QJL) {
+              const float c = up ? __uint_as_float(e.w) : __uint_as_float(e.z);
+              z[2 * n + (i >> 2)][i & 3] = fmaf(-nz, c, z[2 * n + (i >> 2)][i & 3]);
+            }
             const uint32_t code = e.x + (uint32_t)up;
             wn |= code << (KB * i);
           }
           w[n] = wn;
         }
-        if constexpr (!QJL) c2 = sum_rows(c2);
-        if (g == 0 && slot >= 0) {
-          const float nk = __builtin_amdgcn_sqrtf(ss) * kInvSqrtDim;   // ||k|| (H/sqrt(d) is orthogonal)
-          const float nhat = (!QJL && a.key_nc) ? (nk > 0.f ? nk * __builtin_amdgcn_rsqf(c2) : 0.f) : nk;
-          reinterpret_cast<float*>(page_of(slot) + a.f.knorm)[slot & 15] = nhat;
+        if constexpr (!QJL) {
+          // ||C[code]||^2 of the corrected norm from the packed codes, field by field
+          if (a.key_nc) {
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+#pragma unroll
+              for (int f = 0; f < 8 * KB / kFieldBits; ++f)
+                c2 += c2tab[(w[n] >> (kFieldBits * f)) & ((1u << kFieldBits) - 1)];
+            c2 = sum_rows64(c2);
+          }
         }
+        if (g == 0 && slot >= 0)
+          reinterpret_cast<float*>(page_of(slot) + a.f.knorm)[slot & 15] =
+              stored_norm_sq(knorm_lds[wave][j], c2, !QJL && a.key_nc);
         if constexpr (QJL) {
           // p = S r~ on the f16 16x16x32 MFMA, each side split into two f16 terms
           // (r~ scaled by a power of two per token: signs do not change):
@@ -523,7 +565,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
             uint8_t* pg = page_of(slot);
             // lane g stores dword g of token j's sign row
             reinterpret_cast<uint32_t*>(pg + a.f.ksigns + 16 * (slot & 15))[g] = srw;
-            if (g == 0) reinterpret_cast<float*>(pg + a.f.kres)[slot & 15] = __builtin_amdgcn_sqrtf(rr) * kInvSqrtDim;
+            if (g == 0) reinterpret_cast<float*>(pg + a.f.kres)[slot & 15] = sqrtf(rr) * kInvSqrtDim;
           }
         }
         // codes of coordinates 32n + 8g .. +7 are bytes KB*(4n + g) .. +KB-1 of the row
@@ -584,17 +626,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
         constexpr float levels = (float)((1 << VB) - 1);
         const float sc = (mx - mn) / levels;                  // correctly rounded division
         const float inv = sc > 0.f ? 1.f / sc : 0.f;          // correctly rounded
-        // code = floor(fl32(x - mn) * inv + 1/2) in one fma.  Against rint(fl32(fl32(x - mn)
-        // / sc)) it can differ only where the quotient lies within a few ulp (about
-        // 2^-20 for codes up to 15) of a rounding boundary: a normalised distance
+        // code = rint(fl32(x - mn) * inv), round half to even.  The product is within 2 ulp
+        // of the exact quotient (x - mn) / sc, so it decides as the exact quotient does
+        // unless that lies within about 2^-20 of a rounding boundary: a normalised distance
         // (x - mn) / (mx - mn) far below 1e-6, inside the band where either code counts.
+        // v_cvt_pk_u8_f32 rounds to nearest even and writes the code into one byte of a
+        // word; codes e and e + 4 share a word, and the words of 4-bit (2-bit) codes merge
+        // with one shift-or (three) into the packed stream.
         uint32_t w[4];                            // w[n]: the 8 codes of chunk q + 4n (VB bytes)
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
-          uint32_t wn = 0u;
+          const float* xn = &x[8 * n];
+          if constexpr (VB == 4 || VB == 2) {
+            uint32_t by[4];                       // by[r]: byte k = code r + 4k (VB 4: r + 2k)
+            constexpr int per = 8 / VB;           // codes per byte
 #pragma unroll
-          for (int e = 0; e < 8; ++e) wn |= (uint32_t)fmaf(x[8 * n + e] - mn, inv, 0.5f) << (VB * e);
-          w[n] = wn;
+            for (int r = 0; r < per; ++r) {
+              uint32_t t = 0u;
+#pragma unroll
+              for (int k = 0; k < VB; ++k) t = __builtin_amdgcn_cvt_pk_u8_f32((xn[r + per * k] - mn) * inv, k, t);
+              by[r] = t;
+            }
+            uint32_t wn = by[0];
+#pragma unroll
+            for (int r = 1; r < per; ++r) wn |= by[r] << (VB * r);
+            w[n] = wn;
+          } else {
+            uint32_t wn = 0u;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wn |= (uint32_t)rintf((xn[e] - mn) * inv) << (VB * e);
+            w[n] = wn;
+          }
         }
         if (q == 0 && slot >= 0) {
           uint8_t* pg = page_of(slot);

@@ -329,6 +329,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
   return v;
 }
+__device__ __forceinline__ double wave_sum64(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
 
 // Bits 0..15 of e to the even and of o to the odd bit positions of a word.
 __device__ __forceinline__ uint32_t interleave16(uint32_t e, uint32_t o) {
@@ -366,6 +371,8 @@ __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, floa
     nhat = 1.f;
     *reinterpret_cast<uint16_t*>(page + a.f.kcodes + so * kDim + 2 * lane) = (uint16_t)(b0 | (b1 << 8));
   } else {
+  // ||k|| of the stored norm in fp64 from the inputs (squares exact, one rounding to fp32 at the end)
+  const double nk64 = sqrt(wave_sum64(fma((double)k0, (double)k0, (double)k1 * (double)k1)));
   // keys: z = H(s * k), then codes of u = z / ||z||
   float x0 = k0 * a.c->signs[2 * lane], x1 = k1 * a.c->signs[2 * lane + 1];
   {
@@ -396,7 +403,7 @@ __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, floa
         codes[0][polar_slot(lv, lane >> (lv - 1))] = (uint8_t)polar_code<KB>(atan2f(v, u), false);
       rad = sqrtf(fmaf(u, u, v * v));
     }
-    nhat = __shfl(rad, 0);
+    nhat = (float)nk64;                                      // the root radius ||y|| = ||k||
     wave_sync_lds();
     float pf = 1.f;
 #pragma unroll
@@ -417,9 +424,9 @@ __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, floa
     kc0 = lut_code(a.c->klut, x0 * inv, a.klut_scale, a.klut_bias, c0);
     kc1 = lut_code(a.c->klut, x1 * inv, a.klut_scale, a.klut_bias, c1);
   }
-  const float nk = sqrtf(ss) * kInvSqrtDim;               // ||k||
-  const float c2 = wave_sum(fmaf(c0, c0, c1 * c1));
-  nhat = (!QJL && a.key_nc) ? (nk > 0.f ? nk / sqrtf(c2) : 0.f) : nk;
+  const float nk = (float)nk64;                            // ||k||
+  const double c2 = wave_sum64(fma((double)c0, (double)c0, (double)c1 * (double)c1));
+  nhat = stored_norm(nk64, c2, !QJL && a.key_nc);
   if constexpr (QJL) {
     // residual in the rotated frame r' = H(s*k)/sqrt(d) - ||k|| C[code], and S r'
     const float r0 = fmaf(-nk, c0, x0 * kInvSqrtDim), r1 = fmaf(-nk, c1, x1 * kInvSqrtDim);
@@ -443,13 +450,13 @@ __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, floa
   }
   }
   }
-  // uniform values, as the append kernel: codes floor(fl32(x - mn) / sc + 1/2)
+  // uniform values, as the append kernel: codes rint(fl32(x - mn) * (1 / sc)), ties to even
   const float mn = -wave_max(-fminf(v0, v1));
   const float mx = wave_max(fmaxf(v0, v1));
   constexpr float levels = (float)((1 << VB) - 1);
   const float sc = (mx - mn) / levels;
   const float vinv = sc > 0.f ? 1.f / sc : 0.f;
-  const uint32_t vc0 = (uint32_t)fmaf(v0 - mn, vinv, 0.5f), vc1 = (uint32_t)fmaf(v1 - mn, vinv, 0.5f);
+  const uint32_t vc0 = (uint32_t)rintf((v0 - mn) * vinv), vc1 = (uint32_t)rintf((v1 - mn) * vinv);
   vhat[2 * lane] = fmaf(sc, (float)vc0, mn);
   vhat[2 * lane + 1] = fmaf(sc, (float)vc1, mn);
   if constexpr (!POLAR) {

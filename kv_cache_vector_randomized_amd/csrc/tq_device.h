@@ -67,6 +67,21 @@ __device__ __forceinline__ float sum_squares(const float (&x)[kDim]) {
   return (s0 + s1) + (s2 + s3);
 }
 
+// Sum of squares accumulated in fp64: the square of an fp32 (or bf16) value is
+// exact in fp64 and the sums keep 53 bits, so sqrt of the result rounded once to
+// fp32 is within 1 ulp of the correctly rounded norm (stored norms are fp32 and
+// must be accurate: ai-navigate-news turboquant-vllm write-up, "Bugs Nobody Else
+// Has Found").
+__device__ __forceinline__ double sumsq64(const float (&x)[kDim]) {
+  double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+  for (int i = 0; i < kDim; i += 2) {
+    s0 = fma((double)x[i], (double)x[i], s0);
+    s1 = fma((double)x[i + 1], (double)x[i + 1], s1);
+  }
+  return s0 + s1;
+}
+
 // code = #{j : t_j <= y} through the look-up grid; also returns C[code].
 __device__ __forceinline__ int lut_code(const QLut* lut, float y, float sc, float bi, float& c) {
   const float f = fminf(fmaxf(fmaf(y, sc, bi), 0.f), (float)(kLutCells - 1));
@@ -137,28 +152,40 @@ __device__ __forceinline__ void apply_signs(float (&x)[kDim], const uint32_t (&s
 
 // Stage 1 on a vector already in registers: signs, norm, rotation, codes.
 // On return x[i] holds the rotated, unnormalized coordinate H(s*x)_i and c[i]
-// is not kept; returns the fp32 norm and fills the packed words and sum C^2.
+// is not kept; returns ||x|| in fp64 and fills the packed words and sum C^2
+// (fp64: the fp32 centroids' squares are exact there).
 template <int B, bool KEEP_C>
-__device__ __forceinline__ float lloyd_codes(float (&x)[kDim], const uint32_t (&sb)[4], const QLut* lut,
-                                             float lsc, float lbi, uint32_t (&w)[B * 4], float& cn2,
-                                             float* cvals, const float* t8 = nullptr, const float* c8 = nullptr) {
+__device__ __forceinline__ double lloyd_codes(float (&x)[kDim], const uint32_t (&sb)[4], const QLut* lut,
+                                              float lsc, float lbi, uint32_t (&w)[B * 4], double& cn2,
+                                              float* cvals, const float* t8 = nullptr, const float* c8 = nullptr) {
+  const double n = sqrt(sumsq64(x));
   apply_signs(x, sb);
-  const float n = sqrtf(sum_squares(x));
+  const float n32 = sqrtf(sum_squares(x));   // scale of the code decisions only
   wht128(x);
-  const float inv = n > 0.f ? 1.f / (n * 11.313708498984761f) : 0.f;
+  const float inv = n32 > 0.f ? 1.f / (n32 * 11.313708498984761f) : 0.f;
 #pragma unroll
   for (int j = 0; j < B * 4; ++j) w[j] = 0u;
-  float a0 = 0.f, a1 = 0.f;
+  double a0 = 0.0, a1 = 0.0;
 #pragma unroll
   for (int i = 0; i < kDim; ++i) {
     float c;
     const int code = B == 8 ? code_bsearch8(t8, c8, x[i] * inv, c) : lut_code(lut, x[i] * inv, lsc, lbi, c);
     put_code<B>(w, i, (uint32_t)code);
-    if (i & 1) a1 = fmaf(c, c, a1); else a0 = fmaf(c, c, a0);
+    if (i & 1) a1 = fma((double)c, (double)c, a1); else a0 = fma((double)c, (double)c, a0);
     if (KEEP_C) cvals[i] = c;
   }
   cn2 = a0 + a1;
   return n;
+}
+
+// Stored key norm: ||k|| (plain) or ||k|| / ||C[code]|| (corrected), from the
+// fp64 sums, rounded once to fp32.  A zero key stores 0.
+__device__ __forceinline__ float stored_norm(double n, double cn2, bool corrected) {
+  return (float)(corrected ? (n > 0.0 ? n / sqrt(cn2) : 0.0) : n);
+}
+// The same from ||k||^2: sqrt(||k||^2 / ||C[code]||^2) (one fp64 square root).
+__device__ __forceinline__ float stored_norm_sq(double n2, double cn2, bool corrected) {
+  return (float)sqrt(corrected ? n2 / cn2 : n2);
 }
 
 // Make a wave's LDS writes visible to the wave's later LDS reads.

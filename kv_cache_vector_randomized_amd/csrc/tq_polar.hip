@@ -32,6 +32,12 @@ __device__ __forceinline__ float wave_max_xor(float v) {
   return v;
 }
 
+__device__ __forceinline__ double wave_sum64_xor(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -47,6 +53,7 @@ __global__ __launch_bounds__(256) void append_polar_kernel(AppendArgs a) {
   if (slot < 0 || slot >= a.num_blocks * kBlockTokensDev) return;
   float x[kDim];
   load_row<BF16>(a.k, th, x);
+  const float radius = (float)sqrt(sumsq64(x));     // ||y|| = ||k||, fp64 sums rounded once
   uint32_t sb[4] = {a.sign_bits[0], a.sign_bits[1], a.sign_bits[2], a.sign_bits[3]};
   apply_signs(x, sb);
   wht128(x);
@@ -68,7 +75,7 @@ __global__ __launch_bounds__(256) void append_polar_kernel(AppendArgs a) {
   uint8_t* page = a.cache + ((slot >> 4) * a.hkv + h) * (int64_t)a.f.page_bytes;
   const int so = (int)(slot & 15);
   store_words<KB>(page + a.f.kcodes + so * (KB * 16), w);
-  reinterpret_cast<float*>(page + a.f.knorm)[so] = x[0];
+  reinterpret_cast<float*>(page + a.f.knorm)[so] = radius;
 }
 
 // ---------------------------------------------------------------------------
@@ -109,6 +116,8 @@ __global__ __launch_bounds__(256) void append_polar_wave_kernel(AppendArgs a) {
       const float2 vv = reinterpret_cast<const float2*>(static_cast<const float*>(a.v) + r * kDim)[lane];
       k0 = kk.x; k1 = kk.y; v0 = vv.x; v1 = vv.y;
     }
+    // the stored radius ||y|| = ||k|| in fp64 from the inputs, rounded once
+    const float radius = (float)sqrt(wave_sum64_xor(fma((double)k0, (double)k0, (double)k1 * (double)k1)));
     // keys: signs, the 128-point butterfly (coordinate bit 0 in the lane, bits
     // 1..6 across lanes 1..32 apart), 1/sqrt(d)
     k0 = __uint_as_float(__float_as_uint(k0) ^ sg0);
@@ -151,7 +160,7 @@ __global__ __launch_bounds__(256) void append_polar_wave_kernel(AppendArgs a) {
     if (lane < 16 * KB) page[a.f.kcodes + so * (KB * 16) + lane] = (uint8_t)stream_byte<KB>(kcod[wave], lane);
     if (lane < 16 * VB) page[a.f.vcodes + 16 * lane + so] = (uint8_t)stream_byte<VB>(vcod[wave], lane);
     if (lane == 0) {
-      reinterpret_cast<float*>(page + a.f.knorm)[so] = rad;   // the root radius: ||y||
+      reinterpret_cast<float*>(page + a.f.knorm)[so] = radius;
       reinterpret_cast<float*>(page + a.f.vmin)[so] = mn;
       reinterpret_cast<float*>(page + a.f.vscale)[so] = sc;
     }

@@ -11,6 +11,37 @@ from oracle import tq_oracle as O
 
 BAND = 1e-6          # coordinates this close to a decision boundary are excluded from bit-exact checks
 REL_TOL = 1e-4       # logits and attention outputs, relative (per (sequence, q head) vector)
+NORM_ULP = 2         # stored fp32 norms: within 2 ulp of the oracle's fp32 rounding
+# QJL residual norm rho: the residual is formed from the fp32 rotation of the key,
+# so |rho_gpu - rho| <= 2^-21 (||k|| + rho) (see the design notes' derivation)
+RHO_REL_K, RHO_REL_RHO = 2.0 ** -21, 2.0 ** -21
+
+# Per-workload parity figures, written out at the end of the session (conftest.py)
+REPORT: dict = {}
+
+
+def report(test: str, workload: str, **fig):
+    """Record parity figures of one test and workload; counts add up, maxima are kept."""
+    rec = REPORT.setdefault((test, workload), {})
+    for k, v in fig.items():
+        if k.startswith("max_") or k.startswith("worst_"):
+            rec[k] = max(rec.get(k, 0.0), float(v))
+        else:
+            rec[k] = rec.get(k, 0) + int(v)
+
+
+def ulp_distance(a, b) -> np.ndarray:
+    """Distance in fp32 ulps between non-negative fp32 values (float arrays)."""
+    ia = np.asarray(a, np.float64).astype(np.float32).view(np.int32).astype(np.int64)
+    ib = np.asarray(b, np.float64).astype(np.float32).view(np.int32).astype(np.int64)
+    return np.abs(ia - ib)
+
+
+def elem_err(a, b) -> float:
+    """Largest elementwise error relative to the largest reference magnitude."""
+    m = np.max(np.abs(b)) if np.size(b) else 0.0
+    d = np.max(np.abs(a - b)) if np.size(b) else 0.0
+    return d / m if m > 0 else d
 
 
 def oracle_config(w: synth.Workload) -> O.Config:
@@ -87,15 +118,23 @@ def compare_append(w, gpu_cache: np.ndarray, slots, qz: O.Quantized, report: dic
         report["key_band_flips"] = report.get("key_band_flips", 0) + int(diff.sum())
         clean = ~diff.any(axis=1)
         if cfg.key_mode != "fp8":        # FP8 keys store no norm
-            rel = np.abs(f["knorm"] - qz.key.norm[:, h]) / np.maximum(np.abs(qz.key.norm[:, h]), 1e-30)
-            assert np.all(rel[clean] <= 2e-6), rel[clean].max()
+            # the corrected norm depends on the codes: rows with a band flip are skipped there
+            rows = clean if cfg.key_mode == "lloyd_nc" else np.ones_like(clean)
+            u = ulp_distance(f["knorm"], qz.key.norm[:, h])[rows]
+            assert np.all(u <= NORM_ULP), u.max()
+            report["max_knorm_ulp"] = max(report.get("max_knorm_ulp", 0), int(u.max()) if u.size else 0)
         if cfg.key_mode == "lloyd_qjl":
             sband = qz.key.qjl_band[:, h] < BAND
             sdiff = f["ksigns"] != qz.key.qjl_bits[:, h]
             assert not np.any(sdiff[clean] & ~sband[clean]), "QJL sign mismatch outside the band"
             report["sign_band"] = report.get("sign_band", 0) + int(sband.sum())
-            rr = np.abs(f["kres"] - qz.key.qjl_norm[:, h]) / np.maximum(qz.key.qjl_norm[:, h], 1e-30)
-            assert np.all(rr[clean] <= 1e-5), rr[clean].max()
+            report["sign_band_flips"] = report.get("sign_band_flips", 0) + int(sdiff[clean].sum())
+            rho, n = qz.key.qjl_norm[:, h], qz.key.norm[:, h]
+            dr = np.abs(f["kres"] - rho)
+            assert np.all((dr <= RHO_REL_K * n + RHO_REL_RHO * rho)[clean]), (dr / (n + rho))[clean].max()
+            rel = (dr / np.maximum(n, 1e-30))[clean]
+            report["max_rho_err_over_knorm"] = max(report.get("max_rho_err_over_knorm", 0.0),
+                                                   float(rel.max()) if rel.size else 0.0)
         vc, vref = f["vcodes"], qz.val_codes[:, h]
         vband = qz.val_band[:, h] < BAND
         vdiff = vc != vref
@@ -110,14 +149,26 @@ def compare_append(w, gpu_cache: np.ndarray, slots, qz: O.Quantized, report: dic
             else:
                 assert np.allclose(f["vscale"], qz.val_b[:, h], rtol=2 ** -23, atol=0)
         else:
-            vclean = ~vdiff.any(axis=1)
-            rel = np.abs(f["vnorm"] - qz.val_a[:, h]) / np.maximum(np.abs(qz.val_a[:, h]), 1e-30)
-            assert np.all(rel[vclean] <= 2e-6)
+            u = ulp_distance(f["vnorm"], qz.val_a[:, h])        # plain norm: independent of the codes
+            assert np.all(u <= NORM_ULP), u.max()
+            report["max_vnorm_ulp"] = max(report.get("max_vnorm_ulp", 0), int(u.max()) if u.size else 0)
 
 
 def rel_err(a, b):
     nb = np.linalg.norm(b)
     return np.linalg.norm(a - b) / nb if nb > 0 else np.linalg.norm(a - b)
+
+
+def check_vec(test: str, workload: str, kind: str, got, ref, ctx=None) -> float:
+    """One (sequence, q head) vector of logits or outputs against the oracle: the
+    L2 relative error and the largest elementwise error (relative to the largest
+    reference magnitude) both within 1e-4; both are recorded for the report."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    l2, el = rel_err(got, ref), elem_err(got, ref)
+    report(test, workload, **{f"worst_{kind}_l2": l2, f"worst_{kind}_elem": el, f"{kind}_vectors": 1})
+    assert l2 <= REL_TOL and el <= REL_TOL, (ctx, kind, l2, el)
+    return max(l2, el)
 
 
 def build_oracle_cache(w, seq_lens, seed, spare_blocks=0):
