@@ -445,7 +445,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
           }
         }
         const double kkt = sum_rows64(kk0 + kk1);
-        if (g == 0) knorm_lds[wave][j] = kkt;
+        // QJL keys store the plain norm, known now; the corrected norm waits for the codes
+        if constexpr (QJL) {
+          if (g == 0 && slot >= 0) reinterpret_cast<float*>(page_of(slot) + a.f.knorm)[slot & 15] = (float)sqrt(kkt);
+        } else {
+          if (g == 0) knorm_lds[wave][j] = kkt;
+        }
+        // QJL: the residual in the rotated frame, times sqrt(d): z - sqrt(d) ||k|| C[code]
+        const float nz = QJL ? (float)sqrt(128.0 * kkt) : 0.f;
         __builtin_amdgcn_sched_barrier(0);     // keep the fp64 sums' registers out of the code loop
         // 8-point butterfly over b: z[b][r] becomes coordinate 32(b/2) + 8g + 4(b%2) + r
 #pragma unroll
@@ -463,8 +470,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
         const float kkf = (float)kkt;
         const float sg = kkf > 0.f ? 11.313708498984761f * __builtin_amdgcn_rsqf(kkf) : 0.f;
         const uint32_t lut_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) QLut*)lut + 0x4C000000u;
-        // QJL: the residual in the rotated frame, times sqrt(d): z - sqrt(d) ||k|| C[code]
-        const float nz = QJL ? (float)sqrt(128.0 * kkt) : 0.f;
         double c2 = 0.0;
         uint32_t w[4];
 #pragma unroll
@@ -496,9 +501,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
             c2 = sum_rows64(c2);
           }
         }
-        if (g == 0 && slot >= 0)
+        if (!QJL && g == 0 && slot >= 0)
           reinterpret_cast<float*>(page_of(slot) + a.f.knorm)[slot & 15] =
-              stored_norm_sq(knorm_lds[wave][j], c2, !QJL && a.key_nc);
+              stored_norm_sq(knorm_lds[wave][j], c2, a.key_nc);
         if constexpr (QJL) {
           // p = S r~ on the f16 16x16x32 MFMA, each side split into two f16 terms
           // (r~ scaled by a power of two per token: signs do not change):
