@@ -116,6 +116,8 @@ def main():
                     help="launch every step from Python instead of replaying a HIP graph of the steps")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run one plain device-to-device copy of this many MiB (counter calibration)")
+    ap.add_argument("--no-stream-ceilings", action="store_true",
+                    help="skip the plain read, write and copy streams of the dominant kernel's byte counts")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path.",
@@ -171,6 +173,7 @@ def main():
         torch.cuda.synchronize()
         del k_dev, v_dev
         append_bytes = B * Hkv * (2 * d * 2 + th) + B * 8
+        dom_rw = (decode_bytes + append_bytes - B * Hkv * th, B * Hkv * th + B * Hq * d * 4)
         if args.separate:
             dominant, dom_bytes, dom_source = "decode_kernel", decode_bytes, "tq_decode.hip"
 
@@ -212,6 +215,7 @@ def main():
         append_bytes = 0
         decode_bytes = B * T * Hkv * (th + 2 * d * eb) + B * T * 8
         dominant, dom_bytes, dom_source = "dequant_kernel", decode_bytes, "tq_dequant.hip"
+        dom_rw = (B * T * Hkv * th + B * T * 8, B * T * Hkv * 2 * d * eb)
 
         def step(i, ev=None):
             c = caches[i % n_layers]
@@ -226,6 +230,7 @@ def main():
     else:
         append_bytes = B * T * Hkv * (2 * d * 2 + th) + B * T * 8
         dominant, dom_bytes, dom_source = "append_page_kernel", append_bytes, "tq_append.hip"
+        dom_rw = (B * T * Hkv * 2 * d * 2 + B * T * 8, B * T * Hkv * th)
         for c in caches:                               # every layer holds a full cache before timing
             c.append(k_dev, v_dev, slots_all)
         torch.cuda.synchronize()
@@ -322,6 +327,42 @@ def main():
                  "traffic": counter_traffic(args.workload + ":" + name2, source2),
                  "algorithmic_bytes_per_launch": bytes2, "avg_launch_us": round(avg2 * 1e3, 2)}
 
+    # Plain device streams of the dominant kernel's read and write byte counts (outside
+    # the timed region): what the memory system gives a kernel that does nothing but
+    # read, write or copy, to set the roofline fractions beside.
+    ceilings = None
+    if not args.no_stream_ceilings:
+        import ctypes
+        sl = ctypes.CDLL(os.path.join(ROOT, "kv_cache_vector_randomized_amd", "libtqstream.so"))
+        for f in (sl.tqs_read, sl.tqs_write, sl.tqs_copy):
+            f.restype = ctypes.c_int
+        P, SZ, U32, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_int
+        sl.tqs_read.argtypes = [P, SZ, P, I, P]
+        sl.tqs_write.argtypes = [P, SZ, U32, I, P]
+        sl.tqs_copy.argtypes = [P, P, SZ, I, P]
+        rd, wr = (x // 16 * 16 for x in dom_rw)
+        cp = min(rd, wr) // 16 * 16
+        src = torch.ones(rd // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty(max(wr, 16) // 4, dtype=torch.int32, device="cuda")
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        hs = lambda: torch.cuda.current_stream().cuda_stream   # the capturing stream inside a graph capture
+        blocks = 2048                          # 8 work-groups of 256 threads per compute unit
+        t_rd = timed(lambda i: sl.tqs_read(src.data_ptr(), rd, sink.data_ptr(), blocks, hs()), 0) / args.steps
+        t_wr = timed(lambda i: sl.tqs_write(dst.data_ptr(), wr, i & 7, blocks, hs()), 0) / args.steps
+        t_cp = timed(lambda i: sl.tqs_copy(src.data_ptr(), dst.data_ptr(), cp, blocks, hs()), 0) / args.steps
+        ceilings = {"read_GBs": round(rd / (t_rd * 1e-3) / 1e9, 1), "read_bytes": rd,
+                    "write_GBs": round(wr / (t_wr * 1e-3) / 1e9, 1), "write_bytes": wr,
+                    "copy_GBs": round(2 * cp / (t_cp * 1e-3) / 1e9, 1), "copy_bytes": 2 * cp,
+                    "read_then_write_us": round((t_rd + t_wr) * 1e3, 2),
+                    "kernel_us": round(dom_avg * 1e3, 2),
+                    "ops": ("plain streaming kernels (16-byte nontemporal loads/stores, 2048 work-groups of 256): "
+                            "read the kernel's read bytes, write its write bytes, copy min of the two; "
+                            "graph-replayed back to back")}
+        log(f"[bench] streams: read {ceilings['read_GBs']} GB/s, write {ceilings['write_GBs']} GB/s, copy "
+            f"{ceilings['copy_GBs']} GB/s; reading then writing the kernel's bytes takes "
+            f"{ceilings['read_then_write_us']} us (kernel {dom_avg * 1e3:.1f} us)")
+        del src, dst, sink
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, kind, k_all, v_all, q_np, lay, np)
@@ -370,6 +411,7 @@ def main():
             "p10_p50_p90_us": [round(pct[10], 2), round(pct[50], 2), round(pct[90], 2)],
         },
         "roofline_decode": roof2,
+        "stream_ceilings": ceilings,
         "cpu_baseline": cpu,
         "launch": ("eager" if args.eager else "; ".join(launch_notes) if launch_notes
                    else "hip graph of the timed steps (replayed once untimed first)"),

@@ -1,7 +1,8 @@
 """Build libtq.so (the C-ABI library) in-tree with hipcc for gfx950.
 
 Sources are compiled in parallel to objects under _build/ and linked into
-kv_cache_vector_randomized_amd/libtq.so.  Every call rebuilds.
+kv_cache_vector_randomized_amd/libtq.so; the plain streaming kernels of the
+benchmark's memory ceilings go to libtqstream.so.  Every call rebuilds.
 """
 from __future__ import annotations
 
@@ -15,6 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libtq.so")
+STREAM_OUT = os.path.join(PKG, "libtqstream.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["tq_host.cpp", "tq_append.hip", "tq_decode.hip", "tq_dequant.hip", "tq_transfer.hip", "tq_polar.hip"]
 
@@ -50,8 +52,15 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-4000:]}")
     os.replace(tmp, OUT)
+    # the plain streaming kernels bench.py measures the memory ceilings with (not part of tq.h)
+    tmp = STREAM_OUT + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", os.path.join(CSRC, "stream_probe.hip"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for stream_probe.hip:\n{r.stderr[-4000:]}")
+    os.replace(tmp, STREAM_OUT)
     if verbose:
-        print(f"built {OUT}", file=sys.stderr)
+        print(f"built {OUT} and {STREAM_OUT}", file=sys.stderr)
     return OUT
 
 

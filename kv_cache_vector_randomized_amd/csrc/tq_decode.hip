@@ -1105,6 +1105,16 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
       store_agent(dst + 2 + 2 * lane, o0);
       store_agent(dst + 3 + 2 * lane, o1);
     }
+    // Ordering without cache-wide fences.  The partials above are agent-scope atomic
+    // stores, so they are performed at the device's coherence point (not held in this
+    // XCD's L2), and s_waitcnt(0) returns only once every one of them has completed
+    // there.  The barrier then orders all threads' completed stores before the arrival
+    // increment, an atomic performed at the same coherence point.  The work-group that
+    // reads splits - 1 was therefore the last to arrive: every other work-group's
+    // stores had completed before its increment, and the loads below are agent-scope
+    // atomic loads, served by the coherence point, issued only after the increment
+    // returned.  (A release increment and an acquire fence would write back and
+    // invalidate the whole L2 of each XCD: measured 45.7 against 33.5 us per step.)
     __builtin_amdgcn_s_waitcnt(0);            // every store of this thread has completed
     __syncthreads();
     __shared__ int last;
