@@ -51,6 +51,17 @@ __device__ __forceinline__ void store_agent(float* p, float v) {
 __device__ __forceinline__ float load_agent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Two adjacent floats (8-byte aligned) as one agent-scope access.
+__device__ __forceinline__ void store_agent2(float* p, float x, float y) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p),
+                     (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_agent2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
 
 // Wave-wide max (prologue only): DPP within rows of 16 lanes, then the row
 // broadcasts; rows outside ROW_MASK keep their own value, neutral for max.
@@ -1098,12 +1109,9 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     // cache-wide write-back or invalidate is needed around the arrival counter.
     if (h < G) {
       float* dst = a.ws + ((((int64_t)b * a.hkv + kvh) * a.splits + split) * 4 + h) * (2 + kDim);
-      if (lane == 0) {
-        store_agent(dst, M);
-        store_agent(dst + 1, L);
-      }
-      store_agent(dst + 2 + 2 * lane, o0);
-      store_agent(dst + 3 + 2 * lane, o1);
+      // (records of 2 + 128 floats: every pair below is 8-byte aligned)
+      if (lane == 0) store_agent2(dst, M, L);
+      store_agent2(dst + 2 + 2 * lane, o0, o1);
     }
     // Ordering without cache-wide fences.  The partials above are agent-scope atomic
     // stores, so they are performed at the device's coherence point (not held in this
@@ -1126,38 +1134,68 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     }
     __syncthreads();
     if (!last) return;
+    // Every wave merges: head wave % 4 over the splits of parity wave / 4, 16 of
+    // them per round trip (all their loads in flight together), then the two
+    // parities combine through LDS.
+    const int mh = wave & 3, par = wave >> 2;
     M = -INFINITY;
     L = o0 = o1 = 0.f;
-    if (h < G) {
-      // Splits are merged 8 at a time, all loads of a batch in flight together.
+    if (mh < G) {
       const int64_t stride = 4 * (2 + kDim);
-      const float* src = a.ws + (((int64_t)b * a.hkv + kvh) * a.splits * 4 + h) * (2 + kDim);
-      for (int sp0 = 0; sp0 < a.splits; sp0 += 8) {
-        float ms[8], ls[8], p0[8], p1[8];
+      const float* src = a.ws + (((int64_t)b * a.hkv + kvh) * a.splits * 4 + mh) * (2 + kDim);
+      for (int sp0 = par; sp0 < a.splits; sp0 += 32) {
+        float ms[16], ls[16], p0[16], p1[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float* s = src + (int64_t)min(sp0 + u, a.splits - 1) * stride;
-          ms[u] = load_agent(s);
-          ls[u] = load_agent(s + 1);
-          p0[u] = load_agent(s + 2 + 2 * lane);
-          p1[u] = load_agent(s + 3 + 2 * lane);
+        for (int u = 0; u < 16; ++u) {
+          ms[u] = -INFINITY;
+          ls[u] = p0[u] = p1[u] = 0.f;
+          if (sp0 + 2 * u < a.splits) {           // uniform: only the splits that exist are read
+            const float* s = src + (int64_t)(sp0 + 2 * u) * stride;
+            const float2 ml = load_agent2(s), pp = load_agent2(s + 2 + 2 * lane);
+            ms[u] = ml.x;
+            ls[u] = ml.y;
+            p0[u] = pp.x;
+            p1[u] = pp.y;
+          }
         }
         float mc = M;
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (sp0 + u < a.splits) mc = fmaxf(mc, ms[u]);
+        for (int u = 0; u < 16; ++u) mc = fmaxf(mc, ms[u]);
         if (mc == -INFINITY) continue;
         const float r = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - mc);
         L *= r;
         o0 *= r;
         o1 *= r;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float f = (sp0 + u < a.splits && ms[u] != -INFINITY) ? __builtin_amdgcn_exp2f(ms[u] - mc) : 0.f;
+        for (int u = 0; u < 16; ++u) {
+          const float f = ms[u] != -INFINITY ? __builtin_amdgcn_exp2f(ms[u] - mc) : 0.f;
           L = fmaf(f, ls[u], L);
           o0 = fmaf(f, p0[u], o0);
           o1 = fmaf(f, p1[u], o1);
         }
+        M = mc;
+      }
+    }
+    // the odd splits' sums (waves 4..7) join the even ones' (waves 0..3)
+    __syncthreads();                           // the wave-merge reads of part_ml / part_o are done
+    if (par == 1 && mh < G) {
+      if (lane == 0) {
+        part_ml[0][mh][0] = M;
+        part_ml[0][mh][1] = L;
+      }
+      part_o[0][mh][2 * lane] = o0;
+      part_o[0][mh][2 * lane + 1] = o1;
+    }
+    __syncthreads();
+    if (par == 0 && mh < G) {
+      const float m1 = part_ml[0][mh][0];
+      const float mc = fmaxf(M, m1);
+      if (mc != -INFINITY) {
+        const float f0 = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - mc);
+        const float f1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - mc);
+        L = fmaf(f1, part_ml[0][mh][1], L * f0);
+        o0 = fmaf(f1, part_o[0][mh][2 * lane], o0 * f0);
+        o1 = fmaf(f1, part_o[0][mh][2 * lane + 1], o1 * f0);
         M = mc;
       }
     }
