@@ -327,9 +327,11 @@ def main():
                  "traffic": counter_traffic(args.workload + ":" + name2, source2),
                  "algorithmic_bytes_per_launch": bytes2, "avg_launch_us": round(avg2 * 1e3, 2)}
 
-    # Plain device streams of the dominant kernel's read and write byte counts (outside
-    # the timed region): what the memory system gives a kernel that does nothing but
-    # read, write or copy, to set the roofline fractions beside.
+    # Plain device streams of each roofline kernel's read and write byte counts
+    # (outside the timed region): what the memory system gives a kernel that does
+    # nothing but read, write or copy, to set the roofline fractions beside.  Like
+    # the kernels, the streams rotate over `--layers` buffers, so that sizes below
+    # the 256 MB Infinity Cache are not served from it.
     ceilings = None
     if not args.no_stream_ceilings:
         import ctypes
@@ -340,28 +342,41 @@ def main():
         sl.tqs_read.argtypes = [P, SZ, P, I, P]
         sl.tqs_write.argtypes = [P, SZ, U32, I, P]
         sl.tqs_copy.argtypes = [P, P, SZ, I, P]
-        rd, wr = (x // 16 * 16 for x in dom_rw)
-        cp = min(rd, wr) // 16 * 16
-        src = torch.ones(rd // 4, dtype=torch.int32, device="cuda")
-        dst = torch.empty(max(wr, 16) // 4, dtype=torch.int32, device="cuda")
-        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
         hs = lambda: torch.cuda.current_stream().cuda_stream   # the capturing stream inside a graph capture
         blocks = 2048                          # 8 work-groups of 256 threads per compute unit
-        t_rd = timed(lambda i: sl.tqs_read(src.data_ptr(), rd, sink.data_ptr(), blocks, hs()), 0) / args.steps
-        t_wr = timed(lambda i: sl.tqs_write(dst.data_ptr(), wr, i & 7, blocks, hs()), 0) / args.steps
-        t_cp = timed(lambda i: sl.tqs_copy(src.data_ptr(), dst.data_ptr(), cp, blocks, hs()), 0) / args.steps
-        ceilings = {"read_GBs": round(rd / (t_rd * 1e-3) / 1e9, 1), "read_bytes": rd,
-                    "write_GBs": round(wr / (t_wr * 1e-3) / 1e9, 1), "write_bytes": wr,
-                    "copy_GBs": round(2 * cp / (t_cp * 1e-3) / 1e9, 1), "copy_bytes": 2 * cp,
-                    "read_then_write_us": round((t_rd + t_wr) * 1e3, 2),
-                    "kernel_us": round(dom_avg * 1e3, 2),
-                    "ops": ("plain streaming kernels (16-byte nontemporal loads/stores, 2048 work-groups of 256): "
-                            "read the kernel's read bytes, write its write bytes, copy min of the two; "
-                            "graph-replayed back to back")}
-        log(f"[bench] streams: read {ceilings['read_GBs']} GB/s, write {ceilings['write_GBs']} GB/s, copy "
-            f"{ceilings['copy_GBs']} GB/s; reading then writing the kernel's bytes takes "
-            f"{ceilings['read_then_write_us']} us (kernel {dom_avg * 1e3:.1f} us)")
-        del src, dst, sink
+        nrot = n_layers
+
+        def streams(rd, wr, kernel_us, copy=True):
+            rd, wr = rd // 16 * 16, max(wr // 16 * 16, 16)
+            cp = min(rd, wr) // 16 * 16
+            src = torch.ones(nrot * rd // 4, dtype=torch.int32, device="cuda")
+            dst = torch.empty(nrot * wr // 4, dtype=torch.int32, device="cuda")
+            sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+            s0, d0 = src.data_ptr(), dst.data_ptr()
+            t_rd = timed(lambda i: sl.tqs_read(s0 + (i % nrot) * rd, rd, sink.data_ptr(), blocks, hs()), 0) / args.steps
+            t_wr = timed(lambda i: sl.tqs_write(d0 + (i % nrot) * wr, wr, i & 7, blocks, hs()), 0) / args.steps
+            c = {"read_GBs": round(rd / (t_rd * 1e-3) / 1e9, 1), "read_bytes": rd, "read_us": round(t_rd * 1e3, 2),
+                 "write_GBs": round(wr / (t_wr * 1e-3) / 1e9, 1), "write_bytes": wr, "write_us": round(t_wr * 1e3, 2)}
+            if copy:
+                t_cp = timed(lambda i: sl.tqs_copy(s0 + (i % nrot) * rd, d0 + (i % nrot) * wr, cp, blocks, hs()),
+                             0) / args.steps
+                c.update({"copy_GBs": round(2 * cp / (t_cp * 1e-3) / 1e9, 1), "copy_bytes": 2 * cp})
+            c.update({"read_then_write_us": round((t_rd + t_wr) * 1e3, 2), "kernel_us": round(kernel_us, 2)})
+            del src, dst, sink
+            return c
+
+        ceilings = streams(*dom_rw, dom_avg * 1e3)
+        ceilings["ops"] = ("plain streaming kernels (16-byte nontemporal loads/stores, 2048 work-groups of 256): "
+                           "read the kernel's read bytes, write its write bytes, copy min of the two; each rotated "
+                           "over the layer buffers and graph-replayed back to back")
+        log(f"[bench] streams: read {ceilings['read_GBs']} GB/s ({ceilings['read_us']} us), write "
+            f"{ceilings['write_GBs']} GB/s ({ceilings['write_us']} us), copy {ceilings['copy_GBs']} GB/s; "
+            f"read then write {ceilings['read_then_write_us']} us (kernel {dom_avg * 1e3:.1f} us)")
+        if roof2 is not None:
+            c2 = streams(roof2["algorithmic_bytes_per_launch"], 16, roof2["avg_launch_us"], copy=False)
+            roof2["stream_read"] = {k: c2[k] for k in ("read_GBs", "read_bytes", "read_us")}
+            log(f"[bench] {roof2['kernel']}: a plain read of its bytes takes {c2['read_us']} us "
+                f"({c2['read_GBs']} GB/s; kernel {roof2['avg_launch_us']} us)")
 
     cpu = None
     if not args.no_cpu_baseline:

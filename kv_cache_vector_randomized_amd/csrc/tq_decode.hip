@@ -1035,9 +1035,17 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
       }
       load_value_planes<VB>(vp, a, tpn, kvh, lane, blk_stride, head_stride);
     } else {
-      // Fixed-point weights on the grid 2^(E-27), 2^E just above the tile's
-      // largest scale (p <= 1, so every weight is below 2^27, four 7-bit limbs).
-      const int E = __builtin_amdgcn_frexp_expf(smax);
+      // Fixed-point weights of head grp on the grid 2^(E-27), 2^E just above the
+      // bound pmax * smax of the tile's weights p_t * scale_t (pmax = exp2(mt - ms),
+      // the weight of the tile's largest logit; every weight is below 2^27 units,
+      // four 7-bit limbs).  Rounding costs at most half a unit per token, so the
+      // error of a tile's sum is below 64 (2^b - 1) 2^-27 pmax smax, and the
+      // tiles' pmax add up to at most the softmax denominator: the error of the
+      // normalised output stays below (2^b - 1) 2^-21 times the largest scale,
+      // at any context length.  (The rows of the MFMA are per head, so each head
+      // takes its own grid.)
+      const float pmax = __builtin_amdgcn_exp2f(mt - ms);
+      const int E = __builtin_amdgcn_frexp_expf(pmax * smax);
 #pragma unroll
       for (int pg = 0; pg < 4; ++pg)
         wt[grp][16 * pg + j16] = (uint32_t)fmaf(pr[pg], ldexpf(vb[pg], 27 - E), 0.5f);   // round to nearest
