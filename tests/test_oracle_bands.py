@@ -143,3 +143,33 @@ def test_polar_key_band_of_a_known_angle():
         slot = O.polar_slot_map(D).index((1, 0))
         assert abs(kq.band[0, slot] - 4e-7) < 1e-12
         assert kq.codes[0, slot] == 5          # [pi/4, pi/2) is cell 5 of [-pi, pi)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_value_band_covers_the_fp32_quotient(bits):
+    """The oracle's value codes round the exact quotient (v - min) / scale with the
+    stored fp32 min and scale; the kernels round fl32(fl32(v - min) * fl32(1 / scale)).
+    Over many vectors of fp32 inputs, including ones placed next to rounding
+    boundaries, every code on which the two forms disagree lies inside the value
+    band, and some disagreements occur (so the check is not empty)."""
+    rng = np.random.default_rng(17 + bits)
+    levels = (1 << bits) - 1
+    v = rng.standard_normal((4000, D)).astype(np.float32)
+    # half of the vectors get coordinates within a few ulps of a rounding boundary
+    mn, mx = v.min(axis=1, keepdims=True), v.max(axis=1, keepdims=True)
+    sc = ((mx.astype(np.float64) - mn) / levels).astype(np.float32)
+    k = rng.integers(0, levels, size=(2000, D))
+    near = (mn[:2000] + sc[:2000] * (k + 0.5)).astype(np.float32)
+    near = np.nextafter(near, np.where(rng.integers(0, 2, near.shape) == 1, np.inf, -np.inf).astype(np.float32))
+    v[:2000, 1:-1] = near[:, 1:-1]
+    v[:2000, 0], v[:2000, -1] = mn[:2000, 0], mx[:2000, 0]         # keep the range
+    q = O.quantize_values_uniform(v.astype(np.float64), bits)
+    vmin, scale = q.vmin.astype(np.float32)[:, None], q.scale.astype(np.float32)[:, None]
+    with np.errstate(divide="ignore"):
+        inv = np.where(scale > 0, np.float32(1) / scale, np.float32(0)).astype(np.float32)
+    prod = ((v - vmin).astype(np.float32) * inv).astype(np.float32)
+    fp32_codes = np.clip(np.rint(prod), 0, levels).astype(np.int64)    # rint: half to even
+    diff = fp32_codes != q.codes
+    assert diff.any(), "no disagreement: the boundary cases did not reach the band"
+    assert np.all(q.band[diff] < BAND), q.band[diff].max()
+    assert np.all(np.abs(fp32_codes - q.codes) <= 1)
