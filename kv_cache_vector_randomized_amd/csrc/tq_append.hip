@@ -475,18 +475,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
           uint32_t wn = 0u;
+          if constexpr (QJL) {
+            // two cells requested at a time (16-byte reads: the centroids come along);
+            // one at a time waits out every LDS round trip at two waves per SIMD
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float gv = z[2 * n + (i >> 2)][i & 3] * sg;
-            const uint32_t addr = (__float_as_uint(gv + kUnitMagic) << 4) + lut_addr;
-            const u32x4 e = *reinterpret_cast<lds_u32x4*>((uintptr_t)addr);
-            const bool up = gv >= __uint_as_float(e.y);
-            if constexpr (QJL) {
-              const float c = up ? __uint_as_float(e.w) : __uint_as_float(e.z);
-              z[2 * n + (i >> 2)][i & 3] = fmaf(-nz, c, z[2 * n + (i >> 2)][i & 3]);
+            for (int pr2 = 0; pr2 < 4; ++pr2) {
+              floatx4& zz = z[2 * n + (pr2 >> 1)];
+              float gv[2];
+              u32x4 e[2];
+#pragma unroll
+              for (int r = 0; r < 2; ++r) {
+                gv[r] = zz[2 * (pr2 & 1) + r] * sg;
+                const uint32_t addr = (__float_as_uint(gv[r] + kUnitMagic) << 4) + lut_addr;
+                e[r] = *reinterpret_cast<lds_u32x4*>((uintptr_t)addr);
+              }
+#pragma unroll
+              for (int r = 0; r < 2; ++r) {
+                const bool up = gv[r] >= __uint_as_float(e[r].y);
+                const float c = up ? __uint_as_float(e[r].w) : __uint_as_float(e[r].z);
+                zz[2 * (pr2 & 1) + r] = fmaf(-nz, c, zz[2 * (pr2 & 1) + r]);
+                wn |= (e[r].x + (uint32_t)up) << (KB * (2 * pr2 + r));
+              }
             }
-            const uint32_t code = e.x + (uint32_t)up;
-            wn |= code << (KB * i);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const float gv = z[2 * n + (i >> 2)][i & 3] * sg;
+              const uint32_t addr = (__float_as_uint(gv + kUnitMagic) << 4) + lut_addr;
+              const u32x4 e = *reinterpret_cast<lds_u32x4*>((uintptr_t)addr);
+              wn |= (e.x + (uint32_t)(gv >= __uint_as_float(e.y))) << (KB * i);
+            }
           }
           w[n] = wn;
         }

@@ -109,8 +109,9 @@ def test_append_decode_matches_oracle(name):
 
 
 def test_append_decode_equals_two_launches():
-    """The fused step and tq_quantize_append + tq_decode_attention agree (same
-    shapes, same bytes of context)."""
+    """The fused step and tq_quantize_append + tq_decode_attention store the same
+    codes outside the decision band, and each output meets the oracle's bar over
+    the bytes it attended to."""
     from kv_cache_vector_randomized_amd.torch_api import PagedKVCache
     w = synth.WORKLOADS["gqa_decode"]
     lens = np.array([300, 45, 1], np.int64)
@@ -144,12 +145,21 @@ def test_append_decode_equals_two_launches():
         outs.append((out.cpu().numpy().astype(np.float64), cache.data.cpu().numpy()))
     (o1, c1), (o2, c2) = outs
     cfg = H.oracle_config(w)
+    # codes agree except inside the oracle's decision band (the two paths round in
+    # different fp32 forms, exact ties of bf16 data included); scalars up to rounding
+    qz = H.oracle_quantize(w, k[new_rows], v[new_rows])
     for h in range(cfg.num_kv_heads):
         a = O.read_tokens(cfg, c1, new_slots, h)
         r = O.read_tokens(cfg, c2, new_slots, h)
-        # codes agree up to the decision band; scalars up to rounding
-        assert np.mean(a["kcodes"] == r["kcodes"]) > 0.999
-        assert np.mean(a["vcodes"] == r["vcodes"]) > 0.999
-    worst = max(H.rel_err(o1[b, hq], o2[b, hq]) for b in range(B) for hq in range(w.num_q_heads))
-    assert worst <= H.REL_TOL, worst
-    print(f"  fused vs two launches: worst relative difference {worst:.2e}")
+        assert np.all((a["kcodes"] == r["kcodes"]) | (qz.key.band[:, h] < H.BAND))
+        assert np.all((a["vcodes"] == r["vcodes"]) | (qz.val_band[:, h] < H.BAND))
+    # a code inside the band may differ between the two caches, and for a short
+    # sequence one value code moves the output by a visible amount: each output is
+    # checked against the oracle attending over its own cache's bytes
+    worst = 0.0
+    for out, cache_np in ((o1, c1), (o2, c2)):
+        _, ref = H.oracle_decode(w, q, cache_np, lay)
+        for b in range(B):
+            for hq in range(w.num_q_heads):
+                worst = max(worst, H.check_vec("fused vs two launches", w.name, "out", out[b, hq], ref[b, hq], (b, hq)))
+    print(f"  fused and two launches, each against the oracle over its bytes: worst {worst:.2e}")
