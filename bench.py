@@ -66,6 +66,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+FP32_MFMA_PEAK_TFS = 157.3     # MI355X dense fp32 matrix peak, published
+F16_MFMA_PEAK_TFS = 2500.0     # MI355X dense fp16 matrix peak, published (no sparsity)
 # workload -> (synthetic workload, step kind)
 MODES = {
     "gqa_decode": ("gqa_decode", "decode"),
@@ -316,6 +318,20 @@ def main():
     log(f"[bench] step {ms_step * 1e3:.1f} us; {dominant} avg {dom_avg * 1e3:.1f} us "
         f"(p10 {pct[10]:.1f}, p50 {pct[50]:.1f}, p90 {pct[90]:.1f}); "
         f"{achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of HBM peak")
+    # The QJL cache build also carries its dense contraction: S r for every
+    # token-head, 2 d^2 flops of fp32 arithmetic each, priced at the fp32 MFMA peak;
+    # the kernel runs it on the f16 MFMA as three products of split operands.
+    roof_mfma = None
+    if kind == "append" and w.key_mode == "lloyd_qjl":
+        flops = 2.0 * d * d * B * T * Hkv
+        tf = flops / (dom_avg * 1e-3) / 1e12
+        roof_mfma = {"kernel": dominant, "bound": "mfma", "achieved": round(tf, 2), "peak": FP32_MFMA_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": round(tf / FP32_MFMA_PEAK_TFS, 4),
+                     "algorithmic_flops_per_launch": flops,
+                     "as_run": {"dtype": "f16 MFMA, three split products", "flops": 3 * flops,
+                                "peak": F16_MFMA_PEAK_TFS,
+                                "frac": round(3 * tf / F16_MFMA_PEAK_TFS, 4)}}
+        log(f"[bench] S r contraction: {tf:.1f} TFLOP/s = {tf / FP32_MFMA_PEAK_TFS:.1%} of the fp32 MFMA peak")
     roof2 = None
     if second is not None:
         name2, bytes2, source2, fn2 = second
@@ -426,6 +442,7 @@ def main():
             "p10_p50_p90_us": [round(pct[10], 2), round(pct[50], 2), round(pct[90], 2)],
         },
         "roofline_decode": roof2,
+        "roofline_mfma": roof_mfma,
         "stream_ceilings": ceilings,
         "cpu_baseline": cpu,
         "launch": ("eager" if args.eager else "; ".join(launch_notes) if launch_notes
