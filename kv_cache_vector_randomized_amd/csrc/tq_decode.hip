@@ -23,12 +23,13 @@
 //
 // Values (uniform): sum_t p_t (min_t + scale_t * code_t).  The min part is a
 // per-head scalar; the code part is an exact integer product on the int8 16x16x64
-// MFMA: per tile the weights p_t * scale_t go on a fixed-point grid tied to the
-// tile's largest scale, split into four 7-bit limbs (rows = head x limb, columns
-// = coordinates, K = the tile's 64 tokens).  Value codes are plane-major in a
-// page, so lane l loads the planes of coordinates 8j..8j+7 (j = l%16) of page
-// l/16 with contiguous 16-byte loads.  Lloyd-Max values are accumulated on the
-// fp32 4x4x1 MFMA in the rotated basis and rotated back once at the end.
+// MFMA: per tile the weights p_t * scale_t of each head go on a fixed-point grid
+// tied to that head's largest weight in the tile, split into four 7-bit limbs
+// (rows = head x limb, columns = coordinates, K = the tile's 64 tokens).  Value
+// codes are plane-major in a page, so lane l loads the planes of coordinates
+// 8j..8j+7 (j = l%16) of page l/16 with contiguous 16-byte loads.  Lloyd-Max
+// values are accumulated on the fp32 4x4x1 MFMA in the rotated basis and rotated
+// back once at the end.
 //
 // Per-split partials (max, sum, 128 outputs) go to the workspace; the last
 // work-group of each (sequence, kv head) to finish, found with a self-resetting
