@@ -1,5 +1,7 @@
 """The benchmark's CPU leg (the oracle timed on the host) runs and reports the
 agreed fields, on shrunk copies of each kind of workload (no GPU needed)."""
+import os
+
 import numpy as np
 import pytest
 
@@ -19,3 +21,13 @@ def test_cpu_baseline_reports_the_contract_fields(mode):
     assert set(rec) == {"value", "unit", "cores", "kind", "sample"}
     assert rec["kind"] == "oracle" and rec["unit"] == "GB/s" and rec["value"] > 0 and rec["cores"] >= 1
     assert isinstance(rec["sample"], str) and rec["sample"]
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py runs on one GPU: --gpus N > 1 exits with a message before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
