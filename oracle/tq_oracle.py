@@ -21,7 +21,7 @@ Sources (cited by page and section):
   [P4] qiita, AMD 4-bit KV caching in LMCache, sections "4bitという名前だけでは…"
        (two 4-bit codes per uint8) and "小さな保存・復元コードで…" (byte example).
 
-Readings taken where the pages are silent (each is listed in the design notes):
+Readings taken where the pages are silent:
   R1  rotation y = H (s * x) / sqrt(d), Sylvester H in natural order, signs first.
   R2  codebook = Lloyd-Max for N(0, 1/d), solved on the positive half and mirrored.
   R5  norm correction: stored norm = ||k|| / ||C[code]||, so ||k_hat|| = ||k||.
