@@ -370,7 +370,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
   // In pass i the waves 0, 1 (i even) or 2, 3 (i odd) quantize the keys of the
   // pair's two groups and the other two their values, so that every SIMD gets
   // both kinds of work.
-  uint32_t p = blockIdx.x;                 // the launcher keeps gridDim.x <= npairs
+  // Pair of round r for this work-group (npairs: none), per the launcher's round plan;
+  // round 0 is pair blockIdx.x (the launcher keeps gridDim.x <= npairs).
+  const uint32_t slot_wgs = (uint32_t)a.slot_wgs;
+  const uint32_t my_rounds = (uint32_t)a.rounds[min(blockIdx.x / slot_wgs, 2u)];
+  auto pair_of = [&](uint32_t r) -> uint32_t {
+    if (r >= my_rounds) return npairs;
+    const uint32_t q = slot_wgs * (min(r, (uint32_t)a.rounds[0]) + min(r, (uint32_t)a.rounds[1]) +
+                                   min(r, (uint32_t)a.rounds[2])) + blockIdx.x;
+    return q < npairs ? q : npairs;
+  };
+  uint32_t p = blockIdx.x;
+  uint32_t round = 0;
   const bool keys0 = wave < 2;             // role in even passes
   uint4 inA[4], inB[4];
   int64_t rawA, rawB;
@@ -556,7 +567,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
           }
           // Sign rows of the wave's 16 tokens: lane (j, g) computes bits 16mt + 4g + r
           // (mt = 0..7, r = 0..3) of token j's row, nibble mt of `mine`.
-          uint32_t mine = 0u;
+          // p >= 0 is read off the fp32 sign bit: the accumulators start at +0 and add
+          // finite terms, so p is never -0 or NaN.  Each step shifts `neg` left by one
+          // and brings in the sign bit of p (one funnel shift), so the bit of step
+          // k = 4mt + r ends at 31 - k; one bit reversal and a complement give `mine`.
+          uint32_t neg = 0u;
 #pragma unroll 2
           for (int mt = 0; mt < 8; ++mt) {
             // the three products in separate accumulators: three MFMA chains instead of one
@@ -570,12 +585,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
               acc = mfma_f16x32(sh, rh[n], acc);
             }
             acc = acc + (acc1 + acc2);
-            // lane (j, g) holds p[16mt + 4g + r] of token j: sign bit 1 for p >= 0
-            uint32_t nib = 0u;
+            // lane (j, g) holds p[16mt + 4g + r] of token j
 #pragma unroll
-            for (int r = 0; r < 4; ++r) nib |= (acc[r] >= 0.f ? 1u : 0u) << r;
-            mine |= nib << (4 * mt);
+            for (int r = 0; r < 4; ++r) neg = __builtin_amdgcn_alignbit(neg, __float_as_uint(acc[r]), 31);
           }
+          const uint32_t mine = __builtin_bitreverse32(~neg);
           // Dword g of token j's row (rows 32g..32g+31) takes nibbles 2g and 2g+1
           // of each lane (j, g'), at bits 4g' + r and 16 + 4g' + r.
           uint32_t srw = 0u;
@@ -715,17 +729,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL ? 2 : 3
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // Pairs p, p + gridDim.x, ...: the next pair's inputs are loaded while this
-  // one is quantized, into the other of two register sets (a copy of registers
-  // still being loaded would wait for the load).
+  // Pairs of rounds 0, 1, ...: the next pair's inputs are loaded while this one
+  // is quantized, into the other of two register sets (a copy of registers still
+  // being loaded would wait for the load).
   for (;;) {
-    uint32_t pn = p + gridDim.x;
+    uint32_t pn = pair_of(++round);
     bool more = pn < npairs;
     load_group(more ? pn : p, !keys0, inB, rawB);
     run_pass(p, keys0, inA, rawA);
     if (!more) break;
     p = pn;
-    pn = p + gridDim.x;
+    pn = pair_of(++round);
     more = pn < npairs;
     load_group(more ? pn : p, keys0, inA, rawA);
     run_pass(p, !keys0, inB, rawB);
@@ -789,10 +803,40 @@ hipError_t values_mode(const AppendArgs& a, int dtype, int val_mode, hipStream_t
 }
 
 template <int KB, bool QJL>
-hipError_t page_vb(const AppendArgs& a, int val_bits, hipStream_t s) {
+hipError_t page_vb(const AppendArgs& args, int val_bits, hipStream_t s) {
   // one pair of 16-token groups per work-group and pass; at most a.page_wgs work-groups
+  AppendArgs a = args;
   const int64_t pairs = ((a.num_tokens + 15) / 16 * a.hkv + 1) / 2;
-  const dim3 grid((unsigned)std::min<int64_t>(pairs, std::max(1, a.page_wgs)));
+  const int64_t wgs = std::max(1, a.page_wgs);
+  const dim3 grid((unsigned)std::min<int64_t>(pairs, wgs));
+  // Round plan.  The resident work-groups of a compute unit do not progress at the
+  // same rate: the first dispatched to it (ids below wgs / n with n per unit, as
+  // the dispatcher fills every unit once before the next) issue first and finish
+  // earlier.  Long appends give the slots of each unit shares of its pairs that
+  // make them end together: 120 : 110 : 100 with three work-groups per unit
+  // (1.7% faster than equal shares on 131072 tokens x 8 heads), 130 : 100 with
+  // two (the QJL kernel: about 2.5% faster on 8 x 16384 tokens x 8 heads), the
+  // best of the shares timed.  Other appends take pairs round-robin (one slot).  Every
+  // pair belongs to exactly one (work-group, round) either way; the plan only
+  // moves work, never drops it.
+  a.slot_wgs = (int32_t)grid.x;
+  a.rounds[0] = (int32_t)((pairs + grid.x - 1) / grid.x);
+  a.rounds[1] = a.rounds[2] = 0;
+  const int ns = a.page_per_cu;
+  if ((ns == 2 || ns == 3) && (int64_t)grid.x == wgs && wgs % ns == 0 && pairs >= 8 * wgs) {
+    const int64_t c = wgs / ns;
+    const int64_t per_unit = (pairs + c - 1) / c;
+    const int64_t w[3] = {ns == 3 ? 120 : 130, ns == 3 ? 110 : 100, ns == 3 ? 100 : 0};
+    const int64_t wsum = w[0] + w[1] + w[2];
+    int64_t n[3] = {0, 0, 0}, sum = 0;
+    for (int i = 0; i < ns; ++i) {
+      n[i] = per_unit * w[i] / wsum;
+      sum += n[i];
+    }
+    for (int i = 0; sum < per_unit; i = (i + 1) % ns, ++sum) ++n[i];   // the remainder to the first slots
+    a.slot_wgs = (int32_t)c;
+    for (int i = 0; i < 3; ++i) a.rounds[i] = (int32_t)n[i];
+  }
   switch (val_bits) {
     case 2: hipLaunchKernelGGL((append_page_kernel<KB, 2, QJL>), grid, dim3(256), 0, s, a); break;
     case 3: hipLaunchKernelGGL((append_page_kernel<KB, 3, QJL>), grid, dim3(256), 0, s, a); break;

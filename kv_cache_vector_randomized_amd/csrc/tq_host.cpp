@@ -22,6 +22,7 @@ struct tq_ctx {
   float klut_scale, klut_bias, vlut_scale, vlut_bias;
   int unit_grid_ok;        // the page-append key grid resolves every threshold
   int page_wgs;            // page-append grid: resident work-groups on the whole device
+  int page_per_cu;         // resident page-append work-groups per compute unit
   int decode_wgs;          // decode grid target: resident work-groups on the whole device
 };
 
@@ -435,6 +436,7 @@ tq_status tq_create(const tq_config* cfg, const int8_t* signs_host, const float*
     page_per_cu = 2;
   (void)hipGetLastError();
   ctx->page_wgs = page_per_cu * cus;
+  ctx->page_per_cu = page_per_cu;
   (void)scratch_of(ctx->device);   // set-up of the no-allocation decode's scratch on this device
   *out = ctx;
   return TQ_OK;
@@ -475,6 +477,7 @@ tq_status tq_quantize_append(tq_ctx* ctx, const void* k, const void* v, tq_dtype
   a.vlut_scale = ctx->vlut_scale; a.vlut_bias = ctx->vlut_bias;
   a.unit_grid_ok = ctx->unit_grid_ok;
   a.page_wgs = ctx->page_wgs;
+  a.page_per_cu = ctx->page_per_cu;
   hipError_t e = tq::launch_append(a, (int)dt, (int)ctx->cfg.key_bits, (int)ctx->cfg.key_mode,
                                    (int)ctx->cfg.val_bits, (int)ctx->cfg.val_mode, stream);
   return e == hipSuccess ? TQ_OK : hip_fail(e, "append launch");

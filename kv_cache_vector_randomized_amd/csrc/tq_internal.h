@@ -81,6 +81,12 @@ struct AppendArgs {
   float vlut_scale, vlut_bias;
   int32_t unit_grid_ok;          // kulut resolves every key threshold (the page kernel may run)
   int32_t page_wgs;              // grid of the page kernel: its resident work-groups on the device
+  int32_t page_per_cu;           // resident page-kernel work-groups per compute unit
+  // Round plan of the page kernel (set by its launcher): work-group w belongs to
+  // slot w / slot_wgs and takes pairs in rounds r < rounds[slot]; round r's pair of
+  // w is slot_wgs * sum_s min(r, rounds[s]) + w (rounds[] non-increasing).
+  int32_t slot_wgs;
+  int32_t rounds[3];
 };
 
 struct DecodeArgs {
