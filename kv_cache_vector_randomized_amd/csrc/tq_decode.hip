@@ -446,12 +446,20 @@ __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, floa
     rbuf[2 * lane] = r0;
     rbuf[2 * lane + 1] = r1;
     wave_sync_lds();
+    // 32 rows of S^T requested at a time, then used (a sched barrier keeps the
+    // compiler from sinking each load to its use: one round trip per 32 rows
+    // instead of one per 8)
     float p0 = 0.f, p1 = 0.f;
-#pragma unroll 8
-    for (int k = 0; k < kDim; ++k) {
-      const float2 sv = *reinterpret_cast<const float2*>(&a.c->St[k * kDim + 2 * lane]);
-      p0 = fmaf(sv.x, rbuf[k], p0);
-      p1 = fmaf(sv.y, rbuf[k], p1);
+    for (int kb = 0; kb < kDim; kb += 32) {
+      float2 sv[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) sv[u] = *reinterpret_cast<const float2*>(&a.c->St[(kb + u) * kDim + 2 * lane]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        p0 = fmaf(sv[u].x, rbuf[kb + u], p0);
+        p1 = fmaf(sv[u].y, rbuf[kb + u], p1);
+      }
     }
     sgn0 = p0 >= 0.f ? 1.f : -1.f;
     sgn1 = p1 >= 0.f ? 1.f : -1.f;
@@ -767,13 +775,19 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
       q_sh[wave][2 * lane] = x0;
       q_sh[wave][2 * lane + 1] = x1;
       wave_sync_lds();
+      // (32 rows of S^T requested at a time, as in the new token's projection)
       float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll 8
-      for (int k = 0; k < kDim; ++k) {
-        const float2 sv = *reinterpret_cast<const float2*>(&a.c->St[k * kDim + 2 * lane]);
-        const float qk = q_sh[wave][k];
-        acc0 = fmaf(sv.x, qk, acc0);
-        acc1 = fmaf(sv.y, qk, acc1);
+      for (int kb = 0; kb < kDim; kb += 32) {
+        float2 sv[32];
+#pragma unroll
+        for (int u = 0; u < 32; ++u) sv[u] = *reinterpret_cast<const float2*>(&a.c->St[(kb + u) * kDim + 2 * lane]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 32; ++u) {
+          const float qk = q_sh[wave][kb + u];
+          acc0 = fmaf(sv[u].x, qk, acc0);
+          acc1 = fmaf(sv[u].y, qk, acc1);
+        }
       }
       acc0 *= a.qjl_coef;
       acc1 *= a.qjl_coef;
