@@ -54,6 +54,17 @@
  *   (k mod 8) of byte k/8.  All fp32 scalars are little-endian IEEE-754.
  *   Version history: 1 stored the value codes slot-major like the other fields;
  *   2 stores them plane-major.  A reader of transferred pages checks the version.
+ *
+ * Head and group sizes
+ *   head_dim 128 with 1, 2 or 4 query heads per KV head runs on the tuned
+ *   kernels.  head_dim 64 or 256, or any group size from 1 to 16 at head_dim 128,
+ *   runs on the generic path: the same page format, entry points and results (up
+ *   to the decision band and the fp32 summation order), computed by plain
+ *   one-wave-per-vector append and dequantize kernels and a two-launch decode
+ *   (per split, then the merge); its one-launch step is three launches (the new
+ *   tokens, the decode, the merge).  The generic path takes Lloyd-Max keys (2, 3,
+ *   4 or 8 bits; QJL with 2, 3 or 4) and both value modes; FP8 and PolarQuant
+ *   keys need head_dim 128 with 1, 2 or 4 query heads per KV head.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -112,9 +123,9 @@ typedef enum {
 
 typedef struct {
   uint32_t abi_version;   /* must equal TQ_ABI_VERSION                              */
-  uint32_t head_dim;      /* d; the library supports 128                           */
+  uint32_t head_dim;      /* d: 64, 128 or 256 (see "Head and group sizes")        */
   uint32_t num_kv_heads;  /* Hkv >= 1                                               */
-  uint32_t num_q_heads;   /* Hq, a multiple of Hkv; Hq/Hkv must be 1, 2 or 4        */
+  uint32_t num_q_heads;   /* Hq, a multiple of Hkv with Hq/Hkv <= 16                */
   uint32_t key_bits;      /* 2, 3 or 4 (Lloyd-Max modes); 8 (TQ_KEY_FP8)             */
   uint32_t key_mode;      /* tq_key_mode                                            */
   uint32_t val_bits;      /* 2, 3 or 4                                              */
@@ -235,7 +246,8 @@ tq_status tq_decode_attention_noalloc(tq_ctx* ctx, const void* q, tq_dtype dt, c
                                       const int32_t* seq_lens, int32_t batch, int32_t max_seq_len,
                                       float softmax_scale, float* out, float* logits_out, hipStream_t stream);
 
-/* One decode step in one launch: store the new token of every sequence, then
+/* One decode step in one launch (the generic path: see "Head and group sizes"):
+ * store the new token of every sequence, then
  * attend over the context including it (turboquant-vllm write-up, "Incremental
  * dequantization": each step handles only the one new token; "Bugs Nobody Else
  * Has Found": the attention is fused over the compressed cache).  The result
@@ -249,7 +261,8 @@ tq_status tq_decode_attention_noalloc(tq_ctx* ctx, const void* q, tq_dtype dt, c
  *                 a sequence of length 0 takes no new token).
  *   cache:        device, written at those slots only.
  *   all other arguments as for tq_decode_attention.
- * Uniform values only (TQ_ERR_UNSUPPORTED for Lloyd-Max values). */
+ * Uniform values only on the tuned path (TQ_ERR_UNSUPPORTED for Lloyd-Max values
+ * there); the generic path takes both value modes. */
 tq_status tq_append_decode(tq_ctx* ctx, const void* k_new, const void* v_new, const void* q, tq_dtype dt,
                            void* cache, int64_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
                            const int32_t* seq_lens, int32_t batch, int32_t max_seq_len, float softmax_scale,

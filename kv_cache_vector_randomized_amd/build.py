@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libtq.so")
 STREAM_OUT = os.path.join(PKG, "libtqstream.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["tq_host.cpp", "tq_append.hip", "tq_decode.hip", "tq_dequant.hip", "tq_transfer.hip", "tq_polar.hip"]
+SOURCES = ["tq_host.cpp", "tq_append.hip", "tq_decode.hip", "tq_dequant.hip", "tq_transfer.hip", "tq_polar.hip",
+           "tq_generic.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

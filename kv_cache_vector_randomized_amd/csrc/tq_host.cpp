@@ -24,6 +24,12 @@ struct tq_ctx {
   int page_wgs;            // page-append grid: resident work-groups on the whole device
   int page_per_cu;         // resident page-append work-groups per compute unit
   int decode_wgs;          // decode grid target: resident work-groups on the whole device
+  // Generic path (head_dim 64 / 256, or a group size other than 1, 2, 4): its own
+  // constants, S^T for QJL keys, and the device's compute-unit count.
+  int generic;
+  tq::GenConsts* gconsts;  // device
+  float* gSt;              // device [d * d], QJL only
+  int cus;
 };
 
 namespace {
@@ -212,6 +218,13 @@ bool build_unit_lut(int bits, const float* c, const float* t, tq::QLut* lut) {
   return true;
 }
 
+// The tuned kernels take head_dim 128 with 1, 2 or 4 query heads per KV head;
+// every other supported configuration runs on the generic path.
+bool is_generic(const tq_config* c) {
+  const uint32_t g = c->num_q_heads / c->num_kv_heads;
+  return c->head_dim != (uint32_t)tq::kDim || (g != 1 && g != 2 && g != 4);
+}
+
 tq_status layout_of(const tq_config* c, tq_layout* L) {
   const size_t T = TQ_BLOCK_TOKENS, d = c->head_dim;
   std::memset(L, 0, sizeof *L);
@@ -235,7 +248,8 @@ tq_status layout_of(const tq_config* c, tq_layout* L) {
   if (c->val_mode == TQ_VAL_UNIFORM) { L->off_vscale = off; off += T * 4; } else L->off_vscale = none;
   L->page_bytes = off;
   L->token_head_bytes = off / T;
-  if (off > (size_t)tq::kMaxPageBytes) return fail(TQ_ERR_UNSUPPORTED, "page of %zu bytes exceeds %d", off, tq::kMaxPageBytes);
+  const size_t limit = is_generic(c) ? (size_t)tq::kGenMaxPageBytes : (size_t)tq::kMaxPageBytes;
+  if (off > limit) return fail(TQ_ERR_UNSUPPORTED, "page of %zu bytes exceeds %zu", off, limit);
   return TQ_OK;
 }
 
@@ -256,6 +270,18 @@ tq::FieldOffsets offsets_of(const tq_layout& L) {
 // whole 64-token tiles so that the grid is about one round of resident
 // work-groups (`target`, from the kernel's occupancy): more, shorter splits only
 // add prologues and merges, fewer leave SIMDs idle.  A split holds 4 to 64 tiles.
+// Generic decode: splits of whole 64-token blocks, about `target` work-groups in
+// all, at most 64 splits per (sequence, KV head).
+void plan_gen_splits(int target, int batch, int hkv, int max_seq, int* splits, int* chunk) {
+  const int blocks = std::max(1, (max_seq + 63) / 64);
+  const int64_t pairs = std::max<int64_t>(1, (int64_t)batch * hkv);
+  int want = (int)std::min<int64_t>(blocks, std::max<int64_t>(1, (target + pairs - 1) / pairs));
+  want = std::min(want, 64);
+  const int per = (blocks + want - 1) / want;
+  *chunk = per * 64;
+  *splits = (blocks + per - 1) / per;
+}
+
 void plan_splits(int target, int batch, int hkv, int max_seq, int* splits, int* tiles_total) {
   const int tiles = std::max(1, (max_seq + 63) / 64);
   const int pairs = std::max(1, batch * hkv);
@@ -278,6 +304,72 @@ struct DeviceGuard {
 };
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Context of a generic-path configuration (validated by the caller): the
+// codebooks, signs and S^T on the device.
+tq_status create_generic(const tq_config* cfg, const int8_t* signs_host, const float* S_host, tq_ctx** out) {
+  const int d = (int)cfg->head_dim;
+  tq::GenConsts h;
+  std::memset(&h, 0, sizeof h);
+  for (int i = 0; i < d; ++i) h.signs[i] = (float)signs_host[i];
+  codebook_f32((int)cfg->key_bits, d, h.kc, h.kt);
+  if (cfg->val_mode == TQ_VAL_LLOYD) codebook_f32((int)cfg->val_bits, d, h.vc, h.vt);
+  std::vector<float> st;
+  if (cfg->key_mode == TQ_KEY_LLOYD_QJL) {
+    st.resize((size_t)d * d);
+    for (int m = 0; m < d; ++m)
+      for (int k = 0; k < d; ++k) st[(size_t)k * d + m] = S_host[(size_t)m * d + k];
+  }
+  tq_ctx* ctx = new (std::nothrow) tq_ctx();
+  if (!ctx) return fail(TQ_ERR_OUT_OF_MEMORY, "host allocation failed");
+  ctx->cfg = *cfg;
+  tq_status s = layout_of(cfg, &ctx->layout);
+  if (s != TQ_OK) { delete ctx; return s; }
+  ctx->generic = 1;
+  ctx->consts = nullptr;
+  ctx->gconsts = nullptr;
+  ctx->gSt = nullptr;
+  for (int i = 0; i < 4; ++i) ctx->sign_bits[i] = 0;
+  hipError_t e = hipGetDevice(&ctx->device);
+  if (e != hipSuccess) { delete ctx; return hip_fail(e, "hipGetDevice"); }
+  e = hipMalloc((void**)&ctx->gconsts, sizeof(tq::GenConsts));
+  if (e == hipSuccess) e = hipMemcpy(ctx->gconsts, &h, sizeof h, hipMemcpyHostToDevice);
+  if (e == hipSuccess && !st.empty()) {
+    e = hipMalloc((void**)&ctx->gSt, st.size() * sizeof(float));
+    if (e == hipSuccess) e = hipMemcpy(ctx->gSt, st.data(), st.size() * sizeof(float), hipMemcpyHostToDevice);
+  }
+  if (e != hipSuccess) {
+    if (ctx->gconsts) hipFree(ctx->gconsts);
+    if (ctx->gSt) hipFree(ctx->gSt);
+    delete ctx;
+    return e == hipErrorOutOfMemory ? fail(TQ_ERR_OUT_OF_MEMORY, "hipMalloc") : hip_fail(e, "generic constants upload");
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, ctx->device) != hipSuccess || cus <= 0)
+    cus = 256;
+  (void)hipGetLastError();
+  ctx->cus = cus;
+  ctx->decode_wgs = 2 * cus;
+  ctx->page_wgs = 8 * cus;
+  ctx->page_per_cu = 0;
+  ctx->klut_scale = ctx->klut_bias = ctx->vlut_scale = ctx->vlut_bias = 0.f;
+  ctx->unit_grid_ok = 0;
+  (void)scratch_of(ctx->device);   // the no-allocation decode's scratch on this device
+  *out = ctx;
+  return TQ_OK;
+}
+
+tq::GenRows gen_rows(const tq_layout& L) {
+  tq::GenRows r;
+  r.kcodes = (uint32_t)L.row_kcodes;
+  r.ksigns = (uint32_t)L.row_ksigns;
+  r.vcodes = (uint32_t)L.row_vcodes;
+  return r;
+}
+
+int gen_key_mode(const tq_config& c) {
+  return c.key_mode == TQ_KEY_LLOYD_NC ? 1 : c.key_mode == TQ_KEY_LLOYD_QJL ? 2 : 0;
+}
 
 }  // namespace
 
@@ -312,7 +404,14 @@ tq_status tq_validate_config(const tq_config* c) {
   if (c->val_mode > TQ_VAL_LLOYD) return fail(TQ_ERR_INVALID_ARG, "bad val_mode %u", c->val_mode);
   if (c->key_bits < 1 || c->key_bits > 8) return fail(TQ_ERR_INVALID_ARG, "key_bits %u out of [1, 8]", c->key_bits);
   if (c->val_bits < 1 || c->val_bits > 8) return fail(TQ_ERR_INVALID_ARG, "val_bits %u out of [1, 8]", c->val_bits);
-  if (c->head_dim != (uint32_t)tq::kDim) return fail(TQ_ERR_UNSUPPORTED, "head_dim %u: kernels are built for 128", c->head_dim);
+  if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
+    return fail(TQ_ERR_UNSUPPORTED, "head_dim %u: supported 64, 128 (tuned) and 256", c->head_dim);
+  const uint32_t g = c->num_q_heads / c->num_kv_heads;
+  if (g > (uint32_t)tq::kGenMaxGroup)
+    return fail(TQ_ERR_UNSUPPORTED, "group size %u: supported 1..%d", g, tq::kGenMaxGroup);
+  if (is_generic(c) && (c->key_mode == TQ_KEY_FP8 || c->key_mode == TQ_KEY_POLAR))
+    return fail(TQ_ERR_UNSUPPORTED, "FP8 and PolarQuant keys are built for head_dim 128 with 1, 2 or 4 query heads "
+                "per KV head");
   if (c->key_mode == TQ_KEY_FP8) {
     if (c->key_bits != 8) return fail(TQ_ERR_INVALID_ARG, "FP8 keys take key_bits 8 (got %u)", c->key_bits);
     if (c->val_mode != TQ_VAL_UNIFORM) return fail(TQ_ERR_UNSUPPORTED, "FP8 keys are built with uniform values only");
@@ -325,8 +424,6 @@ tq_status tq_validate_config(const tq_config* c) {
     return fail(TQ_ERR_UNSUPPORTED, "key_bits %u: supported 2..4 and 8", c->key_bits);
   }
   if (c->val_bits < 2 || c->val_bits > 4) return fail(TQ_ERR_UNSUPPORTED, "val_bits %u: supported 2..4", c->val_bits);
-  const uint32_t g = c->num_q_heads / c->num_kv_heads;
-  if (g != 1 && g != 2 && g != 4) return fail(TQ_ERR_UNSUPPORTED, "group size %u: supported 1, 2, 4", g);
   if (c->num_kv_heads > 65535) return fail(TQ_ERR_UNSUPPORTED, "num_kv_heads too large");
   return TQ_OK;
 }
@@ -355,6 +452,7 @@ tq_status tq_create(const tq_config* cfg, const int8_t* signs_host, const float*
   for (int i = 0; i < d; ++i)
     if (signs_host[i] != 1 && signs_host[i] != -1) return fail(TQ_ERR_INVALID_ARG, "signs_host[%d] = %d is not +-1", i, signs_host[i]);
   if (cfg->key_mode == TQ_KEY_LLOYD_QJL && !S_host) return fail(TQ_ERR_INVALID_ARG, "QJL keys need qjl_S_host");
+  if (is_generic(cfg)) return create_generic(cfg, signs_host, S_host, out);
 
   tq::DevConsts* h = new (std::nothrow) tq::DevConsts();
   if (!h) return fail(TQ_ERR_OUT_OF_MEMORY, "host allocation failed");
@@ -437,6 +535,10 @@ tq_status tq_create(const tq_config* cfg, const int8_t* signs_host, const float*
   (void)hipGetLastError();
   ctx->page_wgs = page_per_cu * cus;
   ctx->page_per_cu = page_per_cu;
+  ctx->generic = 0;
+  ctx->gconsts = nullptr;
+  ctx->gSt = nullptr;
+  ctx->cus = cus;
   (void)scratch_of(ctx->device);   // set-up of the no-allocation decode's scratch on this device
   *out = ctx;
   return TQ_OK;
@@ -445,7 +547,9 @@ tq_status tq_create(const tq_config* cfg, const int8_t* signs_host, const float*
 void tq_destroy(tq_ctx* ctx) {
   if (!ctx) return;
   DeviceGuard g(ctx->device);
-  hipFree(ctx->consts);
+  if (ctx->consts) hipFree(ctx->consts);
+  if (ctx->gconsts) hipFree(ctx->gconsts);
+  if (ctx->gSt) hipFree(ctx->gSt);
   delete ctx;
 }
 
@@ -467,6 +571,17 @@ tq_status tq_quantize_append(tq_ctx* ctx, const void* k, const void* v, tq_dtype
   if (num_tokens * (int64_t)ctx->cfg.num_kv_heads > ((int64_t)1 << 38))
     return fail(TQ_ERR_UNSUPPORTED, "num_tokens * num_kv_heads too large for one launch");
   DeviceGuard g(ctx->device);
+  if (ctx->generic) {
+    tq::GenAppendArgs ga;
+    std::memset(&ga, 0, sizeof ga);
+    ga.k = k; ga.v = v; ga.bf16 = dt == TQ_BF16; ga.num_tokens = num_tokens; ga.hkv = (int32_t)ctx->cfg.num_kv_heads;
+    ga.key_bits = (int32_t)ctx->cfg.key_bits; ga.key_mode = gen_key_mode(ctx->cfg);
+    ga.val_bits = (int32_t)ctx->cfg.val_bits; ga.val_mode = ctx->cfg.val_mode == TQ_VAL_LLOYD ? 1 : 0;
+    ga.slots = slot_mapping; ga.cache = (uint8_t*)cache; ga.num_blocks = num_blocks;
+    ga.f = offsets_of(ctx->layout); ga.rows = gen_rows(ctx->layout); ga.c = ctx->gconsts; ga.St = ctx->gSt;
+    hipError_t ge = tq::launch_gen_append(ga, (int)ctx->cfg.head_dim, ctx->page_wgs, stream);
+    return ge == hipSuccess ? TQ_OK : hip_fail(ge, "append launch");
+  }
   tq::AppendArgs a;
   a.k = k; a.v = v; a.num_tokens = num_tokens; a.hkv = (int32_t)ctx->cfg.num_kv_heads;
   for (int i = 0; i < 4; ++i) a.sign_bits[i] = ctx->sign_bits[i];
@@ -485,6 +600,11 @@ tq_status tq_quantize_append(tq_ctx* ctx, const void* k, const void* v, tq_dtype
 
 size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t max_seq_len) {
   if (!ctx || batch <= 0 || max_seq_len < 0) return 0;
+  if (ctx->generic) {
+    int splits, chunk;
+    plan_gen_splits(ctx->decode_wgs, batch, (int)ctx->cfg.num_kv_heads, max_seq_len, &splits, &chunk);
+    return tq::kCounterBytes + (size_t)batch * ctx->cfg.num_q_heads * splits * (2 + ctx->cfg.head_dim) * sizeof(float);
+  }
   int splits, tps;
   plan_splits(ctx->decode_wgs, batch, (int)ctx->cfg.num_kv_heads, max_seq_len, &splits, &tps);
   return tq::kCounterBytes +
@@ -514,7 +634,7 @@ tq_status decode_common(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cac
   if (k_new != nullptr) {
     if (!v_new) return fail(TQ_ERR_INVALID_ARG, "v_new is null");
     if (!aligned(k_new, 4) || !aligned(v_new, 4)) return fail(TQ_ERR_INVALID_ARG, "misaligned k_new / v_new");
-    if (ctx->cfg.val_mode == TQ_VAL_LLOYD)
+    if (ctx->cfg.val_mode == TQ_VAL_LLOYD && !ctx->generic)
       return fail(TQ_ERR_UNSUPPORTED, "the fused append takes uniform values only");
   }
   const size_t need = tq_decode_workspace_bytes(ctx, batch, max_seq_len);
@@ -529,6 +649,37 @@ tq_status decode_common(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cac
     workspace = scratch_of(ctx->device);
     if (!workspace) return fail(TQ_ERR_HIP, "no device address for the static scratch on device %d", ctx->device);
     workspace_bytes = tq::kStaticScratchBytes;
+  }
+  if (ctx->generic) {
+    const int hkv = (int)ctx->cfg.num_kv_heads, G = (int)(ctx->cfg.num_q_heads / ctx->cfg.num_kv_heads);
+    const int d = (int)ctx->cfg.head_dim;
+    if (k_new != nullptr) {
+      // the new tokens first (one launch), then the decode over the context including them
+      tq::GenAppendArgs ga;
+      std::memset(&ga, 0, sizeof ga);
+      ga.k = k_new; ga.v = v_new; ga.bf16 = dt == TQ_BF16; ga.num_tokens = batch; ga.hkv = hkv;
+      ga.key_bits = (int32_t)ctx->cfg.key_bits; ga.key_mode = gen_key_mode(ctx->cfg);
+      ga.val_bits = (int32_t)ctx->cfg.val_bits; ga.val_mode = ctx->cfg.val_mode == TQ_VAL_LLOYD ? 1 : 0;
+      ga.slots = nullptr; ga.block_tables = block_tables; ga.max_blocks = max_blocks_per_seq; ga.seq_lens = seq_lens;
+      ga.max_seq = max_seq_len; ga.cache = (uint8_t*)const_cast<void*>(cache); ga.num_blocks = num_blocks;
+      ga.f = offsets_of(ctx->layout); ga.rows = gen_rows(ctx->layout); ga.c = ctx->gconsts; ga.St = ctx->gSt;
+      hipError_t ge = tq::launch_gen_append(ga, d, ctx->page_wgs, stream);
+      if (ge != hipSuccess) return hip_fail(ge, "append launch");
+    }
+    tq::GenDecodeArgs ga;
+    std::memset(&ga, 0, sizeof ga);
+    ga.q = q; ga.q_bf16 = dt == TQ_BF16; ga.cache = (const uint8_t*)cache; ga.num_blocks = num_blocks;
+    ga.block_tables = block_tables; ga.max_blocks = max_blocks_per_seq; ga.seq_lens = seq_lens;
+    ga.batch = batch; ga.max_seq = max_seq_len; ga.hkv = hkv; ga.group = G;
+    ga.key_bits = (int32_t)ctx->cfg.key_bits; ga.key_mode = gen_key_mode(ctx->cfg);
+    ga.val_bits = (int32_t)ctx->cfg.val_bits; ga.val_mode = ctx->cfg.val_mode == TQ_VAL_LLOYD ? 1 : 0;
+    ga.scale = softmax_scale; ga.qjl_coef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / d);
+    ga.logits = logits_out; ga.out = out;
+    ga.ws = (float*)((uint8_t*)workspace + tq::kCounterBytes);
+    plan_gen_splits(ctx->decode_wgs, batch, hkv, max_seq_len, &ga.splits, &ga.chunk);
+    ga.f = offsets_of(ctx->layout); ga.rows = gen_rows(ctx->layout); ga.c = ctx->gconsts; ga.St = ctx->gSt;
+    hipError_t ge = tq::launch_gen_decode(ga, d, stream);
+    return ge == hipSuccess ? TQ_OK : hip_fail(ge, "decode launch");
   }
   tq::DecodeArgs a;
   a.q = q; a.q_dtype = (int32_t)dt; a.cache = (const uint8_t*)cache; a.num_blocks = num_blocks;
@@ -637,6 +788,18 @@ tq_status tq_dequantize_rows(tq_ctx* ctx, const void* cache, int64_t num_blocks,
   if ((n + 15) / 16 * (int64_t)ctx->cfg.num_kv_heads >= (int64_t(1) << 32))
     return fail(TQ_ERR_INVALID_ARG, "n too large for one launch (below 2^36 / num_kv_heads entries)");
   DeviceGuard g(ctx->device);
+  if (ctx->generic) {
+    tq::GenDequantArgs ga;
+    std::memset(&ga, 0, sizeof ga);
+    ga.cache = (const uint8_t*)cache; ga.num_blocks = num_blocks; ga.slots = slots; ga.rows = rows; ga.n = n;
+    ga.buf_rows = buf_rows; ga.hkv = (int32_t)ctx->cfg.num_kv_heads;
+    ga.key_bits = (int32_t)ctx->cfg.key_bits; ga.key_mode = gen_key_mode(ctx->cfg);
+    ga.val_bits = (int32_t)ctx->cfg.val_bits; ga.val_mode = ctx->cfg.val_mode == TQ_VAL_LLOYD ? 1 : 0;
+    ga.k_out = k_buf; ga.v_out = v_buf; ga.bf16_out = out_dt == TQ_BF16;
+    ga.f = offsets_of(ctx->layout); ga.rows_b = gen_rows(ctx->layout); ga.c = ctx->gconsts;
+    hipError_t ge = tq::launch_gen_dequant(ga, (int)ctx->cfg.head_dim, ctx->page_wgs, stream);
+    return ge == hipSuccess ? TQ_OK : hip_fail(ge, "dequantize launch");
+  }
   tq::DequantArgs a;
   for (int i = 0; i < 4; ++i) a.sign_bits[i] = ctx->sign_bits[i];
   a.cache = (const uint8_t*)cache; a.num_blocks = num_blocks; a.slots = slots; a.rows = rows; a.n = n;

@@ -153,4 +153,88 @@ hipError_t launch_polar_dequant(const DequantArgs& a, int key_bits, int val_bits
 hipError_t launch_dequant(const DequantArgs& a, int key_bits, int key_mode, int val_bits, int val_mode, bool bf16_out,
                           hipStream_t s);
 
+// ---- Generic path: head sizes 64, 128 and 256 and up to 16 query heads per KV
+// head, for the configurations the tuned kernels above do not take (head_dim
+// other than 128, or a group size other than 1, 2 and 4).  Same page format,
+// same results up to the decision band and fp32 summation order (tq_generic.hip).
+constexpr int kGenMaxDim = 256;
+constexpr int kGenMaxGroup = 16;
+constexpr int kGenMaxPageBytes = 8192;   // largest page of a generic configuration (d = 256)
+
+struct GenConsts {
+  float signs[kGenMaxDim];   // +-1 of the rotation (head_dim used)
+  float kc[256];             // key centroids, 2^key_bits used
+  float kt[256];             // key thresholds, 2^key_bits - 1 used, ascending
+  float vc[16];              // value centroids (Lloyd-Max values)
+  float vt[16];              // value thresholds (Lloyd-Max values)
+};
+
+struct GenRows {
+  uint32_t kcodes, ksigns, vcodes;   // bytes per token slot of the code fields
+};
+
+struct GenAppendArgs {
+  const void* k;
+  const void* v;
+  int32_t bf16;              // 1: bf16 inputs, 0: fp32
+  int64_t num_tokens;        // rows of k / v (the batch for the one-launch step)
+  int32_t hkv;
+  int32_t key_bits, key_mode, val_bits, val_mode;   // key_mode: 0 plain, 1 corrected norm, 2 QJL
+  const int64_t* slots;      // slot of each token, or null: the new token of each sequence
+  const int32_t* block_tables;   // (slots == null) new token b goes to position seq_lens[b] - 1
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  int32_t max_seq;
+  uint8_t* cache;
+  int64_t num_blocks;
+  FieldOffsets f;
+  GenRows rows;
+  const GenConsts* c;
+  const float* St;           // QJL: S transposed, St[k * d + m] = S[m][k]
+};
+
+struct GenDecodeArgs {
+  const void* q;
+  int32_t q_bf16;
+  const uint8_t* cache;
+  int64_t num_blocks;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  const int32_t* seq_lens;
+  int32_t batch, max_seq, hkv, group;
+  int32_t key_bits, key_mode, val_bits, val_mode;
+  float scale;
+  float qjl_coef;            // sqrt(pi/2) / d
+  float* logits;             // may be null
+  float* out;                // [batch][hkv * group][d]
+  float* ws;                 // partials [batch][hkv][splits][group][2 + d]
+  int32_t splits;
+  int32_t chunk;             // tokens of one split (a multiple of 64)
+  FieldOffsets f;
+  GenRows rows;
+  const GenConsts* c;
+  const float* St;
+};
+
+struct GenDequantArgs {
+  const uint8_t* cache;
+  int64_t num_blocks;
+  const int64_t* slots;
+  const int64_t* rows;       // output row of entry i (nullptr: row i)
+  int64_t n;
+  int64_t buf_rows;
+  int32_t hkv;
+  int32_t key_bits, key_mode, val_bits, val_mode;
+  void* k_out;               // fp32 or bf16 [buf_rows][hkv][d]
+  void* v_out;
+  int32_t bf16_out;
+  FieldOffsets f;
+  GenRows rows_b;
+  const GenConsts* c;
+};
+
+hipError_t launch_gen_append(const GenAppendArgs& a, int d, int grid, hipStream_t s);
+hipError_t launch_gen_decode(const GenDecodeArgs& a, int d, hipStream_t s);
+hipError_t launch_gen_dequant(const GenDequantArgs& a, int d, int grid, hipStream_t s);
+
 }  // namespace tq

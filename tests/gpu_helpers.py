@@ -59,8 +59,12 @@ def qjl_S(w):
     return synth.qjl_matrix(w.head_dim) if w.key_mode == "lloyd_qjl" else None
 
 
+def signs(w):
+    return synth.sign_vector(w.seed, w.head_dim)
+
+
 def make_context(w):
-    return tq.Context(lib_config(w), synth.sign_vector(w.seed), qjl_S(w))
+    return tq.Context(lib_config(w), signs(w), qjl_S(w))
 
 
 def oracle_codebooks(w):
@@ -82,7 +86,7 @@ def upload(x, w, torch):
 def oracle_quantize(w, k, v):
     kcb, vcb = oracle_codebooks(w)
     S = qjl_S(w)
-    return O.quantize_tokens(oracle_config(w), as_f64(k, w), as_f64(v, w), synth.sign_vector(w.seed), kcb, vcb,
+    return O.quantize_tokens(oracle_config(w), as_f64(k, w), as_f64(v, w), signs(w), kcb, vcb,
                              None if S is None else S.astype(np.float64))
 
 
@@ -192,5 +196,5 @@ def oracle_decode(w, q, cache, lay, heads=None):
     kcb, vcb = oracle_codebooks(w)
     S = qjl_S(w)
     return O.decode_attention(oracle_config(w), as_f64(q, w), cache, lay.block_tables, lay.seq_lens,
-                              1.0 / math.sqrt(w.head_dim), synth.sign_vector(w.seed), kcb, vcb,
+                              1.0 / math.sqrt(w.head_dim), signs(w), kcb, vcb,
                               None if S is None else S.astype(np.float64), heads=heads)

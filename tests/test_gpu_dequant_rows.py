@@ -112,7 +112,7 @@ def test_incremental_buffer_equals_full_dequantize(name):
     kf, vf = kf.numpy(), vf.numpy()
     worst = 0.0
     for h in range(hkv):
-        rk, rv, _ = H.O.dequantize_slots(H.oracle_config(w), cache_np, all_slots, h, synth.sign_vector(w.seed),
+        rk, rv, _ = H.O.dequantize_slots(H.oracle_config(w), cache_np, all_slots, h, H.signs(w),
                                          kcb, vcb)
         for i in range(len(all_slots)):
             e = max(H.rel_err(kf[i, h], rk[i]), H.rel_err(vf[i, h], rv[i]))

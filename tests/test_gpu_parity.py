@@ -196,7 +196,7 @@ def test_dequantize_matches_oracle(name):
     kh, vh = kh.cpu().numpy(), vh.cpu().numpy()
     kcb, vcb = H.oracle_codebooks(w)
     for h in range(w.num_kv_heads):
-        rk, rv, _ = H.O.dequantize_slots(H.oracle_config(w), cache_np, slots, h, synth.sign_vector(w.seed), kcb, vcb)
+        rk, rv, _ = H.O.dequantize_slots(H.oracle_config(w), cache_np, slots, h, H.signs(w), kcb, vcb)
         for i in range(len(slots)):
             assert H.rel_err(kh[i, h], rk[i]) <= 1e-5
             assert H.rel_err(vh[i, h], rv[i]) <= 1e-5
@@ -222,6 +222,6 @@ def test_decode_skips_out_of_range_blocks_and_clamps_lengths():
             cfg = H.oracle_config(w)
             kv = h // cfg.group
             s = lay.slots(b, 0, lens[b])[keep]
-            kh, vh, _ = H.O.dequantize_slots(cfg, cache_np, s, kv, synth.sign_vector(w.seed), kcb, vcb)
+            kh, vh, _ = H.O.dequantize_slots(cfg, cache_np, s, kv, H.signs(w), kcb, vcb)
             _, ref = H.O.attention_one(H.as_f64(q, w)[b, h], kh, vh, 1 / math.sqrt(128))
             assert H.rel_err(out[b, h], ref) <= H.REL_TOL

@@ -54,7 +54,7 @@ def _peaked_case():
     # the tail's logit is scale * q . k_hat_tail and the first token's twice that, so a
     # query along k_hat_tail with logit g ln 2 puts 2^-g on every tail token
     kcb, _ = H.oracle_codebooks(w)
-    k_hat = H.O.dequantize_keys(qz.key.codes[1, 0], qz.key.norm[1, 0], synth.sign_vector(w.seed), kcb)
+    k_hat = H.O.dequantize_keys(qz.key.codes[1, 0], qz.key.norm[1, 0], H.signs(w), kcb)
     scale = 1.0 / math.sqrt(w.head_dim)
     u = k_hat / np.linalg.norm(k_hat)
     q = np.stack([to_bf16(u * g * math.log(2.0) / (scale * np.linalg.norm(k_hat))) for g in GAPS])[None]

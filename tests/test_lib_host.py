@@ -51,9 +51,20 @@ def test_status_strings():
     (dict(), tq.TQ_OK),
     (dict(num_kv_heads=8, num_q_heads=32), tq.TQ_OK),
     (dict(num_kv_heads=8, num_q_heads=12), tq.TQ_ERR_INVALID_ARG),
-    (dict(num_kv_heads=2, num_q_heads=16), tq.TQ_ERR_UNSUPPORTED),   # group 8
+    (dict(num_kv_heads=2, num_q_heads=16), tq.TQ_OK),                # group 8: the generic path
+    (dict(num_kv_heads=1, num_q_heads=3), tq.TQ_OK),                 # group 3: the generic path
+    (dict(num_kv_heads=1, num_q_heads=16), tq.TQ_OK),
+    (dict(num_kv_heads=1, num_q_heads=17), tq.TQ_ERR_UNSUPPORTED),   # more than 16 q heads per KV head
     (dict(head_dim=96), tq.TQ_ERR_INVALID_ARG),
-    (dict(head_dim=64), tq.TQ_ERR_UNSUPPORTED),
+    (dict(head_dim=64), tq.TQ_OK),
+    (dict(head_dim=256), tq.TQ_OK),
+    (dict(head_dim=256, key_bits=8, key_mode="lloyd_nc"), tq.TQ_OK),
+    (dict(head_dim=256, key_bits=2, key_mode="lloyd_qjl", val_mode="lloyd"), tq.TQ_OK),
+    (dict(head_dim=32), tq.TQ_ERR_UNSUPPORTED),
+    (dict(head_dim=512), tq.TQ_ERR_UNSUPPORTED),
+    (dict(head_dim=64, key_bits=8, key_mode="fp8"), tq.TQ_ERR_UNSUPPORTED),   # FP8 / polar: d 128, groups 1, 2, 4
+    (dict(head_dim=256, key_bits=3, key_mode="polar"), tq.TQ_ERR_UNSUPPORTED),
+    (dict(num_kv_heads=1, num_q_heads=8, key_bits=8, key_mode="fp8"), tq.TQ_ERR_UNSUPPORTED),
     (dict(key_bits=0), tq.TQ_ERR_INVALID_ARG),
     (dict(key_bits=8), tq.TQ_OK),                    # 8-bit Lloyd-Max keys
     (dict(key_bits=5), tq.TQ_ERR_UNSUPPORTED),
@@ -103,17 +114,19 @@ def test_every_call_refuses_a_null_context():
         assert b"null" in lib.tq_last_error_message(), name
 
 
-@pytest.mark.parametrize("kb,km,vb,vm", [(4, "lloyd", 4, "lloyd"), (4, "lloyd_nc", 4, "uniform"),
-                                         (3, "lloyd_nc", 3, "uniform"), (2, "lloyd_qjl", 4, "uniform"),
-                                         (2, "lloyd", 2, "uniform"), (3, "lloyd_qjl", 3, "lloyd"),
-                                         (8, "fp8", 4, "uniform"), (8, "fp8", 3, "uniform"),
-                                         (8, "lloyd_nc", 3, "uniform"), (3, "polar", 4, "uniform")])
-def test_layout_matches_format(kb, km, vb, vm):
-    lay = tq.layout_for_config(tq.make_config(128, 8, 32, kb, km, vb, vm)).as_dict()
-    f = O.page_fields(O.Config(128, 8, 32, kb, km, vb, vm))
+@pytest.mark.parametrize("d,kb,km,vb,vm", [(128, 4, "lloyd", 4, "lloyd"), (128, 4, "lloyd_nc", 4, "uniform"),
+                                           (128, 3, "lloyd_nc", 3, "uniform"), (128, 2, "lloyd_qjl", 4, "uniform"),
+                                           (128, 2, "lloyd", 2, "uniform"), (128, 3, "lloyd_qjl", 3, "lloyd"),
+                                           (128, 8, "fp8", 4, "uniform"), (128, 8, "fp8", 3, "uniform"),
+                                           (128, 8, "lloyd_nc", 3, "uniform"), (128, 3, "polar", 4, "uniform"),
+                                           (64, 3, "lloyd_qjl", 3, "uniform"), (64, 4, "lloyd_nc", 2, "lloyd"),
+                                           (256, 8, "lloyd_nc", 4, "uniform"), (256, 2, "lloyd_qjl", 4, "lloyd")])
+def test_layout_matches_format(d, kb, km, vb, vm):
+    lay = tq.layout_for_config(tq.make_config(d, 8, 32, kb, km, vb, vm)).as_dict()
+    f = O.page_fields(O.Config(d, 8, 32, kb, km, vb, vm))
     none = (1 << 64) - 1
     assert lay["format_version"] == O.FORMAT_VERSION
-    assert lay["page_bytes"] == O.page_bytes(O.Config(128, 8, 32, kb, km, vb, vm))
+    assert lay["page_bytes"] == O.page_bytes(O.Config(d, 8, 32, kb, km, vb, vm))
     assert lay["token_head_bytes"] * 16 == lay["page_bytes"]
     assert (lay["off_kcodes"], lay["row_kcodes"]) == f["kcodes"]
     assert lay["off_knorm"] == (f["knorm"][0] if km != "fp8" else none)
