@@ -11,6 +11,7 @@ bit-exact, attention outputs within 1e-5 relative per (sequence, q head) vector
 (the decode's waves take tiles in arrival order, so the fp32 sums may round
 differently from launch to launch).
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -23,6 +24,11 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 GRAPH_TOL = 1e-5
+# generic-path configurations (head_dim 256; 8 query heads per KV head)
+GENERIC = {
+    "gqa_decode@d256": dataclasses.replace(synth.WORKLOADS["gqa_decode"], head_dim=256),
+    "qjl@group8": dataclasses.replace(synth.WORKLOADS["qjl"], num_kv_heads=2, num_q_heads=16),
+}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -33,10 +39,10 @@ def _cuda():
 
 
 @pytest.mark.parametrize("name,fused", [("gqa_decode", True), ("qjl", True), ("turbo8v3", True), ("polar3", True),
-                                        ("polar3", False)])
+                                        ("polar3", False), ("gqa_decode@d256", True), ("qjl@group8", True)])
 def test_graph_replays_match_eager(name, fused):
     from kv_cache_vector_randomized_amd.torch_api import PagedKVCache
-    w = synth.WORKLOADS[name]
+    w = GENERIC.get(name) or synth.WORKLOADS[name]
     print(f"[graph] {name} ({'one launch' if fused else 'append, then decode'})", flush=True)
     lens = np.array([300, 97, 16, 1], np.int64)
     B, T = len(lens), int(lens.max())

@@ -10,6 +10,7 @@ checks, in its order.
   remapped) equals decode over the original cache, and both match the oracle;
 * timing: t_copy ~ t0 + B / beta fitted over transfer sizes (printed).
 """
+import dataclasses
 import math
 import time
 
@@ -79,8 +80,9 @@ def test_round_trip_bytes_and_sentinels():
 
 def test_decode_through_host_equals_decode_in_hbm():
     from kv_cache_vector_randomized_amd.torch_api import PagedKVCache
-    for name in ("gqa_decode", "qjl"):
-        w = synth.WORKLOADS[name]
+    generic = dataclasses.replace(synth.WORKLOADS["qjl"], head_dim=64)      # the generic path
+    for name in ("gqa_decode", "qjl", "qjl@d64"):
+        w = generic if name == "qjl@d64" else synth.WORKLOADS[name]
         lens = [300, 77, 16]
         ctx, lay, cache = _filled_cache(w, lens, 53)
         used = np.unique(lay.block_tables[lay.block_tables >= 0]).astype(np.int32)
