@@ -80,17 +80,46 @@ __device__ __forceinline__ void gen_fwht(T (&x)[M], int lane) {
 }
 
 // This lane's coordinates of row `row` of a [rows][d] activation array (bf16 or fp32).
+// (one vector load per lane when the array is 16-byte aligned -- M bf16 values
+// are 2, 4 or 8 bytes, M fp32 values 4, 8 or 16 and rows are whole multiples of
+// 16 bytes -- else one load per value)
 template <int M>
 __device__ __forceinline__ void gen_load(const void* base, int64_t row, bool bf16, int lane, float (&x)[M]) {
   constexpr int D = 64 * M;
+  const bool vec = ((uintptr_t)base & 15u) == 0;
   if (bf16) {
     const uint16_t* p = static_cast<const uint16_t*>(base) + row * D + lane * M;
+    if (vec && M > 1) {
+      uint32_t w[(M + 1) / 2];
+      if constexpr (M == 2) {
+        w[0] = *reinterpret_cast<const uint32_t*>(p);
+      } else if constexpr (M == 4) {
+        const uint2 u = *reinterpret_cast<const uint2*>(p);
+        w[0] = u.x;
+        w[1] = u.y;
+      }
 #pragma unroll
-    for (int i = 0; i < M; ++i) x[i] = __uint_as_float((uint32_t)p[i] << 16);
+      for (int i = 0; i < M; ++i) x[i] = __uint_as_float(i & 1 ? w[i / 2] & 0xffff0000u : w[i / 2] << 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < M; ++i) x[i] = __uint_as_float((uint32_t)p[i] << 16);
+    }
   } else {
     const float* p = static_cast<const float*>(base) + row * D + lane * M;
+    if (vec && M == 4) {
+      const float4 u = *reinterpret_cast<const float4*>(p);
+      x[0] = u.x;
+      x[1] = u.y;
+      x[2] = u.z;
+      x[3] = u.w;
+    } else if (vec && M == 2) {
+      const float2 u = *reinterpret_cast<const float2*>(p);
+      x[0] = u.x;
+      x[1] = u.y;
+    } else {
 #pragma unroll
-    for (int i = 0; i < M; ++i) x[i] = p[i];
+      for (int i = 0; i < M; ++i) x[i] = p[i];
+    }
   }
 }
 
@@ -213,19 +242,21 @@ __global__ __launch_bounds__(64 * kGenWaves) void gen_append_kernel(GenAppendArg
       }
       rr = gw_sum64(rr);
       gen_wave_sync();   // the residual is in LDS, the key bytes are read
-      // rows lane*M + i of S r: 16 rows of S^T requested before they are used
+      // rows lane*M + i of S r
       double pr[M];
 #pragma unroll
       for (int i = 0; i < M; ++i) pr[i] = 0.0;
-      for (int k0 = 0; k0 < D; k0 += 16) {
-        float sv[16][M];
+#pragma unroll 1
+      for (int k0 = 0; k0 < D; k0 += 32 / M) {
+        constexpr int SR = 32 / M;   // rows of S^T per batch, requested before they are used
+        float sv[SR][M];
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
+        for (int u = 0; u < SR; ++u)
 #pragma unroll
           for (int i = 0; i < M; ++i) sv[u][i] = a.St[(k0 + u) * D + lane * M + i];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
+        for (int u = 0; u < SR; ++u) {
           const double rk = s_r[wave][k0 + u];
 #pragma unroll
           for (int i = 0; i < M; ++i) pr[i] = fma((double)sv[u][i], rk, pr[i]);
@@ -271,12 +302,12 @@ __global__ __launch_bounds__(64 * kGenWaves) void gen_append_kernel(GenAppendArg
         vs = fma((double)vf[i], (double)vf[i], vs);
         zv[i] = (double)vf[i] * (double)sg[i];
       }
-      const double vn = sqrt(gw_sum64(vs));
+      const double vnorm = sqrt(gw_sum64(vs));
       gen_fwht<M, double>(zv, lane);
-      const double ivu = vn > 0.0 ? isd / vn : 0.0;
+      const double ivu = vnorm > 0.0 ? isd / vnorm : 0.0;
 #pragma unroll
       for (int i = 0; i < M; ++i) s_codes[wave][lane * M + i] = (uint8_t)gen_code(s_vt, a.val_bits, zv[i] * ivu);
-      if (lane == 0) reinterpret_cast<float*>(page + a.f.vmin)[so] = (float)vn;
+      if (lane == 0) reinterpret_cast<float*>(page + a.f.vmin)[so] = (float)vnorm;
     }
     gen_wave_sync();
     for (int p = lane; p < (int)a.rows.vcodes; p += 64)
@@ -290,23 +321,53 @@ __global__ __launch_bounds__(64 * kGenWaves) void gen_append_kernel(GenAppendArg
 // [split * chunk, (split + 1) * chunk) of the sequence, wave w the 64-token blocks
 // w, w + 4, ...  Logits are base 2: the query rows are rotated and scaled by
 // softmax_scale * log2(e) / sqrt(d), so logit_2 = norm * <q'', C[code]> (+ rho *
-// <coef S q'', 2 sigma - 1> for QJL keys).  Each wave keeps a running max, sum and
-// weighted value sum per head; the work-group's four are merged through LDS and
-// stored as the split's partial (max, sum, d sums) per head.
-template <int D>
-__global__ __launch_bounds__(64 * kGenWaves) void gen_decode_kernel(GenDecodeArgs a) {
+// <coef S q'', 2 sigma - 1> for QJL keys).  A lane takes one token of the block:
+// its code row (KB bits per code, whole words) in registers, 32 centroids at a
+// time, every head's dot product against the query rows in LDS.  The block's value
+// planes (4 pages) and value scalars are staged in LDS, and every lane adds the 64
+// weighted value rows for its M coordinates.  Each wave keeps a running max, sum
+// and weighted value sum per head; the work-group's four are merged through LDS
+// and stored as the split's partial (max, sum, d sums) per head.
+// Dynamic LDS of the decode work-group, sized for the group and value width at
+// launch: the query rows, their QJL projections, the softmax weights of each
+// wave's block, the wave partials, the staged value planes and value scalars.
+struct GenDecodeLds {
+  int q, p, w, part, v, vs, bytes;
+};
+__host__ __device__ inline GenDecodeLds gen_decode_lds(int d, int group, bool qjl, int vrow) {
+  GenDecodeLds L;
+  L.q = 0;
+  L.p = L.q + 4 * group * d;
+  L.w = L.p + (qjl ? 4 * group * d : 0);
+  L.part = L.w + 4 * kGenWaves * group * 64;
+  L.v = L.part + 4 * kGenWaves * (2 + d);
+  L.v = (L.v + 15) & ~15;
+  L.vs = L.v + kGenWaves * 4 * 16 * vrow;
+  L.bytes = L.vs + 4 * kGenWaves * 2 * 64;
+  return L;
+}
+
+template <int D, int KB, int GM>
+__global__ __launch_bounds__(64 * kGenWaves) __attribute__((amdgpu_waves_per_eu(GM <= 4 ? 3 : 2)))
+void gen_decode_kernel(GenDecodeArgs a) {
   constexpr int M = D / 64;
-  constexpr int GM = kGenMaxGroup;
+  constexpr int NW = KB * D / 32;        // words of a key code row
+  constexpr int NS = D / 32;             // words of a sign row
   constexpr float isd = (float)inv_sqrt_dim<D>();
-  __shared__ float s_q[GM][D];
-  __shared__ float s_p[GM][D];
+  extern __shared__ __align__(16) unsigned char gsm[];
   __shared__ float s_kc[256], s_vc[16];
-  __shared__ float s_w[kGenWaves][GM][64];
-  __shared__ float s_part[kGenWaves][2 + D];
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.group;
   const int hq = a.hkv * G;
+  const int vrow = (int)a.rows.vcodes;
+  const GenDecodeLds L = gen_decode_lds(D, G, a.key_mode == 2, vrow);
+  float* s_q = reinterpret_cast<float*>(gsm + L.q);                      // [G][D]
+  float* s_p = reinterpret_cast<float*>(gsm + L.p);                      // [G][D] (QJL)
+  float* s_w = reinterpret_cast<float*>(gsm + L.w) + wave * G * 64;      // this wave's [G][64]
+  float* s_part = reinterpret_cast<float*>(gsm + L.part);                // [waves][2 + D]
+  uint8_t* s_v = gsm + L.v + wave * 4 * 16 * vrow;                       // this wave's [4][16 * vrow]
+  float* s_vs = reinterpret_cast<float*>(gsm + L.vs) + wave * 2 * 64;    // this wave's [2][64]
   for (int i = tid; i < 256; i += 64 * kGenWaves) s_kc[i] = a.c->kc[i];
   if (tid < 16) s_vc[tid] = a.c->vc[tid];
   for (int h = wave; h < G; h += kGenWaves) {
@@ -317,7 +378,7 @@ __global__ __launch_bounds__(64 * kGenWaves) void gen_decode_kernel(GenDecodeArg
     gen_fwht<M, float>(x, lane);
     const float f = a.scale * isd * kGenLog2e;
 #pragma unroll
-    for (int i = 0; i < M; ++i) s_q[h][lane * M + i] = x[i] * f;
+    for (int i = 0; i < M; ++i) s_q[h * D + lane * M + i] = x[i] * f;
   }
   __syncthreads();
   const bool qjl = a.key_mode == 2;
@@ -326,22 +387,24 @@ __global__ __launch_bounds__(64 * kGenWaves) void gen_decode_kernel(GenDecodeArg
       float acc[M];
 #pragma unroll
       for (int i = 0; i < M; ++i) acc[i] = 0.f;
-      for (int k0 = 0; k0 < D; k0 += 16) {
-        float sv[16][M];
+#pragma unroll 1
+      for (int k0 = 0; k0 < D; k0 += 32 / M) {
+        constexpr int SR = 32 / M;   // rows of S^T per batch, requested before they are used
+        float sv[SR][M];
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
+        for (int u = 0; u < SR; ++u)
 #pragma unroll
           for (int i = 0; i < M; ++i) sv[u][i] = a.St[(k0 + u) * D + lane * M + i];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const float qk = s_q[h][k0 + u];
+        for (int u = 0; u < SR; ++u) {
+          const float qk = s_q[h * D + k0 + u];
 #pragma unroll
           for (int i = 0; i < M; ++i) acc[i] = fmaf(sv[u][i], qk, acc[i]);
         }
       }
 #pragma unroll
-      for (int i = 0; i < M; ++i) s_p[h][lane * M + i] = acc[i] * a.qjl_coef;
+      for (int i = 0; i < M; ++i) s_p[h * D + lane * M + i] = acc[i] * a.qjl_coef;
     }
     __syncthreads();
   }
@@ -367,43 +430,109 @@ __global__ __launch_bounds__(64 * kGenWaves) void gen_decode_kernel(GenDecodeArg
     if (t < t1) blk = a.block_tables[(int64_t)b * a.max_blocks + t / 16];
     const bool valid = t < t1 && blk >= 0 && blk < a.num_blocks;
     const int so = t & 15;
+    const uint8_t* page = a.cache + ((int64_t)(valid ? blk : 0) * a.hkv + kvh) * pstride;
     float lg[GM];
 #pragma unroll
     for (int h = 0; h < GM; ++h) lg[h] = -INFINITY;
+    float vs0 = 0.f, vs1 = 0.f;
     if (valid) {
-      const uint8_t* page = a.cache + ((int64_t)blk * a.hkv + kvh) * pstride;
       const float norm = reinterpret_cast<const float*>(page + a.f.knorm)[so];
-      const uint8_t* krow = page + a.f.kcodes + so * a.rows.kcodes;
+      uint32_t w[NW];
+      const uint2* kr = reinterpret_cast<const uint2*>(page + a.f.kcodes + so * (4 * NW));
+#pragma unroll
+      for (int j = 0; j < NW / 2; ++j) {
+        const uint2 u2 = kr[j];
+        w[2 * j] = u2.x;
+        w[2 * j + 1] = u2.y;
+      }
       float dot[GM];
 #pragma unroll
       for (int h = 0; h < GM; ++h) dot[h] = 0.f;
-      for (int i = 0; i < D; ++i) {
-        const float c = s_kc[gen_read_code(krow, 1, a.key_bits, i)];
 #pragma unroll
-        for (int h = 0; h < GM; ++h)
-          if (h < G) dot[h] = fmaf(s_q[h][i], c, dot[h]);
+      for (int c0 = 0; c0 < D; c0 += 32) {
+        float cv[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) cv[j] = s_kc[get_code<KB>(w, c0 + j)];
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+          if (h < G) {
+            float acc = dot[h];
+#pragma unroll
+            for (int j = 0; j < 32; j += 4) {
+              const float4 qv = *reinterpret_cast<const float4*>(&s_q[h * D + c0 + j]);
+              acc = fmaf(qv.x, cv[j], acc);
+              acc = fmaf(qv.y, cv[j + 1], acc);
+              acc = fmaf(qv.z, cv[j + 2], acc);
+              acc = fmaf(qv.w, cv[j + 3], acc);
+            }
+            dot[h] = acc;
+          }
+        }
       }
 #pragma unroll
       for (int h = 0; h < GM; ++h) lg[h] = norm * dot[h];
       if (qjl) {
         const float rho = reinterpret_cast<const float*>(page + a.f.kres)[so];
-        const uint8_t* srow = page + a.f.ksigns + so * a.rows.ksigns;
+        uint32_t sw[NS];
+        const uint2* sr = reinterpret_cast<const uint2*>(page + a.f.ksigns + so * (4 * NS));
+#pragma unroll
+        for (int j = 0; j < NS / 2; ++j) {
+          const uint2 u2 = sr[j];
+          sw[2 * j] = u2.x;
+          sw[2 * j + 1] = u2.y;
+        }
         float cs[GM];
 #pragma unroll
         for (int h = 0; h < GM; ++h) cs[h] = 0.f;
-        for (int j = 0; j < D; ++j) {
-          const float sgn = ((srow[j >> 3] >> (j & 7)) & 1u) ? 1.f : -1.f;
 #pragma unroll
-          for (int h = 0; h < GM; ++h)
-            if (h < G) cs[h] = fmaf(sgn, s_p[h][j], cs[h]);
+        for (int c0 = 0; c0 < D; c0 += 32) {
+          const uint32_t bits = sw[c0 / 32];
+#pragma unroll
+          for (int h = 0; h < GM; ++h) {
+            if (h < G) {
+              float acc = cs[h];
+#pragma unroll
+              for (int j = 0; j < 32; j += 4) {
+                const float4 pv = *reinterpret_cast<const float4*>(&s_p[h * D + c0 + j]);
+                acc += ((bits >> j) & 1u) ? pv.x : -pv.x;
+                acc += ((bits >> (j + 1)) & 1u) ? pv.y : -pv.y;
+                acc += ((bits >> (j + 2)) & 1u) ? pv.z : -pv.z;
+                acc += ((bits >> (j + 3)) & 1u) ? pv.w : -pv.w;
+              }
+              cs[h] = acc;
+            }
+          }
         }
 #pragma unroll
-        for (int h = 0; h < GM; ++h) lg[h] = fmaf(norm, dot[h], rho * cs[h]);
+        for (int h = 0; h < GM; ++h) lg[h] = fmaf(rho, cs[h], lg[h]);
       }
       if (a.logits != nullptr) {
 #pragma unroll
         for (int h = 0; h < GM; ++h)
           if (h < G) a.logits[((int64_t)b * hq + (int64_t)kvh * G + h) * a.max_seq + t] = lg[h] * kGenLn2;
+      }
+      vs0 = reinterpret_cast<const float*>(page + a.f.vmin)[so];
+      if (a.val_mode == 0) vs1 = reinterpret_cast<const float*>(page + a.f.vscale)[so];
+    }
+    s_vs[lane] = vs0;
+    s_vs[64 + lane] = vs1;
+    // the value planes of the block's four pages (page pg holds tokens tb + 16 pg ..
+    // tb + 16 pg + 15, one block id; a page with no valid token is not read)
+    const uint64_t vmask = __ballot(valid);
+    int bpg[4];
+    bool pvld[4];
+#pragma unroll
+    for (int pg = 0; pg < 4; ++pg) {
+      bpg[pg] = __shfl(blk, 16 * pg);
+      pvld[pg] = ((vmask >> (16 * pg)) & 0xFFFFull) != 0;
+    }
+    for (int e = lane; e < 4 * vrow; e += 64) {
+      const int pg = e / vrow, q = e - pg * vrow;
+      const int bb = pg == 0 ? bpg[0] : pg == 1 ? bpg[1] : pg == 2 ? bpg[2] : bpg[3];
+      const bool ok = pg == 0 ? pvld[0] : pg == 1 ? pvld[1] : pg == 2 ? pvld[2] : pvld[3];
+      if (ok) {
+        const uint4* src = reinterpret_cast<const uint4*>(a.cache + ((int64_t)bb * a.hkv + kvh) * pstride + a.f.vcodes);
+        *reinterpret_cast<uint4*>(&s_v[(pg * vrow + q) * 16]) = src[q];
       }
     }
     // online softmax of each head over the block's 64 tokens
@@ -420,39 +549,34 @@ __global__ __launch_bounds__(64 * kGenWaves) void gen_decode_kernel(GenDecodeArg
           for (int i = 0; i < M; ++i) o[h][i] *= al;
           m_run[h] = mnew;
         }
-        s_w[wave][h][lane] = p;
+        s_w[h * 64 + lane] = p;
       }
     }
     gen_wave_sync();
     // values of the block's tokens: lane l adds coordinates l*M .. l*M + M - 1
     for (int u = 0; u < 64; ++u) {
-      if (__shfl(valid ? 1 : 0, u) == 0) continue;   // uniform
-      const int bu = __shfl(blk, u);
-      const int su = (tb + u) & 15;
-      const uint8_t* pg = a.cache + ((int64_t)bu * a.hkv + kvh) * pstride;
-      const uint8_t* vrow = pg + a.f.vcodes + su;
+      if (((vmask >> u) & 1ull) == 0) continue;   // uniform
+      const uint8_t* vr = &s_v[(u >> 4) * 16 * vrow + (u & 15)];
+      const float v0 = s_vs[u], v1 = s_vs[64 + u];
       float vh[M];
       if (a.val_mode == 0) {
-        const float mn = reinterpret_cast<const float*>(pg + a.f.vmin)[su];
-        const float sc = reinterpret_cast<const float*>(pg + a.f.vscale)[su];
 #pragma unroll
-        for (int i = 0; i < M; ++i) vh[i] = fmaf(sc, (float)gen_read_code(vrow, 16, a.val_bits, lane * M + i), mn);
+        for (int i = 0; i < M; ++i) vh[i] = fmaf(v1, (float)gen_read_code(vr, 16, a.val_bits, lane * M + i), v0);
       } else {
         // Lloyd-Max values are summed in the rotated basis (rotated back after the merge)
-        const float vn = reinterpret_cast<const float*>(pg + a.f.vmin)[su];
 #pragma unroll
-        for (int i = 0; i < M; ++i) vh[i] = vn * s_vc[gen_read_code(vrow, 16, a.val_bits, lane * M + i)];
+        for (int i = 0; i < M; ++i) vh[i] = v0 * s_vc[gen_read_code(vr, 16, a.val_bits, lane * M + i)];
       }
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
         if (h < G) {
-          const float w = s_w[wave][h][u];
+          const float wt = s_w[h * 64 + u];
 #pragma unroll
-          for (int i = 0; i < M; ++i) o[h][i] = fmaf(w, vh[i], o[h][i]);
+          for (int i = 0; i < M; ++i) o[h][i] = fmaf(wt, vh[i], o[h][i]);
         }
       }
     }
-    gen_wave_sync();   // s_w is rewritten by the next block
+    gen_wave_sync();   // s_w, s_v and s_vs are rewritten by the next block
   }
 
   // merge the four waves, head by head, into the split's partial
@@ -460,31 +584,31 @@ __global__ __launch_bounds__(64 * kGenWaves) void gen_decode_kernel(GenDecodeArg
   for (int h = 0; h < GM; ++h) {
     if (h >= G) continue;   // uniform over the work-group
     if (lane == 0) {
-      s_part[wave][0] = m_run[h];
-      s_part[wave][1] = l_run[h];
+      s_part[wave * (2 + D)] = m_run[h];
+      s_part[wave * (2 + D) + 1] = l_run[h];
     }
 #pragma unroll
-    for (int i = 0; i < M; ++i) s_part[wave][2 + lane * M + i] = o[h][i];
+    for (int i = 0; i < M; ++i) s_part[wave * (2 + D) + 2 + lane * M + i] = o[h][i];
     __syncthreads();
     if (wave == 0) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kGenWaves; ++w) mx = fmaxf(mx, s_part[w][0]);
-      float L = 0.f, O[M];
+      for (int w = 0; w < kGenWaves; ++w) mx = fmaxf(mx, s_part[w * (2 + D)]);
+      float Ls = 0.f, O[M];
 #pragma unroll
       for (int i = 0; i < M; ++i) O[i] = 0.f;
 #pragma unroll
       for (int w = 0; w < kGenWaves; ++w) {
-        const float mw = s_part[w][0];
-        const float f = mw == -INFINITY ? 0.f : exp2f(mw - mx);
-        L = fmaf(f, s_part[w][1], L);
+        const float* pw = s_part + w * (2 + D);
+        const float f = pw[0] == -INFINITY ? 0.f : exp2f(pw[0] - mx);
+        Ls = fmaf(f, pw[1], Ls);
 #pragma unroll
-        for (int i = 0; i < M; ++i) O[i] = fmaf(f, s_part[w][2 + lane * M + i], O[i]);
+        for (int i = 0; i < M; ++i) O[i] = fmaf(f, pw[2 + lane * M + i], O[i]);
       }
       float* dst = a.ws + ((((int64_t)b * a.hkv + kvh) * a.splits + split) * G + h) * (2 + D);
       if (lane == 0) {
         dst[0] = mx;
-        dst[1] = L;
+        dst[1] = Ls;
       }
 #pragma unroll
       for (int i = 0; i < M; ++i) dst[2 + lane * M + i] = O[i];
@@ -615,25 +739,37 @@ hipError_t launch_gen_append(const GenAppendArgs& a, int d, int grid, hipStream_
   return hipGetLastError();
 }
 
-hipError_t launch_gen_decode(const GenDecodeArgs& a, int d, hipStream_t s) {
+template <int D, int GM>
+hipError_t gen_decode_dg(const GenDecodeArgs& a, hipStream_t s) {
   const dim3 g((unsigned)a.splits, (unsigned)a.hkv, (unsigned)a.batch);
-  const dim3 gm((unsigned)(a.hkv * a.group), (unsigned)a.batch);
-  switch (d) {
-    case 64:
-      hipLaunchKernelGGL(gen_decode_kernel<64>, g, dim3(64 * kGenWaves), 0, s, a);
-      hipLaunchKernelGGL(gen_merge_kernel<64>, gm, dim3(64), 0, s, a);
-      break;
-    case 128:
-      hipLaunchKernelGGL(gen_decode_kernel<128>, g, dim3(64 * kGenWaves), 0, s, a);
-      hipLaunchKernelGGL(gen_merge_kernel<128>, gm, dim3(64), 0, s, a);
-      break;
-    case 256:
-      hipLaunchKernelGGL(gen_decode_kernel<256>, g, dim3(64 * kGenWaves), 0, s, a);
-      hipLaunchKernelGGL(gen_merge_kernel<256>, gm, dim3(64), 0, s, a);
-      break;
+  const size_t lds = (size_t)gen_decode_lds(D, a.group, a.key_mode == 2, (int)a.rows.vcodes).bytes;
+  switch (a.key_bits) {
+    case 2: hipLaunchKernelGGL((gen_decode_kernel<D, 2, GM>), g, dim3(64 * kGenWaves), lds, s, a); break;
+    case 3: hipLaunchKernelGGL((gen_decode_kernel<D, 3, GM>), g, dim3(64 * kGenWaves), lds, s, a); break;
+    case 4: hipLaunchKernelGGL((gen_decode_kernel<D, 4, GM>), g, dim3(64 * kGenWaves), lds, s, a); break;
+    case 8: hipLaunchKernelGGL((gen_decode_kernel<D, 8, GM>), g, dim3(64 * kGenWaves), lds, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t gen_decode_d(const GenDecodeArgs& a, hipStream_t s) {
+  // register arrays sized for up to 4 or up to 16 query heads per KV head
+  const hipError_t e = a.group <= 4 ? gen_decode_dg<D, 4>(a, s) : gen_decode_dg<D, kGenMaxGroup>(a, s);
+  if (e != hipSuccess) return e;
+  const dim3 gm((unsigned)(a.hkv * a.group), (unsigned)a.batch);
+  hipLaunchKernelGGL(gen_merge_kernel<D>, gm, dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gen_decode(const GenDecodeArgs& a, int d, hipStream_t s) {
+  switch (d) {
+    case 64: return gen_decode_d<64>(a, s);
+    case 128: return gen_decode_d<128>(a, s);
+    case 256: return gen_decode_d<256>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_gen_dequant(const GenDequantArgs& a, int d, int grid, hipStream_t s) {
