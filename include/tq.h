@@ -63,8 +63,9 @@
  *   one-wave-per-vector append and dequantize kernels and a two-launch decode
  *   (per split, then the merge); its one-launch step is three launches (the new
  *   tokens, the decode, the merge).  The generic path takes Lloyd-Max keys (2, 3,
- *   4 or 8 bits; QJL with 2, 3 or 4) and both value modes; FP8 and PolarQuant
- *   keys need head_dim 128 with 1, 2 or 4 query heads per KV head.
+ *   4 or 8 bits; QJL with 2, 3 or 4), FP8 keys and both value modes; PolarQuant
+ *   keys need head_dim 128 with 1, 2 or 4 query heads per KV head (their code
+ *   order is laid out for 128 coordinates).
  */
 #ifndef TQ_H
 #define TQ_H

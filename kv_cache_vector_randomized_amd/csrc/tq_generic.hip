@@ -160,7 +160,8 @@ __device__ __forceinline__ void gen_wave_sync() {
 }
 
 // ---------------------------------------------------------------------------
-// Quantize-append: one wave per (token, KV head).  Keys: ||k|| and the rotation in
+// Quantize-append: one wave per (token, KV head).  FP8 keys: the E4M3 byte of each
+// coordinate.  Lloyd-Max keys: ||k|| and the rotation in
 // fp64 (the squares of fp32 or bf16 values are exact there), codes of the unit
 // coordinate, the stored norm (plain or corrected) rounded once to fp32, and for
 // QJL keys the residual r = y - norm * C[code] in the rotated frame, its norm and
@@ -208,6 +209,12 @@ __global__ __launch_bounds__(64 * kGenWaves) void gen_append_kernel(GenAppendArg
     // ---- keys
     float kf[M];
     gen_load<M>(a.k, vi, a.bf16 != 0, lane, kf);
+    if (a.key_mode == 3) {
+      // FP8 keys: the E4M3 byte of every coordinate, coordinate i at byte i; no norm
+      uint8_t* krow = page + a.f.kcodes + so * a.rows.kcodes + lane * M;
+#pragma unroll
+      for (int i = 0; i < M; ++i) krow[i] = (uint8_t)fp8_e4m3(kf[i]);
+    } else {
     double z[M], ss = 0.0;
 #pragma unroll
     for (int i = 0; i < M; ++i) {
@@ -268,6 +275,7 @@ __global__ __launch_bounds__(64 * kGenWaves) void gen_append_kernel(GenAppendArg
       for (int p = lane; p < (int)a.rows.ksigns; p += 64)
         page[a.f.ksigns + so * a.rows.ksigns + p] = (uint8_t)gen_stream_byte(s_codes[wave], D, 1, p);
       if (lane == 0) reinterpret_cast<float*>(page + a.f.kres)[so] = (float)sqrt(rr);
+    }
     }
     gen_wave_sync();   // every read of s_codes is done before the values overwrite it
 
@@ -373,10 +381,14 @@ void gen_decode_kernel(GenDecodeArgs a) {
   for (int h = wave; h < G; h += kGenWaves) {
     float x[M];
     gen_load<M>(a.q, (int64_t)b * hq + (int64_t)kvh * G + h, a.q_bf16 != 0, lane, x);
+    // FP8 keys are stored unrotated: their query rows are only scaled
+    const bool rot = a.key_mode != 3;
+    if (rot) {
 #pragma unroll
-    for (int i = 0; i < M; ++i) x[i] *= a.c->signs[lane * M + i];
-    gen_fwht<M, float>(x, lane);
-    const float f = a.scale * isd * kGenLog2e;
+      for (int i = 0; i < M; ++i) x[i] *= a.c->signs[lane * M + i];
+      gen_fwht<M, float>(x, lane);
+    }
+    const float f = a.scale * (rot ? isd : 1.f) * kGenLog2e;
 #pragma unroll
     for (int i = 0; i < M; ++i) s_q[h * D + lane * M + i] = x[i] * f;
   }
@@ -436,7 +448,7 @@ void gen_decode_kernel(GenDecodeArgs a) {
     for (int h = 0; h < GM; ++h) lg[h] = -INFINITY;
     float vs0 = 0.f, vs1 = 0.f;
     if (valid) {
-      const float norm = reinterpret_cast<const float*>(page + a.f.knorm)[so];
+      const float norm = a.key_mode == 3 ? 1.f : reinterpret_cast<const float*>(page + a.f.knorm)[so];   // FP8: no norm
       uint32_t w[NW];
       const uint2* kr = reinterpret_cast<const uint2*>(page + a.f.kcodes + so * (4 * NW));
 #pragma unroll
@@ -681,13 +693,15 @@ __global__ __launch_bounds__(64 * kGenWaves) void gen_dequant_kernel(GenDequantA
     if (slot >= 0 && slot < a.num_blocks * 16) {
       const uint8_t* page = a.cache + ((slot >> 4) * a.hkv + h) * (int64_t)a.f.page_bytes;
       const int so = (int)(slot & 15);
-      const float norm = reinterpret_cast<const float*>(page + a.f.knorm)[so];
       const uint8_t* krow = page + a.f.kcodes + so * a.rows_b.kcodes;
 #pragma unroll
       for (int i = 0; i < M; ++i) kx[i] = a.c->kc[gen_read_code(krow, 1, a.key_bits, lane * M + i)];
-      gen_fwht<M, float>(kx, lane);
+      if (a.key_mode != 3) {   // FP8 keys: the E4M3 values themselves
+        const float norm = reinterpret_cast<const float*>(page + a.f.knorm)[so];
+        gen_fwht<M, float>(kx, lane);
 #pragma unroll
-      for (int i = 0; i < M; ++i) kx[i] *= sg[i] * isd * norm;
+        for (int i = 0; i < M; ++i) kx[i] *= sg[i] * isd * norm;
+      }
       const uint8_t* vrow = page + a.f.vcodes + so;
       if (a.val_mode == 0) {
         const float mn = reinterpret_cast<const float*>(page + a.f.vmin)[so];

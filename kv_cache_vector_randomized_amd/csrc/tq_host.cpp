@@ -312,7 +312,17 @@ tq_status create_generic(const tq_config* cfg, const int8_t* signs_host, const f
   tq::GenConsts h;
   std::memset(&h, 0, sizeof h);
   for (int i = 0; i < d; ++i) h.signs[i] = (float)signs_host[i];
-  codebook_f32((int)cfg->key_bits, d, h.kc, h.kt);
+  if (cfg->key_mode == TQ_KEY_FP8) {
+    // the value of every E4M3 byte (sign, 4 exponent bits with bias 7, 3 mantissa bits;
+    // exponent 0 holds m * 2^-9; S.1111.111 is NaN and never written)
+    for (int code = 0; code < 256; ++code) {
+      const int e = (code >> 3) & 15, m = code & 7;
+      const double mag = e == 0 ? m * std::ldexp(1.0, -9) : (1.0 + m / 8.0) * std::ldexp(1.0, e - 7);
+      h.kc[code] = (code & 0x7F) == 0x7F ? std::numeric_limits<float>::quiet_NaN() : (float)((code & 0x80) ? -mag : mag);
+    }
+  } else {
+    codebook_f32((int)cfg->key_bits, d, h.kc, h.kt);
+  }
   if (cfg->val_mode == TQ_VAL_LLOYD) codebook_f32((int)cfg->val_bits, d, h.vc, h.vt);
   std::vector<float> st;
   if (cfg->key_mode == TQ_KEY_LLOYD_QJL) {
@@ -367,8 +377,9 @@ tq::GenRows gen_rows(const tq_layout& L) {
   return r;
 }
 
+// generic kernels' key mode: 0 plain Lloyd-Max, 1 corrected norm, 2 QJL, 3 FP8
 int gen_key_mode(const tq_config& c) {
-  return c.key_mode == TQ_KEY_LLOYD_NC ? 1 : c.key_mode == TQ_KEY_LLOYD_QJL ? 2 : 0;
+  return c.key_mode == TQ_KEY_LLOYD_NC ? 1 : c.key_mode == TQ_KEY_LLOYD_QJL ? 2 : c.key_mode == TQ_KEY_FP8 ? 3 : 0;
 }
 
 }  // namespace
@@ -409,9 +420,8 @@ tq_status tq_validate_config(const tq_config* c) {
   const uint32_t g = c->num_q_heads / c->num_kv_heads;
   if (g > (uint32_t)tq::kGenMaxGroup)
     return fail(TQ_ERR_UNSUPPORTED, "group size %u: supported 1..%d", g, tq::kGenMaxGroup);
-  if (is_generic(c) && (c->key_mode == TQ_KEY_FP8 || c->key_mode == TQ_KEY_POLAR))
-    return fail(TQ_ERR_UNSUPPORTED, "FP8 and PolarQuant keys are built for head_dim 128 with 1, 2 or 4 query heads "
-                "per KV head");
+  if (is_generic(c) && c->key_mode == TQ_KEY_POLAR)
+    return fail(TQ_ERR_UNSUPPORTED, "PolarQuant keys are built for head_dim 128 with 1, 2 or 4 query heads per KV head");
   if (c->key_mode == TQ_KEY_FP8) {
     if (c->key_bits != 8) return fail(TQ_ERR_INVALID_ARG, "FP8 keys take key_bits 8 (got %u)", c->key_bits);
     if (c->val_mode != TQ_VAL_UNIFORM) return fail(TQ_ERR_UNSUPPORTED, "FP8 keys are built with uniform values only");

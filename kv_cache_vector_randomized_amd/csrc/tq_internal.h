@@ -179,7 +179,7 @@ struct GenAppendArgs {
   int32_t bf16;              // 1: bf16 inputs, 0: fp32
   int64_t num_tokens;        // rows of k / v (the batch for the one-launch step)
   int32_t hkv;
-  int32_t key_bits, key_mode, val_bits, val_mode;   // key_mode: 0 plain, 1 corrected norm, 2 QJL
+  int32_t key_bits, key_mode, val_bits, val_mode;   // key_mode: 0 plain, 1 corrected norm, 2 QJL, 3 FP8
   const int64_t* slots;      // slot of each token, or null: the new token of each sequence
   const int32_t* block_tables;   // (slots == null) new token b goes to position seq_lens[b] - 1
   int32_t max_blocks;

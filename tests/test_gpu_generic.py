@@ -1,5 +1,5 @@
 """GPU parity of the generic path (head_dim 64 and 256; groups other than 1, 2, 4
-at head_dim 128) against the fp64 oracle, through the C ABI.
+at head_dim 128; Lloyd-Max, QJL and FP8 keys) against the fp64 oracle, through the C ABI.
 
 Same bars as the tuned path: codes and packed bytes bit-exact outside the 1e-6
 decision band, fp32 scalars within their rounding tolerance, logits and outputs
@@ -35,6 +35,8 @@ CASES = {
     "d128_group8": (_w("gqa_decode", num_kv_heads=2, num_q_heads=16), [400, 90]),
     "d64_group3_qjl3": (_w("k3qjl_v2", head_dim=64, num_kv_heads=2, num_q_heads=6), [300, 5]),
     "d128_group16_qjl": (_w("qjl", num_kv_heads=1, num_q_heads=16), [260, 0]),
+    "d64_fp8_v4": (_w("k8v4", head_dim=64), [300, 0, 33]),
+    "d256_fp8_group8": (_w("k8v4", head_dim=256, num_kv_heads=2, num_q_heads=16), [200, 64]),
 }
 
 
@@ -148,7 +150,8 @@ def test_generic_noalloc_equals_workspace_decode(name):
         assert np.array_equal(la[i, :, :n], lb[i, :, :n])
 
 
-@pytest.mark.parametrize("name", ["d64_k4nc_v4", "d256_qjl2_v4", "d256_toy_lloyd_values", "d128_group8"])
+@pytest.mark.parametrize("name", ["d64_k4nc_v4", "d256_qjl2_v4", "d256_toy_lloyd_values", "d128_group8",
+                                  "d256_fp8_group8"])
 def test_generic_one_launch_step_matches_oracle(name):
     """tq_append_decode: the new token of every sequence is stored (bytes as the
     oracle's, outside the band), then attended with the context."""
@@ -194,7 +197,7 @@ def test_generic_one_launch_step_matches_oracle(name):
             H.check_vec("generic one-launch step", name, "out", o[b, h], ref[b, h], (b, h))
 
 
-@pytest.mark.parametrize("name", ["d64_k4nc_v4", "d256_qjl2_v4", "d256_toy_lloyd_values", "d64_k8nc_v3"])
+@pytest.mark.parametrize("name", ["d64_k4nc_v4", "d256_qjl2_v4", "d256_toy_lloyd_values", "d64_k8nc_v3", "d64_fp8_v4"])
 @pytest.mark.parametrize("bf16_out", [False, True])
 def test_generic_dequantize_matches_oracle(name, bf16_out):
     from kv_cache_vector_randomized_amd import tq

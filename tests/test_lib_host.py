@@ -62,9 +62,10 @@ def test_status_strings():
     (dict(head_dim=256, key_bits=2, key_mode="lloyd_qjl", val_mode="lloyd"), tq.TQ_OK),
     (dict(head_dim=32), tq.TQ_ERR_UNSUPPORTED),
     (dict(head_dim=512), tq.TQ_ERR_UNSUPPORTED),
-    (dict(head_dim=64, key_bits=8, key_mode="fp8"), tq.TQ_ERR_UNSUPPORTED),   # FP8 / polar: d 128, groups 1, 2, 4
-    (dict(head_dim=256, key_bits=3, key_mode="polar"), tq.TQ_ERR_UNSUPPORTED),
-    (dict(num_kv_heads=1, num_q_heads=8, key_bits=8, key_mode="fp8"), tq.TQ_ERR_UNSUPPORTED),
+    (dict(head_dim=64, key_bits=8, key_mode="fp8"), tq.TQ_OK),                 # FP8 keys on the generic path
+    (dict(num_kv_heads=1, num_q_heads=8, key_bits=8, key_mode="fp8"), tq.TQ_OK),
+    (dict(head_dim=256, key_bits=3, key_mode="polar"), tq.TQ_ERR_UNSUPPORTED),  # polar: d 128, groups 1, 2, 4
+    (dict(num_kv_heads=1, num_q_heads=8, key_bits=3, key_mode="polar"), tq.TQ_ERR_UNSUPPORTED),
     (dict(key_bits=0), tq.TQ_ERR_INVALID_ARG),
     (dict(key_bits=8), tq.TQ_OK),                    # 8-bit Lloyd-Max keys
     (dict(key_bits=5), tq.TQ_ERR_UNSUPPORTED),
