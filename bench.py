@@ -352,12 +352,13 @@ def main():
     if not args.no_stream_ceilings:
         import ctypes
         sl = ctypes.CDLL(os.path.join(ROOT, "kv_cache_vector_randomized_amd", "libtqstream.so"))
-        for f in (sl.tqs_read, sl.tqs_write, sl.tqs_copy):
+        for f in (sl.tqs_read, sl.tqs_write, sl.tqs_copy, sl.tqs_mix):
             f.restype = ctypes.c_int
         P, SZ, U32, I = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_int
         sl.tqs_read.argtypes = [P, SZ, P, I, P]
         sl.tqs_write.argtypes = [P, SZ, U32, I, P]
         sl.tqs_copy.argtypes = [P, P, SZ, I, P]
+        sl.tqs_mix.argtypes = [P, P, SZ, I, I, P]
         hs = lambda: torch.cuda.current_stream().cuda_stream   # the capturing stream inside a graph capture
         blocks = 2048                          # 8 work-groups of 256 threads per compute unit
         nrot = n_layers
@@ -377,17 +378,37 @@ def main():
                 t_cp = timed(lambda i: sl.tqs_copy(s0 + (i % nrot) * rd, d0 + (i % nrot) * wr, cp, blocks, hs()),
                              0) / args.steps
                 c.update({"copy_GBs": round(2 * cp / (t_cp * 1e-3) / 1e9, 1), "copy_bytes": 2 * cp})
+                # One kernel reading m words for each word it writes (m = ceil(read / write)), the
+                # faster of two grid sizes; its rate applied to this kernel's bytes.
+                m = -(-rd // wr)
+                if m <= 8:
+                    n_out = rd // 16 // m
+                    best = None
+                    for nb in (2048, 8192):
+                        t = timed(lambda i: sl.tqs_mix(s0 + (i % nrot) * rd, d0 + (i % nrot) * wr, rd, m, nb, hs()),
+                                  0) / args.steps
+                        best = t if best is None or t < best else best
+                    mix_bytes = n_out * 16 * (m + 1)
+                    rate = mix_bytes / (best * 1e-3)
+                    c.update({"mixed_GBs": round(rate / 1e9, 1), "mixed_reads_per_write": m,
+                              "mixed_bytes": mix_bytes, "mixed_us": round(best * 1e3, 2),
+                              "mixed_projected_us": round((rd + wr) / rate * 1e6, 2)})
             c.update({"read_then_write_us": round((t_rd + t_wr) * 1e3, 2), "kernel_us": round(kernel_us, 2)})
             del src, dst, sink
             return c
 
         ceilings = streams(*dom_rw, dom_avg * 1e3)
         ceilings["ops"] = ("plain streaming kernels (16-byte nontemporal loads/stores, 2048 work-groups of 256): "
-                           "read the kernel's read bytes, write its write bytes, copy min of the two; each rotated "
-                           "over the layer buffers and graph-replayed back to back")
+                           "read the kernel's read bytes, write its write bytes, copy min of the two; mixed: one "
+                           "kernel with plain 16-byte loads and stores reading m words per word written "
+                           "(m = ceil(read/write)), the faster of 2048 and 8192 work-groups, its rate applied to "
+                           "the kernel's bytes (mixed_projected_us); each rotated over the layer buffers and "
+                           "graph-replayed back to back")
+        mixed = (f"; mixed {ceilings['mixed_reads_per_write']}:1 {ceilings['mixed_GBs']} GB/s, "
+                 f"{ceilings['mixed_projected_us']} us for these bytes") if "mixed_GBs" in ceilings else ""
         log(f"[bench] streams: read {ceilings['read_GBs']} GB/s ({ceilings['read_us']} us), write "
             f"{ceilings['write_GBs']} GB/s ({ceilings['write_us']} us), copy {ceilings['copy_GBs']} GB/s; "
-            f"read then write {ceilings['read_then_write_us']} us (kernel {dom_avg * 1e3:.1f} us)")
+            f"read then write {ceilings['read_then_write_us']} us{mixed} (kernel {dom_avg * 1e3:.1f} us)")
         if roof2 is not None:
             c2 = streams(roof2["algorithmic_bytes_per_launch"], 16, roof2["avg_launch_us"], copy=False)
             roof2["stream_read"] = {k: c2[k] for k in ("read_GBs", "read_bytes", "read_us")}
