@@ -46,9 +46,11 @@ Readings taken where the pages are silent:
       OCP E4M3 of each raw key coordinate (no rotation, no per-token scale),
       nearest value with ties to the even code, magnitudes above 448 saturate.
 
-Parity unpinned (no page fixes them; pinned only to their stated definitions):
-  the norm-correction definition (R5), the value scheme of the toy and QJL
-  workloads, the QJL frame and m (R13), the 3-bit bit order (R12).
+Readings no page fixes (conventions; each function is pinned to mathematics,
+not to a page): the norm-correction definition (R5: the reconstruction keeps
+the key's norm), the toy workload's Lloyd-Max values (the key quantizer's
+pins), the QJL frame and m (R13: unbiased, closed-form variance), the 2- and
+3-bit bit order (R12: exhaustive pack/unpack, the page's 4-bit bytes).
 """
 from __future__ import annotations
 
