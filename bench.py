@@ -38,6 +38,11 @@ Other workloads (--workload):
                   reconstructed into a bf16 buffer (--dequant-f32: fp32) in one
                   tq_dequantize_rows call: the whole-cache reconstruction that
                   incremental dequantization replaces by one token per step.
+  gqa_d64, gqa_d256, gqa_group8
+                  the GQA shape at head_dim 64 and 256, and at head_dim 128 with 2
+                  KV heads of 8 query heads each: the generic path (same step; its
+                  one-launch step is three launches: the new tokens, the decode
+                  per split, the merge).
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.  `value` is packed-KV
 GB/s: algorithmic bytes of the step (bf16 inputs read, packed rows written,
@@ -81,7 +86,19 @@ MODES = {
     "k8v4": ("k8v4", "decode"),
     "turbo8v3": ("turbo8v3", "decode"),
     "polar3": ("polar3", "decode"),
+    "gqa_d64": ("gqa_d64", "decode"),
+    "gqa_d256": ("gqa_d256", "decode"),
+    "gqa_group8": ("gqa_group8", "decode"),
 }
+
+
+def generic_workloads(synth):
+    """Shapes that run on the generic path (head_dim 64 / 256, 8 query heads per KV head)."""
+    import dataclasses
+    g = synth.WORKLOADS["gqa_decode"]
+    return {"gqa_d64": dataclasses.replace(g, name="gqa_d64", head_dim=64),
+            "gqa_d256": dataclasses.replace(g, name="gqa_d256", head_dim=256),
+            "gqa_group8": dataclasses.replace(g, name="gqa_group8", num_kv_heads=2, num_q_heads=16)}
 
 
 def log(*a):
@@ -136,11 +153,12 @@ def main():
         sys.exit(1)
     torch.cuda.init()
     wname, kind = MODES[args.workload]
-    w = synth.WORKLOADS[wname]
+    w = generic_workloads(synth).get(wname) or synth.WORKLOADS[wname]
     B, T, Hkv, Hq, d = w.batch, w.context, w.num_kv_heads, w.num_q_heads, w.head_dim
+    generic = d != 128 or Hq // Hkv not in (1, 2, 4)
     cfg = tq.make_config(d, Hkv, Hq, w.key_bits, w.key_mode, w.val_bits, w.val_mode)
     S = synth.qjl_matrix(d) if w.key_mode == "lloyd_qjl" else None
-    ctx = tq.Context(cfg, synth.sign_vector(w.seed), S)
+    ctx = tq.Context(cfg, synth.sign_vector(w.seed, d), S)
     lay = synth.paged_layout(B, [T] * B, w.seed)
     scale = 1.0 / math.sqrt(d)
     log(f"[bench] workload={args.workload} B={B} T={T} Hkv={Hkv} Hq={Hq} page_bytes={ctx.page_bytes}")
@@ -178,6 +196,8 @@ def main():
         dom_rw = (decode_bytes + append_bytes - B * Hkv * th, B * Hkv * th + B * Hq * d * 4)
         if args.separate:
             dominant, dom_bytes, dom_source = "decode_kernel", decode_bytes, "tq_decode.hip"
+            if generic:
+                dominant, dom_source = "gen_decode_kernel + gen_merge_kernel", "tq_generic.hip"
 
             def step(i, ev=None):
                 c = caches[i % n_layers]
@@ -194,6 +214,9 @@ def main():
             # one launch: the decode kernel also quantizes and stores the new tokens
             # (their slots are those of position T-1 in the block tables)
             dominant, dom_bytes, dom_source = "decode_kernel (fused append)", decode_bytes + append_bytes, "tq_decode.hip"
+            if generic:
+                dominant = "gen_append_kernel + gen_decode_kernel + gen_merge_kernel (one-launch step)"
+                dom_source = "tq_generic.hip"
 
             def step(i, ev=None):
                 c = caches[i % n_layers]
@@ -430,10 +453,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"append": "bf16 in; fp32 (append), f16x3/i8 MFMA + fp32 (decode)",
-                  "decode": "bf16 in; f16x3/i8 MFMA + fp32 (decode and new-token append)",
-                  "dequant": "fp32 (bf16 or fp32 out)"}[kind],
-        "arithmetic": ("append: bf16 inputs, rotation on the bf16 MFMA with fp32 sums, codes decided in fp32, "
+        "dtype": ("bf16 in; f64 (new-token append), f32 (decode)" if generic else
+                  {"append": "bf16 in; fp32 (append), f16x3/i8 MFMA + fp32 (decode)",
+                   "decode": "bf16 in; f16x3/i8 MFMA + fp32 (decode and new-token append)",
+                   "dequant": "fp32 (bf16 or fp32 out)"}[kind]),
+        "arithmetic": ("generic path: append with the rotation, norms, codes and values in fp64; decode with "
+                       "fp32 dot products (one token per lane), softmax and value sums in fp32"
+                       if generic else
+                       "append: bf16 inputs, rotation on the bf16 MFMA with fp32 sums, codes decided in fp32, "
                        "stored norms from fp64 sums; decode: logits on the f16 MFMA with the query and centroids "
                        "split into f16 terms (about 22 significant bits), value sums on the int8 MFMA with "
                        "fixed-point weights, softmax and accumulation in fp32"),
@@ -482,7 +509,7 @@ def cpu_baseline(w, kind, k_all, v_all, q_np, lay, np):
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     T, Hkv, Hq, d = w.context, w.num_kv_heads, w.num_q_heads, w.head_dim
     cfg = O.Config(d, Hkv, Hq, w.key_bits, w.key_mode, w.val_bits, w.val_mode)
-    signs = synth.sign_vector(w.seed)
+    signs = synth.sign_vector(w.seed, d)
     kcb = O.codebook(w.key_bits, d) if w.key_mode != "fp8" else None   # FP8 keys have no codebook
     S = synth.qjl_matrix(d).astype(np.float64) if w.key_mode == "lloyd_qjl" else None
     f64 = lambda x: synth.bf16_bits_to_f32(x).astype(np.float64)

@@ -565,26 +565,58 @@ void gen_decode_kernel(GenDecodeArgs a) {
       }
     }
     gen_wave_sync();
-    // values of the block's tokens: lane l adds coordinates l*M .. l*M + M - 1
-    for (int u = 0; u < 64; ++u) {
-      if (((vmask >> u) & 1ull) == 0) continue;   // uniform
-      const uint8_t* vr = &s_v[(u >> 4) * 16 * vrow + (u & 15)];
-      const float v0 = s_vs[u], v1 = s_vs[64 + u];
-      float vh[M];
-      if (a.val_mode == 0) {
+    // Values of the block's tokens: lane l adds coordinates l*M .. l*M + M - 1.  Their
+    // codes are bits [l*M*b, (l+1)*M*b) of a value row, which lie in two planes at
+    // most (M*b <= 16, whole bytes when b = 4); a page's two planes are read for its
+    // 16 tokens at once (16 bytes each), and the weights and value scalars four
+    // tokens at a time.  Tokens that are not valid have weight 0 and scalars 0.
+    {
+      const int vb = a.val_bits;
+      const int bit0 = lane * M * vb;
+      const int q0 = bit0 >> 3, sh = bit0 & 7;
+      const int q1 = min(q0 + 1, vrow - 1);
+      const uint32_t cmask = (1u << vb) - 1u;
+#pragma unroll 1
+      for (int pg = 0; pg < 4; ++pg) {
+        const bool ok = pg == 0 ? pvld[0] : pg == 1 ? pvld[1] : pg == 2 ? pvld[2] : pvld[3];
+        if (!ok) continue;   // uniform: no valid token in this page
+        const uint4 P0 = *reinterpret_cast<const uint4*>(&s_v[(pg * vrow + q0) * 16]);
+        const uint4 P1 = *reinterpret_cast<const uint4*>(&s_v[(pg * vrow + q1) * 16]);
 #pragma unroll
-        for (int i = 0; i < M; ++i) vh[i] = fmaf(v1, (float)gen_read_code(vr, 16, a.val_bits, lane * M + i), v0);
-      } else {
-        // Lloyd-Max values are summed in the rotated basis (rotated back after the merge)
+        for (int t4 = 0; t4 < 4; ++t4) {
+          const int u0 = pg * 16 + 4 * t4;
+          const float4 v0q = *reinterpret_cast<const float4*>(&s_vs[u0]);
+          const float4 v1q = *reinterpret_cast<const float4*>(&s_vs[64 + u0]);
+          const uint32_t w0 = t4 == 0 ? P0.x : t4 == 1 ? P0.y : t4 == 2 ? P0.z : P0.w;
+          const uint32_t w1 = t4 == 0 ? P1.x : t4 == 1 ? P1.y : t4 == 2 ? P1.z : P1.w;
+          float vh[4][M];
 #pragma unroll
-        for (int i = 0; i < M; ++i) vh[i] = v0 * s_vc[gen_read_code(vr, 16, a.val_bits, lane * M + i)];
-      }
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t word = ((w0 >> (8 * e)) & 0xFFu) | (((w1 >> (8 * e)) & 0xFFu) << 8);
+            const float v0 = e == 0 ? v0q.x : e == 1 ? v0q.y : e == 2 ? v0q.z : v0q.w;
+            const float v1 = e == 0 ? v1q.x : e == 1 ? v1q.y : e == 2 ? v1q.z : v1q.w;
 #pragma unroll
-      for (int h = 0; h < GM; ++h) {
-        if (h < G) {
-          const float wt = s_w[h * 64 + u];
+            for (int i = 0; i < M; ++i) {
+              const uint32_t c = (word >> (sh + i * vb)) & cmask;
+              // Lloyd-Max values are summed in the rotated basis (rotated back after the merge)
+              vh[e][i] = a.val_mode == 0 ? fmaf(v1, (float)c, v0) : v0 * s_vc[c];
+            }
+          }
 #pragma unroll
-          for (int i = 0; i < M; ++i) o[h][i] = fmaf(wt, vh[i], o[h][i]);
+          for (int h = 0; h < GM; ++h) {
+            if (h < G) {
+              const float4 wq = *reinterpret_cast<const float4*>(&s_w[h * 64 + u0]);
+#pragma unroll
+              for (int i = 0; i < M; ++i) {
+                float acc = o[h][i];
+                acc = fmaf(wq.x, vh[0][i], acc);
+                acc = fmaf(wq.y, vh[1][i], acc);
+                acc = fmaf(wq.z, vh[2][i], acc);
+                acc = fmaf(wq.w, vh[3][i], acc);
+                o[h][i] = acc;
+              }
+            }
+          }
         }
       }
     }

@@ -9,10 +9,12 @@ import bench
 from kv_cache_vector_randomized_amd import synth
 
 
-@pytest.mark.parametrize("mode", ["gqa_decode", "qjl", "polar3", "prefill_append", "dequant_layer"])
+@pytest.mark.parametrize("mode", ["gqa_decode", "qjl", "polar3", "prefill_append", "dequant_layer", "gqa_d256",
+                                  "gqa_group8"])
 def test_cpu_baseline_reports_the_contract_fields(mode):
     wname, kind = bench.MODES[mode]
-    w = synth.shrink(synth.WORKLOADS[wname], batch=2, context=48)
+    base = bench.generic_workloads(synth).get(wname) or synth.WORKLOADS[wname]
+    w = synth.shrink(base, batch=2, context=48)
     lay = synth.paged_layout(w.batch, [w.context] * w.batch, w.seed)
     k = synth.kv_tensor(w, w.batch * w.context, "k")
     v = synth.kv_tensor(w, w.batch * w.context, "v")
