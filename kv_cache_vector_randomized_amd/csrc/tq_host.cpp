@@ -272,11 +272,18 @@ tq::FieldOffsets offsets_of(const tq_layout& L) {
 // add prologues and merges, fewer leave SIMDs idle.  A split holds 4 to 64 tiles.
 // Generic decode: splits of whole 64-token blocks, about `target` work-groups in
 // all, at most 64 splits per (sequence, KV head).
-void plan_gen_splits(int target, int batch, int hkv, int max_seq, int* splits, int* chunk) {
+// Splits of the generic decode: whole 64-token blocks per split, one 4-wave
+// work-group each.  Each wave should get about two blocks (four at head_dim 64,
+// whose blocks are cheap next to a work-group's prologue: the query rotation and
+// the tables), with at most 4 * target work-groups in the grid and 64 splits.
+void plan_gen_splits(int target, int batch, int hkv, int max_seq, int head_dim, int* splits, int* chunk) {
+  constexpr int kWaves = 4;
   const int blocks = std::max(1, (max_seq + 63) / 64);
   const int64_t pairs = std::max<int64_t>(1, (int64_t)batch * hkv);
-  int want = (int)std::min<int64_t>(blocks, std::max<int64_t>(1, (target + pairs - 1) / pairs));
-  want = std::min(want, 64);
+  const int per_wave = head_dim == 64 ? 4 : 2;
+  const int64_t by_grid = std::max<int64_t>(1, (4 * (int64_t)target + pairs - 1) / pairs);
+  const int64_t by_work = std::max(1, (blocks + per_wave * kWaves - 1) / (per_wave * kWaves));
+  int want = (int)std::min<int64_t>(std::min<int64_t>(blocks, by_grid), std::min<int64_t>(by_work, 64));
   const int per = (blocks + want - 1) / want;
   *chunk = per * 64;
   *splits = (blocks + per - 1) / per;
@@ -612,7 +619,8 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t max_s
   if (!ctx || batch <= 0 || max_seq_len < 0) return 0;
   if (ctx->generic) {
     int splits, chunk;
-    plan_gen_splits(ctx->decode_wgs, batch, (int)ctx->cfg.num_kv_heads, max_seq_len, &splits, &chunk);
+    plan_gen_splits(ctx->decode_wgs, batch, (int)ctx->cfg.num_kv_heads, max_seq_len, (int)ctx->cfg.head_dim,
+                    &splits, &chunk);
     return tq::kCounterBytes + (size_t)batch * ctx->cfg.num_q_heads * splits * (2 + ctx->cfg.head_dim) * sizeof(float);
   }
   int splits, tps;
@@ -686,7 +694,7 @@ tq_status decode_common(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cac
     ga.scale = softmax_scale; ga.qjl_coef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / d);
     ga.logits = logits_out; ga.out = out;
     ga.ws = (float*)((uint8_t*)workspace + tq::kCounterBytes);
-    plan_gen_splits(ctx->decode_wgs, batch, hkv, max_seq_len, &ga.splits, &ga.chunk);
+    plan_gen_splits(ctx->decode_wgs, batch, hkv, max_seq_len, d, &ga.splits, &ga.chunk);
     ga.f = offsets_of(ctx->layout); ga.rows = gen_rows(ctx->layout); ga.c = ctx->gconsts; ga.St = ctx->gSt;
     hipError_t ge = tq::launch_gen_decode(ga, d, stream);
     return ge == hipSuccess ? TQ_OK : hip_fail(ge, "decode launch");
