@@ -25,24 +25,47 @@ constexpr int kGenWaves = 4;   // waves per work-group
 constexpr float kGenLog2e = 1.4426950408889634f;
 constexpr float kGenLn2 = 0.6931471805599453f;
 
+// Lane l's copy of the value of lane l ^ m.  m = 1 and 2 are quad permutations,
+// m = 4 the half-row mirror (l ^ 7) followed by the quad reversal (^ 3), m = 8
+// the row mirror (l ^ 15) followed by the half-row mirror (^ 7): DPP moves within
+// a row of 16 lanes.  m = 16 and 32 go through the LDS crossbar.  (m is a constant
+// once the callers' loops are unrolled, and the other branches fold away.)
+template <int CTRL>
+__device__ __forceinline__ uint32_t gdpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t gxor(uint32_t v, int m) {
+  if (m == 1) return gdpp<0xB1>(v);                    // quad_perm [1,0,3,2]
+  if (m == 2) return gdpp<0x4E>(v);                    // quad_perm [2,3,0,1]
+  if (m == 4) return gdpp<0x1B>(gdpp<0x141>(v));       // row_half_mirror, quad_perm [3,2,1,0]
+  if (m == 8) return gdpp<0x141>(gdpp<0x140>(v));      // row_mirror, row_half_mirror
+  return (uint32_t)__shfl_xor((int)v, m);
+}
+__device__ __forceinline__ float gxor(float v, int m) { return __uint_as_float(gxor(__float_as_uint(v), m)); }
+__device__ __forceinline__ double gxor(double v, int m) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = gxor((uint32_t)b, m), hi = gxor((uint32_t)(b >> 32), m);
+  return __builtin_bit_cast(double, lo | (hi << 32));
+}
+
 __device__ __forceinline__ float gw_sum(float v) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  for (int m = 32; m >= 1; m >>= 1) v += gxor(v, m);
   return v;
 }
 __device__ __forceinline__ double gw_sum64(double v) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  for (int m = 32; m >= 1; m >>= 1) v += gxor(v, m);
   return v;
 }
 __device__ __forceinline__ float gw_max(float v) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, gxor(v, m));
   return v;
 }
 __device__ __forceinline__ float gw_min(float v) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fminf(v, __shfl_xor(v, m));
+  for (int m = 32; m >= 1; m >>= 1) v = fminf(v, gxor(v, m));
   return v;
 }
 
@@ -73,7 +96,7 @@ __device__ __forceinline__ void gen_fwht(T (&x)[M], int lane) {
     const bool upper = (lane & m) != 0;
 #pragma unroll
     for (int i = 0; i < M; ++i) {
-      const T p = __shfl_xor(x[i], m);
+      const T p = gxor(x[i], m);
       x[i] = upper ? p - x[i] : x[i] + p;
     }
   }
@@ -123,6 +146,27 @@ __device__ __forceinline__ void gen_load(const void* base, int64_t row, bool bf1
   }
 }
 
+// The raw words of lane's M coordinates of a row (bf16 bits or fp32 bits), loads
+// only, so that several rows can be requested before any of them is waited for.
+template <int M>
+__device__ __forceinline__ void gen_fetch(const void* base, int64_t row, bool bf16, int lane, uint32_t (&w)[M]) {
+  constexpr int D = 64 * M;
+  if (bf16) {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + row * D + lane * M;
+#pragma unroll
+    for (int i = 0; i < M; ++i) w[i] = p[i];
+  } else {
+    const uint32_t* p = static_cast<const uint32_t*>(base) + row * D + lane * M;
+#pragma unroll
+    for (int i = 0; i < M; ++i) w[i] = p[i];
+  }
+}
+template <int M>
+__device__ __forceinline__ void gen_cvt(const uint32_t (&w)[M], bool bf16, float (&x)[M]) {
+#pragma unroll
+  for (int i = 0; i < M; ++i) x[i] = __uint_as_float(bf16 ? w[i] << 16 : w[i]);
+}
+
 // code = #{j : t_j <= y} over the 2^bits - 1 ascending thresholds t (binary search:
 // each step keeps the count of thresholds known to be <= y).
 __device__ __forceinline__ int gen_code(const float* t, int bits, double y) {
@@ -168,7 +212,7 @@ __device__ __forceinline__ void gen_wave_sync() {
 // the signs of S r (fp64 sums of fp32 S).  Values: uniform (min, scale =
 // fl32((max - min) / (2^b - 1)), code = rint((v - min) / scale) with the quotient
 // in fp64) or Lloyd-Max as the keys with a plain norm.
-template <int D>
+template <int D, bool BF16>
 __global__ __launch_bounds__(64 * kGenWaves) void gen_append_kernel(GenAppendArgs a) {
   constexpr int M = D / 64;
   constexpr double isd = inv_sqrt_dim<D>();
@@ -190,6 +234,11 @@ __global__ __launch_bounds__(64 * kGenWaves) void gen_append_kernel(GenAppendArg
   for (int64_t vi = (int64_t)blockIdx.x * kGenWaves + wave; vi < nvec; vi += (int64_t)gridDim.x * kGenWaves) {
     const int64_t t = vi / a.hkv;
     const int h = (int)(vi - t * a.hkv);
+    // the vector's key and value rows are requested with its slot, before any of
+    // them is used: one round trip per vector instead of three
+    uint32_t kw[M], vw[M];
+    gen_fetch<M>(a.k, vi, BF16, lane, kw);
+    gen_fetch<M>(a.v, vi, BF16, lane, vw);
     int64_t slot = -1;
     if (a.slots) {
       slot = a.slots[t];
@@ -206,9 +255,11 @@ __global__ __launch_bounds__(64 * kGenWaves) void gen_append_kernel(GenAppendArg
     uint8_t* page = a.cache + ((slot >> 4) * a.hkv + h) * (int64_t)a.f.page_bytes;
     const int so = (int)(slot & 15);
 
+    float kf[M], vf[M];
+    gen_cvt<M>(kw, BF16, kf);
+    gen_cvt<M>(vw, BF16, vf);
+
     // ---- keys
-    float kf[M];
-    gen_load<M>(a.k, vi, a.bf16 != 0, lane, kf);
     if (a.key_mode == 3) {
       // FP8 keys: the E4M3 byte of every coordinate, coordinate i at byte i; no norm
       uint8_t* krow = page + a.f.kcodes + so * a.rows.kcodes + lane * M;
@@ -280,8 +331,6 @@ __global__ __launch_bounds__(64 * kGenWaves) void gen_append_kernel(GenAppendArg
     gen_wave_sync();   // every read of s_codes is done before the values overwrite it
 
     // ---- values
-    float vf[M];
-    gen_load<M>(a.v, vi, a.bf16 != 0, lane, vf);
     if (a.val_mode == 0) {
       float mn = vf[0], mx = vf[0];
 #pragma unroll
@@ -777,9 +826,18 @@ hipError_t launch_gen_append(const GenAppendArgs& a, int d, int grid, hipStream_
   if (waves <= 0) return hipSuccess;
   const dim3 g((unsigned)std::min<int64_t>((waves + kGenWaves - 1) / kGenWaves, std::max(1, grid)));
   switch (d) {
-    case 64: hipLaunchKernelGGL(gen_append_kernel<64>, g, dim3(64 * kGenWaves), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(gen_append_kernel<128>, g, dim3(64 * kGenWaves), 0, s, a); break;
-    case 256: hipLaunchKernelGGL(gen_append_kernel<256>, g, dim3(64 * kGenWaves), 0, s, a); break;
+    case 64:
+      if (a.bf16) hipLaunchKernelGGL((gen_append_kernel<64, true>), g, dim3(64 * kGenWaves), 0, s, a);
+      else hipLaunchKernelGGL((gen_append_kernel<64, false>), g, dim3(64 * kGenWaves), 0, s, a);
+      break;
+    case 128:
+      if (a.bf16) hipLaunchKernelGGL((gen_append_kernel<128, true>), g, dim3(64 * kGenWaves), 0, s, a);
+      else hipLaunchKernelGGL((gen_append_kernel<128, false>), g, dim3(64 * kGenWaves), 0, s, a);
+      break;
+    case 256:
+      if (a.bf16) hipLaunchKernelGGL((gen_append_kernel<256, true>), g, dim3(64 * kGenWaves), 0, s, a);
+      else hipLaunchKernelGGL((gen_append_kernel<256, false>), g, dim3(64 * kGenWaves), 0, s, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
