@@ -239,7 +239,9 @@ tq_status tq_decode_attention(tq_ctx* ctx, const void* q, tq_dtype dt, const voi
  *   Arguments as for tq_decode_attention, without the workspace.
  *   Returns TQ_ERR_WORKSPACE_TOO_SMALL, before any launch, when
  *   tq_decode_workspace_bytes(ctx, batch, max_seq_len) exceeds
- *   TQ_STATIC_SCRATCH_BYTES; TQ_ERR_HIP when the scratch's device address could
+ *   TQ_STATIC_SCRATCH_BYTES (on the generic path, when one split's partials do
+ *   not fit: it plans fewer splits to fit the scratch, which changes only the
+ *   fp32 summation order); TQ_ERR_HIP when the scratch's device address could
  *   not be obtained on this GPU. */
 #define TQ_STATIC_SCRATCH_BYTES (65536u + 8388608u)
 tq_status tq_decode_attention_noalloc(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cache, int64_t num_blocks,

@@ -276,14 +276,16 @@ tq::FieldOffsets offsets_of(const tq_layout& L) {
 // work-group each.  Each wave should get about two blocks (four at head_dim 64,
 // whose blocks are cheap next to a work-group's prologue: the query rotation and
 // the tables), with at most 4 * target work-groups in the grid and 64 splits.
-void plan_gen_splits(int target, int batch, int hkv, int max_seq, int head_dim, int* splits, int* chunk) {
+void plan_gen_splits(int target, int batch, int hkv, int max_seq, int head_dim, int* splits, int* chunk,
+                     int max_splits = 64) {
   constexpr int kWaves = 4;
   const int blocks = std::max(1, (max_seq + 63) / 64);
   const int64_t pairs = std::max<int64_t>(1, (int64_t)batch * hkv);
   const int per_wave = head_dim == 64 ? 4 : 2;
   const int64_t by_grid = std::max<int64_t>(1, (4 * (int64_t)target + pairs - 1) / pairs);
   const int64_t by_work = std::max(1, (blocks + per_wave * kWaves - 1) / (per_wave * kWaves));
-  int want = (int)std::min<int64_t>(std::min<int64_t>(blocks, by_grid), std::min<int64_t>(by_work, 64));
+  int want = (int)std::min<int64_t>(std::min<int64_t>(blocks, by_grid),
+                                    std::min<int64_t>(by_work, std::max(1, std::min(max_splits, 64))));
   const int per = (blocks + want - 1) / want;
   *chunk = per * 64;
   *splits = (blocks + per - 1) / per;
@@ -655,7 +657,20 @@ tq_status decode_common(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cac
     if (ctx->cfg.val_mode == TQ_VAL_LLOYD && !ctx->generic)
       return fail(TQ_ERR_UNSUPPORTED, "the fused append takes uniform values only");
   }
-  const size_t need = tq_decode_workspace_bytes(ctx, batch, max_seq_len);
+  // The generic decode in the static scratch plans no more splits than its
+  // partials can hold there (a different split count changes only the fp32
+  // summation order).
+  int gen_max_splits = 64;
+  size_t need = tq_decode_workspace_bytes(ctx, batch, max_seq_len);
+  if (ctx->generic && static_scratch) {
+    const size_t per_split = (size_t)batch * ctx->cfg.num_q_heads * (2 + ctx->cfg.head_dim) * sizeof(float);
+    const size_t fit = (tq::kStaticScratchBytes - tq::kCounterBytes) / per_split;
+    gen_max_splits = (int)std::min<size_t>(fit, 64);
+    int splits, chunk;
+    plan_gen_splits(ctx->decode_wgs, batch, (int)ctx->cfg.num_kv_heads, max_seq_len, (int)ctx->cfg.head_dim,
+                    &splits, &chunk, std::max(1, gen_max_splits));
+    need = tq::kCounterBytes + (size_t)splits * per_split;
+  }
   if (static_scratch && need > tq::kStaticScratchBytes)
     return fail(TQ_ERR_WORKSPACE_TOO_SMALL, "batch %d x %u kv heads up to %d tokens needs %zu bytes of scratch; "
                 "the static scratch holds %zu", batch, ctx->cfg.num_kv_heads, max_seq_len, need,
@@ -694,7 +709,7 @@ tq_status decode_common(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cac
     ga.scale = softmax_scale; ga.qjl_coef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / d);
     ga.logits = logits_out; ga.out = out;
     ga.ws = (float*)((uint8_t*)workspace + tq::kCounterBytes);
-    plan_gen_splits(ctx->decode_wgs, batch, hkv, max_seq_len, d, &ga.splits, &ga.chunk);
+    plan_gen_splits(ctx->decode_wgs, batch, hkv, max_seq_len, d, &ga.splits, &ga.chunk, std::max(1, gen_max_splits));
     ga.f = offsets_of(ctx->layout); ga.rows = gen_rows(ctx->layout); ga.c = ctx->gconsts; ga.St = ctx->gSt;
     hipError_t ge = tq::launch_gen_decode(ga, d, stream);
     return ge == hipSuccess ? TQ_OK : hip_fail(ge, "decode launch");

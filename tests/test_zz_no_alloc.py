@@ -4,7 +4,8 @@ called through the C ABI, against tq_decode_attention on the same inputs: two
 calls in a row, the second with a smaller batch and shorter contexts, each to
 the 1e-4 relative bar per (sequence, q head) vector for outputs and logits (the
 two launches may sum in different orders), the first also against the oracle.
-A request larger than the static scratch is refused before any launch."""
+A request larger than the static scratch is refused before any launch; on the
+generic path the entry point plans fewer splits instead, to fit its scratch."""
 import math
 
 import numpy as np
@@ -85,3 +86,35 @@ def test_noalloc_refuses_more_than_its_scratch_before_launch():
         ctx.decode_attention_noalloc(small, tq.TQ_BF16, cache, 16, small, 1, small, batch, max_seq, 0.1, out)
     assert e.value.status == tq.TQ_ERR_WORKSPACE_TOO_SMALL
     torch.cuda.synchronize()
+
+
+def test_generic_noalloc_plans_fewer_splits_to_fit_its_scratch():
+    """head_dim 256, 128 sequences x 1088 tokens x 8 KV heads of 4 query heads: the
+    workspace plan (2 splits of 4.2 MB of partials each) exceeds the static scratch,
+    so the entry point that allocates nothing plans one split; its outputs and
+    logits match the workspace call to the 1e-4 bar (the sums run in another order)."""
+    import dataclasses
+    from kv_cache_vector_randomized_amd.torch_api import PagedKVCache
+    w = dataclasses.replace(synth.WORKLOADS["gqa_decode"], head_dim=256, batch=128, context=1088)
+    B, T = w.batch, w.context
+    print("[noalloc] generic head_dim 256, 128 x 1088 tokens", flush=True)
+    ctx = H.make_context(w)
+    assert ctx.workspace_bytes(B, T) > tq.STATIC_SCRATCH_BYTES
+    lay = synth.paged_layout(B, [T] * B, 71)
+    gen = torch.Generator(device="cuda").manual_seed(71)
+    k = torch.randn((B * T, w.num_kv_heads, w.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn((B * T, w.num_kv_heads, w.head_dim), generator=gen, device="cuda").to(torch.bfloat16)
+    slots = torch.from_numpy(np.concatenate([lay.slots(b, 0, T) for b in range(B)])).cuda()
+    cache = PagedKVCache(ctx, lay.num_blocks)
+    cache.append(k, v, slots)
+    torch.cuda.synchronize()
+    del k, v
+    q = synth.query_tensor(w, B, 71)
+    (o_ws, l_ws), (o_na, l_na) = _both(ctx, w, cache.data, lay, q, B, T)
+    worst = 0.0
+    for b in range(B):
+        for h in range(w.num_q_heads):
+            e = max(H.rel_err(o_na[b, h], o_ws[b, h]), H.rel_err(l_na[b, h], l_ws[b, h]))
+            worst = max(worst, e)
+            assert e <= H.REL_TOL, (b, h, e)
+    print(f"  worst difference between the entry points {worst:.2e}")
