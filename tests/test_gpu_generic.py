@@ -37,6 +37,10 @@ CASES = {
     "d128_group16_qjl": (_w("qjl", num_kv_heads=1, num_q_heads=16), [260, 0]),
     "d64_fp8_v4": (_w("k8v4", head_dim=64), [300, 0, 33]),
     "d256_fp8_group8": (_w("k8v4", head_dim=256, num_kv_heads=2, num_q_heads=16), [200, 64]),
+    # groups below four at head_dim 64 / 256: the 4-head register arrays with unused heads
+    "d256_group2_k4nc": (_w("gqa_decode", head_dim=256, num_kv_heads=4, num_q_heads=8), [130, 64, 1]),
+    "d64_group3_k2v2": (_w("gqa_decode", head_dim=64, num_kv_heads=2, num_q_heads=6, key_bits=2, val_bits=2),
+                        [517, 16]),
 }
 
 
