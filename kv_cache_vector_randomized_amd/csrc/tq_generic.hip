@@ -721,18 +721,32 @@ __global__ __launch_bounds__(64) void gen_merge_kernel(GenDecodeArgs a) {
   const int G = a.group, kvh = qh / G, h = qh - kvh * G;
   const int64_t stride = (int64_t)G * (2 + D);
   const float* src = a.ws + (((int64_t)b * a.hkv + kvh) * a.splits * G + h) * (2 + D);
-  float mx = -INFINITY;
-  for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, src[s * stride]);
-  float L = 0.f, O[M];
+  // lane s holds split s's max and sum (at most 64 splits), so they are read in one
+  // round trip; each split's weight then reaches every lane from its own lane
+  const int ns = a.splits;
+  float ms = -INFINITY, ls = 0.f;
+  if (lane < ns) {
+    ms = src[lane * stride];
+    ls = src[lane * stride + 1];
+  }
+  const float mx = gw_max(ms);
+  const float fl = (ms == -INFINITY || mx == -INFINITY) ? 0.f : exp2f(ms - mx);
+  const float L = gw_sum(fl * ls);
+  float O[M];
 #pragma unroll
   for (int i = 0; i < M; ++i) O[i] = 0.f;
-  if (mx != -INFINITY) {
-    for (int s = 0; s < a.splits; ++s) {
-      const float* p = src + s * stride;
-      const float f = p[0] == -INFINITY ? 0.f : exp2f(p[0] - mx);
-      L = fmaf(f, p[1], L);
+  // the splits' rows, eight at a time with their loads in flight together
+  for (int s0 = 0; s0 < ns; s0 += 8) {
+    float pv[8][M];
 #pragma unroll
-      for (int i = 0; i < M; ++i) O[i] = fmaf(f, p[2 + lane * M + i], O[i]);
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int i = 0; i < M; ++i) pv[u][i] = s0 + u < ns ? src[(s0 + u) * stride + 2 + lane * M + i] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float f = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, fl), min(s0 + u, 63)));
+#pragma unroll
+      for (int i = 0; i < M; ++i) O[i] = fmaf(f, pv[u][i], O[i]);
     }
   }
   float r[M];
