@@ -380,14 +380,15 @@ __global__ __launch_bounds__(64 * kGenWaves) void gen_append_kernel(GenAppendArg
 // softmax_scale * log2(e) / sqrt(d), so logit_2 = norm * <q'', C[code]> (+ rho *
 // <coef S q'', 2 sigma - 1> for QJL keys).  A lane takes one token of the block:
 // its code row (KB bits per code, whole words) in registers, 32 centroids at a
-// time, every head's dot product against the query rows in LDS.  The block's value
-// planes (4 pages) and value scalars are staged in LDS, and every lane adds the 64
-// weighted value rows for its M coordinates.  Each wave keeps a running max, sum
+// time, every head's dot product against the query rows in LDS.  Each lane reads
+// the two value planes of each of the block's 4 pages that hold its M coordinates'
+// codes, the value scalars go through LDS, and every lane adds the 64 weighted
+// value rows for its M coordinates.  Each wave keeps a running max, sum
 // and weighted value sum per head; the work-group's four are merged through LDS
 // and stored as the split's partial (max, sum, d sums) per head.
 // Dynamic LDS of the decode work-group, sized for the group and value width at
 // launch: the query rows, their QJL projections, the softmax weights of each
-// wave's block, the wave partials, the staged value planes and value scalars.
+// wave's block, the wave partials and the value scalars.
 struct GenDecodeLds {
   int q, p, w, part, v, vs, bytes;
 };
@@ -399,7 +400,7 @@ __host__ __device__ inline GenDecodeLds gen_decode_lds(int d, int group, bool qj
   L.part = L.w + 4 * kGenWaves * group * 64;
   L.v = L.part + 4 * kGenWaves * (2 + d);
   L.v = (L.v + 15) & ~15;
-  L.vs = L.v + kGenWaves * 4 * 16 * vrow;
+  L.vs = L.v;   // (value planes are read straight into registers)
   L.bytes = L.vs + 4 * kGenWaves * 2 * 64;
   return L;
 }
@@ -423,7 +424,6 @@ void gen_decode_kernel(GenDecodeArgs a) {
   float* s_p = reinterpret_cast<float*>(gsm + L.p);                      // [G][D] (QJL)
   float* s_w = reinterpret_cast<float*>(gsm + L.w) + wave * G * 64;      // this wave's [G][64]
   float* s_part = reinterpret_cast<float*>(gsm + L.part);                // [waves][2 + D]
-  uint8_t* s_v = gsm + L.v + wave * 4 * 16 * vrow;                       // this wave's [4][16 * vrow]
   float* s_vs = reinterpret_cast<float*>(gsm + L.vs) + wave * 2 * 64;    // this wave's [2][64]
   for (int i = tid; i < 256; i += 64 * kGenWaves) s_kc[i] = a.c->kc[i];
   if (tid < 16) s_vc[tid] = a.c->vc[tid];
@@ -587,13 +587,23 @@ void gen_decode_kernel(GenDecodeArgs a) {
       bpg[pg] = __shfl(blk, 16 * pg);
       pvld[pg] = ((vmask >> (16 * pg)) & 0xFFFFull) != 0;
     }
-    for (int e = lane; e < 4 * vrow; e += 64) {
-      const int pg = e / vrow, q = e - pg * vrow;
-      const int bb = pg == 0 ? bpg[0] : pg == 1 ? bpg[1] : pg == 2 ? bpg[2] : bpg[3];
-      const bool ok = pg == 0 ? pvld[0] : pg == 1 ? pvld[1] : pg == 2 ? pvld[2] : pvld[3];
-      if (ok) {
-        const uint4* src = reinterpret_cast<const uint4*>(a.cache + ((int64_t)bb * a.hkv + kvh) * pstride + a.f.vcodes);
-        *reinterpret_cast<uint4*>(&s_v[(pg * vrow + q) * 16]) = src[q];
+    // Lane l's value codes (coordinates l*M .. l*M + M - 1) are bits [l*M*b,
+    // (l+1)*M*b) of a value row, which lie in two planes at most (M*b <= 16, whole
+    // bytes when b = 4): each page's two planes hold them for its 16 tokens, read
+    // from the cache here (16 bytes each), before the softmax needs the wave.
+    const int vb = a.val_bits;
+    const int vbit0 = lane * M * vb;
+    const int q0 = vbit0 >> 3, vsh = vbit0 & 7;
+    const int q1 = min(q0 + 1, vrow - 1);
+    uint4 P0[4], P1[4];
+#pragma unroll
+    for (int pg = 0; pg < 4; ++pg) {
+      P0[pg] = P1[pg] = make_uint4(0u, 0u, 0u, 0u);
+      if (pvld[pg]) {   // uniform
+        const uint4* vp = reinterpret_cast<const uint4*>(a.cache + ((int64_t)bpg[pg] * a.hkv + kvh) * pstride +
+                                                         a.f.vcodes);
+        P0[pg] = vp[q0];
+        P1[pg] = vp[q1];
       }
     }
     // online softmax of each head over the block's 64 tokens
@@ -614,30 +624,22 @@ void gen_decode_kernel(GenDecodeArgs a) {
       }
     }
     gen_wave_sync();
-    // Values of the block's tokens: lane l adds coordinates l*M .. l*M + M - 1.  Their
-    // codes are bits [l*M*b, (l+1)*M*b) of a value row, which lie in two planes at
-    // most (M*b <= 16, whole bytes when b = 4); a page's two planes are read for its
-    // 16 tokens at once (16 bytes each), and the weights and value scalars four
-    // tokens at a time.  Tokens that are not valid have weight 0 and scalars 0.
+    // Values of the block's tokens: lane l adds coordinates l*M .. l*M + M - 1 from
+    // the planes read above; the weights and value scalars are read four tokens at
+    // a time.  Tokens that are not valid have weight 0 and scalars 0.
     {
-      const int vb = a.val_bits;
-      const int bit0 = lane * M * vb;
-      const int q0 = bit0 >> 3, sh = bit0 & 7;
-      const int q1 = min(q0 + 1, vrow - 1);
+      const int sh = vsh;
       const uint32_t cmask = (1u << vb) - 1u;
-#pragma unroll 1
+#pragma unroll
       for (int pg = 0; pg < 4; ++pg) {
-        const bool ok = pg == 0 ? pvld[0] : pg == 1 ? pvld[1] : pg == 2 ? pvld[2] : pvld[3];
-        if (!ok) continue;   // uniform: no valid token in this page
-        const uint4 P0 = *reinterpret_cast<const uint4*>(&s_v[(pg * vrow + q0) * 16]);
-        const uint4 P1 = *reinterpret_cast<const uint4*>(&s_v[(pg * vrow + q1) * 16]);
+        if (!pvld[pg]) continue;   // uniform: no valid token in this page
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
           const int u0 = pg * 16 + 4 * t4;
           const float4 v0q = *reinterpret_cast<const float4*>(&s_vs[u0]);
           const float4 v1q = *reinterpret_cast<const float4*>(&s_vs[64 + u0]);
-          const uint32_t w0 = t4 == 0 ? P0.x : t4 == 1 ? P0.y : t4 == 2 ? P0.z : P0.w;
-          const uint32_t w1 = t4 == 0 ? P1.x : t4 == 1 ? P1.y : t4 == 2 ? P1.z : P1.w;
+          const uint32_t w0 = t4 == 0 ? P0[pg].x : t4 == 1 ? P0[pg].y : t4 == 2 ? P0[pg].z : P0[pg].w;
+          const uint32_t w1 = t4 == 0 ? P1[pg].x : t4 == 1 ? P1[pg].y : t4 == 2 ? P1[pg].z : P1[pg].w;
           float vh[4][M];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -669,7 +671,7 @@ void gen_decode_kernel(GenDecodeArgs a) {
         }
       }
     }
-    gen_wave_sync();   // s_w, s_v and s_vs are rewritten by the next block
+    gen_wave_sync();   // s_w and s_vs are rewritten by the next block
   }
 
   // merge the four waves, head by head, into the split's partial
