@@ -389,10 +389,20 @@ __global__ __launch_bounds__(64 * kGenWaves) void gen_append_kernel(GenAppendArg
 // Dynamic LDS of the decode work-group, sized for the group and value width at
 // launch: the query rows, their QJL projections, the softmax weights of each
 // wave's block, the wave partials and the value scalars.
+// With the logits on the matrix cores (`mf`), also the A operands of every K step
+// and the centroid-term table of every code byte.
 struct GenDecodeLds {
-  int q, p, w, part, v, vs, bytes;
+  int q, p, w, part, v, vs, qa, kt2, bytes;
 };
-__host__ __device__ inline GenDecodeLds gen_decode_lds(int d, int group, bool qjl, int vrow) {
+typedef _Float16 genhalf8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ floatx4 gen_mfma_f16(const uint4& a, const uint4& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(genhalf8, a), __builtin_bit_cast(genhalf8, b), c,
+                                                0, 0, 0);
+}
+__device__ __forceinline__ uint32_t gen_pack_f16(_Float16 lo, _Float16 hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+__host__ __device__ inline GenDecodeLds gen_decode_lds(int d, int group, bool qjl, int vrow, bool mf) {
   GenDecodeLds L;
   L.q = 0;
   L.p = L.q + 4 * group * d;
@@ -401,7 +411,9 @@ __host__ __device__ inline GenDecodeLds gen_decode_lds(int d, int group, bool qj
   L.v = L.part + 4 * kGenWaves * (2 + d);
   L.v = (L.v + 15) & ~15;
   L.vs = L.v;   // (value planes are read straight into registers)
-  L.bytes = L.vs + 4 * kGenWaves * 2 * 64;
+  L.qa = L.vs + 4 * kGenWaves * 2 * 64;
+  L.kt2 = L.qa + (mf ? (d / 16) * 64 * 16 : 0);
+  L.bytes = L.kt2 + (mf ? 256 * 8 : 0);
   return L;
 }
 
@@ -419,7 +431,8 @@ void gen_decode_kernel(GenDecodeArgs a) {
   const int G = a.group;
   const int hq = a.hkv * G;
   const int vrow = (int)a.rows.vcodes;
-  const GenDecodeLds L = gen_decode_lds(D, G, a.key_mode == 2, vrow);
+  constexpr bool MF = KB == 4 && GM == 4;
+  const GenDecodeLds L = gen_decode_lds(D, G, a.key_mode == 2, vrow, MF);
   float* s_q = reinterpret_cast<float*>(gsm + L.q);                      // [G][D]
   float* s_p = reinterpret_cast<float*>(gsm + L.p);                      // [G][D] (QJL)
   float* s_w = reinterpret_cast<float*>(gsm + L.w) + wave * G * 64;      // this wave's [G][64]
@@ -470,6 +483,66 @@ void gen_decode_kernel(GenDecodeArgs a) {
     __syncthreads();
   }
 
+  // Logits on the f16 matrix cores (4-bit codes, up to 4 heads).  Rows of the A
+  // operand are (head h, term t) = 4h + t: head h's rotated query row times 2^s1[h]
+  // split into three f16 terms (row 4h + 3 is zero).  In K step ks the K slots
+  // 2i and 2i + 1 of lane (m, kg) (m = lane % 16, kg = lane / 16) hold coordinate
+  // kg*D/4 + 4ks + i, against the two f16 terms (hi, lo) of that coordinate's
+  // centroid times 2^s2 in the B operand, so a lane's four codes of a K step are
+  // two consecutive bytes of its token's code row, turned into B through a table
+  // of the centroid terms of each code byte.  Products carry about 22 significant
+  // bits; the A operands of every K step are built once per work-group in LDS.
+  int s1v[4] = {0, 0, 0, 0};
+  int s2 = 0;
+  if constexpr (MF) {
+    uint2* s_kt2 = reinterpret_cast<uint2*>(gsm + L.kt2);
+    uint4* s_qa = reinterpret_cast<uint4*>(gsm + L.qa);
+    float cm = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) cm = fmaxf(cm, fabsf(s_kc[c]));
+    s2 = cm > 0.f ? 14 - __builtin_amdgcn_frexp_expf(cm) : 0;
+    for (int i = tid; i < 256; i += 64 * kGenWaves) {
+      uint32_t e[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const float y = ldexpf(s_kc[(i >> (4 * hh)) & 15], s2);
+        const _Float16 hi = (_Float16)y;
+        e[hh] = gen_pack_f16(hi, (_Float16)(y - (float)hi));
+      }
+      s_kt2[i] = make_uint2(e[0], e[1]);
+    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      if (h < G) {
+        float mx = 0.f;
+#pragma unroll
+        for (int i = 0; i < M; ++i) mx = fmaxf(mx, fabsf(s_q[h * D + lane * M + i]));
+        mx = gw_max(mx);
+        s1v[h] = mx > 0.f ? 14 - __builtin_amdgcn_frexp_expf(mx) : 0;
+      }
+    }
+    const int m = lane & 15, kg = lane >> 4, hA = m >> 2, tA = m & 3;
+    const int s1a = hA == 0 ? s1v[0] : hA == 1 ? s1v[1] : hA == 2 ? s1v[2] : s1v[3];
+    for (int ks = wave; ks < D / 16; ks += kGenWaves) {
+      uint32_t dw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dw[i] = 0u;
+        if (hA < G && tA < 3) {
+          const float x = ldexpf(s_q[hA * D + kg * (D / 4) + 4 * ks + i], s1a);
+          const _Float16 q0 = (_Float16)x;
+          const float r1 = x - (float)q0;
+          const _Float16 q1 = (_Float16)r1;
+          const _Float16 q2 = (_Float16)(r1 - (float)q1);
+          const _Float16 qt = tA == 0 ? q0 : tA == 1 ? q1 : q2;
+          dw[i] = gen_pack_f16(qt, qt);
+        }
+      }
+      s_qa[ks * 64 + lane] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+    }
+    __syncthreads();
+  }
+
   int seq_len = a.seq_lens[b];
   seq_len = max(0, min(seq_len, min(a.max_seq, 16 * a.max_blocks)));
   if (a.num_blocks <= 0) seq_len = 0;
@@ -495,9 +568,68 @@ void gen_decode_kernel(GenDecodeArgs a) {
     float lg[GM];
 #pragma unroll
     for (int h = 0; h < GM; ++h) lg[h] = -INFINITY;
+    float dm[GM];    // matrix-core dot products of this lane's token, per head
+    if constexpr (MF) {
+      // tile ct = page ct of the block (tokens tb + 16ct .. + 15): lane (n, kg) reads
+      // bytes kg*D/8 .. (kg+1)*D/8 - 1 of token 16ct + n's code row (a page with no
+      // valid token reads block 0's: in range, and its dot products are not used)
+      const uint64_t vm = __ballot(valid);
+      const uint2* s_kt2 = reinterpret_cast<const uint2*>(gsm + L.kt2);
+      const uint4* s_qa = reinterpret_cast<const uint4*>(gsm + L.qa);
+      const int n = lane & 15, kg = lane >> 4;
+      constexpr int QW = D / 32;
+      uint32_t qr[4][QW];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int bc = __builtin_amdgcn_readlane(blk, 16 * ct);
+        const bool tv = ((vm >> (16 * ct)) & 0xFFFFull) != 0;
+        const uint8_t* rp = a.cache + ((int64_t)(tv ? bc : 0) * a.hkv + kvh) * pstride + a.f.kcodes + n * (D / 2) +
+                            kg * (D / 8);
+        if constexpr (QW >= 4) {
+#pragma unroll
+          for (int j = 0; j < QW / 4; ++j) {
+            const uint4 u = reinterpret_cast<const uint4*>(rp)[j];
+            qr[ct][4 * j] = u.x; qr[ct][4 * j + 1] = u.y; qr[ct][4 * j + 2] = u.z; qr[ct][4 * j + 3] = u.w;
+          }
+        } else {
+          const uint2 u = *reinterpret_cast<const uint2*>(rp);
+          qr[ct][0] = u.x; qr[ct][1] = u.y;
+        }
+      }
+      floatx4 acc[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const uint4 A = s_qa[ks * 64 + lane];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const uint32_t two = (qr[ct][ks >> 1] >> (16 * (ks & 1))) & 0xFFFFu;
+          const uint2 e0 = s_kt2[two & 0xFFu], e1 = s_kt2[two >> 8];
+          acc[ct] = gen_mfma_f16(A, make_uint4(e0.x, e0.y, e1.x, e1.y), acc[ct]);
+        }
+      }
+      // lane (n, h) holds head h's dot product for token 16ct + n: through s_w to the
+      // token's lane (the previous block's weights in s_w are no longer read)
+      const int hO = lane >> 4;
+      const int s1o = hO == 0 ? s1v[0] : hO == 1 ? s1v[1] : hO == 2 ? s1v[2] : s1v[3];
+      const float sc2 = ldexpf(1.f, -s2), sc1 = ldexpf(1.f, -s1o);   // two steps: neither underflows alone
+      if (hO < G) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          s_w[hO * 64 + 16 * ct + n] = ((acc[ct][0] + acc[ct][1] + acc[ct][2]) * sc2) * sc1;
+      }
+      gen_wave_sync();
+#pragma unroll
+      for (int h = 0; h < GM; ++h) dm[h] = h < G ? s_w[h * 64 + lane] : 0.f;
+    }
     float vs0 = 0.f, vs1 = 0.f;
     if (valid) {
       const float norm = a.key_mode == 3 ? 1.f : reinterpret_cast<const float*>(page + a.f.knorm)[so];   // FP8: no norm
+      float dot[GM];
+#pragma unroll
+      for (int h = 0; h < GM; ++h) dot[h] = MF ? dm[h] : 0.f;
+      if constexpr (!MF) {
       uint32_t w[NW];
       const uint2* kr = reinterpret_cast<const uint2*>(page + a.f.kcodes + so * (4 * NW));
 #pragma unroll
@@ -506,9 +638,6 @@ void gen_decode_kernel(GenDecodeArgs a) {
         w[2 * j] = u2.x;
         w[2 * j + 1] = u2.y;
       }
-      float dot[GM];
-#pragma unroll
-      for (int h = 0; h < GM; ++h) dot[h] = 0.f;
 #pragma unroll
       for (int c0 = 0; c0 < D; c0 += 32) {
         float cv[32];
@@ -530,6 +659,7 @@ void gen_decode_kernel(GenDecodeArgs a) {
           }
         }
       }
+      }   // !MF
 #pragma unroll
       for (int h = 0; h < GM; ++h) lg[h] = norm * dot[h];
       if (qjl) {
@@ -862,7 +992,8 @@ hipError_t launch_gen_append(const GenAppendArgs& a, int d, int grid, hipStream_
 template <int D, int GM>
 hipError_t gen_decode_dg(const GenDecodeArgs& a, hipStream_t s) {
   const dim3 g((unsigned)a.splits, (unsigned)a.hkv, (unsigned)a.batch);
-  const size_t lds = (size_t)gen_decode_lds(D, a.group, a.key_mode == 2, (int)a.rows.vcodes).bytes;
+  const size_t lds =
+      (size_t)gen_decode_lds(D, a.group, a.key_mode == 2, (int)a.rows.vcodes, a.key_bits == 4 && a.group <= 4).bytes;
   switch (a.key_bits) {
     case 2: hipLaunchKernelGGL((gen_decode_kernel<D, 2, GM>), g, dim3(64 * kGenWaves), lds, s, a); break;
     case 3: hipLaunchKernelGGL((gen_decode_kernel<D, 3, GM>), g, dim3(64 * kGenWaves), lds, s, a); break;

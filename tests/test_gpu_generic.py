@@ -41,6 +41,7 @@ CASES = {
     "d256_group2_k4nc": (_w("gqa_decode", head_dim=256, num_kv_heads=4, num_q_heads=8), [130, 64, 1]),
     "d64_group3_k2v2": (_w("gqa_decode", head_dim=64, num_kv_heads=2, num_q_heads=6, key_bits=2, val_bits=2),
                         [517, 16]),
+    "d128_group3_k4nc": (_w("gqa_decode", num_kv_heads=2, num_q_heads=6), [260, 77]),
 }
 
 
