@@ -412,7 +412,7 @@ __host__ __device__ inline GenDecodeLds gen_decode_lds(int d, int group, bool qj
   L.v = (L.v + 15) & ~15;
   L.vs = L.v;   // (value planes are read straight into registers)
   L.qa = L.vs + 4 * kGenWaves * 2 * 64;
-  L.kt2 = L.qa + (mf ? (d / 16) * 64 * 16 : 0);
+  L.kt2 = L.qa + (mf ? ((group + 3) / 4) * (d / 16) * 64 * 16 : 0);
   L.bytes = L.kt2 + (mf ? 256 * 8 : 0);
   return L;
 }
@@ -431,7 +431,9 @@ void gen_decode_kernel(GenDecodeArgs a) {
   const int G = a.group;
   const int hq = a.hkv * G;
   const int vrow = (int)a.rows.vcodes;
-  constexpr bool MF = KB == 4 && GM == 4;
+  constexpr bool MF = KB == 4;
+  constexpr int NRB = GM / 4;          // row blocks of 4 heads in the register arrays
+  const int nrb = (G + 3) / 4;         // row blocks in use
   const GenDecodeLds L = gen_decode_lds(D, G, a.key_mode == 2, vrow, MF);
   float* s_q = reinterpret_cast<float*>(gsm + L.q);                      // [G][D]
   float* s_p = reinterpret_cast<float*>(gsm + L.p);                      // [G][D] (QJL)
@@ -483,16 +485,16 @@ void gen_decode_kernel(GenDecodeArgs a) {
     __syncthreads();
   }
 
-  // Logits on the f16 matrix cores (4-bit codes, up to 4 heads).  Rows of the A
-  // operand are (head h, term t) = 4h + t: head h's rotated query row times 2^s1[h]
-  // split into three f16 terms (row 4h + 3 is zero).  In K step ks the K slots
+  // Logits on the f16 matrix cores (4-bit codes).  Rows of the A operand of row
+  // block rb are (head 4rb + h, term t) = 4h + t: the head's rotated query row
+  // times 2^s1 split into three f16 terms (row 4h + 3 is zero).  In K step ks the K slots
   // 2i and 2i + 1 of lane (m, kg) (m = lane % 16, kg = lane / 16) hold coordinate
   // kg*D/4 + 4ks + i, against the two f16 terms (hi, lo) of that coordinate's
   // centroid times 2^s2 in the B operand, so a lane's four codes of a K step are
   // two consecutive bytes of its token's code row, turned into B through a table
   // of the centroid terms of each code byte.  Products carry about 22 significant
   // bits; the A operands of every K step are built once per work-group in LDS.
-  int s1v[4] = {0, 0, 0, 0};
+  __shared__ int s_s1[MF ? kGenMaxGroup : 1];   // 2^s1[h]: head h's query scale
   int s2 = 0;
   if constexpr (MF) {
     uint2* s_kt2 = reinterpret_cast<uint2*>(gsm + L.kt2);
@@ -511,19 +513,19 @@ void gen_decode_kernel(GenDecodeArgs a) {
       }
       s_kt2[i] = make_uint2(e[0], e[1]);
     }
+    for (int h = wave; h < G; h += kGenWaves) {
+      float mx = 0.f;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      if (h < G) {
-        float mx = 0.f;
-#pragma unroll
-        for (int i = 0; i < M; ++i) mx = fmaxf(mx, fabsf(s_q[h * D + lane * M + i]));
-        mx = gw_max(mx);
-        s1v[h] = mx > 0.f ? 14 - __builtin_amdgcn_frexp_expf(mx) : 0;
-      }
+      for (int i = 0; i < M; ++i) mx = fmaxf(mx, fabsf(s_q[h * D + lane * M + i]));
+      mx = gw_max(mx);
+      if (lane == 0) s_s1[h] = mx > 0.f ? 14 - __builtin_amdgcn_frexp_expf(mx) : 0;
     }
-    const int m = lane & 15, kg = lane >> 4, hA = m >> 2, tA = m & 3;
-    const int s1a = hA == 0 ? s1v[0] : hA == 1 ? s1v[1] : hA == 2 ? s1v[2] : s1v[3];
-    for (int ks = wave; ks < D / 16; ks += kGenWaves) {
+    __syncthreads();
+    const int m = lane & 15, kg = lane >> 4, tA = m & 3;
+    for (int idx = wave; idx < nrb * (D / 16); idx += kGenWaves) {
+      const int rb = idx / (D / 16), ks = idx - rb * (D / 16);
+      const int hA = 4 * rb + (m >> 2);
+      const int s1a = hA < G ? s_s1[hA] : 0;
       uint32_t dw[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -538,7 +540,7 @@ void gen_decode_kernel(GenDecodeArgs a) {
           dw[i] = gen_pack_f16(qt, qt);
         }
       }
-      s_qa[ks * 64 + lane] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
+      s_qa[idx * 64 + lane] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
     }
     __syncthreads();
   }
@@ -596,28 +598,40 @@ void gen_decode_kernel(GenDecodeArgs a) {
           qr[ct][0] = u.x; qr[ct][1] = u.y;
         }
       }
-      floatx4 acc[4];
+      floatx4 acc[NRB][4];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[rb][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const uint4 A = s_qa[ks * 64 + lane];
+        uint4 A[NRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+          if (NRB == 1 || rb < nrb) A[rb] = s_qa[(rb * (D / 16) + ks) * 64 + lane];   // uniform
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           const uint32_t two = (qr[ct][ks >> 1] >> (16 * (ks & 1))) & 0xFFFFu;
           const uint2 e0 = s_kt2[two & 0xFFu], e1 = s_kt2[two >> 8];
-          acc[ct] = gen_mfma_f16(A, make_uint4(e0.x, e0.y, e1.x, e1.y), acc[ct]);
+          const uint4 B = make_uint4(e0.x, e0.y, e1.x, e1.y);
+#pragma unroll
+          for (int rb = 0; rb < NRB; ++rb)
+            if (NRB == 1 || rb < nrb) acc[rb][ct] = gen_mfma_f16(A[rb], B, acc[rb][ct]);   // uniform
         }
       }
-      // lane (n, h) holds head h's dot product for token 16ct + n: through s_w to the
-      // token's lane (the previous block's weights in s_w are no longer read)
-      const int hO = lane >> 4;
-      const int s1o = hO == 0 ? s1v[0] : hO == 1 ? s1v[1] : hO == 2 ? s1v[2] : s1v[3];
-      const float sc2 = ldexpf(1.f, -s2), sc1 = ldexpf(1.f, -s1o);   // two steps: neither underflows alone
-      if (hO < G) {
+      // lane (n, h) of row block rb holds head 4rb + h's dot product for token
+      // 16ct + n: through s_w to the token's lane (the previous block's weights in
+      // s_w are no longer read)
+      const float sc2 = ldexpf(1.f, -s2);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-          s_w[hO * 64 + 16 * ct + n] = ((acc[ct][0] + acc[ct][1] + acc[ct][2]) * sc2) * sc1;
+      for (int rb = 0; rb < NRB; ++rb) {
+        const int hO = 4 * rb + (lane >> 4);
+        if ((NRB == 1 || rb < nrb) && hO < G) {
+          const float sc1 = ldexpf(1.f, -s_s1[hO]);   // two steps: neither underflows alone
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            s_w[hO * 64 + 16 * ct + n] = ((acc[rb][ct][0] + acc[rb][ct][1] + acc[rb][ct][2]) * sc2) * sc1;
+        }
       }
       gen_wave_sync();
 #pragma unroll
@@ -993,7 +1007,7 @@ template <int D, int GM>
 hipError_t gen_decode_dg(const GenDecodeArgs& a, hipStream_t s) {
   const dim3 g((unsigned)a.splits, (unsigned)a.hkv, (unsigned)a.batch);
   const size_t lds =
-      (size_t)gen_decode_lds(D, a.group, a.key_mode == 2, (int)a.rows.vcodes, a.key_bits == 4 && a.group <= 4).bytes;
+      (size_t)gen_decode_lds(D, a.group, a.key_mode == 2, (int)a.rows.vcodes, a.key_bits == 4).bytes;
   switch (a.key_bits) {
     case 2: hipLaunchKernelGGL((gen_decode_kernel<D, 2, GM>), g, dim3(64 * kGenWaves), lds, s, a); break;
     case 3: hipLaunchKernelGGL((gen_decode_kernel<D, 3, GM>), g, dim3(64 * kGenWaves), lds, s, a); break;

@@ -42,6 +42,9 @@ CASES = {
     "d64_group3_k2v2": (_w("gqa_decode", head_dim=64, num_kv_heads=2, num_q_heads=6, key_bits=2, val_bits=2),
                         [517, 16]),
     "d128_group3_k4nc": (_w("gqa_decode", num_kv_heads=2, num_q_heads=6), [260, 77]),
+    # 4-bit codes with groups of 16 and of 5: four and two row blocks of the logits MFMA
+    "d64_group16_k4nc": (_w("gqa_decode", head_dim=64, num_kv_heads=1, num_q_heads=16), [190, 64]),
+    "d256_group5_k4nc": (_w("gqa_decode", head_dim=256, num_kv_heads=1, num_q_heads=5), [150, 3]),
 }
 
 
