@@ -431,7 +431,7 @@ void gen_decode_kernel(GenDecodeArgs a) {
   const int G = a.group;
   const int hq = a.hkv * G;
   const int vrow = (int)a.rows.vcodes;
-  constexpr bool MF = KB == 4;
+  constexpr bool MF = KB == 4;         // 4-bit codes: logits on the f16 matrix cores
   constexpr int NRB = GM / 4;          // row blocks of 4 heads in the register arrays
   const int nrb = (G + 3) / 4;         // row blocks in use
   const GenDecodeLds L = gen_decode_lds(D, G, a.key_mode == 2, vrow, MF);
