@@ -413,7 +413,7 @@ __host__ __device__ inline GenDecodeLds gen_decode_lds(int d, int group, bool qj
   L.vs = L.v;   // (value planes are read straight into registers)
   L.qa = L.vs + 4 * kGenWaves * 2 * 64;
   L.kt2 = L.qa + (mf ? ((group + 3) / 4) * (d / 16) * 64 * 16 : 0);
-  L.bytes = L.kt2 + (mf ? 256 * 8 : 0);
+  L.bytes = L.kt2 + (mf ? 256 * 16 : 0);
   return L;
 }
 
@@ -431,7 +431,7 @@ void gen_decode_kernel(GenDecodeArgs a) {
   const int G = a.group;
   const int hq = a.hkv * G;
   const int vrow = (int)a.rows.vcodes;
-  constexpr bool MF = KB == 4;         // 4-bit codes: logits on the f16 matrix cores
+  constexpr bool MF = KB == 4 || KB == 2;   // 4- and 2-bit codes: logits on the f16 matrix cores
   constexpr int NRB = GM / 4;          // row blocks of 4 heads in the register arrays
   const int nrb = (G + 3) / 4;         // row blocks in use
   const GenDecodeLds L = gen_decode_lds(D, G, a.key_mode == 2, vrow, MF);
@@ -485,33 +485,37 @@ void gen_decode_kernel(GenDecodeArgs a) {
     __syncthreads();
   }
 
-  // Logits on the f16 matrix cores (4-bit codes).  Rows of the A operand of row
+  // Logits on the f16 matrix cores (4- and 2-bit codes).  Rows of the A operand of row
   // block rb are (head 4rb + h, term t) = 4h + t: the head's rotated query row
   // times 2^s1 split into three f16 terms (row 4h + 3 is zero).  In K step ks the K slots
   // 2i and 2i + 1 of lane (m, kg) (m = lane % 16, kg = lane / 16) hold coordinate
   // kg*D/4 + 4ks + i, against the two f16 terms (hi, lo) of that coordinate's
   // centroid times 2^s2 in the B operand, so a lane's four codes of a K step are
-  // two consecutive bytes of its token's code row, turned into B through a table
-  // of the centroid terms of each code byte.  Products carry about 22 significant
+  // two consecutive bytes (4-bit codes) or one byte (2-bit codes) of its token's
+  // code row, turned into B through a table of the centroid terms of each code
+  // byte.  Products carry about 22 significant
   // bits; the A operands of every K step are built once per work-group in LDS.
   __shared__ int s_s1[MF ? kGenMaxGroup : 1];   // 2^s1[h]: head h's query scale
   int s2 = 0;
   if constexpr (MF) {
-    uint2* s_kt2 = reinterpret_cast<uint2*>(gsm + L.kt2);
     uint4* s_qa = reinterpret_cast<uint4*>(gsm + L.qa);
     float cm = 0.f;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) cm = fmaxf(cm, fabsf(s_kc[c]));
+    for (int c = 0; c < (1 << KB); ++c) cm = fmaxf(cm, fabsf(s_kc[c]));
     s2 = cm > 0.f ? 14 - __builtin_amdgcn_frexp_expf(cm) : 0;
+    // per code byte, the (hi, lo) f16 terms of its codes' centroids in stream order:
+    // two codes (8 bytes) for 4-bit codes, four (16 bytes) for 2-bit codes
+    constexpr int PER = 8 / KB;
     for (int i = tid; i < 256; i += 64 * kGenWaves) {
-      uint32_t e[2];
+      uint32_t e[4];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const float y = ldexpf(s_kc[(i >> (4 * hh)) & 15], s2);
+      for (int hh = 0; hh < PER; ++hh) {
+        const float y = ldexpf(s_kc[(i >> (KB * hh)) & ((1 << KB) - 1)], s2);
         const _Float16 hi = (_Float16)y;
         e[hh] = gen_pack_f16(hi, (_Float16)(y - (float)hi));
       }
-      s_kt2[i] = make_uint2(e[0], e[1]);
+      if constexpr (KB == 4) reinterpret_cast<uint2*>(gsm + L.kt2)[i] = make_uint2(e[0], e[1]);
+      else reinterpret_cast<uint4*>(gsm + L.kt2)[i] = make_uint4(e[0], e[1], e[2], e[3]);
     }
     for (int h = wave; h < G; h += kGenWaves) {
       float mx = 0.f;
@@ -576,26 +580,29 @@ void gen_decode_kernel(GenDecodeArgs a) {
       // bytes kg*D/8 .. (kg+1)*D/8 - 1 of token 16ct + n's code row (a page with no
       // valid token reads block 0's: in range, and its dot products are not used)
       const uint64_t vm = __ballot(valid);
-      const uint2* s_kt2 = reinterpret_cast<const uint2*>(gsm + L.kt2);
+      const uint2* s_kt2 = reinterpret_cast<const uint2*>(gsm + L.kt2);   // 4-bit codes
+      const uint4* s_kt4 = reinterpret_cast<const uint4*>(gsm + L.kt2);   // 2-bit codes
       const uint4* s_qa = reinterpret_cast<const uint4*>(gsm + L.qa);
       const int n = lane & 15, kg = lane >> 4;
-      constexpr int QW = D / 32;
+      constexpr int QW = D * KB / 128;   // dwords of a quarter row
       uint32_t qr[4][QW];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const int bc = __builtin_amdgcn_readlane(blk, 16 * ct);
         const bool tv = ((vm >> (16 * ct)) & 0xFFFFull) != 0;
-        const uint8_t* rp = a.cache + ((int64_t)(tv ? bc : 0) * a.hkv + kvh) * pstride + a.f.kcodes + n * (D / 2) +
-                            kg * (D / 8);
+        const uint8_t* rp = a.cache + ((int64_t)(tv ? bc : 0) * a.hkv + kvh) * pstride + a.f.kcodes +
+                            n * (D * KB / 8) + kg * (4 * QW);
         if constexpr (QW >= 4) {
 #pragma unroll
           for (int j = 0; j < QW / 4; ++j) {
             const uint4 u = reinterpret_cast<const uint4*>(rp)[j];
             qr[ct][4 * j] = u.x; qr[ct][4 * j + 1] = u.y; qr[ct][4 * j + 2] = u.z; qr[ct][4 * j + 3] = u.w;
           }
-        } else {
+        } else if constexpr (QW == 2) {
           const uint2 u = *reinterpret_cast<const uint2*>(rp);
           qr[ct][0] = u.x; qr[ct][1] = u.y;
+        } else {
+          qr[ct][0] = *reinterpret_cast<const uint32_t*>(rp);
         }
       }
       floatx4 acc[NRB][4];
@@ -611,9 +618,14 @@ void gen_decode_kernel(GenDecodeArgs a) {
           if (NRB == 1 || rb < nrb) A[rb] = s_qa[(rb * (D / 16) + ks) * 64 + lane];   // uniform
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-          const uint32_t two = (qr[ct][ks >> 1] >> (16 * (ks & 1))) & 0xFFFFu;
-          const uint2 e0 = s_kt2[two & 0xFFu], e1 = s_kt2[two >> 8];
-          const uint4 B = make_uint4(e0.x, e0.y, e1.x, e1.y);
+          uint4 B;
+          if constexpr (KB == 4) {   // the K step's four codes: two bytes
+            const uint32_t two = (qr[ct][ks >> 1] >> (16 * (ks & 1))) & 0xFFFFu;
+            const uint2 e0 = s_kt2[two & 0xFFu], e1 = s_kt2[two >> 8];
+            B = make_uint4(e0.x, e0.y, e1.x, e1.y);
+          } else {                   // one byte
+            B = s_kt4[(qr[ct][ks >> 2] >> (8 * (ks & 3))) & 0xFFu];
+          }
 #pragma unroll
           for (int rb = 0; rb < NRB; ++rb)
             if (NRB == 1 || rb < nrb) acc[rb][ct] = gen_mfma_f16(A[rb], B, acc[rb][ct]);   // uniform
@@ -1007,7 +1019,8 @@ template <int D, int GM>
 hipError_t gen_decode_dg(const GenDecodeArgs& a, hipStream_t s) {
   const dim3 g((unsigned)a.splits, (unsigned)a.hkv, (unsigned)a.batch);
   const size_t lds =
-      (size_t)gen_decode_lds(D, a.group, a.key_mode == 2, (int)a.rows.vcodes, a.key_bits == 4).bytes;
+      (size_t)gen_decode_lds(D, a.group, a.key_mode == 2, (int)a.rows.vcodes, a.key_bits == 4 || a.key_bits == 2)
+          .bytes;
   switch (a.key_bits) {
     case 2: hipLaunchKernelGGL((gen_decode_kernel<D, 2, GM>), g, dim3(64 * kGenWaves), lds, s, a); break;
     case 3: hipLaunchKernelGGL((gen_decode_kernel<D, 3, GM>), g, dim3(64 * kGenWaves), lds, s, a); break;
