@@ -39,10 +39,11 @@ Other workloads (--workload):
                   tq_dequantize_rows call: the whole-cache reconstruction that
                   incremental dequantization replaces by one token per step.
   gqa_d64, gqa_d256, gqa_group8
-                  the GQA shape at head_dim 64 and 256, and at head_dim 128 with 2
-                  KV heads of 8 query heads each: the generic path (same step; its
-                  one-launch step is three launches: the new tokens, the decode
-                  per split, the merge).
+                  the GQA shape at head_dim 64 and 256 (the generic path: same
+                  step, its one-launch step three launches: the new tokens, the
+                  decode per split, the merge), and at head_dim 128 with 2 KV
+                  heads of 8 query heads each (the tuned kernels, the decode in
+                  two sub-groups of 4 query heads per KV head).
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.  `value` is packed-KV
 GB/s: algorithmic bytes of the step (bf16 inputs read, packed rows written,
@@ -93,7 +94,7 @@ MODES = {
 
 
 def generic_workloads(synth):
-    """Shapes that run on the generic path (head_dim 64 / 256, 8 query heads per KV head)."""
+    """The GQA shape at head_dim 64 / 256 (the generic path) and with 8 query heads per KV head."""
     import dataclasses
     g = synth.WORKLOADS["gqa_decode"]
     return {"gqa_d64": dataclasses.replace(g, name="gqa_d64", head_dim=64),
@@ -155,7 +156,7 @@ def main():
     wname, kind = MODES[args.workload]
     w = generic_workloads(synth).get(wname) or synth.WORKLOADS[wname]
     B, T, Hkv, Hq, d = w.batch, w.context, w.num_kv_heads, w.num_q_heads, w.head_dim
-    generic = d != 128 or Hq // Hkv not in (1, 2, 4)
+    generic = d != 128 or (Hq // Hkv not in (1, 2) and (Hq // Hkv) % 4 != 0)
     cfg = tq.make_config(d, Hkv, Hq, w.key_bits, w.key_mode, w.val_bits, w.val_mode)
     S = synth.qjl_matrix(d) if w.key_mode == "lloyd_qjl" else None
     ctx = tq.Context(cfg, synth.sign_vector(w.seed, d), S)

@@ -368,7 +368,8 @@ __device__ __forceinline__ uint32_t interleave16(uint32_t e, uint32_t o) {
 // vhat.  codes / rbuf are LDS scratch of the wave.
 template <int KB, bool QJL, int VB, bool FP8, bool POLAR>
 __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, float v0, float v1, int lane,
-                                   uint8_t* page, int so, uint8_t (&codes)[2][kDim], float* vhat, float* rbuf,
+                                   uint8_t* page, bool st, int so, uint8_t (&codes)[2][kDim], float* vhat,
+                                   float* rbuf,
                                    float& c0, float& c1, float& nhat, float& rho, float& sgn0, float& sgn1) {
   rho = 0.f;
   sgn0 = sgn1 = 1.f;
@@ -381,7 +382,7 @@ __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, floa
     c0 = cv.x;
     c1 = cv.y;
     nhat = 1.f;
-    *reinterpret_cast<uint16_t*>(page + a.f.kcodes + so * kDim + 2 * lane) = (uint16_t)(b0 | (b1 << 8));
+    if (st) *reinterpret_cast<uint16_t*>(page + a.f.kcodes + so * kDim + 2 * lane) = (uint16_t)(b0 | (b1 << 8));
   } else {
   // ||k|| of the stored norm in fp64 from the inputs (squares exact, one rounding to fp32 at the end)
   const double nk64 = sqrt(wave_sum64(fma((double)k0, (double)k0, (double)k1 * (double)k1)));
@@ -464,7 +465,7 @@ __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, floa
     sgn0 = p0 >= 0.f ? 1.f : -1.f;
     sgn1 = p1 >= 0.f ? 1.f : -1.f;
     const uint64_t em = __ballot(p0 >= 0.f), om = __ballot(p1 >= 0.f);
-    if (lane < 4)
+    if (st && lane < 4)
       reinterpret_cast<uint32_t*>(page + a.f.ksigns + 16 * so)[lane] =
           interleave16((uint32_t)(em >> (16 * lane)), (uint32_t)(om >> (16 * lane)));
   }
@@ -488,12 +489,12 @@ __device__ void new_token_quantize(const DecodeArgs& a, float k0, float k1, floa
   wave_sync_lds();
   if constexpr (KB == 8) {
     // 8-bit codes (and FP8 above): one byte per coordinate, the lane's two bytes
-    if (!FP8) *reinterpret_cast<uint16_t*>(page + a.f.kcodes + so * kDim + 2 * lane) = (uint16_t)(kc0 | (kc1 << 8));
-  } else if (lane < 16 * KB) {
+    if (st && !FP8) *reinterpret_cast<uint16_t*>(page + a.f.kcodes + so * kDim + 2 * lane) = (uint16_t)(kc0 | (kc1 << 8));
+  } else if (st && lane < 16 * KB) {
     page[a.f.kcodes + so * 16 * KB + lane] = (uint8_t)stream_byte<KB>(codes[0], lane);
   }
-  if (lane < 16 * VB) page[a.f.vcodes + 16 * lane + so] = (uint8_t)stream_byte<VB>(codes[1], lane);
-  if (lane == 0) {
+  if (st && lane < 16 * VB) page[a.f.vcodes + 16 * lane + so] = (uint8_t)stream_byte<VB>(codes[1], lane);
+  if (st && lane == 0) {
     if (!FP8) reinterpret_cast<float*>(page + a.f.knorm)[so] = nhat;
     reinterpret_cast<float*>(page + a.f.vmin)[so] = mn;
     reinterpret_cast<float*>(page + a.f.vscale)[so] = sc;
@@ -552,7 +553,10 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   constexpr bool POLAR = KM == kKmPolar;   // PolarQuant keys: leaf factors from the angles, radius as norm
   __shared__ float2 ptab[POLAR ? 16 : 1];  // (cos, sin) per code of levels 3..7
   __shared__ float2 pjt[POLAR ? 512 : 1];  // levels 2 and 1 jointly, times 2^14 (see polar_leaves)
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // head group hg = the query heads hg*group .. hg*group + group - 1 of KV head hg / hsub
+  const int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  const int kvh = hg / a.hsub;
+  const int ngrp = a.hkv * a.hsub;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j16 = lane & 15, grp = lane >> 4;   // column (token of a page) and row group (head) of the lane
 
@@ -632,7 +636,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   uint32_t qw0, qw1;
   {
     const bool f32 = a.q_dtype != TQ_BF16;
-    const int64_t qo = ((int64_t)b * a.hq + (int64_t)kvh * G + (wave < G ? wave : 0)) * kDim + 2 * lane;
+    const int64_t qo = ((int64_t)b * a.hq + (int64_t)hg * G + (wave < G ? wave : 0)) * kDim + 2 * lane;
     const uint32_t* qp = f32 ? reinterpret_cast<const uint32_t*>(static_cast<const float*>(a.q) + qo)
                              : reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.q) + qo);
     qw0 = qp[0];
@@ -851,7 +855,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
       const float nt_v1 = f32 ? __uint_as_float(nt_vw1) : bf16hi(nt_vw0);
       float nt_c0, nt_c1, nt_nhat, nt_rho, nt_s0, nt_s1;
       uint8_t* page = const_cast<uint8_t*>(a.cache) + (int64_t)new_blk * blk_stride + kvh * head_stride;
-      new_token_quantize<KB, QJL, VB, FP8, POLAR>(a, nt_k0, nt_k1, nt_v0, nt_v1, lane, page, (seq_len - 1) & 15, nt_codes,
+      new_token_quantize<KB, QJL, VB, FP8, POLAR>(a, nt_k0, nt_k1, nt_v0, nt_v1, lane, page, hg == kvh * a.hsub,
+                                                  (seq_len - 1) & 15, nt_codes,
                                       nt_vhat, nt_r, nt_c0, nt_c1, nt_nhat, nt_rho, nt_s0, nt_s1);
       // the new token's base-2 logit for each head, then the wave's softmax state
       // starts from it (weight 1 at its own max)
@@ -870,7 +875,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
       }
       if (a.logits != nullptr && lane < G) {
         const float mine = lane == 0 ? ell[0] : lane == 1 ? ell[1] : lane == 2 ? ell[2] : ell[3];
-        a.logits[((int64_t)b * a.hq + (int64_t)kvh * G + lane) * a.max_seq + seq_len - 1] = mine * kLn2;
+        a.logits[((int64_t)b * a.hq + (int64_t)hg * G + lane) * a.max_seq + seq_len - 1] = mine * kLn2;
       }
     }
   }
@@ -975,7 +980,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
       vb[pg] = valid[pg] ? cur.vb[pg] : 0.f;
     }
     if (a.logits != nullptr && grp < G) {
-      float* lrow = a.logits + ((int64_t)b * a.hq + (int64_t)kvh * G + grp) * a.max_seq + tile * 64 + j16;
+      float* lrow = a.logits + ((int64_t)b * a.hq + (int64_t)hg * G + grp) * a.max_seq + tile * 64 + j16;
 #pragma unroll
       for (int pg = 0; pg < 4; ++pg)
         if (valid[pg]) lrow[16 * pg] = lg[pg] * kLn2;
@@ -1131,7 +1136,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     // are written and read with agent-scope (device-coherent) accesses, so no
     // cache-wide write-back or invalidate is needed around the arrival counter.
     if (h < G) {
-      float* dst = a.ws + ((((int64_t)b * a.hkv + kvh) * a.splits + split) * 4 + h) * (2 + kDim);
+      float* dst = a.ws + ((((int64_t)b * ngrp + hg) * a.splits + split) * 4 + h) * (2 + kDim);
       // (records of 2 + 128 floats: every pair below is 8-byte aligned)
       if (lane == 0) store_agent2(dst, M, L);
       store_agent2(dst + 2 + 2 * lane, o0, o1);
@@ -1151,7 +1156,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     __shared__ int last;
     if (tid == 0) {
       // wraps back to 0 after `splits` arrivals, so the counter is left zero
-      const unsigned prev = __builtin_amdgcn_atomic_inc32(a.counters + (int64_t)b * a.hkv + kvh,
+      const unsigned prev = __builtin_amdgcn_atomic_inc32(a.counters + (int64_t)b * ngrp + hg,
                                                          (unsigned)(a.splits - 1), __ATOMIC_RELAXED, "agent");
       last = prev == (unsigned)(a.splits - 1);
     }
@@ -1165,7 +1170,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     L = o0 = o1 = 0.f;
     if (mh < G) {
       const int64_t stride = 4 * (2 + kDim);
-      const float* src = a.ws + (((int64_t)b * a.hkv + kvh) * a.splits * 4 + mh) * (2 + kDim);
+      const float* src = a.ws + (((int64_t)b * ngrp + hg) * a.splits * 4 + mh) * (2 + kDim);
       for (int sp0 = par; sp0 < a.splits; sp0 += 32) {
         float ms[16], ls[16], p0[16], p1[16];
 #pragma unroll
@@ -1245,7 +1250,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     r1 = buf[2 * lane + 1] * a.c->signs[2 * lane + 1] * kInvSqrtDim;
   }
   if (h < G) {
-    float2* o = reinterpret_cast<float2*>(a.out + ((int64_t)b * a.hq + (int64_t)kvh * G + h) * kDim);
+    float2* o = reinterpret_cast<float2*>(a.out + ((int64_t)b * a.hq + (int64_t)hg * G + h) * kDim);
     o[lane] = make_float2(r0, r1);
   }
 }
@@ -1254,7 +1259,7 @@ namespace {
 
 template <int KB, int KM, int VB>
 hipError_t decode_v(const DecodeArgs& a, int val_mode, hipStream_t s) {
-  const dim3 grid((unsigned)a.splits, (unsigned)a.hkv, (unsigned)a.batch);
+  const dim3 grid((unsigned)a.splits, (unsigned)(a.hkv * a.hsub), (unsigned)a.batch);
   if (val_mode == TQ_VAL_LLOYD) {
     if constexpr (KB == 8 || KM == kKmPolar) return hipErrorInvalidValue;   // these pair with uniform values
     else hipLaunchKernelGGL((decode_kernel<KB, KM, VB, true>), grid, dim3(64 * kDecodeWaves), 0, s, a);

@@ -24,7 +24,7 @@ struct tq_ctx {
   int page_wgs;            // page-append grid: resident work-groups on the whole device
   int page_per_cu;         // resident page-append work-groups per compute unit
   int decode_wgs;          // decode grid target: resident work-groups on the whole device
-  // Generic path (head_dim 64 / 256, or a group size other than 1, 2, 4): its own
+  // Generic path (head_dim 64 / 256, or a group size other than 1, 2, 4k): its own
   // constants, S^T for QJL keys, and the device's compute-unit count.
   int generic;
   tq::GenConsts* gconsts;  // device
@@ -220,9 +220,18 @@ bool build_unit_lut(int bits, const float* c, const float* t, tq::QLut* lut) {
 
 // The tuned kernels take head_dim 128 with 1, 2 or 4 query heads per KV head;
 // every other supported configuration runs on the generic path.
+// The tuned kernels take head_dim 128 with 1, 2 or 4 query heads per KV head, and
+// multiples of 4 (up to the group limit) as sub-groups of 4 query heads.
 bool is_generic(const tq_config* c) {
   const uint32_t g = c->num_q_heads / c->num_kv_heads;
-  return c->head_dim != (uint32_t)tq::kDim || (g != 1 && g != 2 && g != 4);
+  return c->head_dim != (uint32_t)tq::kDim || (g != 1 && g != 2 && g % 4 != 0);
+}
+
+// Query heads per decode work-group and work-groups per KV head of the tuned decode.
+void tuned_groups(const tq_config& c, int* group, int* hsub) {
+  const int g = (int)(c.num_q_heads / c.num_kv_heads);
+  *group = g > 4 ? 4 : g;
+  *hsub = g > 4 ? g / 4 : 1;
 }
 
 tq_status layout_of(const tq_config* c, tq_layout* L) {
@@ -430,7 +439,7 @@ tq_status tq_validate_config(const tq_config* c) {
   if (g > (uint32_t)tq::kGenMaxGroup)
     return fail(TQ_ERR_UNSUPPORTED, "group size %u: supported 1..%d", g, tq::kGenMaxGroup);
   if (is_generic(c) && c->key_mode == TQ_KEY_POLAR)
-    return fail(TQ_ERR_UNSUPPORTED, "PolarQuant keys are built for head_dim 128 with 1, 2 or 4 query heads per KV head");
+    return fail(TQ_ERR_UNSUPPORTED, "PolarQuant keys are built for head_dim 128 with 1, 2 or a multiple of 4 query heads per KV head");
   if (c->key_mode == TQ_KEY_FP8) {
     if (c->key_bits != 8) return fail(TQ_ERR_INVALID_ARG, "FP8 keys take key_bits 8 (got %u)", c->key_bits);
     if (c->val_mode != TQ_VAL_UNIFORM) return fail(TQ_ERR_UNSUPPORTED, "FP8 keys are built with uniform values only");
@@ -625,10 +634,11 @@ size_t tq_decode_workspace_bytes(const tq_ctx* ctx, int32_t batch, int32_t max_s
                     &splits, &chunk);
     return tq::kCounterBytes + (size_t)batch * ctx->cfg.num_q_heads * splits * (2 + ctx->cfg.head_dim) * sizeof(float);
   }
-  int splits, tps;
-  plan_splits(ctx->decode_wgs, batch, (int)ctx->cfg.num_kv_heads, max_seq_len, &splits, &tps);
+  int splits, tps, group, hsub;
+  tuned_groups(ctx->cfg, &group, &hsub);
+  plan_splits(ctx->decode_wgs, batch, (int)ctx->cfg.num_kv_heads * hsub, max_seq_len, &splits, &tps);
   return tq::kCounterBytes +
-         (size_t)batch * ctx->cfg.num_kv_heads * splits * tq::kMaxGroup * (2 + tq::kDim) * sizeof(float);
+         (size_t)batch * ctx->cfg.num_kv_heads * hsub * splits * tq::kMaxGroup * (2 + tq::kDim) * sizeof(float);
 }
 
 namespace {
@@ -645,8 +655,11 @@ tq_status decode_common(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cac
   if (!std::isfinite(softmax_scale)) return fail(TQ_ERR_INVALID_ARG, "softmax_scale is not finite");
   if (batch == 0) return TQ_OK;
   if (batch > 65535) return fail(TQ_ERR_UNSUPPORTED, "batch > 65535");
-  if ((size_t)batch * ctx->cfg.num_kv_heads * sizeof(uint32_t) > tq::kCounterBytes)
-    return fail(TQ_ERR_UNSUPPORTED, "batch * num_kv_heads > %zu", tq::kCounterBytes / sizeof(uint32_t));
+  int group = 0, hsub = 1;   // tuned decode: query heads per work-group, work-groups per KV head
+  if (!ctx->generic) tuned_groups(ctx->cfg, &group, &hsub);
+  if ((size_t)batch * ctx->cfg.num_kv_heads * hsub * sizeof(uint32_t) > tq::kCounterBytes)
+    return fail(TQ_ERR_UNSUPPORTED, "batch * num_kv_heads * (query heads per KV head / 4) > %zu",
+                tq::kCounterBytes / sizeof(uint32_t));
   if (!q || !cache || !block_tables || !seq_lens || !out || (!workspace && !static_scratch))
     return fail(TQ_ERR_INVALID_ARG, "null device pointer");
   if (!aligned(cache, 16) || (!static_scratch && !aligned(workspace, 16)) || !aligned(q, 4) || !aligned(out, 4))
@@ -718,12 +731,12 @@ tq_status decode_common(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cac
   a.q = q; a.q_dtype = (int32_t)dt; a.cache = (const uint8_t*)cache; a.num_blocks = num_blocks;
   a.block_tables = block_tables; a.max_blocks = max_blocks_per_seq; a.seq_lens = seq_lens;
   a.batch = batch; a.max_seq = max_seq_len; a.hkv = (int32_t)ctx->cfg.num_kv_heads; a.hq = (int32_t)ctx->cfg.num_q_heads;
-  a.group = a.hq / a.hkv; a.scale = softmax_scale;
+  a.group = group; a.hsub = hsub; a.scale = softmax_scale;
   a.qjl_coef = (float)(std::sqrt(std::acos(-1.0) / 2.0) / ctx->cfg.head_dim);
   a.logits = logits_out; a.out = out;
   a.counters = (uint32_t*)workspace;
   a.ws = (float*)((uint8_t*)workspace + tq::kCounterBytes);
-  plan_splits(ctx->decode_wgs, batch, a.hkv, max_seq_len, &a.splits, &a.tiles_total);
+  plan_splits(ctx->decode_wgs, batch, a.hkv * hsub, max_seq_len, &a.splits, &a.tiles_total);
   if ((int64_t)(a.splits + 1) * a.tiles_total >= ((int64_t)1 << 31))
     return fail(TQ_ERR_UNSUPPORTED, "max_seq_len too large");
   a.f = offsets_of(ctx->layout); a.c = ctx->consts;
@@ -732,7 +745,7 @@ tq_status decode_common(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cac
   a.klut_scale = ctx->klut_scale; a.klut_bias = ctx->klut_bias;
   if (static_scratch) {
     // the shared scratch keeps the last call's contents: zero the counters this call uses
-    hipError_t ce = tq::launch_clear_words(a.counters, batch * a.hkv, stream);
+    hipError_t ce = tq::launch_clear_words(a.counters, batch * a.hkv * hsub, stream);
     if (ce != hipSuccess) return hip_fail(ce, "scratch clear launch");
   }
   hipError_t e = tq::launch_decode(a, (int)ctx->cfg.key_bits, (int)ctx->cfg.key_mode, (int)ctx->cfg.val_bits,

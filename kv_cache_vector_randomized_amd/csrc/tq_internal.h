@@ -97,13 +97,16 @@ struct DecodeArgs {
   const int32_t* block_tables;
   int32_t max_blocks;
   const int32_t* seq_lens;
-  int32_t batch, max_seq, hkv, hq, group;
+  // group: query heads of one work-group (1, 2 or 4); hsub: work-groups per KV
+  // head, each taking `group` consecutive query heads (groups of 8, 12, 16 query
+  // heads per KV head run as 2, 3, 4 sub-groups of 4 over the same pages)
+  int32_t batch, max_seq, hkv, hq, group, hsub;
   float scale;                // softmax scale
   float qjl_coef;             // sqrt(pi/2) / m
   float* logits;              // may be null
   float* out;                 // [batch][hq][128]
-  float* ws;                  // partials [batch][hkv][splits][4][2 + 128]
-  uint32_t* counters;         // [batch][hkv] arrival counters, zero between calls
+  float* ws;                  // partials [batch][hkv * hsub][splits][4][2 + 128]
+  uint32_t* counters;         // [batch][hkv * hsub] arrival counters, zero between calls
   int32_t splits;
   int32_t tiles_total;        // 64-token tiles of the longest sequence, split evenly
   FieldOffsets f;

@@ -1,5 +1,7 @@
-"""GPU parity of the generic path (head_dim 64 and 256; groups other than 1, 2, 4
-at head_dim 128; Lloyd-Max, QJL and FP8 keys) against the fp64 oracle, through the C ABI.
+"""GPU parity of the generic path (head_dim 64 and 256; groups of 3 at head_dim
+128; Lloyd-Max, QJL and FP8 keys) against the fp64 oracle, through the C ABI, and
+of the tuned kernels' sub-group decode (groups of 8 and 16 at head_dim 128: the
+`d128_group8` and `d128_group16_qjl` cases).
 
 Same bars as the tuned path: codes and packed bytes bit-exact outside the 1e-6
 decision band, fp32 scalars within their rounding tolerance, logits and outputs
