@@ -554,7 +554,20 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   __shared__ float2 ptab[POLAR ? 16 : 1];  // (cos, sin) per code of levels 3..7
   __shared__ float2 pjt[POLAR ? 512 : 1];  // levels 2 and 1 jointly, times 2^14 (see polar_leaves)
   // head group hg = the query heads hg*group .. hg*group + group - 1 of KV head hg / hsub
-  const int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
+  if (a.hsub > 1 && a.xcd_pairs) {
+    // The head groups of one (split, KV head, sequence) read the same pages: give
+    // them linear ids 8 apart, which the dispatcher sends to the same XCD (its own
+    // L2) one after the other.  Linear id f = 8q + r: head group q % hsub of unit
+    // 8 (q / hsub) + r, units in the grid's own order (split, KV head, sequence).
+    // The launcher sets xcd_pairs only when 8 * hsub divides the grid size.
+    const uint32_t f = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const uint32_t q = f >> 3, u = (q / (uint32_t)a.hsub) * 8u + (f & 7u);
+    const uint32_t t = u / gridDim.x;
+    split = (int)(u - t * gridDim.x);
+    b = (int)(t / (uint32_t)a.hkv);
+    hg = (int)(t - (uint32_t)b * a.hkv) * a.hsub + (int)(q % (uint32_t)a.hsub);
+  }
   const int kvh = hg / a.hsub;
   const int ngrp = a.hkv * a.hsub;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

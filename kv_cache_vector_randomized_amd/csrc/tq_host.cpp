@@ -737,6 +737,7 @@ tq_status decode_common(tq_ctx* ctx, const void* q, tq_dtype dt, const void* cac
   a.counters = (uint32_t*)workspace;
   a.ws = (float*)((uint8_t*)workspace + tq::kCounterBytes);
   plan_splits(ctx->decode_wgs, batch, a.hkv * hsub, max_seq_len, &a.splits, &a.tiles_total);
+  a.xcd_pairs = hsub > 1 && ((int64_t)a.splits * a.hkv * hsub * batch) % (8 * hsub) == 0;
   if ((int64_t)(a.splits + 1) * a.tiles_total >= ((int64_t)1 << 31))
     return fail(TQ_ERR_UNSUPPORTED, "max_seq_len too large");
   a.f = offsets_of(ctx->layout); a.c = ctx->consts;

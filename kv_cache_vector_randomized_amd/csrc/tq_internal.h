@@ -101,6 +101,7 @@ struct DecodeArgs {
   // head, each taking `group` consecutive query heads (groups of 8, 12, 16 query
   // heads per KV head run as 2, 3, 4 sub-groups of 4 over the same pages)
   int32_t batch, max_seq, hkv, hq, group, hsub;
+  int32_t xcd_pairs;          // 1: head groups of a unit on linear ids 8 apart (hsub > 1)
   float scale;                // softmax scale
   float qjl_coef;             // sqrt(pi/2) / m
   float* logits;              // may be null
