@@ -43,7 +43,7 @@ Other workloads (--workload):
                   step, its one-launch step three launches: the new tokens, the
                   decode per split, the merge), and at head_dim 128 with 2 KV
                   heads of 8 query heads each (the tuned kernels, the decode in
-                  two sub-groups of 4 query heads per KV head).
+                  two head groups of 4 query heads per KV head).
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.  `value` is packed-KV
 GB/s: algorithmic bytes of the step (bf16 inputs read, packed rows written,
@@ -156,7 +156,7 @@ def main():
     wname, kind = MODES[args.workload]
     w = generic_workloads(synth).get(wname) or synth.WORKLOADS[wname]
     B, T, Hkv, Hq, d = w.batch, w.context, w.num_kv_heads, w.num_q_heads, w.head_dim
-    generic = d != 128 or (Hq // Hkv not in (1, 2) and (Hq // Hkv) % 4 != 0)
+    generic = d != 128
     cfg = tq.make_config(d, Hkv, Hq, w.key_bits, w.key_mode, w.val_bits, w.val_mode)
     S = synth.qjl_matrix(d) if w.key_mode == "lloyd_qjl" else None
     ctx = tq.Context(cfg, synth.sign_vector(w.seed, d), S)

@@ -56,17 +56,16 @@
  *   2 stores them plane-major.  A reader of transferred pages checks the version.
  *
  * Head and group sizes
- *   head_dim 128 with 1, 2, 4, 8, 12 or 16 query heads per KV head runs on the
- *   tuned kernels (groups above 4 decode as sub-groups of 4 query heads, one
+ *   head_dim 128 with 1 to 16 query heads per KV head runs on the tuned kernels
+ *   (the decode takes a KV head's query heads in head groups of up to 4, one
  *   work-group each, over the same pages; only the first stores the new token of
- *   a one-launch step).  head_dim 64 or 256, or a group size of 3, 5, 6, 7, 9,
- *   10, 11, 13, 14 or 15 at head_dim 128, runs on the generic path: the same page format, entry points and results (up
+ *   a one-launch step).  head_dim 64 or 256 runs on the generic path: the same page format, entry points and results (up
  *   to the decision band and the fp32 summation order), computed by plain
  *   one-wave-per-vector append and dequantize kernels and a two-launch decode
  *   (per split, then the merge); its one-launch step is three launches (the new
  *   tokens, the decode, the merge).  The generic path takes Lloyd-Max keys (2, 3,
  *   4 or 8 bits; QJL with 2, 3 or 4), FP8 keys and both value modes; PolarQuant
- *   keys need the tuned kernels' head and group sizes (their code
+ *   keys need head_dim 128 (their code
  *   order is laid out for 128 coordinates).
  */
 #ifndef TQ_H

@@ -553,7 +553,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   constexpr bool POLAR = KM == kKmPolar;   // PolarQuant keys: leaf factors from the angles, radius as norm
   __shared__ float2 ptab[POLAR ? 16 : 1];  // (cos, sin) per code of levels 3..7
   __shared__ float2 pjt[POLAR ? 512 : 1];  // levels 2 and 1 jointly, times 2^14 (see polar_leaves)
-  // head group hg = the query heads hg*group .. hg*group + group - 1 of KV head hg / hsub
+  // head group hg = query heads 4*sub .. 4*sub + G - 1 (sub = hg % hsub) of KV head hg / hsub
   int split = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
   if (a.hsub > 1 && a.xcd_pairs) {
     // The head groups of one (split, KV head, sequence) read the same pages: give
@@ -570,6 +570,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   }
   const int kvh = hg / a.hsub;
   const int ngrp = a.hkv * a.hsub;
+  const int sub = hg - kvh * a.hsub;
+  const int64_t qh0 = (int64_t)kvh * a.group + 4 * sub;   // first query head of the work-group
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j16 = lane & 15, grp = lane >> 4;   // column (token of a page) and row group (head) of the lane
 
@@ -604,7 +606,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   __shared__ __align__(16) float nt_vhat[VLM ? 1 : kDim];
   __shared__ __align__(16) float nt_r[QJL ? kDim : 1];
 
-  const int G = a.group;
+  const int G = min(4, a.group - 4 * sub);   // query heads of this work-group (1..4)
   // Split `split` owns tiles [tile_begin, tile_end): an even share of the longest
   // sequence's tiles (at most 64).
   const int tile_begin = (int)((uint32_t)(split * a.tiles_total) / (uint32_t)a.splits);
@@ -649,7 +651,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
   uint32_t qw0, qw1;
   {
     const bool f32 = a.q_dtype != TQ_BF16;
-    const int64_t qo = ((int64_t)b * a.hq + (int64_t)hg * G + (wave < G ? wave : 0)) * kDim + 2 * lane;
+    const int64_t qo = ((int64_t)b * a.hq + qh0 + (wave < G ? wave : 0)) * kDim + 2 * lane;
     const uint32_t* qp = f32 ? reinterpret_cast<const uint32_t*>(static_cast<const float*>(a.q) + qo)
                              : reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.q) + qo);
     qw0 = qp[0];
@@ -868,7 +870,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
       const float nt_v1 = f32 ? __uint_as_float(nt_vw1) : bf16hi(nt_vw0);
       float nt_c0, nt_c1, nt_nhat, nt_rho, nt_s0, nt_s1;
       uint8_t* page = const_cast<uint8_t*>(a.cache) + (int64_t)new_blk * blk_stride + kvh * head_stride;
-      new_token_quantize<KB, QJL, VB, FP8, POLAR>(a, nt_k0, nt_k1, nt_v0, nt_v1, lane, page, hg == kvh * a.hsub,
+      new_token_quantize<KB, QJL, VB, FP8, POLAR>(a, nt_k0, nt_k1, nt_v0, nt_v1, lane, page, sub == 0,
                                                   (seq_len - 1) & 15, nt_codes,
                                       nt_vhat, nt_r, nt_c0, nt_c1, nt_nhat, nt_rho, nt_s0, nt_s1);
       // the new token's base-2 logit for each head, then the wave's softmax state
@@ -888,7 +890,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
       }
       if (a.logits != nullptr && lane < G) {
         const float mine = lane == 0 ? ell[0] : lane == 1 ? ell[1] : lane == 2 ? ell[2] : ell[3];
-        a.logits[((int64_t)b * a.hq + (int64_t)hg * G + lane) * a.max_seq + seq_len - 1] = mine * kLn2;
+        a.logits[((int64_t)b * a.hq + qh0 + lane) * a.max_seq + seq_len - 1] = mine * kLn2;
       }
     }
   }
@@ -993,7 +995,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
       vb[pg] = valid[pg] ? cur.vb[pg] : 0.f;
     }
     if (a.logits != nullptr && grp < G) {
-      float* lrow = a.logits + ((int64_t)b * a.hq + (int64_t)hg * G + grp) * a.max_seq + tile * 64 + j16;
+      float* lrow = a.logits + ((int64_t)b * a.hq + qh0 + grp) * a.max_seq + tile * 64 + j16;
 #pragma unroll
       for (int pg = 0; pg < 4; ++pg)
         if (valid[pg]) lrow[16 * pg] = lg[pg] * kLn2;
@@ -1263,7 +1265,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(DecodeArgs a)
     r1 = buf[2 * lane + 1] * a.c->signs[2 * lane + 1] * kInvSqrtDim;
   }
   if (h < G) {
-    float2* o = reinterpret_cast<float2*>(a.out + ((int64_t)b * a.hq + (int64_t)hg * G + h) * kDim);
+    float2* o = reinterpret_cast<float2*>(a.out + ((int64_t)b * a.hq + qh0 + h) * kDim);
     o[lane] = make_float2(r0, r1);
   }
 }

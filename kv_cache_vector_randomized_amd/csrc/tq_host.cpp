@@ -24,7 +24,7 @@ struct tq_ctx {
   int page_wgs;            // page-append grid: resident work-groups on the whole device
   int page_per_cu;         // resident page-append work-groups per compute unit
   int decode_wgs;          // decode grid target: resident work-groups on the whole device
-  // Generic path (head_dim 64 / 256, or a group size other than 1, 2, 4k): its own
+  // Generic path (head_dim 64 / 256): its own
   // constants, S^T for QJL keys, and the device's compute-unit count.
   int generic;
   tq::GenConsts* gconsts;  // device
@@ -220,18 +220,15 @@ bool build_unit_lut(int bits, const float* c, const float* t, tq::QLut* lut) {
 
 // The tuned kernels take head_dim 128 with 1, 2 or 4 query heads per KV head;
 // every other supported configuration runs on the generic path.
-// The tuned kernels take head_dim 128 with 1, 2 or 4 query heads per KV head, and
-// multiples of 4 (up to the group limit) as sub-groups of 4 query heads.
-bool is_generic(const tq_config* c) {
-  const uint32_t g = c->num_q_heads / c->num_kv_heads;
-  return c->head_dim != (uint32_t)tq::kDim || (g != 1 && g != 2 && g % 4 != 0);
-}
+// The tuned kernels take head_dim 128 with any group size (up to the group limit);
+// the decode takes the query heads of a KV head in head groups of up to 4.
+bool is_generic(const tq_config* c) { return c->head_dim != (uint32_t)tq::kDim; }
 
-// Query heads per decode work-group and work-groups per KV head of the tuned decode.
+// Query heads per KV head and head groups per KV head of the tuned decode.
 void tuned_groups(const tq_config& c, int* group, int* hsub) {
   const int g = (int)(c.num_q_heads / c.num_kv_heads);
-  *group = g > 4 ? 4 : g;
-  *hsub = g > 4 ? g / 4 : 1;
+  *group = g;
+  *hsub = (g + 3) / 4;
 }
 
 tq_status layout_of(const tq_config* c, tq_layout* L) {
@@ -439,7 +436,7 @@ tq_status tq_validate_config(const tq_config* c) {
   if (g > (uint32_t)tq::kGenMaxGroup)
     return fail(TQ_ERR_UNSUPPORTED, "group size %u: supported 1..%d", g, tq::kGenMaxGroup);
   if (is_generic(c) && c->key_mode == TQ_KEY_POLAR)
-    return fail(TQ_ERR_UNSUPPORTED, "PolarQuant keys are built for head_dim 128 with 1, 2 or a multiple of 4 query heads per KV head");
+    return fail(TQ_ERR_UNSUPPORTED, "PolarQuant keys are built for head_dim 128");
   if (c->key_mode == TQ_KEY_FP8) {
     if (c->key_bits != 8) return fail(TQ_ERR_INVALID_ARG, "FP8 keys take key_bits 8 (got %u)", c->key_bits);
     if (c->val_mode != TQ_VAL_UNIFORM) return fail(TQ_ERR_UNSUPPORTED, "FP8 keys are built with uniform values only");

@@ -97,9 +97,9 @@ struct DecodeArgs {
   const int32_t* block_tables;
   int32_t max_blocks;
   const int32_t* seq_lens;
-  // group: query heads of one work-group (1, 2 or 4); hsub: work-groups per KV
-  // head, each taking `group` consecutive query heads (groups of 8, 12, 16 query
-  // heads per KV head run as 2, 3, 4 sub-groups of 4 over the same pages)
+  // group: query heads per KV head (1..16); hsub = ceil(group / 4) work-groups per
+  // KV head, each taking 4 consecutive query heads (the last one the rest), over
+  // the same pages
   int32_t batch, max_seq, hkv, hq, group, hsub;
   int32_t xcd_pairs;          // 1: head groups of a unit on linear ids 8 apart (hsub > 1)
   float scale;                // softmax scale

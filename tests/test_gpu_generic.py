@@ -1,8 +1,8 @@
-"""GPU parity of the generic path (head_dim 64 and 256; groups of 3 at head_dim
-128; Lloyd-Max, QJL and FP8 keys) against the fp64 oracle, through the C ABI, and
-of the tuned kernels' sub-group decode (groups of 8 and 16 at head_dim 128: the
-`d128_group8`, `d128_group12_k3v4` and `d128_group16_qjl` cases: two, three and
-four head groups of 4).
+"""GPU parity of the generic path (head_dim 64 and 256; Lloyd-Max, QJL and FP8
+keys) against the fp64 oracle, through the C ABI, and of the tuned kernels at
+group sizes beyond the named workloads (head_dim 128, the `d128_*` cases: one
+head group of 3; two, three and four head groups of 4; groups of 7 and 6 as 4 + 3
+and 4 + 2, the latter with PolarQuant keys).
 
 Same bars as the tuned path: codes and packed bytes bit-exact outside the 1e-6
 decision band, fp32 scalars within their rounding tolerance, logits and outputs
@@ -39,6 +39,8 @@ CASES = {
     "d64_group3_qjl3": (_w("k3qjl_v2", head_dim=64, num_kv_heads=2, num_q_heads=6), [300, 5]),
     "d128_group16_qjl": (_w("qjl", num_kv_heads=1, num_q_heads=16), [260, 0]),
     "d128_group12_k3v4": (_w("k3v4_nc", num_kv_heads=2, num_q_heads=24), [300, 65, 1]),
+    "d128_group7_qjl3": (_w("k3qjl_v2", num_kv_heads=4, num_q_heads=28), [333, 64]),
+    "d128_group6_polar3": (_w("polar3", num_kv_heads=2, num_q_heads=12), [200, 33]),
     "d64_fp8_v4": (_w("k8v4", head_dim=64), [300, 0, 33]),
     "d256_fp8_group8": (_w("k8v4", head_dim=256, num_kv_heads=2, num_q_heads=16), [200, 64]),
     # groups below four at head_dim 64 / 256: the 4-head register arrays with unused heads
@@ -147,7 +149,8 @@ def test_generic_decode_matches_oracle_on_identical_bytes(name):
     print(f"  worst relative error {worst:.3e}")
 
 
-@pytest.mark.parametrize("name", ["d64_k4nc_v4", "d256_qjl2_v4", "d128_group8", "d128_group12_k3v4"])
+@pytest.mark.parametrize("name", ["d64_k4nc_v4", "d256_qjl2_v4", "d128_group8", "d128_group12_k3v4",
+                                  "d128_group7_qjl3"])
 def test_generic_noalloc_equals_workspace_decode(name):
     w, lens = CASES[name]
     print(f"[generic no-allocation decode] {name}", flush=True)
@@ -163,7 +166,7 @@ def test_generic_noalloc_equals_workspace_decode(name):
 
 
 @pytest.mark.parametrize("name", ["d64_k4nc_v4", "d256_qjl2_v4", "d256_toy_lloyd_values", "d128_group8",
-                                  "d128_group12_k3v4",
+                                  "d128_group12_k3v4", "d128_group7_qjl3", "d128_group3_k4nc",
                                   "d256_fp8_group8"])
 def test_generic_one_launch_step_matches_oracle(name):
     """tq_append_decode: the new token of every sequence is stored (bytes as the

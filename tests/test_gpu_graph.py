@@ -24,8 +24,8 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 GRAPH_TOL = 1e-5
-# configurations beyond the named workloads: the generic path (head_dim 256; 3 query
-# heads per KV head) and the tuned decode in sub-groups (8 query heads per KV head)
+# configurations beyond the named workloads: the generic path (head_dim 256) and the
+# tuned decode's head groups (8 and 3 query heads per KV head)
 GENERIC = {
     "gqa_decode@d256": dataclasses.replace(synth.WORKLOADS["gqa_decode"], head_dim=256),
     "qjl@group8": dataclasses.replace(synth.WORKLOADS["qjl"], num_kv_heads=2, num_q_heads=16),

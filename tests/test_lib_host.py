@@ -52,7 +52,7 @@ def test_status_strings():
     (dict(num_kv_heads=8, num_q_heads=32), tq.TQ_OK),
     (dict(num_kv_heads=8, num_q_heads=12), tq.TQ_ERR_INVALID_ARG),
     (dict(num_kv_heads=2, num_q_heads=16), tq.TQ_OK),                # group 8: tuned, two sub-groups of 4
-    (dict(num_kv_heads=1, num_q_heads=3), tq.TQ_OK),                 # group 3: the generic path
+    (dict(num_kv_heads=1, num_q_heads=3), tq.TQ_OK),                 # group 3: tuned, one head group of 3
     (dict(num_kv_heads=1, num_q_heads=16), tq.TQ_OK),
     (dict(num_kv_heads=1, num_q_heads=17), tq.TQ_ERR_UNSUPPORTED),   # more than 16 q heads per KV head
     (dict(head_dim=96), tq.TQ_ERR_INVALID_ARG),
@@ -64,9 +64,9 @@ def test_status_strings():
     (dict(head_dim=512), tq.TQ_ERR_UNSUPPORTED),
     (dict(head_dim=64, key_bits=8, key_mode="fp8"), tq.TQ_OK),                 # FP8 keys on the generic path
     (dict(num_kv_heads=1, num_q_heads=8, key_bits=8, key_mode="fp8"), tq.TQ_OK),
-    (dict(head_dim=256, key_bits=3, key_mode="polar"), tq.TQ_ERR_UNSUPPORTED),  # polar: d 128, groups 1, 2, 4k
+    (dict(head_dim=256, key_bits=3, key_mode="polar"), tq.TQ_ERR_UNSUPPORTED),  # polar: head_dim 128 only
     (dict(num_kv_heads=1, num_q_heads=8, key_bits=3, key_mode="polar"), tq.TQ_OK),
-    (dict(num_kv_heads=1, num_q_heads=6, key_bits=3, key_mode="polar"), tq.TQ_ERR_UNSUPPORTED),
+    (dict(num_kv_heads=1, num_q_heads=7, key_bits=3, key_mode="polar"), tq.TQ_OK),
     (dict(key_bits=0), tq.TQ_ERR_INVALID_ARG),
     (dict(key_bits=8), tq.TQ_OK),                    # 8-bit Lloyd-Max keys
     (dict(key_bits=5), tq.TQ_ERR_UNSUPPORTED),
