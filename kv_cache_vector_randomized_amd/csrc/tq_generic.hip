@@ -1,6 +1,6 @@
-// Generic path for gfx950: head_dim 64, 128 or 256 and up to 16 query heads per
-// KV head, for the configurations the tuned kernels do not take (head_dim other
-// than 128, or a group size other than 1, 2 and 4).  Same page format and the
+// Generic path for gfx950: head_dim 64 or 256 and up to 16 query heads per KV
+// head, the head sizes the tuned kernels (head_dim 128) do not take.  Same page
+// format and the
 // same results as the tuned path up to the decision band and the fp32 summation
 // order; the aim is a plain structure, not speed:
 //   * append and dequantize: one wave per (token, KV head) vector, lane l holding
@@ -1002,10 +1002,6 @@ hipError_t launch_gen_append(const GenAppendArgs& a, int d, int grid, hipStream_
       if (a.bf16) hipLaunchKernelGGL((gen_append_kernel<64, true>), g, dim3(64 * kGenWaves), 0, s, a);
       else hipLaunchKernelGGL((gen_append_kernel<64, false>), g, dim3(64 * kGenWaves), 0, s, a);
       break;
-    case 128:
-      if (a.bf16) hipLaunchKernelGGL((gen_append_kernel<128, true>), g, dim3(64 * kGenWaves), 0, s, a);
-      else hipLaunchKernelGGL((gen_append_kernel<128, false>), g, dim3(64 * kGenWaves), 0, s, a);
-      break;
     case 256:
       if (a.bf16) hipLaunchKernelGGL((gen_append_kernel<256, true>), g, dim3(64 * kGenWaves), 0, s, a);
       else hipLaunchKernelGGL((gen_append_kernel<256, false>), g, dim3(64 * kGenWaves), 0, s, a);
@@ -1044,7 +1040,6 @@ hipError_t gen_decode_d(const GenDecodeArgs& a, hipStream_t s) {
 hipError_t launch_gen_decode(const GenDecodeArgs& a, int d, hipStream_t s) {
   switch (d) {
     case 64: return gen_decode_d<64>(a, s);
-    case 128: return gen_decode_d<128>(a, s);
     case 256: return gen_decode_d<256>(a, s);
     default: return hipErrorInvalidValue;
   }
@@ -1056,7 +1051,6 @@ hipError_t launch_gen_dequant(const GenDequantArgs& a, int d, int grid, hipStrea
   const dim3 g((unsigned)std::min<int64_t>((waves + kGenWaves - 1) / kGenWaves, std::max(1, grid)));
   switch (d) {
     case 64: hipLaunchKernelGGL(gen_dequant_kernel<64>, g, dim3(64 * kGenWaves), 0, s, a); break;
-    case 128: hipLaunchKernelGGL(gen_dequant_kernel<128>, g, dim3(64 * kGenWaves), 0, s, a); break;
     case 256: hipLaunchKernelGGL(gen_dequant_kernel<256>, g, dim3(64 * kGenWaves), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
