@@ -218,8 +218,6 @@ bool build_unit_lut(int bits, const float* c, const float* t, tq::QLut* lut) {
   return true;
 }
 
-// The tuned kernels take head_dim 128 with 1, 2 or 4 query heads per KV head;
-// every other supported configuration runs on the generic path.
 // The tuned kernels take head_dim 128 with any group size (up to the group limit);
 // the decode takes the query heads of a KV head in head groups of up to 4.
 bool is_generic(const tq_config* c) { return c->head_dim != (uint32_t)tq::kDim; }

@@ -157,9 +157,9 @@ hipError_t launch_polar_dequant(const DequantArgs& a, int key_bits, int val_bits
 hipError_t launch_dequant(const DequantArgs& a, int key_bits, int key_mode, int val_bits, int val_mode, bool bf16_out,
                           hipStream_t s);
 
-// ---- Generic path: head sizes 64, 128 and 256 and up to 16 query heads per KV
-// head, for the configurations the tuned kernels above do not take (head_dim
-// other than 128, or a group size other than 1, 2 and 4).  Same page format,
+// ---- Generic path: head sizes 64 and 256 and up to 16 query heads per KV head,
+// the head sizes the tuned kernels above (head_dim 128) do not take.  Same page
+// format,
 // same results up to the decision band and fp32 summation order (tq_generic.hip).
 constexpr int kGenMaxDim = 256;
 constexpr int kGenMaxGroup = 16;
